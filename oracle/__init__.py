@@ -1,0 +1,16 @@
+"""CPU oracle for replay attention: test infrastructure only.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import this
+package.  It is plain float64 numpy written from the definition of attention and shares
+no code with the HIP library.
+"""
+from .attention import (  # noqa: F401
+    backward,
+    capture_pages,
+    delta,
+    forward,
+    forward_parts,
+    gather_pages,
+    lse_merge,
+    shard_token_bounds,
+)
