@@ -1,0 +1,218 @@
+/*
+ * longstraw.h -- C ABI of the replay-attention library for AMD MI355X (gfx950).
+ *
+ * The operation: exact attention of a short block of response rows over a long prompt
+ * whose keys and values were captured once, without gradients, into pages, plus the
+ * response itself under a causal mask; forward and backward.  This is the attention
+ * slice of LongStraw's capture-once / replay-suffix GRPO step ("LongStraw: Long-Context
+ * RL Beyond 2M Tokens under a Fixed GPU Budget"; paper digest, section "Method", steps 1
+ * and 3; explainer, sections "The move: change the graph boundary" and "Two incompatible
+ * architectures, same transaction").
+ *
+ * Conventions for every entry point:
+ *  - All functions are callable from C, return int (LS_OK == 0 on success, a negative
+ *    LS_ERR_* code otherwise) and never throw.  On failure ls_last_error() returns a
+ *    message for the calling thread.  Every argument check happens before the first
+ *    launch: a call that returns an error has enqueued nothing.
+ *  - Pointers named *device* point to GPU memory of the current device; pointers named
+ *    *host* point to host memory that is read during the call only.  The caller owns
+ *    all memory.  The library allocates no device memory, keeps no pointer after
+ *    returning and does not synchronise with the host: work is enqueued on `stream` (a
+ *    hipStream_t; NULL is the null stream) and buffers must stay alive until it is done.
+ *    Device faults caused by bad pointers surface at the caller's next synchronisation.
+ *  - Dense tensors are contiguous, row-major, with the shapes given below.
+ *  - Element types: LS_DTYPE_F32 (IEEE binary32) or LS_DTYPE_BF16 (bfloat16).  Softmax
+ *    statistics, gradients, partial results and merges are always float32.  bf16
+ *    outputs are rounded to nearest-even from float32.
+ *  - Scores are s = softmax_scale * q.k.  LSE values are natural logarithms of
+ *    sum exp(s).  Query head h reads kv head h / (hq / hkv).
+ *
+ * Supported shapes: hq % hkv == 0; d in {64, 128, 256}; page_size == 64;
+ * 1 <= n_shards <= 64.  The bf16 path runs on matrix cores; the f32 path is exact f32.
+ */
+#ifndef LONGSTRAW_H
+#define LONGSTRAW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LS_VERSION 100 /* 1.0.0 */
+
+#define LS_OK 0
+#define LS_ERR_INVALID (-1)     /* a null pointer, a bad size, a range or a layout      */
+#define LS_ERR_UNSUPPORTED (-2) /* a dtype / head-dim / page-size combination not built */
+#define LS_ERR_WORKSPACE (-3)   /* workspace missing or smaller than the query says     */
+#define LS_ERR_HIP (-4)         /* a HIP launch failed; the message names the kernel    */
+
+#define LS_DTYPE_F32 0
+#define LS_DTYPE_BF16 1
+
+typedef void* ls_stream_t; /* a hipStream_t */
+
+/*
+ * The captured prompt: paged keys and values of one attention layer (digest, "Method",
+ * step 1: the retained conditional state holds KV pages; explainer, "The move": a
+ * read-only resident state).
+ *
+ *   page_table      device int32 [ceil(prefix_len / page_size)]: logical page -> physical
+ *                   page.  Must be injective with entries in [0, n_phys_pages).
+ *   k_pages/v_pages device [n_phys_pages, hkv, page_size, d] of `dtype`: row r of physical
+ *                   page table[i] holds logical prompt token i * page_size + r.  Rows of a
+ *                   last, partial page past prefix_len are never read.
+ *   n_shards, shard_page_bounds
+ *                   host int64 [n_shards + 1], non-decreasing, from 0 to the number of
+ *                   logical pages: shard s owns logical pages [b[s], b[s+1]).  The shards
+ *                   are the context-parallel owners whose local softmax statistics are
+ *                   merged into the exact result (digest, "Method", Qwen implementation;
+ *                   explainer, "Two incompatible architectures").  Empty shards are allowed.
+ *   softmax_scale   usually 1 / sqrt(d).
+ */
+typedef struct ls_prefix {
+    int hq;
+    int hkv;
+    int d;
+    int page_size;
+    int dtype;
+    int n_shards;
+    int64_t prefix_len;
+    int64_t n_phys_pages;
+    const int32_t* page_table;
+    const void* k_pages;
+    const void* v_pages;
+    const int64_t* shard_page_bounds;
+    float softmax_scale;
+} ls_prefix_t;
+
+/* Library version (LS_VERSION of the build). */
+int ls_version(void);
+
+/* Message of the calling thread's last failure ("" if none).  Valid until its next call. */
+const char* ls_last_error(void);
+
+/*
+ * ls_capture_pages -- write captured prompt keys and values into page pools (digest,
+ * "Method", step 1: the prompt is evaluated once without autograd and its KV pages are
+ * kept).  Chunked capture is allowed: tokens [first_tok, first_tok + n_tok) of the prompt
+ * are written, so a prompt can be captured in pieces.
+ *
+ *   k_src, v_src    device [n_tok, hkv, d] of src_dtype, logical token order.
+ *   first_tok       multiple of page_size.
+ *   page_table      device int32 [n_logical_pages]; must cover the written tokens.
+ *   k_pages,v_pages device [n_phys_pages, hkv, page_size, d] of page_dtype.
+ *   page_dtype      equal to src_dtype (a bit copy) or BF16 from an F32 source (rounded to
+ *                   nearest-even).
+ * Rows of a partial last page past the written tokens are left untouched.
+ * Errors: LS_ERR_INVALID (null pointer, negative size, misaligned first_tok, a page index
+ * past n_logical_pages), LS_ERR_UNSUPPORTED (dtype pair, d, page_size).
+ */
+int ls_capture_pages(const void* k_src, const void* v_src, int src_dtype, int64_t n_tok,
+                     int64_t first_tok, const int32_t* page_table, int64_t n_logical_pages,
+                     void* k_pages, void* v_pages, int page_dtype, int64_t n_phys_pages,
+                     int hkv, int d, int page_size, ls_stream_t stream);
+
+/*
+ * ls_gather_pages -- read tokens [first_tok, first_tok + n_tok) of a pool back into logical
+ * order: dst device [n_tok, hkv, d] of `dtype`, a bit copy.  The inverse of capture, for
+ * checking the page-table walk.  Errors as for ls_capture_pages.
+ */
+int ls_gather_pages(const void* pages, int dtype, const int32_t* page_table,
+                    int64_t n_logical_pages, int64_t n_phys_pages, int64_t first_tok,
+                    int64_t n_tok, int hkv, int d, int page_size, void* dst,
+                    ls_stream_t stream);
+
+/*
+ * Workspace bytes that ls_replay_fwd / ls_replay_bwd need for a block of n_rows response
+ * rows (0 on invalid arguments, with ls_last_error set).
+ *
+ * Forward workspace layout (float32, from offset 0; n_parts = n_shards + 1):
+ *   o_parts   [n_parts, n_rows, hq, d]   part p < n_shards: shard p; last: response keys
+ *   lse_parts [n_parts, n_rows, hq]      -inf where a part has no key (O part = 0 there)
+ * so that callers may inspect each owner's local result.
+ * Backward workspace layout (float32, from offset 0):
+ *   delta     [n_rows, hq]              rowsum(dO * O) of the O passed in
+ *   dq_parts  [n_parts, n_rows, hq, d]
+ */
+size_t ls_fwd_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows);
+size_t ls_bwd_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows);
+
+/*
+ * ls_replay_fwd -- forward of one replayed response block (digest, "Method", step 3:
+ * serial response replay; explainer, "Serial replay makes G a schedule": exact attention;
+ * "Two incompatible architectures": local softmax statistics composed into the exact
+ * global output).
+ *
+ * Rows are response positions [q_start, q_start + n_rows).  Row i sees every prompt key
+ * and response keys [0, q_start + i] (the response follows the prompt).  Each shard and
+ * the response keys give one local (O, LSE) written to the workspace, then the parts are
+ * merged in float32 as by ls_lse_merge.
+ *
+ *   q               device [n_rows, hq, d] of pre->dtype.
+ *   k_resp, v_resp  device [n_resp_keys, hkv, d] of pre->dtype; n_resp_keys >=
+ *                   q_start + n_rows.  Keys at or past q_start + n_rows are never read.
+ *   o               device [n_rows, hq, d] of pre->dtype (written).
+ *   lse             device float32 [n_rows, hq] (written).
+ *   workspace       device, ws_bytes >= ls_fwd_workspace_bytes(pre, n_rows).
+ * Errors: LS_ERR_INVALID, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP.
+ */
+int ls_replay_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start,
+                  const void* k_resp, const void* v_resp, int64_t n_resp_keys, void* o,
+                  float* lse, void* workspace, size_t ws_bytes, ls_stream_t stream);
+
+/*
+ * ls_replay_bwd -- backward of one replayed response block for the loss sum(O * dO)
+ * (digest, "Method", step 3: backpropagate and accumulate; explainer, "Two incompatible
+ * architectures": response blocks replayed in reverse, K/V gradient pages allocated when
+ * a response backward touches them).  P is recomputed from the stored LSE.
+ *
+ *   q, k_resp, v_resp, n_resp_keys, q_start, n_rows   as for ls_replay_fwd.
+ *   o               device [n_rows, hq, d] of pre->dtype: the forward's output.
+ *   lse             device float32 [n_rows, hq]: the forward's LSE.
+ *   dout            device [n_rows, hq, d] of pre->dtype: dL/dO.
+ *   dq              device float32 [n_rows, hq, d]: overwritten with dL/dq.
+ *   dk_resp,dv_resp device float32 [n_resp_keys, hkv, d]: gradients of response keys
+ *                   [0, q_start + n_rows) are added in (written instead when
+ *                   resp_first_touch != 0, in which case keys past that range are set
+ *                   to zero).
+ *   dk_pages,dv_pages
+ *                   device float32 [n_phys_pages, hkv, page_size, d], indexed like the
+ *                   pools: prompt-key gradients are added in, or written for shards whose
+ *                   shard_first_touch[s] != 0 (rows past prefix_len in a partial last
+ *                   page are then written as zero).
+ *   shard_first_touch  host uint8 [n_shards], or NULL for "accumulate everywhere".
+ *   workspace       device, ws_bytes >= ls_bwd_workspace_bytes(pre, n_rows).
+ * Each gradient element has one writer per call (no atomics); results are
+ * deterministic.  Errors as for ls_replay_fwd.
+ */
+int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start,
+                  const void* k_resp, const void* v_resp, int64_t n_resp_keys,
+                  const void* o, const float* lse, const void* dout, float* dq,
+                  float* dk_resp, float* dv_resp, int resp_first_touch, float* dk_pages,
+                  float* dv_pages, const uint8_t* shard_first_touch, void* workspace,
+                  size_t ws_bytes, ls_stream_t stream);
+
+/*
+ * ls_lse_merge -- compose local softmax results into the global one in float32 (digest,
+ * "Method", Qwen implementation: global LSE/output merge; the pages keep a BF16 numerator,
+ * explainer "The fine print", here every step is float32):
+ *   L = m + log sum_p exp(L_p - m), m = max_p L_p;  O = sum_p exp(L_p - L) O_p.
+ * A part with L_p = -inf adds nothing; a row where every part is -inf gets L = -inf and
+ * O = 0.  With n_parts == 1 the result equals the input exactly.
+ *
+ *   o_parts   device float32 [n_parts, n_rows, d]
+ *   lse_parts device float32 [n_parts, n_rows]
+ *   o_out     device [n_rows, d] of out_dtype;  lse_out device float32 [n_rows].
+ * Errors: LS_ERR_INVALID, LS_ERR_UNSUPPORTED (d not a multiple of 4 or > 1024, dtype).
+ */
+int ls_lse_merge(int n_parts, int64_t n_rows, int d, const float* o_parts,
+                 const float* lse_parts, void* o_out, int out_dtype, float* lse_out,
+                 ls_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LONGSTRAW_H */

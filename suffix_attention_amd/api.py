@@ -1,0 +1,234 @@
+"""Python binding of the replay-attention C ABI (include/longstraw.h).
+
+Argument marshalling only: shapes and dtypes are checked, device pointers and torch's
+current HIP stream are passed through, and every step runs in the library's kernels.  torch
+supplies device memory (outputs and workspaces are allocated here as torch tensors, so the
+caching allocator owns them) and streams.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+from . import _lib
+from ._lib import LS_DTYPE_BF16, LS_DTYPE_F32, LongStrawError, check, lib
+
+PAGE = 64
+
+_DT = {torch.float32: LS_DTYPE_F32, torch.bfloat16: LS_DTYPE_BF16}
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t not in _DT:
+        raise LongStrawError(_lib.LS_ERR_UNSUPPORTED, f"dtype {t} (only float32 and bfloat16)")
+    return _DT[t]
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def n_logical_pages(n_tok: int) -> int:
+    return (n_tok + PAGE - 1) // PAGE
+
+
+def even_shard_bounds(n_pages: int, n_shards: int) -> list[int]:
+    """Contiguous logical page ranges [floor(s n / S), floor((s+1) n / S))."""
+    return [(s * n_pages) // n_shards for s in range(n_shards + 1)]
+
+
+@dataclass
+class Prefix:
+    """A captured prompt: paged K/V pools, the page table and the shard split."""
+    hq: int
+    hkv: int
+    d: int
+    dtype: torch.dtype
+    prefix_len: int
+    page_table: torch.Tensor          # int32 [n_logical_pages] on device
+    k_pages: torch.Tensor             # [n_phys, hkv, 64, d]
+    v_pages: torch.Tensor
+    shard_bounds: list = field(default_factory=list)
+    softmax_scale: float | None = None
+
+    def __post_init__(self):
+        if self.softmax_scale is None:
+            self.softmax_scale = 1.0 / math.sqrt(self.d)
+        if not self.shard_bounds:
+            self.shard_bounds = even_shard_bounds(n_logical_pages(self.prefix_len), 1)
+        self._bounds = (C.c_int64 * len(self.shard_bounds))(*self.shard_bounds)
+
+    @property
+    def n_shards(self) -> int:
+        return len(self.shard_bounds) - 1
+
+    @property
+    def n_phys(self) -> int:
+        return int(self.k_pages.shape[0])
+
+    def struct(self) -> _lib.ls_prefix_t:
+        s = _lib.ls_prefix_t()
+        s.hq, s.hkv, s.d, s.page_size = self.hq, self.hkv, self.d, PAGE
+        s.dtype = _dtype_code(self.dtype)
+        s.n_shards = self.n_shards
+        s.prefix_len = self.prefix_len
+        s.n_phys_pages = self.n_phys
+        s.page_table = self.page_table.data_ptr() if self.page_table.numel() else None
+        s.k_pages = self.k_pages.data_ptr() if self.k_pages.numel() else None
+        s.v_pages = self.v_pages.data_ptr() if self.v_pages.numel() else None
+        s.shard_page_bounds = C.cast(self._bounds, C.POINTER(C.c_int64))
+        s.softmax_scale = float(self.softmax_scale)
+        return s
+
+
+def version() -> int:
+    return lib().ls_version()
+
+
+def capture_pages(k: torch.Tensor, v: torch.Tensor, page_table: torch.Tensor, n_phys: int,
+                  page_dtype: torch.dtype | None = None, first_tok: int = 0,
+                  k_pages: torch.Tensor | None = None, v_pages: torch.Tensor | None = None):
+    """Write prompt keys/values [n_tok, hkv, d] (tokens first_tok ..) into page pools
+    [n_phys, hkv, 64, d]; allocates the pools (zeroed) when not given."""
+    _dev(k, "k")
+    _dev(v, "v", dtype=k.dtype, shape=k.shape)
+    _dev(page_table, "page_table", dtype=torch.int32)
+    n_tok, hkv, d = k.shape
+    page_dtype = page_dtype or k.dtype
+    if k_pages is None:
+        k_pages = torch.zeros((n_phys, hkv, PAGE, d), dtype=page_dtype, device=k.device)
+        v_pages = torch.zeros_like(k_pages)
+    _dev(k_pages, "k_pages", dtype=page_dtype)
+    _dev(v_pages, "v_pages", dtype=page_dtype, shape=k_pages.shape)
+    check(lib().ls_capture_pages(_ptr(k), _ptr(v), _dtype_code(k.dtype), n_tok, first_tok, _ptr(page_table),
+                                 page_table.numel(), _ptr(k_pages), _ptr(v_pages), _dtype_code(page_dtype),
+                                 k_pages.shape[0], hkv, d, PAGE, _stream()))
+    return k_pages, v_pages
+
+
+def gather_pages(pages: torch.Tensor, page_table: torch.Tensor, n_tok: int, first_tok: int = 0):
+    """Tokens [first_tok, first_tok + n_tok) of a pool, back in logical order."""
+    _dev(pages, "pages")
+    _dev(page_table, "page_table", dtype=torch.int32)
+    n_phys, hkv, _, d = pages.shape
+    out = torch.empty((n_tok, hkv, d), dtype=pages.dtype, device=pages.device)
+    check(lib().ls_gather_pages(_ptr(pages), _dtype_code(pages.dtype), _ptr(page_table), page_table.numel(),
+                                n_phys, first_tok, n_tok, hkv, d, PAGE, _ptr(out), _stream()))
+    return out
+
+
+def fwd_workspace_bytes(prefix: Prefix, n_rows: int) -> int:
+    st = prefix.struct()
+    n = lib().ls_fwd_workspace_bytes(C.byref(st), n_rows)
+    if n == 0 and n_rows > 0:
+        raise LongStrawError(_lib.LS_ERR_INVALID, lib().ls_last_error().decode())
+    return n
+
+
+def bwd_workspace_bytes(prefix: Prefix, n_rows: int) -> int:
+    st = prefix.struct()
+    n = lib().ls_bwd_workspace_bytes(C.byref(st), n_rows)
+    if n == 0 and n_rows > 0:
+        raise LongStrawError(_lib.LS_ERR_INVALID, lib().ls_last_error().decode())
+    return n
+
+
+def _workspace(nbytes: int, device, given: torch.Tensor | None):
+    if given is not None:
+        if given.numel() * given.element_size() < nbytes:
+            raise LongStrawError(_lib.LS_ERR_WORKSPACE, f"workspace of {nbytes} bytes needed")
+        return given
+    return torch.empty((max(1, (nbytes + 15) // 16) * 4,), dtype=torch.float32, device=device)
+
+
+def fwd_parts(prefix: Prefix, n_rows: int, workspace: torch.Tensor):
+    """Views of the forward workspace: (o_parts [n_parts, n_rows, hq, d], lse_parts)."""
+    n_parts = prefix.n_shards + 1
+    n_o = n_parts * n_rows * prefix.hq * prefix.d
+    o = workspace[:n_o].view(n_parts, n_rows, prefix.hq, prefix.d)
+    lse = workspace[n_o:n_o + n_parts * n_rows * prefix.hq].view(n_parts, n_rows, prefix.hq)
+    return o, lse
+
+
+def replay_fwd(prefix: Prefix, q: torch.Tensor, q_start: int, k_resp: torch.Tensor, v_resp: torch.Tensor,
+               workspace: torch.Tensor | None = None, o: torch.Tensor | None = None,
+               lse: torch.Tensor | None = None):
+    """Forward of response rows [q_start, q_start + n_rows): returns (o, lse, workspace)."""
+    _dev(q, "q", dtype=prefix.dtype)
+    n_rows = q.shape[0]
+    _dev(k_resp, "k_resp", dtype=prefix.dtype)
+    _dev(v_resp, "v_resp", dtype=prefix.dtype, shape=k_resp.shape)
+    o = torch.empty_like(q) if o is None else _dev(o, "o", dtype=prefix.dtype, shape=q.shape)
+    if lse is None:
+        lse = torch.empty((n_rows, prefix.hq), dtype=torch.float32, device=q.device)
+    _dev(lse, "lse", dtype=torch.float32, shape=(n_rows, prefix.hq))
+    ws_bytes = fwd_workspace_bytes(prefix, n_rows)
+    ws = _workspace(ws_bytes, q.device, workspace)
+    st = prefix.struct()
+    check(lib().ls_replay_fwd(C.byref(st), _ptr(q), n_rows, q_start, _ptr(k_resp), _ptr(v_resp), k_resp.shape[0],
+                              _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return o, lse, ws
+
+
+def replay_bwd(prefix: Prefix, q, q_start: int, k_resp, v_resp, o, lse, dout, dk_resp, dv_resp,
+               resp_first_touch: bool, dk_pages, dv_pages, shard_first_touch=None,
+               workspace: torch.Tensor | None = None, dq: torch.Tensor | None = None):
+    """Backward of one block: returns dq (float32); accumulates or writes the response and
+    prompt key/value gradients in place."""
+    _dev(q, "q", dtype=prefix.dtype)
+    n_rows = q.shape[0]
+    _dev(o, "o", dtype=prefix.dtype, shape=q.shape)
+    _dev(dout, "dout", dtype=prefix.dtype, shape=q.shape)
+    _dev(lse, "lse", dtype=torch.float32, shape=(n_rows, prefix.hq))
+    _dev(dk_resp, "dk_resp", dtype=torch.float32, shape=k_resp.shape)
+    _dev(dv_resp, "dv_resp", dtype=torch.float32, shape=k_resp.shape)
+    if prefix.prefix_len > 0:
+        _dev(dk_pages, "dk_pages", dtype=torch.float32, shape=prefix.k_pages.shape)
+        _dev(dv_pages, "dv_pages", dtype=torch.float32, shape=prefix.k_pages.shape)
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _dev(dq, "dq", dtype=torch.float32, shape=q.shape)
+    flags = None
+    if shard_first_touch is not None:
+        flags = (C.c_uint8 * prefix.n_shards)(*[1 if f else 0 for f in shard_first_touch])
+    ws_bytes = bwd_workspace_bytes(prefix, n_rows)
+    ws = _workspace(ws_bytes, q.device, workspace)
+    st = prefix.struct()
+    check(lib().ls_replay_bwd(C.byref(st), _ptr(q), n_rows, q_start, _ptr(k_resp), _ptr(v_resp), k_resp.shape[0],
+                              _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk_resp), _ptr(dv_resp),
+                              1 if resp_first_touch else 0, _ptr(dk_pages) if dk_pages is not None else None,
+                              _ptr(dv_pages) if dv_pages is not None else None,
+                              C.cast(flags, C.c_void_p) if flags is not None else None,
+                              _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return dq
+
+
+def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype: torch.dtype = torch.float32):
+    """Merge [n_parts, n_rows, d] partial outputs by their LSE [n_parts, n_rows] in float32."""
+    _dev(o_parts, "o_parts", dtype=torch.float32)
+    n_parts, n_rows, d = o_parts.shape
+    _dev(lse_parts, "lse_parts", dtype=torch.float32, shape=(n_parts, n_rows))
+    o = torch.empty((n_rows, d), dtype=out_dtype, device=o_parts.device)
+    lse = torch.empty((n_rows,), dtype=torch.float32, device=o_parts.device)
+    check(lib().ls_lse_merge(n_parts, n_rows, d, _ptr(o_parts), _ptr(lse_parts), _ptr(o), _dtype_code(out_dtype),
+                             _ptr(lse), _stream()))
+    return o, lse

@@ -1,0 +1,287 @@
+// C ABI front end of the replay-attention library: argument checks (all before any launch),
+// workspace sizing, kernel dispatch and the per-thread error message.  No exception crosses
+// the boundary and nothing here allocates device memory or synchronises with the host.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/longstraw.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(LS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool d_supported(int d) { return d == 64 || d == 128 || d == 256; }
+
+// The generic (vector-ALU) kernels run the f32 path; bf16 runs on the matrix cores unless
+// LS_KERNELS=generic asks for the generic kernels (a debugging aid).
+bool force_generic() {
+    static const bool v = [] {
+        const char* e = std::getenv("LS_KERNELS");
+        return e && std::strcmp(e, "generic") == 0;
+    }();
+    return v;
+}
+
+int64_t logical_pages(int64_t n_tok, int page_size) { return (n_tok + page_size - 1) / page_size; }
+
+int check_prefix(const ls_prefix_t* p) {
+    if (!p) return fail(LS_ERR_INVALID, "prefix descriptor is NULL");
+    if (p->hq < 1 || p->hkv < 1 || p->hq % p->hkv != 0)
+        return fail(LS_ERR_INVALID, "hq (%d) must be a positive multiple of hkv (%d)", p->hq, p->hkv);
+    if (!d_supported(p->d)) return fail(LS_ERR_UNSUPPORTED, "head dim d=%d not in {64,128,256}", p->d);
+    if (p->page_size != ls::kPage) return fail(LS_ERR_UNSUPPORTED, "page_size=%d, only 64 is built", p->page_size);
+    if (p->dtype != LS_DTYPE_F32 && p->dtype != LS_DTYPE_BF16)
+        return fail(LS_ERR_UNSUPPORTED, "dtype %d unknown", p->dtype);
+    if (p->n_shards < 1 || p->n_shards > ls::kMaxShards)
+        return fail(LS_ERR_INVALID, "n_shards=%d outside [1, %d]", p->n_shards, ls::kMaxShards);
+    if (p->prefix_len < 0) return fail(LS_ERR_INVALID, "prefix_len=%lld < 0", (long long)p->prefix_len);
+    if (!std::isfinite(p->softmax_scale)) return fail(LS_ERR_INVALID, "softmax_scale is not finite");
+    const int64_t nlp = logical_pages(p->prefix_len, p->page_size);
+    if (nlp > 0) {
+        if (!p->page_table || !p->k_pages || !p->v_pages)
+            return fail(LS_ERR_INVALID, "page_table/k_pages/v_pages must be non-NULL for a non-empty prompt");
+        if (p->n_phys_pages < 1) return fail(LS_ERR_INVALID, "n_phys_pages=%lld < 1", (long long)p->n_phys_pages);
+        if (nlp > (int64_t)INT32_MAX) return fail(LS_ERR_INVALID, "too many logical pages");
+    }
+    if (!p->shard_page_bounds) return fail(LS_ERR_INVALID, "shard_page_bounds is NULL");
+    const int64_t* b = p->shard_page_bounds;
+    if (b[0] != 0 || b[p->n_shards] != nlp)
+        return fail(LS_ERR_INVALID, "shard bounds must run from 0 to %lld logical pages (got %lld..%lld)",
+                    (long long)nlp, (long long)b[0], (long long)b[p->n_shards]);
+    for (int s = 0; s < p->n_shards; s++)
+        if (b[s + 1] < b[s]) return fail(LS_ERR_INVALID, "shard bounds decrease at shard %d", s);
+    return LS_OK;
+}
+
+int check_block(const ls_prefix_t* p, const void* q, int64_t n_rows, int64_t q_start, const void* k_resp,
+                const void* v_resp, int64_t n_resp_keys) {
+    if (n_rows < 0 || q_start < 0) return fail(LS_ERR_INVALID, "n_rows=%lld, q_start=%lld must be >= 0",
+                                               (long long)n_rows, (long long)q_start);
+    if (n_resp_keys < q_start + n_rows)
+        return fail(LS_ERR_INVALID, "n_resp_keys=%lld < q_start + n_rows = %lld", (long long)n_resp_keys,
+                    (long long)(q_start + n_rows));
+    if (n_rows > 0 && !q) return fail(LS_ERR_INVALID, "q is NULL");
+    if (q_start + n_rows > 0 && (!k_resp || !v_resp)) return fail(LS_ERR_INVALID, "k_resp/v_resp is NULL");
+    const int64_t rows_g = n_rows * (p->hq / p->hkv);
+    if (rows_g > (int64_t)1 << 30) return fail(LS_ERR_INVALID, "block too large (%lld group rows)", (long long)rows_g);
+    return LS_OK;
+}
+
+ls::AttnArgs make_args(const ls_prefix_t* p, const void* q, int64_t n_rows, int64_t q_start, const void* k_resp,
+                       const void* v_resp) {
+    ls::AttnArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.k_pages = p->k_pages;
+    a.v_pages = p->v_pages;
+    a.table = p->page_table;
+    a.prefix_len = p->prefix_len;
+    a.n_logical_pages = logical_pages(p->prefix_len, p->page_size);
+    a.n_phys = p->n_phys_pages;
+    a.hq = p->hq;
+    a.hkv = p->hkv;
+    a.g = p->hq / p->hkv;
+    a.d = p->d;
+    a.scale = p->softmax_scale;
+    a.scale_log2 = p->softmax_scale * ls::kLog2e;
+    a.q = q;
+    a.k_resp = k_resp;
+    a.v_resp = v_resp;
+    a.n_rows = n_rows;
+    a.q_start = q_start;
+    a.key_end = q_start + n_rows;
+    a.n_shards = p->n_shards;
+    a.n_parts = p->n_shards + 1;
+    for (int s = 0; s <= p->n_shards; s++) a.shard_lo[s] = p->shard_page_bounds[s];
+    return a;
+}
+
+size_t fwd_ws(const ls_prefix_t* p, int64_t n_rows) {
+    return sizeof(float) * (size_t)(p->n_shards + 1) * (size_t)n_rows * (size_t)p->hq * (size_t)(p->d + 1);
+}
+
+size_t bwd_ws(const ls_prefix_t* p, int64_t n_rows) {
+    return sizeof(float) * ((size_t)n_rows * p->hq + (size_t)(p->n_shards + 1) * n_rows * p->hq * p->d);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ls_version(void) { return LS_VERSION; }
+
+const char* ls_last_error(void) { return g_err.c_str(); }
+
+int ls_capture_pages(const void* k_src, const void* v_src, int src_dtype, int64_t n_tok, int64_t first_tok,
+                     const int32_t* page_table, int64_t n_logical_pages, void* k_pages, void* v_pages,
+                     int page_dtype, int64_t n_phys_pages, int hkv, int d, int page_size, ls_stream_t stream) {
+    g_err.clear();
+    if (n_tok < 0 || first_tok < 0) return fail(LS_ERR_INVALID, "n_tok and first_tok must be >= 0");
+    if (hkv < 1) return fail(LS_ERR_INVALID, "hkv=%d < 1", hkv);
+    if (!d_supported(d)) return fail(LS_ERR_UNSUPPORTED, "head dim d=%d not in {64,128,256}", d);
+    if (page_size != ls::kPage) return fail(LS_ERR_UNSUPPORTED, "page_size=%d, only 64 is built", page_size);
+    const bool same = src_dtype == page_dtype && (src_dtype == LS_DTYPE_F32 || src_dtype == LS_DTYPE_BF16);
+    const bool down = src_dtype == LS_DTYPE_F32 && page_dtype == LS_DTYPE_BF16;
+    if (!same && !down) return fail(LS_ERR_UNSUPPORTED, "capture from dtype %d into dtype %d", src_dtype, page_dtype);
+    if (first_tok % page_size != 0) return fail(LS_ERR_INVALID, "first_tok=%lld is not page aligned", (long long)first_tok);
+    if (n_tok == 0) return LS_OK;
+    if (!k_src || !v_src || !page_table || !k_pages || !v_pages) return fail(LS_ERR_INVALID, "NULL pointer argument");
+    if (n_phys_pages < 1) return fail(LS_ERR_INVALID, "n_phys_pages=%lld < 1", (long long)n_phys_pages);
+    if (logical_pages(first_tok + n_tok, page_size) > n_logical_pages)
+        return fail(LS_ERR_INVALID, "tokens up to %lld need more than %lld logical pages", (long long)(first_tok + n_tok),
+                    (long long)n_logical_pages);
+    hipError_t e = ls::launch_capture(k_src, v_src, src_dtype, n_tok, first_tok, page_table, k_pages, v_pages, page_dtype,
+                                      n_phys_pages, hkv, d, (hipStream_t)stream);
+    return e == hipSuccess ? LS_OK : hip_fail(e, "capture kernel");
+}
+
+int ls_gather_pages(const void* pages, int dtype, const int32_t* page_table, int64_t n_logical_pages,
+                    int64_t n_phys_pages, int64_t first_tok, int64_t n_tok, int hkv, int d, int page_size, void* dst,
+                    ls_stream_t stream) {
+    g_err.clear();
+    if (n_tok < 0 || first_tok < 0) return fail(LS_ERR_INVALID, "n_tok and first_tok must be >= 0");
+    if (hkv < 1) return fail(LS_ERR_INVALID, "hkv=%d < 1", hkv);
+    if (!d_supported(d)) return fail(LS_ERR_UNSUPPORTED, "head dim d=%d not in {64,128,256}", d);
+    if (page_size != ls::kPage) return fail(LS_ERR_UNSUPPORTED, "page_size=%d, only 64 is built", page_size);
+    if (dtype != LS_DTYPE_F32 && dtype != LS_DTYPE_BF16) return fail(LS_ERR_UNSUPPORTED, "dtype %d unknown", dtype);
+    if (n_tok == 0) return LS_OK;
+    if (!pages || !page_table || !dst) return fail(LS_ERR_INVALID, "NULL pointer argument");
+    if (n_phys_pages < 1) return fail(LS_ERR_INVALID, "n_phys_pages=%lld < 1", (long long)n_phys_pages);
+    if (logical_pages(first_tok + n_tok, page_size) > n_logical_pages)
+        return fail(LS_ERR_INVALID, "tokens up to %lld need more than %lld logical pages", (long long)(first_tok + n_tok),
+                    (long long)n_logical_pages);
+    hipError_t e = ls::launch_gather(pages, dtype, page_table, n_phys_pages, first_tok, n_tok, hkv, d, dst,
+                                     (hipStream_t)stream);
+    return e == hipSuccess ? LS_OK : hip_fail(e, "gather kernel");
+}
+
+size_t ls_fwd_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows) {
+    g_err.clear();
+    if (check_prefix(pre) != LS_OK) return 0;
+    if (n_rows < 0) {
+        fail(LS_ERR_INVALID, "n_rows < 0");
+        return 0;
+    }
+    return fwd_ws(pre, n_rows);
+}
+
+size_t ls_bwd_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows) {
+    g_err.clear();
+    if (check_prefix(pre) != LS_OK) return 0;
+    if (n_rows < 0) {
+        fail(LS_ERR_INVALID, "n_rows < 0");
+        return 0;
+    }
+    return bwd_ws(pre, n_rows);
+}
+
+int ls_replay_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start, const void* k_resp,
+                  const void* v_resp, int64_t n_resp_keys, void* o, float* lse, void* workspace, size_t ws_bytes,
+                  ls_stream_t stream) {
+    g_err.clear();
+    int rc = check_prefix(pre);
+    if (rc != LS_OK) return rc;
+    rc = check_block(pre, q, n_rows, q_start, k_resp, v_resp, n_resp_keys);
+    if (rc != LS_OK) return rc;
+    if (n_rows == 0) return LS_OK;
+    if (!o || !lse) return fail(LS_ERR_INVALID, "o/lse is NULL");
+    const size_t need = fwd_ws(pre, n_rows);
+    if (!workspace || ws_bytes < need)
+        return fail(LS_ERR_WORKSPACE, "forward workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+    ls::AttnArgs a = make_args(pre, q, n_rows, q_start, k_resp, v_resp);
+    const int64_t rows = n_rows * pre->hq;
+    a.o_parts = (float*)workspace;
+    a.lse_parts = a.o_parts + (size_t)a.n_parts * rows * pre->d;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = (pre->dtype == LS_DTYPE_BF16 && !force_generic()) ? ls::launch_fwd_mfma(a, s)
+                                                                     : ls::launch_fwd_generic(pre->dtype, a, s);
+    if (e != hipSuccess) return hip_fail(e, "forward kernel");
+    e = ls::launch_lse_merge(a.n_parts, rows, pre->d, a.o_parts, a.lse_parts, o, pre->dtype, lse, s);
+    return e == hipSuccess ? LS_OK : hip_fail(e, "LSE merge kernel");
+}
+
+int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start, const void* k_resp,
+                  const void* v_resp, int64_t n_resp_keys, const void* o, const float* lse, const void* dout, float* dq,
+                  float* dk_resp, float* dv_resp, int resp_first_touch, float* dk_pages, float* dv_pages,
+                  const uint8_t* shard_first_touch, void* workspace, size_t ws_bytes, ls_stream_t stream) {
+    g_err.clear();
+    int rc = check_prefix(pre);
+    if (rc != LS_OK) return rc;
+    rc = check_block(pre, q, n_rows, q_start, k_resp, v_resp, n_resp_keys);
+    if (rc != LS_OK) return rc;
+    if (n_rows > 0 && (!o || !lse || !dout || !dq)) return fail(LS_ERR_INVALID, "o/lse/dout/dq is NULL");
+    if (n_resp_keys > 0 && (!dk_resp || !dv_resp)) return fail(LS_ERR_INVALID, "dk_resp/dv_resp is NULL");
+    if (pre->prefix_len > 0 && (!dk_pages || !dv_pages)) return fail(LS_ERR_INVALID, "dk_pages/dv_pages is NULL");
+    const size_t need = bwd_ws(pre, n_rows);
+    if (need > 0 && (!workspace || ws_bytes < need))
+        return fail(LS_ERR_WORKSPACE, "backward workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+    ls::AttnArgs a = make_args(pre, q, n_rows, q_start, k_resp, v_resp);
+    const int64_t rows = n_rows * pre->hq;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.delta = (float*)workspace;
+    a.dq_parts = (float*)workspace + rows;
+    a.dk_pages = dk_pages;
+    a.dv_pages = dv_pages;
+    a.dk_resp = dk_resp;
+    a.dv_resp = dv_resp;
+    a.resp_first_touch = resp_first_touch != 0;
+    a.first_touch_mask = 0;
+    if (shard_first_touch)
+        for (int s = 0; s < pre->n_shards; s++)
+            if (shard_first_touch[s]) a.first_touch_mask |= 1ull << s;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = ls::launch_delta(o, dout, pre->dtype, rows, pre->d, (float*)a.delta, s);
+    if (e != hipSuccess) return hip_fail(e, "delta kernel");
+    e = (pre->dtype == LS_DTYPE_BF16 && !force_generic()) ? ls::launch_bwd_mfma(a, s)
+                                                          : ls::launch_bwd_generic(pre->dtype, a, s);
+    if (e != hipSuccess) return hip_fail(e, "backward kernels");
+    e = ls::launch_sum_parts(a.n_parts, rows * pre->d, a.dq_parts, dq, s);
+    if (e != hipSuccess) return hip_fail(e, "dQ part sum kernel");
+    if (resp_first_touch && n_resp_keys > a.key_end) {
+        const int64_t off = a.key_end * pre->hkv * pre->d;
+        const int64_t cnt = (n_resp_keys - a.key_end) * pre->hkv * pre->d;
+        e = ls::launch_zero(dk_resp + off, cnt, s);
+        if (e == hipSuccess) e = ls::launch_zero(dv_resp + off, cnt, s);
+        if (e != hipSuccess) return hip_fail(e, "zero kernel");
+    }
+    return LS_OK;
+}
+
+int ls_lse_merge(int n_parts, int64_t n_rows, int d, const float* o_parts, const float* lse_parts, void* o_out,
+                 int out_dtype, float* lse_out, ls_stream_t stream) {
+    g_err.clear();
+    if (n_parts < 1) return fail(LS_ERR_INVALID, "n_parts=%d < 1", n_parts);
+    if (n_rows < 0) return fail(LS_ERR_INVALID, "n_rows < 0");
+    if (d < 4 || d % 4 != 0 || d > 1024) return fail(LS_ERR_UNSUPPORTED, "d=%d must be a multiple of 4 in [4, 1024]", d);
+    if (out_dtype != LS_DTYPE_F32 && out_dtype != LS_DTYPE_BF16) return fail(LS_ERR_UNSUPPORTED, "dtype %d", out_dtype);
+    if (n_rows == 0) return LS_OK;
+    if (!o_parts || !lse_parts || !o_out || !lse_out) return fail(LS_ERR_INVALID, "NULL pointer argument");
+    hipError_t e = ls::launch_lse_merge(n_parts, n_rows, d, o_parts, lse_parts, o_out, out_dtype, lse_out,
+                                        (hipStream_t)stream);
+    return e == hipSuccess ? LS_OK : hip_fail(e, "LSE merge kernel");
+}
+
+}  // extern "C"

@@ -1,0 +1,368 @@
+// Split-prefix replay-attention forward on gfx950 bf16 matrix cores.
+//
+// One workgroup handles BM = 32 * NW query rows of one kv head's group against the keys of
+// one part: a prompt shard (a contiguous range of logical pages, walked through the page
+// table) or the response keys the rows see (causal).  It writes the part's normalised
+// output and LSE, the owner-local softmax statistics that the merge composes into the exact
+// result (LongStraw digest, "Method", Qwen implementation; explainer, "Two incompatible
+// architectures, same transaction").
+//
+// Per wave (32 rows), per 64-key page:
+//   S^T[64 x 32] = K[64 x D] . Q^T        v_mfma_f32_32x32x16_bf16, K from LDS, Q in VGPRs
+//   online softmax in base 2               each lane owns one row: in-lane max/sum, one
+//                                          cross-half exchange (v_permlane32_swap)
+//   O^T[D x 32] += V^T[D x 64] . P^T       V read transposed from LDS (ds_read_b64_tr_b16),
+//                                          P^T taken straight from the S^T accumulators
+// Keys are permuted inside each 16-key MFMA step so that P^T needs no data movement: the
+// order is the same on both operands, so the sum is unchanged.
+//
+// K/V pages (64 x D bf16 each, one contiguous tile per (page, kv head)) are copied into a
+// double-buffered LDS stage by direct global->LDS loads, issued one page ahead.  A 16-byte
+// chunk c of LDS row r holds logical chunk c ^ (r & 15) to spread rows over the banks.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ls {
+namespace {
+
+template <int D>
+struct FwdShape {
+    static constexpr int KCH = D / 8;                        // 16-byte chunks per row
+    static constexpr int KS = D / 16;                        // k-steps of S over d
+    static constexpr int DT = D / 32;                        // 32-wide d tiles of O
+    static constexpr int SWZ = (KCH >= 16 ? 16 : KCH) - 1;   // row -> chunk xor mask
+    static constexpr int TILE = kPage * D * 2;               // bytes of one K or V page tile
+};
+
+struct TileSrc {
+    const bf16_t* k;
+    const bf16_t* v;
+    int64_t stride;  // elements between consecutive key rows
+    int valid;       // rows [0, valid) hold keys; the rest repeat the last valid row
+    int64_t key0;    // first key: logical prompt token, or response position
+};
+
+// Physical page of tile t of a prompt part (clamped so that a bad table cannot fault).
+__device__ __forceinline__ int32_t phys_page(const AttnArgs& a, int part, int64_t t) {
+    int32_t phys = a.table[a.shard_lo[part] + t];
+    return phys < 0 ? 0 : (phys >= a.n_phys ? (int32_t)(a.n_phys - 1) : phys);
+}
+
+// Source of tile t of a part; `phys` is its physical page (prompt parts only).
+__device__ __forceinline__ TileSrc part_tile(const AttnArgs& a, bool resp, int part, int kvh,
+                                             int64_t t, int32_t phys) {
+    TileSrc s;
+    if (!resp) {
+        const int64_t lp = a.shard_lo[part] + t;
+        const int64_t off = ((int64_t)phys * a.hkv + kvh) * kPage * a.d;
+        s.k = (const bf16_t*)a.k_pages + off;
+        s.v = (const bf16_t*)a.v_pages + off;
+        s.stride = a.d;
+        s.key0 = lp * kPage;
+        const int64_t left = a.prefix_len - s.key0;
+        s.valid = left < kPage ? (int)left : kPage;
+    } else {
+        s.key0 = t * kPage;
+        const int64_t off = (s.key0 * a.hkv + kvh) * a.d;
+        s.k = (const bf16_t*)a.k_resp + off;
+        s.v = (const bf16_t*)a.v_resp + off;
+        s.stride = (int64_t)a.hkv * a.d;
+        const int64_t left = a.key_end - s.key0;
+        s.valid = left < kPage ? (int)left : kPage;
+    }
+    return s;
+}
+
+// Issue the direct-to-LDS copies of one K and one V page tile (all waves together).  Wave
+// w's j-th copy fills 1 KiB block j*NW + w of the tile, i.e. RPK = 512/D whole rows; lane l
+// writes 16-byte slot l of the block, so it fetches the logical chunk that the xor swizzle
+// puts there.  `w` must be wave-uniform.
+template <int D, int NW>
+__device__ __forceinline__ void issue_tile(const TileSrc& s, char* lds_k, char* lds_v, int w,
+                                           int lane) {
+    using F = FwdShape<D>;
+    constexpr int RPK = 512 / D;                 // rows per 1 KiB block
+    constexpr int PER_WAVE = F::TILE / 1024 / NW;
+    constexpr int JROWS = NW * RPK;              // rows advanced per j (a power of two)
+    const int low = w * RPK + lane / F::KCH;     // row inside the j-th group of JROWS rows
+    const int pc = lane % F::KCH;                // 16-byte slot inside the row
+    const int lane_x = pc ^ (low & F::SWZ);
+    if (s.valid == kPage) {
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; j++) {
+            const int lc = lane_x ^ ((j * JROWS) & F::SWZ);
+            const uint32_t off = (uint32_t)(low * (int)s.stride + lc * 8) * 2u;
+            const int64_t rowj = (int64_t)(j * JROWS) * s.stride * 2;
+            const char* bk = (const char*)s.k + rowj;
+            const char* bv = (const char*)s.v + rowj;
+            const int blk = j * NW + w;
+            dma16(bk + off, (LS_LDS void*)(lds_k + blk * 1024));
+            dma16(bv + off, (LS_LDS void*)(lds_v + blk * 1024));
+        }
+    } else {
+        // a partial tile: rows past `valid` repeat the last valid row (finite, masked later)
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; j++) {
+            const int r = j * JROWS + low;
+            const int lc = lane_x ^ ((j * JROWS) & F::SWZ);
+            const int rs = r < s.valid ? r : s.valid - 1;
+            const uint32_t off = (uint32_t)(rs * (int)s.stride + lc * 8) * 2u;
+            const int blk = j * NW + w;
+            dma16((const char*)s.k + off, (LS_LDS void*)(lds_k + blk * 1024));
+            dma16((const char*)s.v + off, (LS_LDS void*)(lds_v + blk * 1024));
+        }
+    }
+}
+
+template <int D>
+struct WaveState {
+    bf16x8 qb[FwdShape<D>::KS];   // Q^T operand: row lane%32, d = 16ks + 8(lane/32) .. +8
+    f32x16 o[FwdShape<D>::DT];    // O^T accumulators: col = row, rows = d
+    float m;                      // running max (base-2 scaled scores)
+    float l;                      // running sum of this lane's half of the keys
+};
+
+// Per-lane LDS byte offsets inside a page tile.  With the xor swizzle, the address of
+// chunk `lc` of row `r` is r*2D + ((lc ^ (r & SWZ)) << 4); splitting r and lc into lane-fixed
+// and step-varying bits turns every operand read into (lane base ^ constant) + constant.
+template <int D>
+struct LaneAddr {
+    uint32_t k;  // K rows lane%32: XOR with (ks << 5) selects chunk 2ks + lane/32
+    uint32_t v;  // V^T transpose reads: XOR with ((4dt ^ (8e & SWZ)) << 4)
+    __device__ __forceinline__ LaneAddr(int lane) {
+        using F = FwdShape<D>;
+        const int h = lane >> 5, n = lane & 31;
+        k = n * 2 * D + ((h ^ (n & F::SWZ)) << 4);
+        const int G = lane >> 4, i16 = lane & 15;
+        const int c_lane = 4 * (G >> 1) + (i16 >> 2);          // row within an 8-row group
+        const int l_lane = 2 * (G & 1) + ((i16 & 3) >> 1);     // chunk within a 32-wide d tile
+        const int half8 = (i16 & 1) * 8;                       // byte inside the 16-byte chunk
+        v = c_lane * 2 * D + half8 + ((l_lane ^ c_lane) << 4);
+    }
+};
+
+template <int D>
+__device__ __forceinline__ void compute_tile(WaveState<D>& ws, const LS_LDS char* lds_k,
+                                             const LS_LDS char* lds_v, LaneAddr<D> la,
+                                             const TileSrc& src, bool resp, bool need_mask,
+                                             int64_t vis_limit, float scale_log2, int lane) {
+    using F = FwdShape<D>;
+    const int h = lane >> 5;
+    // keep the per-lane offsets from being hoisted out of the page loop as many registers
+    asm volatile("" : "+v"(la.k), "+v"(la.v));
+    // ---- S^T = K Q^T for the two 32-key halves of the page
+    f32x16 s[2];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < F::KS; ks++) {
+        const LS_LDS char* pk = lds_k + (la.k ^ (uint32_t)(ks << 5));
+        const bf16x8 k0 = *(const LS_LDS bf16x8*)(pk);
+        const bf16x8 k1 = *(const LS_LDS bf16x8*)(pk + 32 * 2 * D);
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ws.qb[ks], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, ws.qb[ks], s[1], 0, 0, 0);
+    }
+    // ---- scale, mask, running max.  Element i of tile kt is key 32kt + 8(i/4) + 4h + i%4 of
+    // the page; the mask compares its lane-free part with two per-lane limits.
+    float mx = -INFINITY;
+    int lim_valid = src.valid - 4 * h;  // keys < valid exist
+    int lim_causal = 64;                // response keys <= vis_limit are visible
+    if (resp) {
+        const int64_t c = vis_limit - src.key0 - 4 * h;
+        lim_causal = c < -1 ? -1 : (c > 64 ? 64 : (int)c);
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            float x = s[kt][i] * scale_log2;
+            if (need_mask) {
+                const int kc = 32 * kt + 8 * (i >> 2) + (i & 3);
+                x = (kc < lim_valid && kc <= lim_causal) ? x : -INFINITY;
+            }
+            s[kt][i] = x;
+            mx = fmaxf(mx, x);
+        }
+    }
+    mx = fmaxf(mx, other_half(mx));
+    const float m_new = fmaxf(ws.m, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(ws.m - m_use);
+    ws.m = m_new;
+    // ---- P = exp2(S - m), packed to bf16 as the P^T operand
+    bf16x8 pb[2][2];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++) {
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            uint32_t w4[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const float p0 = fast_exp2(s[kt][8 * u + 2 * t] - m_use);
+                const float p1 = fast_exp2(s[kt][8 * u + 2 * t + 1] - m_use);
+                lsum += p0 + p1;
+                w4[t] = pack_bf16x2(p0, p1);
+            }
+            pb[kt][u] = __builtin_bit_cast(bf16x8, (u32x4{w4[0], w4[1], w4[2], w4[3]}));
+        }
+    }
+    ws.l = ws.l * alpha + lsum;
+    if (!__all(alpha == 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < F::DT; dt++) ws.o[dt] *= alpha;
+    }
+    // ---- O^T += V^T P^T; rows (keys) 32kt + 16u + 8e + lane row, d tile dt
+#pragma unroll
+    for (int dt = 0; dt < F::DT; dt++) {
+        const uint32_t x0 = la.v ^ (uint32_t)(((4 * dt) ^ (0 & F::SWZ)) << 4);
+        const uint32_t x1 = la.v ^ (uint32_t)(((4 * dt) ^ (8 & F::SWZ)) << 4);
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++) {
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                const int row = 32 * kt + 16 * u;
+                const i16x4 lo = lds_read_tr4(lds_v + x0 + row * 2 * D);
+                const i16x4 hi = lds_read_tr4(lds_v + x1 + (row + 8) * 2 * D);
+                const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                ws.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kt][u], ws.o[dt], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// One pipeline step: start copying the next page into the other LDS stage, then compute on
+// the current one.  The stages are passed as restrict pointers so that, once inlined, the
+// compiler knows the copies cannot alias the reads and does not wait for them.
+template <int D, int NW>
+__device__ __forceinline__ void fwd_step(WaveState<D>& ws, const char* __restrict__ cur,
+                                         char* __restrict__ nxt, bool has_next,
+                                         const TileSrc& next_src, const TileSrc& src,
+                                         LaneAddr<D> la, bool resp, bool need_mask,
+                                         int64_t vis_limit, float scale_log2, int w, int lane) {
+    using F = FwdShape<D>;
+    if (has_next) issue_tile<D, NW>(next_src, nxt, nxt + F::TILE, w, lane);
+    compute_tile<D>(ws, (const LS_LDS char*)cur, (const LS_LDS char*)(cur + F::TILE), la, src, resp,
+                    need_mask, vis_limit, scale_log2, lane);
+}
+
+template <int D, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(1, 1)))
+void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
+    using F = FwdShape<D>;
+    constexpr int BM = 32 * NW;
+    __shared__ __attribute__((aligned(1024))) char st0[2 * F::TILE];
+    __shared__ __attribute__((aligned(1024))) char st1[2 * F::TILE];
+
+    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    if (lb >= n_blocks) return;
+    const int qtile = lb % n_qtiles;
+    const int part = (lb / n_qtiles) % a.n_parts;
+    const int kvh = lb / (n_qtiles * a.n_parts);
+    const bool resp = part == a.n_shards;
+
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5;
+    const int n = lane & 31;
+    const int64_t rows_total = a.n_rows * a.g;
+    const int64_t r0 = (int64_t)qtile * BM;
+    const int64_t my_row = r0 + 32 * w + n;
+    const bool row_ok = my_row < rows_total;
+    const int64_t my_tok = my_row / a.g;
+    const int my_head = kvh * a.g + (int)(my_row % a.g);
+
+    WaveState<D> ws;
+    {
+        // rows past the block (a partial last tile) read a valid row and are never stored
+        const int64_t ld_row = row_ok ? my_row : rows_total - 1;
+        const int64_t ld_tok = ld_row / a.g;
+        const int ld_head = kvh * a.g + (int)(ld_row % a.g);
+        const bf16_t* qrow = (const bf16_t*)a.q + (ld_tok * a.hq + ld_head) * (int64_t)D + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < F::KS; ks++) ws.qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * ks));
+#pragma unroll
+        for (int dt = 0; dt < F::DT; dt++) ws.o[dt] = f32x16{};
+        ws.m = -INFINITY;
+        ws.l = 0.f;
+    }
+    const LaneAddr<D> la(lane);
+
+    // number of key tiles of this part for this query tile
+    int64_t n_tiles;
+    const int64_t tok_min = r0 / a.g;
+    if (!resp) {
+        n_tiles = a.shard_lo[part + 1] - a.shard_lo[part];
+    } else {
+        int64_t tok_max = (r0 + BM - 1) / a.g;
+        if (tok_max > a.n_rows - 1) tok_max = a.n_rows - 1;
+        n_tiles = (a.q_start + tok_max + 1 + kPage - 1) / kPage;
+    }
+    const int64_t vis_limit = a.q_start + my_tok;  // last response key this row sees
+    // Page-table entries are read one tile ahead of their copy, so the lookup latency hides
+    // behind the current tile's compute.
+    int32_t phys_cur = (!resp && n_tiles > 0) ? phys_page(a, part, 0) : 0;
+    int32_t phys_next = (!resp && n_tiles > 1) ? phys_page(a, part, 1) : 0;
+    TileSrc src = part_tile(a, resp, part, kvh, 0, __builtin_amdgcn_readfirstlane(phys_cur));
+    if (n_tiles > 0) issue_tile<D, NW>(src, st0, st0 + F::TILE, w, lane);
+    for (int64_t t = 0; t < n_tiles; t++) {
+        wait_vm_all();
+        __syncthreads();
+        const bool has_next = t + 1 < n_tiles;
+        const TileSrc next_src =
+            part_tile(a, resp, part, kvh, has_next ? t + 1 : t, __builtin_amdgcn_readfirstlane(phys_next));
+        if (!resp && t + 2 < n_tiles) phys_next = phys_page(a, part, t + 2);
+        const bool need_mask = src.valid < kPage || (resp && src.key0 + kPage - 1 > a.q_start + tok_min);
+        char* cur = (t & 1) ? st1 : st0;
+        char* nxt = (t & 1) ? st0 : st1;
+        fwd_step<D, NW>(ws, cur, nxt, has_next, next_src, src, la, resp, need_mask, vis_limit, a.scale_log2, w,
+                        lane);
+        src = next_src;
+    }
+
+    // ---- normalise and write this part's output and LSE
+    const float l = ws.l + other_half(ws.l);
+    if (!row_ok) return;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* dst = a.o_parts + (((int64_t)part * a.n_rows + my_tok) * a.hq + my_head) * (int64_t)D;
+#pragma unroll
+    for (int dt = 0; dt < F::DT; dt++) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+            const int dd = dt * 32 + 8 * q4 + 4 * h;
+            float4 v = make_float4(ws.o[dt][4 * q4] * inv, ws.o[dt][4 * q4 + 1] * inv,
+                                   ws.o[dt][4 * q4 + 2] * inv, ws.o[dt][4 * q4 + 3] * inv);
+            *(float4*)(dst + dd) = v;
+        }
+    }
+    if (h == 0)
+        a.lse_parts[((int64_t)part * a.n_rows + my_tok) * a.hq + my_head] =
+            l > 0.f ? (ws.m + fast_log2(l)) * kLn2 : -INFINITY;
+}
+
+template <int D>
+hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
+    constexpr int NW = 4;
+    constexpr int BM = 32 * NW;
+    const int64_t n_qtiles = (a.n_rows * a.g + BM - 1) / BM;
+    const int64_t n_blocks = n_qtiles * a.n_parts * a.hkv;
+    if (n_blocks == 0) return hipSuccess;
+    const int grid = pad_grid((int)n_blocks);
+    fwd_mfma_kernel<D, NW><<<grid, NW * 64, 0, s>>>(a, (int)n_qtiles, (int)n_blocks);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t s) {
+    switch (a.d) {
+        case 64: return launch_d<64>(a, s);
+        case 128: return launch_d<128>(a, s);
+        case 256: return launch_d<256>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ls

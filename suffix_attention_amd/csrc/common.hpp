@@ -1,0 +1,92 @@
+// Device-side building blocks shared by the replay-attention kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ls {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // storage type of a bfloat16 in memory
+
+#define LS_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kPage = 64;  // tokens per KV page
+
+// ----------------------------------------------------------------------------------------
+// Scalar conversions.  bf16 -> f32 is exact; f32 -> bf16 rounds to nearest-even (NaN kept
+// quiet).
+// ----------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(bf16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float load_f32(const T* p);
+template <> __device__ __forceinline__ float load_f32<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load_f32<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
+
+template <typename T> __device__ __forceinline__ void store_f32(T* p, float v);
+template <> __device__ __forceinline__ void store_f32<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void store_f32<bf16_t>(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+
+// Pack two f32 to two bf16 (round to nearest-even) in one 32-bit word, low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value of x held by lane l ^ 32 (the other half of the wave).
+__device__ __forceinline__ float other_half(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    // r[0]: lanes 32..63 received lanes 0..31; r[1]: lanes 0..31 received lanes 32..63.
+    return __uint_as_float((__lane_id() < 32) ? r[1] : r[0]);
+}
+
+// ----------------------------------------------------------------------------------------
+// XCD-aware block order.  Workgroups are dispatched round-robin over the 8 XCDs of an
+// MI355X, so hardware block b lands on XCD b % 8.  Renumbering as below gives each XCD a
+// contiguous range of logical blocks, so blocks that share operands (the query tiles of
+// one key range) run together behind one L2.  `n` must be a multiple of 8; callers pad
+// the grid and let logical ids >= the real count return at once.
+// ----------------------------------------------------------------------------------------
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_logical_block(int b, int n) {
+    return (b % kXcds) * (n / kXcds) + b / kXcds;
+}
+inline int pad_grid(int n) { return (n + kXcds - 1) / kXcds * kXcds; }
+
+// ----------------------------------------------------------------------------------------
+// Direct global -> LDS copy of 16 bytes per lane.  Lane l's bytes land at
+// lds_wave_base + 16 * l (lds_wave_base must be uniform across the wave).
+// ----------------------------------------------------------------------------------------
+__device__ __forceinline__ void dma16(const void* src, LS_LDS void* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 4 bf16 from LDS through the gfx950 transpose read.  Within each 16-lane group, lane i
+// supplies the address of 4 consecutive elements; it receives element i % 4 of the chunks
+// addressed by lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4 (a 4 x 16 block read as its
+// transpose).
+__device__ __forceinline__ i16x4 lds_read_tr4(const LS_LDS void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LS_LDS i16x4*)(p));
+}
+
+}  // namespace ls

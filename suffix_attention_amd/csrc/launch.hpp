@@ -1,0 +1,81 @@
+// Internal interface between the C ABI front end (abi.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ls {
+
+constexpr int kMaxShards = 64;
+
+// Everything one replay-attention launch needs, passed by value to the kernels.
+struct AttnArgs {
+    // captured prompt (pages)
+    const void* k_pages;
+    const void* v_pages;
+    const int32_t* table;
+    int64_t prefix_len;
+    int64_t n_logical_pages;
+    int64_t n_phys;
+    int hq, hkv, g, d;
+    float scale;       // softmax scale
+    float scale_log2;  // scale * log2(e)
+    // response block: rows are response positions [q_start, q_start + n_rows)
+    const void* q;
+    const void* k_resp;
+    const void* v_resp;
+    int64_t n_rows;
+    int64_t q_start;
+    int64_t key_end;  // q_start + n_rows: response keys [0, key_end) are visible at most
+    // parts: shard s = logical pages [shard_lo[s], shard_lo[s+1]); part n_shards = response
+    int n_shards;
+    int n_parts;
+    int64_t shard_lo[kMaxShards + 1];
+    // forward products
+    float* o_parts;    // [n_parts, n_rows, hq, d]
+    float* lse_parts;  // [n_parts, n_rows, hq]
+    // backward
+    const void* o;
+    const void* dout;
+    const float* lse;    // [n_rows, hq]
+    const float* delta;  // [n_rows, hq]
+    float* dq_parts;     // [n_parts, n_rows, hq, d]
+    float* dk_pages;
+    float* dv_pages;
+    uint64_t first_touch_mask;  // bit s: shard s's gradient pages are written, not added to
+    float* dk_resp;
+    float* dv_resp;
+    int resp_first_touch;
+};
+
+// Rows of one kv head's group are numbered r = token * g + j (query head kv * g + j).
+// Key-range helpers shared by host launch code.
+inline int64_t resp_tiles(int64_t key_end) { return (key_end + 63) / 64; }
+
+// capture.hip
+hipError_t launch_capture(const void* k_src, const void* v_src, int src_dtype, int64_t n_tok,
+                          int64_t first_tok, const int32_t* table, void* k_pages, void* v_pages,
+                          int page_dtype, int64_t n_phys, int hkv, int d, hipStream_t s);
+hipError_t launch_gather(const void* pages, int dtype, const int32_t* table, int64_t n_phys,
+                         int64_t first_tok, int64_t n_tok, int hkv, int d, void* dst,
+                         hipStream_t s);
+
+// reduce.hip
+hipError_t launch_lse_merge(int n_parts, int64_t n_rows, int d, const float* o_parts,
+                            const float* lse_parts, void* o_out, int out_dtype, float* lse_out,
+                            hipStream_t s);
+hipError_t launch_delta(const void* o, const void* dout, int dtype, int64_t n_rows, int d,
+                        float* delta, hipStream_t s);
+hipError_t launch_sum_parts(int n_parts, int64_t n, const float* parts, float* out,
+                            hipStream_t s);
+hipError_t launch_zero(float* p, int64_t n, hipStream_t s);
+
+// attn_generic.hip: LDS-tiled kernels on the vector ALUs (exact f32 path)
+hipError_t launch_fwd_generic(int dtype, const AttnArgs& a, hipStream_t s);
+hipError_t launch_bwd_generic(int dtype, const AttnArgs& a, hipStream_t s);
+
+// attn_mfma_fwd.hip / attn_mfma_bwd.hip: bf16 matrix-core kernels
+hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t s);
+hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t s);
+
+}  // namespace ls

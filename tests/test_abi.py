@@ -1,0 +1,139 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the header
+declares, and rejects bad arguments with the documented code before launching anything."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from suffix_attention_amd import _lib
+from suffix_attention_amd._lib import (LS_DTYPE_BF16, LS_DTYPE_F32, LS_ERR_INVALID, LS_ERR_UNSUPPORTED,
+                                       LS_ERR_WORKSPACE, ls_prefix_t)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "longstraw.h")
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ls_[a-z_]+)\s*\(", text)))
+
+
+def test_header_functions_exported():
+    names = declared_functions()
+    assert {"ls_capture_pages", "ls_replay_fwd", "ls_replay_bwd", "ls_lse_merge"} <= set(names)
+    lib = _lib.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib._SIG), "binding signatures and header disagree"
+
+
+def test_version():
+    assert _lib.lib().ls_version() == 100
+
+
+def _prefix(**kw):
+    b = (C.c_int64 * 3)(0, 1, 2)
+    p = ls_prefix_t()
+    p.hq, p.hkv, p.d, p.page_size, p.dtype, p.n_shards = 8, 2, 256, 64, LS_DTYPE_BF16, 2
+    p.prefix_len, p.n_phys_pages = 128, 2
+    p.page_table = p.k_pages = p.v_pages = FAKE
+    p.shard_page_bounds = C.cast(b, C.POINTER(C.c_int64))
+    p.softmax_scale = 0.0625
+    for k, v in kw.items():
+        if k == "bounds":
+            b = (C.c_int64 * len(v))(*v)
+            p.shard_page_bounds = C.cast(b, C.POINTER(C.c_int64))
+        else:
+            setattr(p, k, v)
+    p._keep = b
+    return p
+
+
+def _fwd(p, n_rows=16, q_start=0, n_resp=16, ws_bytes=1 << 30, ws=FAKE, q=FAKE, o=FAKE, lse=FAKE):
+    lib = _lib.lib()
+    return lib.ls_replay_fwd(C.byref(p), q, n_rows, q_start, FAKE, FAKE, n_resp, o, lse, ws, ws_bytes, None)
+
+
+def _err():
+    return _lib.lib().ls_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(hq=7), LS_ERR_INVALID, "multiple of hkv"),
+    (dict(d=96), LS_ERR_UNSUPPORTED, "head dim"),
+    (dict(page_size=32), LS_ERR_UNSUPPORTED, "page_size"),
+    (dict(dtype=5), LS_ERR_UNSUPPORTED, "dtype"),
+    (dict(n_shards=0), LS_ERR_INVALID, "n_shards"),
+    (dict(n_shards=65), LS_ERR_INVALID, "n_shards"),
+    (dict(bounds=[0, 1, 3]), LS_ERR_INVALID, "shard bounds"),
+    (dict(n_shards=3, bounds=[0, 2, 1, 2]), LS_ERR_INVALID, "decrease"),
+    (dict(page_table=None), LS_ERR_INVALID, "non-NULL"),
+    (dict(prefix_len=-1), LS_ERR_INVALID, "prefix_len"),
+    (dict(softmax_scale=float("nan")), LS_ERR_INVALID, "softmax_scale"),
+])
+def test_fwd_rejects_bad_prefix(kw, code, msg):
+    assert _fwd(_prefix(**kw)) == code
+    assert msg in _err()
+
+
+def test_fwd_rejects_bad_block():
+    p = _prefix()
+    assert _fwd(p, n_rows=16, q_start=8, n_resp=20) == LS_ERR_INVALID
+    assert "n_resp_keys" in _err()
+    assert _fwd(p, n_rows=-1) == LS_ERR_INVALID
+    assert _fwd(p, q=None) == LS_ERR_INVALID
+    assert _fwd(p, o=None) == LS_ERR_INVALID
+
+
+def test_workspace_size_and_errors():
+    p = _prefix()
+    lib = _lib.lib()
+    need = lib.ls_fwd_workspace_bytes(C.byref(p), 16)
+    assert need == 4 * 3 * 16 * 8 * 257
+    assert _fwd(p, ws_bytes=need - 1) == LS_ERR_WORKSPACE
+    assert _fwd(p, ws=None) == LS_ERR_WORKSPACE
+    nb = lib.ls_bwd_workspace_bytes(C.byref(p), 16)
+    assert nb == 4 * (16 * 8 + 3 * 16 * 8 * 256)
+    assert lib.ls_fwd_workspace_bytes(C.byref(_prefix(hq=7)), 16) == 0
+    assert "multiple" in _err()
+
+
+def test_empty_block_is_a_no_op():
+    assert _fwd(_prefix(), n_rows=0, n_resp=0, ws=None, ws_bytes=0) == 0
+
+
+def test_bwd_rejects_missing_gradients():
+    p = _prefix()
+    lib = _lib.lib()
+    rc = lib.ls_replay_bwd(C.byref(p), FAKE, 16, 0, FAKE, FAKE, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
+                           None, FAKE, None, FAKE, 1 << 30, None)
+    assert rc == LS_ERR_INVALID and "dk_pages" in _err()
+    rc = lib.ls_replay_bwd(C.byref(p), FAKE, 16, 0, FAKE, FAKE, 16, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1,
+                           FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert rc == LS_ERR_INVALID and "dk_resp" in _err()
+    rc = lib.ls_replay_bwd(C.byref(p), FAKE, 16, 0, FAKE, FAKE, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
+                           FAKE, FAKE, None, FAKE, 100, None)
+    assert rc == LS_ERR_WORKSPACE
+
+
+def test_capture_and_merge_validation():
+    lib = _lib.lib()
+    # misaligned chunk start
+    assert lib.ls_capture_pages(FAKE, FAKE, LS_DTYPE_BF16, 10, 5, FAKE, 4, FAKE, FAKE, LS_DTYPE_BF16, 4, 2, 256,
+                                64, None) == LS_ERR_INVALID
+    # bf16 -> f32 is not a supported capture
+    assert lib.ls_capture_pages(FAKE, FAKE, LS_DTYPE_BF16, 10, 0, FAKE, 4, FAKE, FAKE, LS_DTYPE_F32, 4, 2, 256,
+                                64, None) == LS_ERR_UNSUPPORTED
+    # tokens past the table
+    assert lib.ls_capture_pages(FAKE, FAKE, LS_DTYPE_BF16, 300, 0, FAKE, 4, FAKE, FAKE, LS_DTYPE_BF16, 4, 2, 256,
+                                64, None) == LS_ERR_INVALID
+    assert lib.ls_capture_pages(FAKE, FAKE, LS_DTYPE_BF16, 0, 0, None, 0, None, None, LS_DTYPE_BF16, 0, 2, 256,
+                                64, None) == 0
+    assert lib.ls_lse_merge(0, 10, 256, FAKE, FAKE, FAKE, LS_DTYPE_F32, FAKE, None) == LS_ERR_INVALID
+    assert lib.ls_lse_merge(2, 10, 6, FAKE, FAKE, FAKE, LS_DTYPE_F32, FAKE, None) == LS_ERR_UNSUPPORTED
+    assert lib.ls_lse_merge(2, 10, 256, None, FAKE, FAKE, LS_DTYPE_F32, FAKE, None) == LS_ERR_INVALID
+    assert lib.ls_gather_pages(FAKE, 7, FAKE, 4, 4, 0, 10, 2, 256, 64, FAKE, None) == LS_ERR_UNSUPPORTED
