@@ -132,9 +132,11 @@ int ls_gather_pages(const void* pages, int dtype, const int32_t* page_table,
  *   o_parts   [n_parts, n_rows, hq, d]   part p < n_shards: shard p; last: response keys
  *   lse_parts [n_parts, n_rows, hq]      -inf where a part has no key (O part = 0 there)
  * so that callers may inspect each owner's local result.
- * Backward workspace layout (float32, from offset 0):
- *   delta     [n_rows, hq]              rowsum(dO * O) of the O passed in
- *   dq_parts  [n_parts, n_rows, hq, d]
+ * Backward workspace layout (from offset 0):
+ *   delta     float32 [n_rows, hq], padded to a multiple of 64 elements: rowsum(dO * O)
+ *   dq_parts  float32 [n_parts, n_rows, hq, d]
+ *   then, for bf16, (LSE * log2 e, delta) pairs per kv head and query row of its group,
+ *   padded to a multiple of 64 rows.
  */
 size_t ls_fwd_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows);
 size_t ls_bwd_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows);

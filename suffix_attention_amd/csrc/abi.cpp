@@ -122,7 +122,8 @@ size_t fwd_ws(const ls_prefix_t* p, int64_t n_rows) {
 }
 
 size_t bwd_ws(const ls_prefix_t* p, int64_t n_rows) {
-    return sizeof(float) * ((size_t)n_rows * p->hq + (size_t)(p->n_shards + 1) * n_rows * p->hq * p->d);
+    return sizeof(float) * ((size_t)ls::bwd_delta_elems(n_rows, p->hq) + (size_t)(p->n_shards + 1) * n_rows * p->hq * p->d) +
+           ls::mfma_bwd_extra_bytes(n_rows, p->hq / p->hkv, p->hkv);
 }
 
 }  // namespace
@@ -242,7 +243,7 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
     a.dout = dout;
     a.lse = lse;
     a.delta = (float*)workspace;
-    a.dq_parts = (float*)workspace + rows;
+    a.dq_parts = (float*)workspace + ls::bwd_delta_elems(n_rows, pre->hq);
     a.dk_pages = dk_pages;
     a.dv_pages = dv_pages;
     a.dk_resp = dk_resp;
@@ -253,10 +254,13 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
         for (int s = 0; s < pre->n_shards; s++)
             if (shard_first_touch[s]) a.first_touch_mask |= 1ull << s;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = ls::launch_delta(o, dout, pre->dtype, rows, pre->d, (float*)a.delta, s);
-    if (e != hipSuccess) return hip_fail(e, "delta kernel");
-    e = (pre->dtype == LS_DTYPE_BF16 && !force_generic()) ? ls::launch_bwd_mfma(a, s)
-                                                          : ls::launch_bwd_generic(pre->dtype, a, s);
+    hipError_t e;
+    if (pre->dtype == LS_DTYPE_BF16 && !force_generic()) {
+        e = ls::launch_bwd_mfma(a, s);  // its prep kernel also writes delta
+    } else {
+        e = ls::launch_delta(o, dout, pre->dtype, rows, pre->d, (float*)a.delta, s);
+        if (e == hipSuccess) e = ls::launch_bwd_generic(pre->dtype, a, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "backward kernels");
     e = ls::launch_sum_parts(a.n_parts, rows * pre->d, a.dq_parts, dq, s);
     if (e != hipSuccess) return hip_fail(e, "dQ part sum kernel");

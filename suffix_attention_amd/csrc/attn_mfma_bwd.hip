@@ -1,9 +1,542 @@
-// Replay-attention backward on gfx950 bf16 matrix cores (placeholder: generic kernels).
-#include "common.hpp"
-#include "launch.hpp"
+// Replay-attention backward on gfx950 bf16 matrix cores, for the loss sum(O * dO).
+//
+// P is recomputed from the forward's LSE, so the backward runs as two passes over the same
+// keys (a dQ row sum over 2M keys cannot be gathered by a key-stationary kernel):
+//
+//  dq_mfma_kernel   (query tile, part, kv head), like the forward: per 64-key page,
+//                   S^T = K Q^T and dP^T = V dO^T (Q, dO in VGPRs, K, V from LDS),
+//                   dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T (K read transposed).
+//                   Writes one dQ part per key part; the parts are summed afterwards.
+//  dkdv_mfma_kernel (two pages, kv head): each wave keeps 32 keys of K and V in VGPRs and
+//                   their dK, dV accumulators in AGPRs, and streams every query row of the
+//                   group that sees them through LDS, 32 rows at a time:
+//                   S = Q K^T, dP = dO V^T, P, dS = P (dP - delta),
+//                   dV += P^T dO, dK += dS^T Q (dO, Q read transposed).
+//                   The result is written to the gradient pages (first touch) or added to
+//                   them; each element has exactly one writer, so no atomics are needed.
+//
+// A prep kernel first writes, per kv head and group row r = token * g + j,
+// (LSE * log2 e, delta = rowsum(dO * O)); rows padded up to a multiple of 64 get
+// (+inf, 0), so their P is exactly 0 wherever they are read.
+#include <math.h>
+
+#include "mfma_tiles.hpp"
 
 namespace ls {
+namespace {
 
-hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t s) { return launch_bwd_generic(1, a, s); }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kRowPad = 64;
+inline int64_t rows_padded(int64_t rows) { return (rows + kRowPad - 1) / kRowPad * kRowPad; }
+
+// ---------------------------------------------------------------------------------------
+// prep: delta and log2-scaled LSE per group row; also delta in [n_rows, hq] order
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(AttnArgs a, int64_t rows_pad, f32x2* __restrict__ lsed,
+                                                       float* __restrict__ delta_th) {
+    const int64_t gw = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // one wave per (kvh, r)
+    const int lane = threadIdx.x % 64;
+    const int64_t rows_total = a.n_rows * a.g;
+    if (gw >= rows_pad * a.hkv) return;
+    const int kvh = (int)(gw / rows_pad);
+    const int64_t r = gw % rows_pad;
+    if (r >= rows_total) {
+        if (lane == 0) lsed[gw] = f32x2{INFINITY, 0.f};
+        return;
+    }
+    const int64_t th = (r / a.g) * a.hq + kvh * a.g + r % a.g;
+    const bf16_t* o = (const bf16_t*)a.o + th * D;
+    const bf16_t* dout = (const bf16_t*)a.dout + th * D;
+    float s = 0.f;
+    for (int k = lane * 4; k < D; k += 256) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) s += bf16_to_f32(o[k + e]) * bf16_to_f32(dout[k + e]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (lane == 0) {
+        lsed[gw] = f32x2{a.lse[th] * kLog2e, s};
+        delta_th[th] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// dQ pass
+// ---------------------------------------------------------------------------------------
+template <int D>
+struct DqState {
+    bf16x8 qb[TileShape<D>::KS];    // Q^T operand (row lane%32)
+    bf16x8 dob[TileShape<D>::KS];   // dO^T operand
+    f32x16 dq[TileShape<D>::DT];    // dQ^T accumulators: col = row, rows = d
+    float lse2;                     // LSE * log2 e of this lane's row
+    float dlt;                      // delta of this lane's row
+};
+
+template <int D>
+__device__ __forceinline__ void dq_tile(DqState<D>& st, const LS_LDS char* lds_k, const LS_LDS char* lds_v,
+                                        LaneAddr<D> la, const TileSrc& src, bool resp, bool need_mask,
+                                        int64_t vis_limit, float scale_log2, int lane) {
+    using F = TileShape<D>;
+    const int h = lane >> 5;
+    asm volatile("" : "+v"(la.k), "+v"(la.v));
+    f32x16 s[2], dp[2];
+    s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < F::KS; ks++) {
+        const uint32_t o = la.k ^ (uint32_t)(ks << 5);
+        const bf16x8 k0 = *(const LS_LDS bf16x8*)(lds_k + o);
+        const bf16x8 k1 = *(const LS_LDS bf16x8*)(lds_k + o + 32 * 2 * D);
+        const bf16x8 v0 = *(const LS_LDS bf16x8*)(lds_v + o);
+        const bf16x8 v1 = *(const LS_LDS bf16x8*)(lds_v + o + 32 * 2 * D);
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, st.qb[ks], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, st.qb[ks], s[1], 0, 0, 0);
+        dp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, st.dob[ks], dp[0], 0, 0, 0);
+        dp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, st.dob[ks], dp[1], 0, 0, 0);
+    }
+    int lim_valid = src.valid - 4 * h;
+    int lim_causal = 64;
+    if (resp) {
+        const int64_t c = vis_limit - src.key0 - 4 * h;
+        lim_causal = c < -1 ? -1 : (c > 64 ? 64 : (int)c);
+    }
+    bf16x8 db[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++) {
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            uint32_t w4[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                float d2[2];
+#pragma unroll
+                for (int e = 0; e < 2; e++) {
+                    const int i = 8 * u + 2 * t + e;
+                    float p = fast_exp2(s[kt][i] * scale_log2 - st.lse2);
+                    if (need_mask) {
+                        const int kc = 32 * kt + 8 * (i >> 2) + (i & 3);
+                        p = (kc < lim_valid && kc <= lim_causal) ? p : 0.f;
+                    }
+                    d2[e] = p * (dp[kt][i] - st.dlt);
+                }
+                w4[t] = pack_bf16x2(d2[0], d2[1]);
+            }
+            db[kt][u] = __builtin_bit_cast(bf16x8, (u32x4{w4[0], w4[1], w4[2], w4[3]}));
+        }
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int dt = 0; dt < F::DT; dt++) {
+        const uint32_t x0 = la.v ^ (uint32_t)(((4 * dt) ^ (0 & F::SWZ)) << 4);
+        const uint32_t x1 = la.v ^ (uint32_t)(((4 * dt) ^ (8 & F::SWZ)) << 4);
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++) {
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                const int row = 32 * kt + 16 * u;
+                const i16x4 lo = lds_read_tr4(lds_k + x0 + row * 2 * D);
+                const i16x4 hi = lds_read_tr4(lds_k + x1 + (row + 8) * 2 * D);
+                const bf16x8 ka = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                st.dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, db[kt][u], st.dq[dt], 0, 0, 0);
+            }
+        }
+    }
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void dq_step(DqState<D>& st, const char* __restrict__ cur, char* __restrict__ nxt,
+                                        bool has_next, const TileSrc& next_src, const TileSrc& src, LaneAddr<D> la,
+                                        bool resp, bool need_mask, int64_t vis_limit, float scale_log2, int w,
+                                        int lane) {
+    using F = TileShape<D>;
+    if (has_next) issue_tile<D, NW>(next_src, nxt, nxt + F::TILE, w, lane);
+    dq_tile<D>(st, (const LS_LDS char*)cur, (const LS_LDS char*)(cur + F::TILE), la, src, resp, need_mask,
+               vis_limit, scale_log2, lane);
+}
+
+template <int D, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(1, 1)))
+void dq_mfma_kernel(AttnArgs a, const f32x2* __restrict__ lsed, int64_t rows_pad, int n_qtiles, int n_blocks) {
+    using F = TileShape<D>;
+    constexpr int BM = 32 * NW;
+    __shared__ __attribute__((aligned(1024))) char st0[2 * F::TILE];
+    __shared__ __attribute__((aligned(1024))) char st1[2 * F::TILE];
+
+    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    if (lb >= n_blocks) return;
+    const int qtile = lb % n_qtiles;
+    const int part = (lb / n_qtiles) % a.n_parts;
+    const int kvh = lb / (n_qtiles * a.n_parts);
+    const bool resp = part == a.n_shards;
+
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5;
+    const int n = lane & 31;
+    const int64_t rows_total = a.n_rows * a.g;
+    const int64_t r0 = (int64_t)qtile * BM;
+    const int64_t my_row = r0 + 32 * w + n;
+    const bool row_ok = my_row < rows_total;
+    const int64_t my_tok = my_row / a.g;
+    const int my_head = kvh * a.g + (int)(my_row % a.g);
+
+    DqState<D> st;
+    {
+        const int64_t ld_row = row_ok ? my_row : rows_total - 1;
+        const int64_t th = (ld_row / a.g) * a.hq + kvh * a.g + ld_row % a.g;
+        const bf16_t* qrow = (const bf16_t*)a.q + th * (int64_t)D + 8 * h;
+        const bf16_t* drow = (const bf16_t*)a.dout + th * (int64_t)D + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < F::KS; ks++) {
+            st.qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * ks));
+            st.dob[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(drow + 16 * ks));
+        }
+#pragma unroll
+        for (int dt = 0; dt < F::DT; dt++) st.dq[dt] = f32x16{};
+        const f32x2 ld = lsed[kvh * rows_pad + (row_ok ? my_row : rows_total - 1)];
+        st.lse2 = ld[0];
+        st.dlt = ld[1];
+    }
+    const LaneAddr<D> la(lane);
+    int64_t n_tiles;
+    const int64_t tok_min = r0 / a.g;
+    if (!resp) {
+        n_tiles = a.shard_lo[part + 1] - a.shard_lo[part];
+    } else {
+        int64_t tok_max = (r0 + BM - 1) / a.g;
+        if (tok_max > a.n_rows - 1) tok_max = a.n_rows - 1;
+        n_tiles = (a.q_start + tok_max + 1 + kPage - 1) / kPage;
+    }
+    const int64_t vis_limit = a.q_start + my_tok;
+
+    int32_t phys_cur = (!resp && n_tiles > 0) ? phys_page(a, part, 0) : 0;
+    int32_t phys_next = (!resp && n_tiles > 1) ? phys_page(a, part, 1) : 0;
+    TileSrc src = part_tile(a, resp, part, kvh, 0, __builtin_amdgcn_readfirstlane(phys_cur));
+    if (n_tiles > 0) issue_tile<D, NW>(src, st0, st0 + F::TILE, w, lane);
+    for (int64_t t = 0; t < n_tiles; t++) {
+        wait_vm_all();
+        __syncthreads();
+        const bool has_next = t + 1 < n_tiles;
+        const TileSrc next_src =
+            part_tile(a, resp, part, kvh, has_next ? t + 1 : t, __builtin_amdgcn_readfirstlane(phys_next));
+        if (!resp && t + 2 < n_tiles) phys_next = phys_page(a, part, t + 2);
+        const bool need_mask = src.valid < kPage || (resp && src.key0 + kPage - 1 > a.q_start + tok_min);
+        char* cur = (t & 1) ? st1 : st0;
+        char* nxt = (t & 1) ? st0 : st1;
+        dq_step<D, NW>(st, cur, nxt, has_next, next_src, src, la, resp, need_mask, vis_limit, a.scale_log2, w,
+                       lane);
+        src = next_src;
+    }
+    if (!row_ok) return;
+    float* dst = a.dq_parts + (((int64_t)part * a.n_rows + my_tok) * a.hq + my_head) * (int64_t)D;
+#pragma unroll
+    for (int dt = 0; dt < F::DT; dt++) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+            const int dd = dt * 32 + 8 * q4 + 4 * h;
+            *(float4*)(dst + dd) = make_float4(a.scale * st.dq[dt][4 * q4], a.scale * st.dq[dt][4 * q4 + 1],
+                                               a.scale * st.dq[dt][4 * q4 + 2], a.scale * st.dq[dt][4 * q4 + 3]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// dK/dV pass
+// ---------------------------------------------------------------------------------------
+constexpr int kRows = 32;  // query rows per LDS stage
+
+template <int D>
+struct RowStage {
+    static constexpr int QBYTES = kRows * D * 2;            // one Q or dO row tile
+    static constexpr int BYTES = 2 * QBYTES + kRows * 8;    // Q, dO, (lse2, delta) per row
+};
+
+// Copy group rows [r0, r0 + 32) of Q and dO (rows past the block repeat the last row; their
+// LSE is +inf so they contribute nothing) and their (lse2, delta) into an LDS stage.
+template <int D>
+__device__ __forceinline__ void issue_rows(const AttnArgs& a, const f32x2* lsed_kvh, int kvh, int64_t r0,
+                                           int64_t rows_total, char* stage, int w, int lane) {
+    using F = TileShape<D>;
+    constexpr int RPK = 512 / D;                     // rows per 1 KiB block
+    constexpr int BLOCKS = RowStage<D>::QBYTES / 1024;
+    constexpr int PER_WAVE = BLOCKS / 4;
+    const int low = lane / F::KCH;
+    const int pc = lane % F::KCH;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; j++) {
+        const int blk = j * 4 + w;
+        const int r = blk * RPK + low;
+        int64_t gr = r0 + r;
+        if (gr >= rows_total) gr = rows_total - 1;
+        const int lc = pc ^ (r & F::SWZ);
+        const int64_t th = (gr / a.g) * a.hq + kvh * a.g + gr % a.g;
+        const int64_t e = th * D + lc * 8;
+        dma16((const bf16_t*)a.q + e, (LS_LDS void*)(stage + blk * 1024));
+        dma16((const bf16_t*)a.dout + e, (LS_LDS void*)(stage + RowStage<D>::QBYTES + blk * 1024));
+    }
+    if (w == 0 && lane < kRows * 8 / 16)
+        dma16((const char*)(lsed_kvh + r0) + lane * 16, (LS_LDS void*)(stage + 2 * RowStage<D>::QBYTES));
+}
+
+template <int D>
+struct DkvState {
+    bf16x8 kb[TileShape<D>::KS];   // K^T operand: key lane%32, d = 16ks + 8(lane/32) .. +8
+    bf16x8 vb[TileShape<D>::KS];   // V^T operand
+    f32x16 dk[TileShape<D>::DT];   // dK accumulators: col = d, rows = keys
+    f32x16 dv[TileShape<D>::DT];
+};
+
+template <int D>
+__device__ __forceinline__ void dkdv_rows(DkvState<D>& st, const LS_LDS char* stage, LaneAddr<D> la,
+                                          bool need_mask, int rmin, float scale_log2, int lane) {
+    using F = TileShape<D>;
+    const int h = lane >> 5;
+    asm volatile("" : "+v"(la.k), "+v"(la.v));
+    const LS_LDS char* lq = stage;
+    const LS_LDS char* ldo = stage + RowStage<D>::QBYTES;
+    const LS_LDS f32x2* lsd = (const LS_LDS f32x2*)(stage + 2 * RowStage<D>::QBYTES);
+    // S = Q K^T, dP = dO V^T for 32 rows x 32 keys
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < F::KS; ks++) {
+        const uint32_t o = la.k ^ (uint32_t)(ks << 5);
+        const bf16x8 qa = *(const LS_LDS bf16x8*)(lq + o);
+        const bf16x8 da = *(const LS_LDS bf16x8*)(ldo + o);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, st.kb[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, st.vb[ks], dp, 0, 0, 0);
+    }
+    // element i is row 8(i/4) + 4h + i%4 of the stage, key lane%32
+    const int rmh = rmin - 4 * h;  // rows (without the 4h of this half) that precede the key
+    bf16x8 pa[2], sa[2];
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        uint32_t wp[4], wd[4];
+#pragma unroll
+        for (int hb = 0; hb < 2; hb++) {
+            const int rbase = 16 * u + 8 * hb + 4 * h;
+            const f32x4 l01 = *(const LS_LDS f32x4*)(lsd + rbase);       // rows rbase, rbase+1
+            const f32x4 l23 = *(const LS_LDS f32x4*)(lsd + rbase + 2);   // rows rbase+2, rbase+3
+            float pv[4], dv[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const float l2 = j < 2 ? l01[2 * j] : l23[2 * (j - 2)];
+                const float dl = j < 2 ? l01[2 * j + 1] : l23[2 * (j - 2) + 1];
+                const int i = 8 * u + 4 * hb + j;
+                float p = fast_exp2(s[i] * scale_log2 - l2);
+                if (need_mask) p = (16 * u + 8 * hb + j) >= rmh ? p : 0.f;
+                pv[j] = p;
+                dv[j] = p * (dp[i] - dl);
+            }
+            wp[2 * hb] = pack_bf16x2(pv[0], pv[1]);
+            wp[2 * hb + 1] = pack_bf16x2(pv[2], pv[3]);
+            wd[2 * hb] = pack_bf16x2(dv[0], dv[1]);
+            wd[2 * hb + 1] = pack_bf16x2(dv[2], dv[3]);
+        }
+        pa[u] = __builtin_bit_cast(bf16x8, (u32x4{wp[0], wp[1], wp[2], wp[3]}));
+        sa[u] = __builtin_bit_cast(bf16x8, (u32x4{wd[0], wd[1], wd[2], wd[3]}));
+    }
+    // dV += P^T dO, dK += dS^T Q   (dO, Q read transposed: rows are the contraction)
+#pragma unroll
+    for (int dt = 0; dt < F::DT; dt++) {
+        const uint32_t x0 = la.v ^ (uint32_t)(((4 * dt) ^ (0 & F::SWZ)) << 4);
+        const uint32_t x1 = la.v ^ (uint32_t)(((4 * dt) ^ (8 & F::SWZ)) << 4);
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int row = 16 * u;
+            const i16x4 dlo = lds_read_tr4(ldo + x0 + row * 2 * D);
+            const i16x4 dhi = lds_read_tr4(ldo + x1 + (row + 8) * 2 * D);
+            const i16x4 qlo = lds_read_tr4(lq + x0 + row * 2 * D);
+            const i16x4 qhi = lds_read_tr4(lq + x1 + (row + 8) * 2 * D);
+            const bf16x8 dob = __builtin_bit_cast(bf16x8, __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7));
+            const bf16x8 qbt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+            st.dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[u], dob, st.dv[dt], 0, 0, 0);
+            st.dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[u], qbt, st.dk[dt], 0, 0, 0);
+        }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void dkdv_step(DkvState<D>& st, const char* __restrict__ cur, char* __restrict__ nxt,
+                                          bool has_next, const AttnArgs& a, const f32x2* lsed_kvh, int kvh,
+                                          int64_t next_r0, int64_t rows_total, LaneAddr<D> la, bool need_mask,
+                                          int rmin, int w, int lane) {
+    if (has_next) issue_rows<D>(a, lsed_kvh, kvh, next_r0, rows_total, nxt, w, lane);
+    dkdv_rows<D>(st, (const LS_LDS char*)cur, la, need_mask, rmin, a.scale_log2, lane);
+}
+
+// One workgroup: 4 waves over two consecutive 64-key pages (wave w: page w/2, keys
+// 32 (w%2) .. +32).  Blocks [0, n_pp) are prompt page pairs, the rest response pairs.
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void dkdv_mfma_kernel(AttnArgs a, const f32x2* __restrict__ lsed, int64_t rows_pad, int n_pp, int n_rp,
+                      int n_blocks) {
+    using F = TileShape<D>;
+    __shared__ __attribute__((aligned(1024))) char st0[RowStage<D>::BYTES];
+    __shared__ __attribute__((aligned(1024))) char st1[RowStage<D>::BYTES];
+
+    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    if (lb >= n_blocks) return;
+    const int per_kvh = n_pp + n_rp;
+    const int kvh = lb / per_kvh;
+    const int pair = lb % per_kvh;
+    const bool resp = pair >= n_pp;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5;
+    const int n = lane & 31;
+    const int64_t rows_total = a.n_rows * a.g;
+    const f32x2* lsed_kvh = lsed + kvh * rows_pad;
+
+    // ---- this wave's 32 keys
+    const int64_t page = 2 * (int64_t)(resp ? pair - n_pp : pair) + (w >> 1);  // logical or response page
+    const int64_t n_pages_here = resp ? (a.key_end + kPage - 1) / kPage : a.n_logical_pages;
+    const bool page_ok = page < n_pages_here;
+    const int64_t src_page = page_ok ? page : page - 1;  // an existing page to read (never written)
+    const int kh = w & 1;
+    int32_t phys = 0;
+    int valid;
+    const bf16_t *ksrc, *vsrc;
+    int64_t stride;
+    if (!resp) {
+        phys = a.table[src_page];
+        phys = phys < 0 ? 0 : (phys >= a.n_phys ? (int32_t)(a.n_phys - 1) : phys);
+        const int64_t off = ((int64_t)phys * a.hkv + kvh) * kPage * D;
+        ksrc = (const bf16_t*)a.k_pages + off;
+        vsrc = (const bf16_t*)a.v_pages + off;
+        stride = D;
+        const int64_t left = a.prefix_len - src_page * kPage;
+        valid = left < kPage ? (int)left : kPage;
+    } else {
+        const int64_t off = (src_page * kPage * a.hkv + kvh) * D;
+        ksrc = (const bf16_t*)a.k_resp + off;
+        vsrc = (const bf16_t*)a.v_resp + off;
+        stride = (int64_t)a.hkv * D;
+        const int64_t left = a.key_end - src_page * kPage;
+        valid = left < kPage ? (int)left : kPage;
+    }
+    DkvState<D> st;
+    {
+        int kr = 32 * kh + n;
+        if (kr >= valid) kr = valid - 1;  // keys past the end: any finite row, never written
+        const bf16_t* krow = ksrc + kr * stride + 8 * h;
+        const bf16_t* vrow = vsrc + kr * stride + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < F::KS; ks++) {
+            st.kb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(krow + 16 * ks));
+            st.vb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(vrow + 16 * ks));
+        }
+#pragma unroll
+        for (int dt = 0; dt < F::DT; dt++) st.dk[dt] = st.dv[dt] = f32x16{};
+    }
+
+    // ---- rows that see these keys: all rows for the prompt; for response keys the rows
+    // whose token is at least (first key of the pair) - q_start
+    const int64_t key0_pair = 2 * (int64_t)(resp ? pair - n_pp : pair) * kPage;
+    int64_t r_begin = 0;
+    if (resp && key0_pair > a.q_start) r_begin = (key0_pair - a.q_start) * a.g / kRows * kRows;
+    const int64_t n_stages = rows_total > r_begin ? (rows_total - r_begin + kRows - 1) / kRows : 0;
+    // causal limit of this lane's key: visible to group rows >= (key - q_start) * g
+    const int64_t my_key = page * kPage + 32 * kh + n;
+    const int64_t row_min = resp ? (my_key - a.q_start) * a.g : 0;
+
+    const LaneAddr<D> la(lane);
+    if (n_stages > 0) issue_rows<D>(a, lsed_kvh, kvh, r_begin, rows_total, st0, w, lane);
+    for (int64_t t = 0; t < n_stages; t++) {
+        wait_vm_all();
+        __syncthreads();
+        const int64_t r0 = r_begin + t * kRows;
+        const bool has_next = t + 1 < n_stages;
+        // this stage needs the causal mask if some row in it precedes some key of the pair
+        const bool need_mask = resp && r0 < (key0_pair + 2 * kPage - 1 - a.q_start) * a.g;
+        int64_t rm = row_min - r0;
+        const int rmin = rm < 0 ? 0 : (rm > kRows ? kRows : (int)rm);
+        char* cur = (t & 1) ? st1 : st0;
+        char* nxt = (t & 1) ? st0 : st1;
+        dkdv_step<D>(st, cur, nxt, has_next, a, lsed_kvh, kvh, r0 + kRows, rows_total, la, need_mask, rmin, w, lane);
+    }
+
+    // ---- write this wave's keys: dK (scaled) and dV, element i is key 8(i/4) + 4h + i%4
+    if (!page_ok) return;
+    bool first;
+    float *gk, *gv;
+    int64_t key_stride;
+    if (!resp) {
+        int s = 0;
+        while (s + 1 < a.n_shards && page >= a.shard_lo[s + 1]) s++;
+        first = (a.first_touch_mask >> s) & 1ull;
+        const int64_t off = ((int64_t)phys * a.hkv + kvh) * kPage * D;
+        gk = a.dk_pages + off;
+        gv = a.dv_pages + off;
+        key_stride = D;
+    } else {
+        first = a.resp_first_touch != 0;
+        const int64_t off = (page * kPage * a.hkv + kvh) * D;
+        gk = a.dk_resp + off;
+        gv = a.dv_resp + off;
+        key_stride = (int64_t)a.hkv * D;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const int kr = 32 * kh + 8 * (i >> 2) + 4 * h + (i & 3);  // key row within the page
+        const bool key_ok = kr < valid;
+        if (!key_ok && (resp || !first)) continue;  // response keys past the block / kept padding
+        float* pk = gk + kr * key_stride + n;
+        float* pv = gv + kr * key_stride + n;
+#pragma unroll
+        for (int dt = 0; dt < F::DT; dt++) {
+            const float vk = key_ok ? a.scale * st.dk[dt][i] : 0.f;
+            const float vv = key_ok ? st.dv[dt][i] : 0.f;
+            if (first) {
+                pk[32 * dt] = vk;
+                pv[32 * dt] = vv;
+            } else {
+                pk[32 * dt] += vk;
+                pv[32 * dt] += vv;
+            }
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_bwd_d(const AttnArgs& a, hipStream_t s) {
+    constexpr int NW = 4;
+    constexpr int BM = 32 * NW;
+    const int64_t rows_total = a.n_rows * a.g;
+    const int64_t rows_pad = rows_padded(rows_total);
+    f32x2* lsed = (f32x2*)(a.dq_parts + (int64_t)a.n_parts * a.n_rows * a.hq * D);
+    float* delta_th = const_cast<float*>(a.delta);
+    if (rows_total > 0) {
+        const int64_t waves = rows_pad * a.hkv;
+        bwd_prep_kernel<D><<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(a, rows_pad, lsed, delta_th);
+    }
+    // dK / dV
+    const int n_pp = (int)((a.n_logical_pages + 1) / 2);
+    const int n_rp = (int)((resp_tiles(a.key_end) + 1) / 2);
+    const int64_t nb_kv = (int64_t)(n_pp + n_rp) * a.hkv;
+    if (nb_kv > 0)
+        dkdv_mfma_kernel<D><<<pad_grid((int)nb_kv), 256, 0, s>>>(a, lsed, rows_pad, n_pp, n_rp, (int)nb_kv);
+    // dQ parts
+    const int64_t n_qtiles = (rows_total + BM - 1) / BM;
+    const int64_t nb_q = n_qtiles * a.n_parts * a.hkv;
+    if (nb_q > 0)
+        dq_mfma_kernel<D, NW><<<pad_grid((int)nb_q), NW * 64, 0, s>>>(a, lsed, rows_pad, (int)n_qtiles, (int)nb_q);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t mfma_bwd_extra_bytes(int64_t n_rows, int g, int hkv) {
+    return sizeof(f32x2) * (size_t)rows_padded(n_rows * g) * (size_t)hkv;
+}
+
+hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t s) {
+    switch (a.d) {
+        case 64: return launch_bwd_d<64>(a, s);
+        case 128: return launch_bwd_d<128>(a, s);
+        case 256: return launch_bwd_d<256>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 }  // namespace ls

@@ -1,0 +1,123 @@
+// Tiles of keys (prompt pages or response positions) staged in LDS for the bf16
+// matrix-core kernels, and the per-lane LDS addressing of their operands.
+//
+// A tile is 64 rows x D bf16 (one page of one kv head, or 64 consecutive response keys,
+// or 64 query rows).  In LDS, 16-byte chunk c of row r holds logical chunk c ^ (r & SWZ),
+// which spreads the 32 rows read by one MFMA operand over the banks.  Tiles are filled by
+// direct global->LDS copies (16 bytes per lane, 1 KiB per wave instruction).
+#pragma once
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ls {
+
+template <int D>
+struct TileShape {
+    static constexpr int KCH = D / 8;                        // 16-byte chunks per row
+    static constexpr int KS = D / 16;                        // k-steps of S over d
+    static constexpr int DT = D / 32;                        // 32-wide d tiles of O
+    static constexpr int SWZ = (KCH >= 16 ? 16 : KCH) - 1;   // row -> chunk xor mask
+    static constexpr int TILE = kPage * D * 2;               // bytes of one K or V page tile
+};
+
+struct TileSrc {
+    const bf16_t* k;
+    const bf16_t* v;
+    int64_t stride;  // elements between consecutive key rows
+    int valid;       // rows [0, valid) hold keys; the rest repeat the last valid row
+    int64_t key0;    // first key: logical prompt token, or response position
+};
+
+// Physical page of tile t of a prompt part (clamped so that a bad table cannot fault).
+__device__ __forceinline__ int32_t phys_page(const AttnArgs& a, int part, int64_t t) {
+    int32_t phys = a.table[a.shard_lo[part] + t];
+    return phys < 0 ? 0 : (phys >= a.n_phys ? (int32_t)(a.n_phys - 1) : phys);
+}
+
+// Source of tile t of a part; `phys` is its physical page (prompt parts only).
+__device__ __forceinline__ TileSrc part_tile(const AttnArgs& a, bool resp, int part, int kvh,
+                                             int64_t t, int32_t phys) {
+    TileSrc s;
+    if (!resp) {
+        const int64_t lp = a.shard_lo[part] + t;
+        const int64_t off = ((int64_t)phys * a.hkv + kvh) * kPage * a.d;
+        s.k = (const bf16_t*)a.k_pages + off;
+        s.v = (const bf16_t*)a.v_pages + off;
+        s.stride = a.d;
+        s.key0 = lp * kPage;
+        const int64_t left = a.prefix_len - s.key0;
+        s.valid = left < kPage ? (int)left : kPage;
+    } else {
+        s.key0 = t * kPage;
+        const int64_t off = (s.key0 * a.hkv + kvh) * a.d;
+        s.k = (const bf16_t*)a.k_resp + off;
+        s.v = (const bf16_t*)a.v_resp + off;
+        s.stride = (int64_t)a.hkv * a.d;
+        const int64_t left = a.key_end - s.key0;
+        s.valid = left < kPage ? (int)left : kPage;
+    }
+    return s;
+}
+
+// Issue the direct-to-LDS copies of one K and one V page tile (all waves together).  Wave
+// w's j-th copy fills 1 KiB block j*NW + w of the tile, i.e. RPK = 512/D whole rows; lane l
+// writes 16-byte slot l of the block, so it fetches the logical chunk that the xor swizzle
+// puts there.  `w` must be wave-uniform.
+template <int D, int NW>
+__device__ __forceinline__ void issue_tile(const TileSrc& s, char* lds_k, char* lds_v, int w,
+                                           int lane) {
+    using F = TileShape<D>;
+    constexpr int RPK = 512 / D;                 // rows per 1 KiB block
+    constexpr int PER_WAVE = F::TILE / 1024 / NW;
+    constexpr int JROWS = NW * RPK;              // rows advanced per j (a power of two)
+    const int low = w * RPK + lane / F::KCH;     // row inside the j-th group of JROWS rows
+    const int pc = lane % F::KCH;                // 16-byte slot inside the row
+    const int lane_x = pc ^ (low & F::SWZ);
+    if (s.valid == kPage) {
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; j++) {
+            const int lc = lane_x ^ ((j * JROWS) & F::SWZ);
+            const uint32_t off = (uint32_t)(low * (int)s.stride + lc * 8) * 2u;
+            const int64_t rowj = (int64_t)(j * JROWS) * s.stride * 2;
+            const char* bk = (const char*)s.k + rowj;
+            const char* bv = (const char*)s.v + rowj;
+            const int blk = j * NW + w;
+            dma16(bk + off, (LS_LDS void*)(lds_k + blk * 1024));
+            dma16(bv + off, (LS_LDS void*)(lds_v + blk * 1024));
+        }
+    } else {
+        // a partial tile: rows past `valid` repeat the last valid row (finite, masked later)
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; j++) {
+            const int r = j * JROWS + low;
+            const int lc = lane_x ^ ((j * JROWS) & F::SWZ);
+            const int rs = r < s.valid ? r : s.valid - 1;
+            const uint32_t off = (uint32_t)(rs * (int)s.stride + lc * 8) * 2u;
+            const int blk = j * NW + w;
+            dma16((const char*)s.k + off, (LS_LDS void*)(lds_k + blk * 1024));
+            dma16((const char*)s.v + off, (LS_LDS void*)(lds_v + blk * 1024));
+        }
+    }
+}
+
+// Per-lane LDS byte offsets inside a page tile.  With the xor swizzle, the address of
+// chunk `lc` of row `r` is r*2D + ((lc ^ (r & SWZ)) << 4); splitting r and lc into lane-fixed
+// and step-varying bits turns every operand read into (lane base ^ constant) + constant.
+template <int D>
+struct LaneAddr {
+    uint32_t k;  // K rows lane%32: XOR with (ks << 5) selects chunk 2ks + lane/32
+    uint32_t v;  // V^T transpose reads: XOR with ((4dt ^ (8e & SWZ)) << 4)
+    __device__ __forceinline__ LaneAddr(int lane) {
+        using F = TileShape<D>;
+        const int h = lane >> 5, n = lane & 31;
+        k = n * 2 * D + ((h ^ (n & F::SWZ)) << 4);
+        const int G = lane >> 4, i16 = lane & 15;
+        const int c_lane = 4 * (G >> 1) + (i16 >> 2);          // row within an 8-row group
+        const int l_lane = 2 * (G & 1) + ((i16 & 3) >> 1);     // chunk within a 32-wide d tile
+        const int half8 = (i16 & 1) * 8;                       // byte inside the 16-byte chunk
+        v = c_lane * 2 * D + half8 + ((l_lane ^ c_lane) << 4);
+    }
+};
+
+}  // namespace ls

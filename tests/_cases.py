@@ -126,7 +126,9 @@ class Case:
                                  self.token_bounds(), q_start)
 
 
-def check_against_oracle(case: Case, q_start: int, n_rows: int, res=None, parts=True):
+def check_against_oracle(case: Case, q_start: int, n_rows: int, res=None, parts=True, atol=None):
+    """atol: optional per-tensor max-abs bounds (for inputs scaled away from N(0, 1))."""
+    atol = atol or {}
     res = res or case.gpu(q_start, n_rows)
     # delta is formed from the O the forward returned (rounded to the input dtype), as the
     # GPU path does; the oracle takes the same O.
@@ -134,9 +136,9 @@ def check_against_oracle(case: Case, q_start: int, n_rows: int, res=None, parts=
     ref_exact = case.oracle(q_start, n_rows)
     assert_close("O", np32(res["o"]), ref_exact["o"])
     assert_close("LSE", np32(res["lse"]), ref_exact["lse"])
-    assert_close("dQ", np32(res["dq"]), ref["dq"])
+    assert_close("dQ", np32(res["dq"]), ref["dq"], atol=atol.get("dQ", ATOL))
     kend = q_start + n_rows
-    assert_close("dK_resp", np32(res["dkr"])[:kend], ref["dkr"][:kend])
+    assert_close("dK_resp", np32(res["dkr"])[:kend], ref["dkr"][:kend], atol=atol.get("dK_resp", ATOL))
     assert_close("dV_resp", np32(res["dvr"])[:kend], ref["dvr"][:kend])
     assert np.all(np32(res["dkr"])[kend:] == 0) and np.all(np32(res["dvr"])[kend:] == 0)
     if case.P > 0:

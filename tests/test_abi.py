@@ -97,7 +97,7 @@ def test_workspace_size_and_errors():
     assert _fwd(p, ws_bytes=need - 1) == LS_ERR_WORKSPACE
     assert _fwd(p, ws=None) == LS_ERR_WORKSPACE
     nb = lib.ls_bwd_workspace_bytes(C.byref(p), 16)
-    assert nb == 4 * (16 * 8 + 3 * 16 * 8 * 256)
+    assert nb == 4 * (128 + 3 * 16 * 8 * 256) + 8 * 64 * 2  # delta, dQ parts, (lse2, delta) per group row
     assert lib.ls_fwd_workspace_bytes(C.byref(_prefix(hq=7)), 16) == 0
     assert "multiple" in _err()
 

@@ -101,7 +101,9 @@ def test_large_magnitude_masked_keys():
     log("case: adversarial masked keys")
     c = Case(256, 128, 6, 2, 256, torch.bfloat16, seed=11, S=1)
     c.kr[40:128] = c.kr[40:128] * 60.0  # keys only later rows see
-    check_against_oracle(c, 0, 128, parts=False)
+    # dQ = scale * sum dS K is linear in |K|: its max-abs bound scales with the x60 keys
+    # (bf16 rounding of dS is relative); every rel-L2 bound is unchanged.
+    check_against_oracle(c, 0, 128, parts=False, atol={"dQ": 60 * 2e-2})
 
 
 def test_accumulation_vs_first_touch():
