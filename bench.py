@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Replay-attention benchmark: fwd+bwd TFLOP/s and % of bf16 matrix-core peak.
+
+One step is one group of the workload replayed in full through the library: G members
+one after another, each member's response in reverse blocks of B rows, every block a
+forward (split-prefix partials + LSE merge) and a backward (prep, dK/dV pages, dQ parts,
+part sum), with the prompt K/V gradient pages accumulated across the whole group.  The
+prompt pages are captured once before timing and every member's inputs are resident in
+HBM before the timed region starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2m]
+
+Prints one JSON line.  Counted work per member is 14 * Hq * d * pairs (4 forward + 10
+backward multiply-add units over visible (row, key) pairs); masked pairs and the second
+recompute of the two-pass backward are not counted.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from suffix_attention_amd import api, configs, datagen, driver  # noqa: E402
+
+METRIC = "replay-attention fwd+bwd TFLOP/s and % bf16 MFMA peak at P=2M, G=8"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+
+# Algorithmic matrix work per visible (row, key) pair and query head, in units of 2*d flops
+# (one multiply-add GEMM over the head dimension), for each kernel that does it.
+KERNEL_UNITS = {"fwd_mfma": 2, "dkdv_mfma": 4, "dq_mfma": 3}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def build_prefix(cfg, dev):
+    table = datagen.page_table(cfg.n_pages, datagen.seed(cfg.cfg_id, datagen.TAG_PERM), dev)
+    kp, vp = datagen.prefix_kv(cfg, dev)
+    k_pages, v_pages = api.capture_pages(kp, vp, table, cfg.n_pages)
+    torch.cuda.synchronize()
+    return api.Prefix(cfg.hq, cfg.hkv, cfg.d, cfg.dtype, cfg.P, table, k_pages, v_pages,
+                      api.even_shard_bounds(cfg.n_pages, cfg.S)), kp, vp
+
+
+def block_pairs(cfg):
+    """Visible pairs per head of every block of one member (reverse order irrelevant)."""
+    out = []
+    for b in range(cfg.n_blocks):
+        a = b * cfg.B
+        n = min(cfg.R, a + cfg.B) - a
+        out.append(configs.pairs(n, a, cfg.P))
+    return out
+
+
+def run_steps(prefix, members, cfg, n):
+    last = None
+    for _ in range(n):
+        last = None  # release the previous group's gradient pages before allocating anew
+        grp = driver.GroupReplay(prefix)
+        results = [grp.replay_member(m["q"], m["kr"], m["vr"], m["do"], cfg.B, keep="none") for m in members]
+        last = (grp, results)
+    return last
+
+
+def cpu_baseline(cfg, kp, vp, member, n_tok=16):
+    """The oracle, untuned, on a bounded sample: the last n_tok response rows of member 0
+    (all heads) against prompt shard 0 and the response keys those rows see."""
+    from oracle import attention as orc  # test infrastructure; used only for this baseline leg
+
+    shard_tokens = min(cfg.P, (cfg.n_pages // cfg.S) * 64)
+    q_start = cfg.R - n_tok
+    to_np = lambda t: t.to("cpu", torch.float32).numpy()  # noqa: E731
+    kps, vps = to_np(kp[:shard_tokens]), to_np(vp[:shard_tokens])
+    kr, vr = to_np(member["kr"]), to_np(member["vr"])
+    q, do = to_np(member["q"][q_start:]), to_np(member["do"][q_start:])
+    t0 = time.perf_counter()
+    O, L = orc.forward(q, kps, vps, kr, vr, q_start)
+    orc.backward(q, kps, vps, kr, vr, do, q_start, o=O, lse=L, prefix_grad_sink=lambda *a: None)
+    dt = time.perf_counter() - t0
+    flops = configs.counted_flops(n_tok, q_start, shard_tokens, cfg.hq, cfg.d)
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 3), "blas_threads": int(os.environ.get("OMP_NUM_THREADS", cores)),
+            "sample": f"float64 numpy oracle fwd+bwd of the last {n_tok} response rows (all {cfg.hq} heads) of "
+                      f"member 0 over prompt shard 0 ({shard_tokens} keys) plus their {cfg.R} causal response "
+                      f"keys; counted with the same 14*Hq*d*pairs convention"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="c2m", choices=sorted(configs.CONFIGS))
+    ap.add_argument("--G", type=int, default=None, help="override the group size")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ns = ap.parse_args()
+    if ns.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (--gpus {ns.gpus} requested)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    cfg = configs.CONFIGS[ns.config]
+    if ns.G:
+        cfg = cfg.with_(G=ns.G)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    log(f"[bench] config {cfg}")
+    prefix, kp, vp = build_prefix(cfg, dev)
+    members = [datagen.member_inputs(cfg, i, dev) for i in range(cfg.G)]
+    torch.cuda.synchronize()
+    log(f"[bench] prefix captured ({cfg.n_pages} pages), {cfg.G} members resident")
+
+    if ns.warmup > 0:
+        t = time.perf_counter()
+        run_steps(prefix, members, cfg, ns.warmup)
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {ns.warmup} step(s) {time.perf_counter() - t:.1f} s")
+
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    api.profile_begin()
+    t0 = time.perf_counter()
+    ev0.record()
+    grp, results = run_steps(prefix, members, cfg, ns.steps)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kstats = api.profile_end()
+    ms = ev0.elapsed_time(ev1)
+    log(f"[bench] timed {ns.steps} step(s): {ms / 1e3:.2f} s (wall {wall:.2f} s)")
+
+    flops_step = cfg.G * configs.member_flops(cfg)
+    tflops = flops_step * ns.steps / (ms / 1e3) / 1e12
+
+    # roofline of the dominant kernel: algorithmic flops per launch / its mean launch time
+    pairs = block_pairs(cfg)
+    blocks_timed = ns.steps * cfg.G * cfg.n_blocks
+    kern = {k: {"launches": v[0], "total_ms": round(v[1], 3), "mean_ms": round(v[1] / max(1, v[0]), 4)}
+            for k, v in kstats.items()}
+    dom = max((k for k in kern if k in KERNEL_UNITS), key=lambda k: kern[k]["total_ms"])
+    alg_flops_total = ns.steps * cfg.G * sum(2 * KERNEL_UNITS[dom] * cfg.hq * cfg.d * p for p in pairs)
+    n_launch = kern[dom]["launches"]
+    assert n_launch == blocks_timed, (dom, n_launch, blocks_timed)
+    achieved = alg_flops_total / (kern[dom]["total_ms"] / 1e3) / 1e12
+    for k in kern:
+        if k in KERNEL_UNITS:
+            f = ns.steps * cfg.G * sum(2 * KERNEL_UNITS[k] * cfg.hq * cfg.d * p for p in pairs)
+            kern[k]["tflops"] = round(f / (kern[k]["total_ms"] / 1e3) / 1e12, 1)
+
+    peaks = [r.peak_bytes for r in results]
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": ns.steps,
+        "warmup": ns.warmup,
+        "ms_per_step": round(ms / ns.steps, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: one attention layer, P={cfg.P} prompt tokens in 64-token pages with "
+                               f"a seeded permuted page table, S={cfg.S} shards, G={cfg.G} members x R={cfg.R} "
+                               f"response rows in reverse blocks of {cfg.B}, Hq={cfg.hq}, Hkv={cfg.hkv}, d={cfg.d}, "
+                               f"N(0,1) inputs",
+                   "P": cfg.P, "R": cfg.R, "B": cfg.B, "G": cfg.G, "S": cfg.S, "hq": cfg.hq, "hkv": cfg.hkv,
+                   "d": cfg.d},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "counted_tflop_per_step": round(flops_step / 1e12, 3),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_unit": f"{2 * KERNEL_UNITS[dom]}*d per visible (row, key) pair and query head",
+                     "mean_launch_ms": kern[dom]["mean_ms"]},
+        "kernels": kern,
+        "peak_mem_gb_per_member": [round(p / 1e9, 3) for p in peaks],
+        "peak_mem_gb": round(torch.cuda.max_memory_allocated(dev) / 1e9, 3),
+    }
+    del grp, results
+    if not ns.no_cpu_baseline:
+        t = time.perf_counter()
+        out["cpu_baseline"] = cpu_baseline(cfg, kp, vp, members[0])
+        log(f"[bench] cpu baseline {time.perf_counter() - t:.1f} s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

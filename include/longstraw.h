@@ -213,6 +213,25 @@ int ls_lse_merge(int n_parts, int64_t n_rows, int d, const float* o_parts,
                  const float* lse_parts, void* o_out, int out_dtype, float* lse_out,
                  ls_stream_t stream);
 
+/*
+ * Kernel timing, for diagnostics and benchmarks.  Between ls_profile_begin() and
+ * ls_profile_end(), every kernel the library launches (from any thread, on any stream) is
+ * bracketed by a pair of HIP events recorded on that kernel's stream, so each record is the
+ * kernel's own duration on the device.  ls_profile_end() waits for the recorded events (a
+ * host synchronisation), sums the durations per kernel name and writes up to max_entries
+ * records, in name order, to `out` (host memory); *n_entries receives the number of
+ * distinct kernels seen.  Recording adds one event pair per launch and nothing else.
+ * Errors: LS_ERR_INVALID (NULL pointers, end without begin), LS_ERR_HIP.
+ */
+typedef struct ls_kernel_stat {
+    char name[48];
+    int64_t launches;
+    double total_ms;
+} ls_kernel_stat_t;
+
+int ls_profile_begin(void);
+int ls_profile_end(ls_kernel_stat_t* out, int max_entries, int* n_entries);
+
 #ifdef __cplusplus
 }
 #endif

@@ -93,9 +93,9 @@ def _key_chunks(n_keys, chunk):
 
 
 def _chunk_len(n_rows):
-    # Keep one float64 score chunk near 64 MB; pure memory bound, no effect on values
-    # beyond summation order.
-    return max(256, (1 << 23) // max(1, n_rows))
+    # Keep one float64 score chunk near 64 MB and one float64 key chunk at most 64K rows;
+    # a pure memory bound, with no effect on values beyond summation order.
+    return min(1 << 16, max(256, (1 << 23) // max(1, n_rows)))
 
 
 def _group_rows(q, kv, g):

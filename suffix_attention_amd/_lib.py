@@ -37,6 +37,10 @@ class ls_prefix_t(C.Structure):
     ]
 
 
+class ls_kernel_stat_t(C.Structure):
+    _fields_ = [("name", C.c_char * 48), ("launches", C.c_int64), ("total_ms", C.c_double)]
+
+
 _P = C.c_void_p
 _I64 = C.c_int64
 _I = C.c_int
@@ -51,6 +55,8 @@ _SIG = {
     "ls_replay_bwd": (_I, [C.POINTER(ls_prefix_t), _P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _I,
                            _P, _P, _P, _P, C.c_size_t, _P]),
     "ls_lse_merge": (_I, [_I, _I64, _I, _P, _P, _P, _I, _P, _P]),
+    "ls_profile_begin": (_I, []),
+    "ls_profile_end": (_I, [C.POINTER(ls_kernel_stat_t), _I, C.POINTER(_I)]),
 }
 
 _lib = None

@@ -232,3 +232,16 @@ def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype: torch.d
     check(lib().ls_lse_merge(n_parts, n_rows, d, _ptr(o_parts), _ptr(lse_parts), _ptr(o), _dtype_code(out_dtype),
                              _ptr(lse), _stream()))
     return o, lse
+
+
+def profile_begin() -> None:
+    """Start timing every library kernel launch with HIP events on its stream."""
+    check(lib().ls_profile_begin())
+
+
+def profile_end() -> dict:
+    """Stop timing; returns {kernel name: (launches, total ms)} (waits for the events)."""
+    buf = (_lib.ls_kernel_stat_t * 64)()
+    n = C.c_int(0)
+    check(lib().ls_profile_end(buf, 64, C.byref(n)))
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n.value, 64))}

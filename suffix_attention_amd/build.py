@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "liblongstraw.so")
-SOURCES = ["abi.cpp", "capture.hip", "reduce.hip", "attn_generic.hip", "attn_mfma_fwd.hip",
+SOURCES = ["abi.cpp", "profile.cpp", "capture.hip", "reduce.hip", "attn_generic.hip", "attn_mfma_fwd.hip",
            "attn_mfma_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

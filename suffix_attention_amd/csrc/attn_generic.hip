@@ -363,6 +363,7 @@ template <typename T>
 hipError_t fwd_dispatch(const AttnArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)((a.n_rows * a.g + TR - 1) / TR), a.n_parts, a.hkv);
     if (a.n_rows == 0) return hipSuccess;
+    KernelTimer kt("fwd_generic", s);
     switch (a.d) {
         case 64: fwd_generic_kernel<T, 64><<<grid, NT, 0, s>>>(a); break;
         case 128: fwd_generic_kernel<T, 128><<<grid, NT, 0, s>>>(a); break;
@@ -380,16 +381,16 @@ hipError_t bwd_dispatch(const AttnArgs& a, hipStream_t s) {
     const bool k_work = n_tiles > 0, q_work = a.n_rows > 0;
     switch (a.d) {
         case 64:
-            if (k_work) dkdv_generic_kernel<T, 64><<<g1, NT, 0, s>>>(a);
-            if (q_work) dq_generic_kernel<T, 64><<<g2, NT, 0, s>>>(a);
+            if (k_work) { KernelTimer kt("dkdv_generic", s); dkdv_generic_kernel<T, 64><<<g1, NT, 0, s>>>(a); }
+            if (q_work) { KernelTimer kt("dq_generic", s); dq_generic_kernel<T, 64><<<g2, NT, 0, s>>>(a); }
             break;
         case 128:
-            if (k_work) dkdv_generic_kernel<T, 128><<<g1, NT, 0, s>>>(a);
-            if (q_work) dq_generic_kernel<T, 128><<<g2, NT, 0, s>>>(a);
+            if (k_work) { KernelTimer kt("dkdv_generic", s); dkdv_generic_kernel<T, 128><<<g1, NT, 0, s>>>(a); }
+            if (q_work) { KernelTimer kt("dq_generic", s); dq_generic_kernel<T, 128><<<g2, NT, 0, s>>>(a); }
             break;
         case 256:
-            if (k_work) dkdv_generic_kernel<T, 256><<<g1, NT, 0, s>>>(a);
-            if (q_work) dq_generic_kernel<T, 256><<<g2, NT, 0, s>>>(a);
+            if (k_work) { KernelTimer kt("dkdv_generic", s); dkdv_generic_kernel<T, 256><<<g1, NT, 0, s>>>(a); }
+            if (q_work) { KernelTimer kt("dq_generic", s); dq_generic_kernel<T, 256><<<g2, NT, 0, s>>>(a); }
             break;
         default: return hipErrorInvalidValue;
     }

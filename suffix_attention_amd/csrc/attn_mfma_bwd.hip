@@ -508,19 +508,24 @@ hipError_t launch_bwd_d(const AttnArgs& a, hipStream_t s) {
     float* delta_th = const_cast<float*>(a.delta);
     if (rows_total > 0) {
         const int64_t waves = rows_pad * a.hkv;
+        KernelTimer kt("bwd_prep", s);
         bwd_prep_kernel<D><<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(a, rows_pad, lsed, delta_th);
     }
     // dK / dV
     const int n_pp = (int)((a.n_logical_pages + 1) / 2);
     const int n_rp = (int)((resp_tiles(a.key_end) + 1) / 2);
     const int64_t nb_kv = (int64_t)(n_pp + n_rp) * a.hkv;
-    if (nb_kv > 0)
+    if (nb_kv > 0) {
+        KernelTimer kt("dkdv_mfma", s);
         dkdv_mfma_kernel<D><<<pad_grid((int)nb_kv), 256, 0, s>>>(a, lsed, rows_pad, n_pp, n_rp, (int)nb_kv);
+    }
     // dQ parts
     const int64_t n_qtiles = (rows_total + BM - 1) / BM;
     const int64_t nb_q = n_qtiles * a.n_parts * a.hkv;
-    if (nb_q > 0)
+    if (nb_q > 0) {
+        KernelTimer kt("dq_mfma", s);
         dq_mfma_kernel<D, NW><<<pad_grid((int)nb_q), NW * 64, 0, s>>>(a, lsed, rows_pad, (int)n_qtiles, (int)nb_q);
+    }
     return hipGetLastError();
 }
 

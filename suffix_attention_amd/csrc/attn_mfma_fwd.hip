@@ -241,6 +241,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
     const int64_t n_blocks = n_qtiles * a.n_parts * a.hkv;
     if (n_blocks == 0) return hipSuccess;
     const int grid = pad_grid((int)n_blocks);
+    KernelTimer kt("fwd_mfma", s);
     fwd_mfma_kernel<D, NW><<<grid, NW * 64, 0, s>>>(a, (int)n_qtiles, (int)n_blocks);
     return hipGetLastError();
 }

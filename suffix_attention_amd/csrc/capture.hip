@@ -93,11 +93,13 @@ hipError_t launch_capture(const void* k_src, const void* v_src, int src_dtype, i
     if (src_dtype == page_dtype) {
         const int row_vecs = d * elem_bytes(src_dtype) / 16;
         const int64_t n = n_tok * hkv * row_vecs;
+        KernelTimer kt("capture", s);
         capture_copy_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
             (const uint4*)k_src, (const uint4*)v_src, n_tok, first_tok, table, (uint4*)k_pages,
             (uint4*)v_pages, n_phys, hkv, row_vecs);
     } else {  // f32 -> bf16
         const int64_t n = n_tok * hkv * (d / 8);
+        KernelTimer kt("capture", s);
         capture_kernel<float, bf16_t><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
             (const float*)k_src, (const float*)v_src, n_tok, first_tok, table,
             (bf16_t*)k_pages, (bf16_t*)v_pages, n_phys, hkv, d);
@@ -111,6 +113,7 @@ hipError_t launch_gather(const void* pages, int dtype, const int32_t* table, int
     if (n_tok == 0) return hipSuccess;
     const int row_vecs = d * elem_bytes(dtype) / 16;
     const int64_t n = n_tok * hkv * row_vecs;
+    KernelTimer kt("gather", s);
     gather_copy_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
         (const uint4*)pages, table, n_phys, first_tok, n_tok, hkv, row_vecs, (uint4*)dst);
     return hipGetLastError();

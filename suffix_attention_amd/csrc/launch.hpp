@@ -48,6 +48,21 @@ struct AttnArgs {
     int resp_first_touch;
 };
 
+// Brackets one kernel launch with HIP events on its stream while profiling is on
+// (ls_profile_begin / ls_profile_end); does nothing otherwise.
+class KernelTimer {
+  public:
+    KernelTimer(const char* name, hipStream_t s);
+    ~KernelTimer();
+    KernelTimer(const KernelTimer&) = delete;
+    KernelTimer& operator=(const KernelTimer&) = delete;
+
+  private:
+    const char* name_;
+    hipStream_t stream_;
+    hipEvent_t start_ = nullptr;
+};
+
 // Rows of one kv head's group are numbered r = token * g + j (query head kv * g + j).
 // Key-range helpers shared by host launch code.
 inline int64_t resp_tiles(int64_t key_end) { return (key_end + 63) / 64; }

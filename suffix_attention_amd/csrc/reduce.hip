@@ -90,6 +90,7 @@ hipError_t launch_lse_merge(int n_parts, int64_t n_rows, int d, const float* o_p
     if (n_rows == 0) return hipSuccess;
     const int rows_per_block = 256 / (d / 4);
     const unsigned grid = (unsigned)((n_rows + rows_per_block - 1) / rows_per_block);
+    KernelTimer kt("lse_merge", s);
     if (out_dtype == 0)
         lse_merge_kernel<float><<<grid, 256, 0, s>>>(n_parts, n_rows, d, o_parts, lse_parts, (float*)o_out, lse_out);
     else
@@ -101,6 +102,7 @@ hipError_t launch_delta(const void* o, const void* dout, int dtype, int64_t n_ro
                         float* delta, hipStream_t s) {
     if (n_rows == 0) return hipSuccess;
     const unsigned grid = (unsigned)((n_rows + 3) / 4);
+    KernelTimer kt("delta", s);
     if (dtype == 0)
         delta_kernel<float><<<grid, 256, 0, s>>>((const float*)o, (const float*)dout, n_rows, d, delta);
     else
@@ -111,12 +113,14 @@ hipError_t launch_delta(const void* o, const void* dout, int dtype, int64_t n_ro
 hipError_t launch_sum_parts(int n_parts, int64_t n, const float* parts, float* out, hipStream_t s) {
     if (n == 0) return hipSuccess;
     const int64_t n4 = n / 4;
+    KernelTimer kt("dq_sum_parts", s);
     sum_parts_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(n_parts, n4, (const float4*)parts, (float4*)out);
     return hipGetLastError();
 }
 
 hipError_t launch_zero(float* p, int64_t n, hipStream_t s) {
     if (n <= 0) return hipSuccess;
+    KernelTimer kt("zero", s);
     zero_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p, n);
     return hipGetLastError();
 }

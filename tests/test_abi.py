@@ -137,3 +137,12 @@ def test_capture_and_merge_validation():
     assert lib.ls_lse_merge(2, 10, 6, FAKE, FAKE, FAKE, LS_DTYPE_F32, FAKE, None) == LS_ERR_UNSUPPORTED
     assert lib.ls_lse_merge(2, 10, 256, None, FAKE, FAKE, LS_DTYPE_F32, FAKE, None) == LS_ERR_INVALID
     assert lib.ls_gather_pages(FAKE, 7, FAKE, 4, 4, 0, 10, 2, 256, 64, FAKE, None) == LS_ERR_UNSUPPORTED
+
+
+def test_profile_begin_end_without_launches():
+    from suffix_attention_amd import api
+    api.profile_begin()
+    assert api.profile_end() == {}
+    n = C.c_int(0)
+    # end without begin is an error
+    assert _lib.lib().ls_profile_end(None, 0, C.byref(n)) == LS_ERR_INVALID
