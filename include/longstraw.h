@@ -69,7 +69,7 @@ typedef void* ls_stream_t; /* a hipStream_t */
  *                   are the context-parallel owners whose local softmax statistics are
  *                   merged into the exact result (digest, "Method", Qwen implementation;
  *                   explainer, "Two incompatible architectures").  Empty shards are allowed.
- *   softmax_scale   usually 1 / sqrt(d).
+ *   softmax_scale   > 0, usually 1 / sqrt(d).
  */
 typedef struct ls_prefix {
     int hq;
@@ -135,8 +135,9 @@ int ls_gather_pages(const void* pages, int dtype, const int32_t* page_table,
  * Backward workspace layout (from offset 0):
  *   delta     float32 [n_rows, hq], padded to a multiple of 64 elements: rowsum(dO * O)
  *   dq_parts  float32 [n_parts, n_rows, hq, d]
- *   then, for bf16, (LSE * log2 e, delta) pairs per kv head and query row of its group,
- *   padded to a multiple of 64 rows.
+ *   then, for bf16, per kv head and query row of its group (padded to a multiple of 64
+ *   rows): (LSE * log2 e, delta) float32 pairs, then the Q rows and the dO rows (bf16).
+ * A block may have at most about 2^32 / (16 * hq * d) rows (174,000 at hq = 24, d = 256).
  */
 size_t ls_fwd_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows);
 size_t ls_bwd_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows);

@@ -57,7 +57,8 @@ int check_prefix(const ls_prefix_t* p) {
     if (p->n_shards < 1 || p->n_shards > ls::kMaxShards)
         return fail(LS_ERR_INVALID, "n_shards=%d outside [1, %d]", p->n_shards, ls::kMaxShards);
     if (p->prefix_len < 0) return fail(LS_ERR_INVALID, "prefix_len=%lld < 0", (long long)p->prefix_len);
-    if (!std::isfinite(p->softmax_scale)) return fail(LS_ERR_INVALID, "softmax_scale is not finite");
+    if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f))
+        return fail(LS_ERR_INVALID, "softmax_scale must be finite and > 0");
     const int64_t nlp = logical_pages(p->prefix_len, p->page_size);
     if (nlp > 0) {
         if (!p->page_table || !p->k_pages || !p->v_pages)
@@ -86,6 +87,9 @@ int check_block(const ls_prefix_t* p, const void* q, int64_t n_rows, int64_t q_s
     if (q_start + n_rows > 0 && (!k_resp || !v_resp)) return fail(LS_ERR_INVALID, "k_resp/v_resp is NULL");
     const int64_t rows_g = n_rows * (p->hq / p->hkv);
     if (rows_g > (int64_t)1 << 30) return fail(LS_ERR_INVALID, "block too large (%lld group rows)", (long long)rows_g);
+    // kernels address one block's rows with 32-bit byte offsets
+    if ((n_rows + 64) * (int64_t)p->hq * p->d * 4 >= ((int64_t)1 << 32))
+        return fail(LS_ERR_INVALID, "block of %lld rows too large: split it into smaller blocks", (long long)n_rows);
     return LS_OK;
 }
 
@@ -123,7 +127,7 @@ size_t fwd_ws(const ls_prefix_t* p, int64_t n_rows) {
 
 size_t bwd_ws(const ls_prefix_t* p, int64_t n_rows) {
     return sizeof(float) * ((size_t)ls::bwd_delta_elems(n_rows, p->hq) + (size_t)(p->n_shards + 1) * n_rows * p->hq * p->d) +
-           ls::mfma_bwd_extra_bytes(n_rows, p->hq / p->hkv, p->hkv);
+           ls::mfma_bwd_extra_bytes(n_rows, p->hq / p->hkv, p->hkv, p->d);
 }
 
 }  // namespace

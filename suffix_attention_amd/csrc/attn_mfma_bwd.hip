@@ -16,8 +16,9 @@
 //                   them; each element has exactly one writer, so no atomics are needed.
 //
 // A prep kernel first writes, per kv head and group row r = token * g + j,
-// (LSE * log2 e, delta = rowsum(dO * O)); rows padded up to a multiple of 64 get
-// (+inf, 0), so their P is exactly 0 wherever they are read.
+// (LSE * log2 e, delta = rowsum(dO * O)) and group-major copies of the Q and dO rows, so the
+// dK/dV pass streams each kv head's rows as one contiguous array.  Rows padded up to a
+// multiple of 64 get (+inf, 0) and zero Q/dO, so their P is exactly 0 wherever they are read.
 #include <math.h>
 
 #include "mfma_tiles.hpp"
@@ -30,34 +31,63 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kRowPad = 64;
 inline int64_t rows_padded(int64_t rows) { return (rows + kRowPad - 1) / kRowPad * kRowPad; }
 
+// Per-kv-head, group-major views of the block: row r of kv head h is (token r / g, query head
+// h * g + r % g); rows_pad rows per head.
+struct GroupRows {
+    f32x2* lsed;     // [hkv][rows_pad] (LSE * log2 e, delta)
+    bf16_t* q;       // [hkv][rows_pad][D]
+    bf16_t* dout;    // [hkv][rows_pad][D]
+    int64_t rows_pad;
+};
+
+inline GroupRows group_rows(void* base, int64_t rows_pad, int hkv, int d) {
+    GroupRows g;
+    g.rows_pad = rows_pad;
+    g.lsed = (f32x2*)base;
+    g.q = (bf16_t*)(g.lsed + (int64_t)hkv * rows_pad);
+    g.dout = g.q + (int64_t)hkv * rows_pad * d;
+    return g;
+}
+
 // ---------------------------------------------------------------------------------------
-// prep: delta and log2-scaled LSE per group row; also delta in [n_rows, hq] order
+// prep: delta, log2-scaled LSE and group-major Q / dO rows; also delta in [n_rows, hq] order
 // ---------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(AttnArgs a, int64_t rows_pad, f32x2* __restrict__ lsed,
-                                                       float* __restrict__ delta_th) {
+__global__ __launch_bounds__(256) void bwd_prep_kernel(AttnArgs a, GroupRows gr, float* __restrict__ delta_th) {
+    static_assert(D % 64 == 0, "4 bf16 per lane per pass");
     const int64_t gw = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // one wave per (kvh, r)
     const int lane = threadIdx.x % 64;
     const int64_t rows_total = a.n_rows * a.g;
-    if (gw >= rows_pad * a.hkv) return;
-    const int kvh = (int)(gw / rows_pad);
-    const int64_t r = gw % rows_pad;
+    if (gw >= gr.rows_pad * a.hkv) return;
+    const int kvh = (int)(gw / gr.rows_pad);
+    const int64_t r = gw % gr.rows_pad;
+    uint2* qd = (uint2*)(gr.q + gw * D);
+    uint2* dd = (uint2*)(gr.dout + gw * D);
     if (r >= rows_total) {
-        if (lane == 0) lsed[gw] = f32x2{INFINITY, 0.f};
+#pragma unroll
+        for (int k = lane; k < D / 4; k += 64) qd[k] = dd[k] = make_uint2(0, 0);
+        if (lane == 0) gr.lsed[gw] = f32x2{INFINITY, 0.f};
         return;
     }
     const int64_t th = (r / a.g) * a.hq + kvh * a.g + r % a.g;
-    const bf16_t* o = (const bf16_t*)a.o + th * D;
-    const bf16_t* dout = (const bf16_t*)a.dout + th * D;
+    const uint2* o = (const uint2*)((const bf16_t*)a.o + th * D);
+    const uint2* dout = (const uint2*)((const bf16_t*)a.dout + th * D);
+    const uint2* q = (const uint2*)((const bf16_t*)a.q + th * D);
     float s = 0.f;
-    for (int k = lane * 4; k < D; k += 256) {
 #pragma unroll
-        for (int e = 0; e < 4; e++) s += bf16_to_f32(o[k + e]) * bf16_to_f32(dout[k + e]);
+    for (int k = lane; k < D / 4; k += 64) {
+        const uint2 ov = o[k], dv = dout[k];
+        qd[k] = q[k];
+        dd[k] = dv;
+        s += bf16_to_f32((bf16_t)(ov.x & 0xffff)) * bf16_to_f32((bf16_t)(dv.x & 0xffff)) +
+             bf16_to_f32((bf16_t)(ov.x >> 16)) * bf16_to_f32((bf16_t)(dv.x >> 16)) +
+             bf16_to_f32((bf16_t)(ov.y & 0xffff)) * bf16_to_f32((bf16_t)(dv.y & 0xffff)) +
+             bf16_to_f32((bf16_t)(ov.y >> 16)) * bf16_to_f32((bf16_t)(dv.y >> 16));
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     if (lane == 0) {
-        lsed[gw] = f32x2{a.lse[th] * kLog2e, s};
+        gr.lsed[gw] = f32x2{a.lse[th] * kLog2e, s};
         delta_th[th] = s;
     }
 }
@@ -83,17 +113,27 @@ __device__ __forceinline__ void dq_tile(DqState<D>& st, const LS_LDS char* lds_k
     asm volatile("" : "+v"(la.k), "+v"(la.v));
     f32x16 s[2], dp[2];
     s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+    // K and V fragments are read PD k-steps ahead of their MFMAs
+    constexpr int PD = 2;
+    bf16x8 kb[PD][4];
+    auto read_kv = [&](int ks, bf16x8* b) {
+        const uint32_t o = la.k ^ (uint32_t)(ks << 5);
+        b[0] = *(const LS_LDS bf16x8*)(lds_k + o);
+        b[1] = *(const LS_LDS bf16x8*)(lds_k + o + 32 * 2 * D);
+        b[2] = *(const LS_LDS bf16x8*)(lds_v + o);
+        b[3] = *(const LS_LDS bf16x8*)(lds_v + o + 32 * 2 * D);
+    };
+#pragma unroll
+    for (int j = 0; j < PD; j++) read_kv(j, kb[j]);
 #pragma unroll
     for (int ks = 0; ks < F::KS; ks++) {
-        const uint32_t o = la.k ^ (uint32_t)(ks << 5);
-        const bf16x8 k0 = *(const LS_LDS bf16x8*)(lds_k + o);
-        const bf16x8 k1 = *(const LS_LDS bf16x8*)(lds_k + o + 32 * 2 * D);
-        const bf16x8 v0 = *(const LS_LDS bf16x8*)(lds_v + o);
-        const bf16x8 v1 = *(const LS_LDS bf16x8*)(lds_v + o + 32 * 2 * D);
+        const bf16x8 k0 = kb[ks % PD][0], k1 = kb[ks % PD][1], v0 = kb[ks % PD][2], v1 = kb[ks % PD][3];
+        if (ks + PD < F::KS) read_kv(ks + PD, kb[ks % PD]);
         s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, st.qb[ks], s[0], 0, 0, 0);
         s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, st.qb[ks], s[1], 0, 0, 0);
         dp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, st.dob[ks], dp[0], 0, 0, 0);
         dp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, st.dob[ks], dp[1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
     int lim_valid = src.valid - 4 * h;
     int lim_causal = 64;
@@ -113,7 +153,7 @@ __device__ __forceinline__ void dq_tile(DqState<D>& st, const LS_LDS char* lds_k
 #pragma unroll
                 for (int e = 0; e < 2; e++) {
                     const int i = 8 * u + 2 * t + e;
-                    float p = fast_exp2(s[kt][i] * scale_log2 - st.lse2);
+                    float p = fast_exp2(__builtin_fmaf(s[kt][i], scale_log2, -st.lse2));
                     if (need_mask) {
                         const int kc = 32 * kt + 8 * (i >> 2) + (i & 3);
                         p = (kc < lim_valid && kc <= lim_causal) ? p : 0.f;
@@ -125,22 +165,25 @@ __device__ __forceinline__ void dq_tile(DqState<D>& st, const LS_LDS char* lds_k
             db[kt][u] = __builtin_bit_cast(bf16x8, (u32x4{w4[0], w4[1], w4[2], w4[3]}));
         }
     }
-    // dQ^T += K^T dS^T
+    // dQ^T += K^T dS^T.  Step st = (kt, u, dt), dt fastest; K^T fragments read PV steps ahead.
+    constexpr int NST = 4 * F::DT;
+    constexpr int PV = 4;
+    i16x4 tlo[PV], thi[PV];
+    auto read_kt = [&](int st_, i16x4& lo, i16x4& hi) {
+        const int dt = st_ % F::DT, ku = st_ / F::DT;
+        const int R = 32 * (ku >> 1) + 16 * (ku & 1);
+        lo = lds_read_tr4(lds_k + (la.v ^ tr_x<D>(dt, R)) + R * 2 * D);
+        hi = lds_read_tr4(lds_k + (la.v ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D);
+    };
 #pragma unroll
-    for (int dt = 0; dt < F::DT; dt++) {
-        const uint32_t x0 = la.v ^ (uint32_t)(((4 * dt) ^ (0 & F::SWZ)) << 4);
-        const uint32_t x1 = la.v ^ (uint32_t)(((4 * dt) ^ (8 & F::SWZ)) << 4);
+    for (int j = 0; j < PV; j++) read_kt(j, tlo[j], thi[j]);
 #pragma unroll
-        for (int kt = 0; kt < 2; kt++) {
-#pragma unroll
-            for (int u = 0; u < 2; u++) {
-                const int row = 32 * kt + 16 * u;
-                const i16x4 lo = lds_read_tr4(lds_k + x0 + row * 2 * D);
-                const i16x4 hi = lds_read_tr4(lds_k + x1 + (row + 8) * 2 * D);
-                const bf16x8 ka = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                st.dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, db[kt][u], st.dq[dt], 0, 0, 0);
-            }
-        }
+    for (int st_ = 0; st_ < NST; st_++) {
+        const int dt = st_ % F::DT, ku = st_ / F::DT;
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tlo[st_ % PV], thi[st_ % PV], 0, 1, 2, 3, 4, 5, 6, 7));
+        if (st_ + PV < NST) read_kt(st_ + PV, tlo[st_ % PV], thi[st_ % PV]);
+        st.dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, db[ku >> 1][ku & 1], st.dq[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -157,7 +200,7 @@ __device__ __forceinline__ void dq_step(DqState<D>& st, const char* __restrict__
 
 template <int D, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(1, 1)))
-void dq_mfma_kernel(AttnArgs a, const f32x2* __restrict__ lsed, int64_t rows_pad, int n_qtiles, int n_blocks) {
+void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
     using F = TileShape<D>;
     constexpr int BM = 32 * NW;
     __shared__ __attribute__((aligned(1024))) char st0[2 * F::TILE];
@@ -191,10 +234,11 @@ void dq_mfma_kernel(AttnArgs a, const f32x2* __restrict__ lsed, int64_t rows_pad
         for (int ks = 0; ks < F::KS; ks++) {
             st.qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * ks));
             st.dob[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(drow + 16 * ks));
+            asm volatile("" : "+a"(st.qb[ks]), "+a"(st.dob[ks]));  // read-only MFMA operands
         }
 #pragma unroll
         for (int dt = 0; dt < F::DT; dt++) st.dq[dt] = f32x16{};
-        const f32x2 ld = lsed[kvh * rows_pad + (row_ok ? my_row : rows_total - 1)];
+        const f32x2 ld = gr.lsed[kvh * gr.rows_pad + (row_ok ? my_row : rows_total - 1)];
         st.lse2 = ld[0];
         st.dlt = ld[1];
     }
@@ -252,31 +296,15 @@ struct RowStage {
     static constexpr int BYTES = 2 * QBYTES + kRows * 8;    // Q, dO, (lse2, delta) per row
 };
 
-// Copy group rows [r0, r0 + 32) of Q and dO (rows past the block repeat the last row; their
-// LSE is +inf so they contribute nothing) and their (lse2, delta) into an LDS stage.
+// Copy group rows [r0, r0 + 32) of Q and dO (group-major, zero padded) and their
+// (lse2, delta) into an LDS stage.
 template <int D>
-__device__ __forceinline__ void issue_rows(const AttnArgs& a, const f32x2* lsed_kvh, int kvh, int64_t r0,
-                                           int64_t rows_total, char* stage, int w, int lane) {
-    using F = TileShape<D>;
-    constexpr int RPK = 512 / D;                     // rows per 1 KiB block
-    constexpr int BLOCKS = RowStage<D>::QBYTES / 1024;
-    constexpr int PER_WAVE = BLOCKS / 4;
-    const int low = lane / F::KCH;
-    const int pc = lane % F::KCH;
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; j++) {
-        const int blk = j * 4 + w;
-        const int r = blk * RPK + low;
-        int64_t gr = r0 + r;
-        if (gr >= rows_total) gr = rows_total - 1;
-        const int lc = pc ^ (r & F::SWZ);
-        const int64_t th = (gr / a.g) * a.hq + kvh * a.g + gr % a.g;
-        const int64_t e = th * D + lc * 8;
-        dma16((const bf16_t*)a.q + e, (LS_LDS void*)(stage + blk * 1024));
-        dma16((const bf16_t*)a.dout + e, (LS_LDS void*)(stage + RowStage<D>::QBYTES + blk * 1024));
-    }
+__device__ __forceinline__ void issue_rows(const GroupRows& gr, int kvh, int64_t r0, char* stage, int w, int lane) {
+    const int64_t base = ((int64_t)kvh * gr.rows_pad + r0) * D;
+    dma_rows<D, 4, kRows>(gr.q + base, gr.dout + base, D, stage, stage + RowStage<D>::QBYTES, w, lane);
     if (w == 0 && lane < kRows * 8 / 16)
-        dma16((const char*)(lsed_kvh + r0) + lane * 16, (LS_LDS void*)(stage + 2 * RowStage<D>::QBYTES));
+        dma16((const char*)(gr.lsed + kvh * gr.rows_pad + r0) + lane * 16,
+              (LS_LDS void*)(stage + 2 * RowStage<D>::QBYTES));
 }
 
 template <int D>
@@ -296,15 +324,27 @@ __device__ __forceinline__ void dkdv_rows(DkvState<D>& st, const LS_LDS char* st
     const LS_LDS char* lq = stage;
     const LS_LDS char* ldo = stage + RowStage<D>::QBYTES;
     const LS_LDS f32x2* lsd = (const LS_LDS f32x2*)(stage + 2 * RowStage<D>::QBYTES);
-    // S = Q K^T, dP = dO V^T for 32 rows x 32 keys
+    // S = Q K^T, dP = dO V^T for 32 rows x 32 keys; Q and dO fragments read PD k-steps ahead
     f32x16 s = f32x16{}, dp = f32x16{};
+    constexpr int PD = 3;
+    bf16x8 qd[PD][2];
+#pragma unroll
+    for (int j = 0; j < PD; j++) {
+        const uint32_t o = la.k ^ (uint32_t)(j << 5);
+        qd[j][0] = *(const LS_LDS bf16x8*)(lq + o);
+        qd[j][1] = *(const LS_LDS bf16x8*)(ldo + o);
+    }
 #pragma unroll
     for (int ks = 0; ks < F::KS; ks++) {
-        const uint32_t o = la.k ^ (uint32_t)(ks << 5);
-        const bf16x8 qa = *(const LS_LDS bf16x8*)(lq + o);
-        const bf16x8 da = *(const LS_LDS bf16x8*)(ldo + o);
+        const bf16x8 qa = qd[ks % PD][0], da = qd[ks % PD][1];
+        if (ks + PD < F::KS) {
+            const uint32_t o = la.k ^ (uint32_t)((ks + PD) << 5);
+            qd[ks % PD][0] = *(const LS_LDS bf16x8*)(lq + o);
+            qd[ks % PD][1] = *(const LS_LDS bf16x8*)(ldo + o);
+        }
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, st.kb[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, st.vb[ks], dp, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
     // element i is row 8(i/4) + 4h + i%4 of the stage, key lane%32
     const int rmh = rmin - 4 * h;  // rows (without the 4h of this half) that precede the key
@@ -323,7 +363,7 @@ __device__ __forceinline__ void dkdv_rows(DkvState<D>& st, const LS_LDS char* st
                 const float l2 = j < 2 ? l01[2 * j] : l23[2 * (j - 2)];
                 const float dl = j < 2 ? l01[2 * j + 1] : l23[2 * (j - 2) + 1];
                 const int i = 8 * u + 4 * hb + j;
-                float p = fast_exp2(s[i] * scale_log2 - l2);
+                float p = fast_exp2(__builtin_fmaf(s[i], scale_log2, -l2));
                 if (need_mask) p = (16 * u + 8 * hb + j) >= rmh ? p : 0.f;
                 pv[j] = p;
                 dv[j] = p * (dp[i] - dl);
@@ -336,32 +376,42 @@ __device__ __forceinline__ void dkdv_rows(DkvState<D>& st, const LS_LDS char* st
         pa[u] = __builtin_bit_cast(bf16x8, (u32x4{wp[0], wp[1], wp[2], wp[3]}));
         sa[u] = __builtin_bit_cast(bf16x8, (u32x4{wd[0], wd[1], wd[2], wd[3]}));
     }
-    // dV += P^T dO, dK += dS^T Q   (dO, Q read transposed: rows are the contraction)
+    // dV += P^T dO, dK += dS^T Q (dO, Q read transposed: rows are the contraction).  Step
+    // st = (u, dt), dt fastest; fragments read PT steps ahead.
+    constexpr int NST = 2 * F::DT;
+    constexpr int PT = 2;
+    i16x4 fr[PT][4];
+    auto read_t = [&](int st_, i16x4* f) {
+        const int dt = st_ % F::DT, u = st_ / F::DT;
+        const int R = 16 * u;
+        const uint32_t a0 = (la.v ^ tr_x<D>(dt, R)) + R * 2 * D;
+        const uint32_t a1 = (la.v ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D;
+        f[0] = lds_read_tr4(ldo + a0);
+        f[1] = lds_read_tr4(ldo + a1);
+        f[2] = lds_read_tr4(lq + a0);
+        f[3] = lds_read_tr4(lq + a1);
+    };
 #pragma unroll
-    for (int dt = 0; dt < F::DT; dt++) {
-        const uint32_t x0 = la.v ^ (uint32_t)(((4 * dt) ^ (0 & F::SWZ)) << 4);
-        const uint32_t x1 = la.v ^ (uint32_t)(((4 * dt) ^ (8 & F::SWZ)) << 4);
+    for (int j = 0; j < PT; j++) read_t(j, fr[j]);
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-            const int row = 16 * u;
-            const i16x4 dlo = lds_read_tr4(ldo + x0 + row * 2 * D);
-            const i16x4 dhi = lds_read_tr4(ldo + x1 + (row + 8) * 2 * D);
-            const i16x4 qlo = lds_read_tr4(lq + x0 + row * 2 * D);
-            const i16x4 qhi = lds_read_tr4(lq + x1 + (row + 8) * 2 * D);
-            const bf16x8 dob = __builtin_bit_cast(bf16x8, __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7));
-            const bf16x8 qbt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
-            st.dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[u], dob, st.dv[dt], 0, 0, 0);
-            st.dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[u], qbt, st.dk[dt], 0, 0, 0);
-        }
+    for (int st_ = 0; st_ < NST; st_++) {
+        const int dt = st_ % F::DT, u = st_ / F::DT;
+        i16x4* f = fr[st_ % PT];
+        const bf16x8 dob = __builtin_bit_cast(bf16x8, __builtin_shufflevector(f[0], f[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 qbt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(f[2], f[3], 0, 1, 2, 3, 4, 5, 6, 7));
+        if (st_ + PT < NST) read_t(st_ + PT, f);
+        st.dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[u], dob, st.dv[dt], 0, 0, 0);
+        st.dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[u], qbt, st.dk[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 template <int D>
 __device__ __forceinline__ void dkdv_step(DkvState<D>& st, const char* __restrict__ cur, char* __restrict__ nxt,
-                                          bool has_next, const AttnArgs& a, const f32x2* lsed_kvh, int kvh,
-                                          int64_t next_r0, int64_t rows_total, LaneAddr<D> la, bool need_mask,
-                                          int rmin, int w, int lane) {
-    if (has_next) issue_rows<D>(a, lsed_kvh, kvh, next_r0, rows_total, nxt, w, lane);
+                                          bool has_next, const AttnArgs& a, const GroupRows& gr, int kvh,
+                                          int64_t next_r0, LaneAddr<D> la, bool need_mask, int rmin, int w,
+                                          int lane) {
+    if (has_next) issue_rows<D>(gr, kvh, next_r0, nxt, w, lane);
     dkdv_rows<D>(st, (const LS_LDS char*)cur, la, need_mask, rmin, a.scale_log2, lane);
 }
 
@@ -369,8 +419,7 @@ __device__ __forceinline__ void dkdv_step(DkvState<D>& st, const char* __restric
 // 32 (w%2) .. +32).  Blocks [0, n_pp) are prompt page pairs, the rest response pairs.
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void dkdv_mfma_kernel(AttnArgs a, const f32x2* __restrict__ lsed, int64_t rows_pad, int n_pp, int n_rp,
-                      int n_blocks) {
+void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks) {
     using F = TileShape<D>;
     __shared__ __attribute__((aligned(1024))) char st0[RowStage<D>::BYTES];
     __shared__ __attribute__((aligned(1024))) char st1[RowStage<D>::BYTES];
@@ -386,7 +435,6 @@ void dkdv_mfma_kernel(AttnArgs a, const f32x2* __restrict__ lsed, int64_t rows_p
     const int h = lane >> 5;
     const int n = lane & 31;
     const int64_t rows_total = a.n_rows * a.g;
-    const f32x2* lsed_kvh = lsed + kvh * rows_pad;
 
     // ---- this wave's 32 keys
     const int64_t page = 2 * (int64_t)(resp ? pair - n_pp : pair) + (w >> 1);  // logical or response page
@@ -441,7 +489,7 @@ void dkdv_mfma_kernel(AttnArgs a, const f32x2* __restrict__ lsed, int64_t rows_p
     const int64_t row_min = resp ? (my_key - a.q_start) * a.g : 0;
 
     const LaneAddr<D> la(lane);
-    if (n_stages > 0) issue_rows<D>(a, lsed_kvh, kvh, r_begin, rows_total, st0, w, lane);
+    if (n_stages > 0) issue_rows<D>(gr, kvh, r_begin, st0, w, lane);
     for (int64_t t = 0; t < n_stages; t++) {
         wait_vm_all();
         __syncthreads();
@@ -453,7 +501,7 @@ void dkdv_mfma_kernel(AttnArgs a, const f32x2* __restrict__ lsed, int64_t rows_p
         const int rmin = rm < 0 ? 0 : (rm > kRows ? kRows : (int)rm);
         char* cur = (t & 1) ? st1 : st0;
         char* nxt = (t & 1) ? st0 : st1;
-        dkdv_step<D>(st, cur, nxt, has_next, a, lsed_kvh, kvh, r0 + kRows, rows_total, la, need_mask, rmin, w, lane);
+        dkdv_step<D>(st, cur, nxt, has_next, a, gr, kvh, r0 + kRows, la, need_mask, rmin, w, lane);
     }
 
     // ---- write this wave's keys: dK (scaled) and dV, element i is key 8(i/4) + 4h + i%4
@@ -504,12 +552,12 @@ hipError_t launch_bwd_d(const AttnArgs& a, hipStream_t s) {
     constexpr int BM = 32 * NW;
     const int64_t rows_total = a.n_rows * a.g;
     const int64_t rows_pad = rows_padded(rows_total);
-    f32x2* lsed = (f32x2*)(a.dq_parts + (int64_t)a.n_parts * a.n_rows * a.hq * D);
+    const GroupRows gr = group_rows(a.dq_parts + (int64_t)a.n_parts * a.n_rows * a.hq * D, rows_pad, a.hkv, D);
     float* delta_th = const_cast<float*>(a.delta);
     if (rows_total > 0) {
         const int64_t waves = rows_pad * a.hkv;
         KernelTimer kt("bwd_prep", s);
-        bwd_prep_kernel<D><<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(a, rows_pad, lsed, delta_th);
+        bwd_prep_kernel<D><<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(a, gr, delta_th);
     }
     // dK / dV
     const int n_pp = (int)((a.n_logical_pages + 1) / 2);
@@ -517,22 +565,23 @@ hipError_t launch_bwd_d(const AttnArgs& a, hipStream_t s) {
     const int64_t nb_kv = (int64_t)(n_pp + n_rp) * a.hkv;
     if (nb_kv > 0) {
         KernelTimer kt("dkdv_mfma", s);
-        dkdv_mfma_kernel<D><<<pad_grid((int)nb_kv), 256, 0, s>>>(a, lsed, rows_pad, n_pp, n_rp, (int)nb_kv);
+        dkdv_mfma_kernel<D><<<pad_grid((int)nb_kv), 256, 0, s>>>(a, gr, n_pp, n_rp, (int)nb_kv);
     }
     // dQ parts
     const int64_t n_qtiles = (rows_total + BM - 1) / BM;
     const int64_t nb_q = n_qtiles * a.n_parts * a.hkv;
     if (nb_q > 0) {
         KernelTimer kt("dq_mfma", s);
-        dq_mfma_kernel<D, NW><<<pad_grid((int)nb_q), NW * 64, 0, s>>>(a, lsed, rows_pad, (int)n_qtiles, (int)nb_q);
+        dq_mfma_kernel<D, NW><<<pad_grid((int)nb_q), NW * 64, 0, s>>>(a, gr, (int)n_qtiles, (int)nb_q);
     }
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t mfma_bwd_extra_bytes(int64_t n_rows, int g, int hkv) {
-    return sizeof(f32x2) * (size_t)rows_padded(n_rows * g) * (size_t)hkv;
+size_t mfma_bwd_extra_bytes(int64_t n_rows, int g, int hkv, int d) {
+    const size_t rp = (size_t)rows_padded(n_rows * g);
+    return (sizeof(f32x2) + 2 * sizeof(bf16_t) * (size_t)d) * rp * (size_t)hkv;
 }
 
 hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t s) {

@@ -47,42 +47,59 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& ws, const LS_LDS char
     f32x16 s[2];
     s[0] = f32x16{};
     s[1] = f32x16{};
+    // LDS operands are read PD k-steps ahead of the MFMAs that use them; each sched_barrier
+    // keeps that order.
+    constexpr int PD = 3;
+    bf16x8 kbuf[PD][2];
+#pragma unroll
+    for (int j = 0; j < PD; j++) {
+        const LS_LDS char* pk = lds_k + (la.k ^ (uint32_t)(j << 5));
+        kbuf[j][0] = *(const LS_LDS bf16x8*)(pk);
+        kbuf[j][1] = *(const LS_LDS bf16x8*)(pk + 32 * 2 * D);
+    }
 #pragma unroll
     for (int ks = 0; ks < F::KS; ks++) {
-        const LS_LDS char* pk = lds_k + (la.k ^ (uint32_t)(ks << 5));
-        const bf16x8 k0 = *(const LS_LDS bf16x8*)(pk);
-        const bf16x8 k1 = *(const LS_LDS bf16x8*)(pk + 32 * 2 * D);
+        const bf16x8 k0 = kbuf[ks % PD][0], k1 = kbuf[ks % PD][1];
+        if (ks + PD < F::KS) {
+            const LS_LDS char* pk = lds_k + (la.k ^ (uint32_t)((ks + PD) << 5));
+            kbuf[ks % PD][0] = *(const LS_LDS bf16x8*)(pk);
+            kbuf[ks % PD][1] = *(const LS_LDS bf16x8*)(pk + 32 * 2 * D);
+        }
         s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ws.qb[ks], s[0], 0, 0, 0);
         s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, ws.qb[ks], s[1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- scale, mask, running max.  Element i of tile kt is key 32kt + 8(i/4) + 4h + i%4 of
-    // the page; the mask compares its lane-free part with two per-lane limits.
+    // ---- mask and running max on the raw scores (scale_log2 > 0 commutes with max).
+    // Element i of tile kt is key 32kt + 8(i/4) + 4h + i%4 of the page; the mask compares
+    // its lane-free part with two per-lane limits.
+    if (need_mask) {
+        const int lim_valid = src.valid - 4 * h;  // keys < valid exist
+        int lim_causal = 64;                      // response keys <= vis_limit are visible
+        if (resp) {
+            const int64_t c = vis_limit - src.key0 - 4 * h;
+            lim_causal = c < -1 ? -1 : (c > 64 ? 64 : (int)c);
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++) {
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int kc = 32 * kt + 8 * (i >> 2) + (i & 3);
+                s[kt][i] = (kc < lim_valid && kc <= lim_causal) ? s[kt][i] : -INFINITY;
+            }
+        }
+    }
     float mx = -INFINITY;
-    int lim_valid = src.valid - 4 * h;  // keys < valid exist
-    int lim_causal = 64;                // response keys <= vis_limit are visible
-    if (resp) {
-        const int64_t c = vis_limit - src.key0 - 4 * h;
-        lim_causal = c < -1 ? -1 : (c > 64 ? 64 : (int)c);
-    }
 #pragma unroll
     for (int kt = 0; kt < 2; kt++) {
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-            float x = s[kt][i] * scale_log2;
-            if (need_mask) {
-                const int kc = 32 * kt + 8 * (i >> 2) + (i & 3);
-                x = (kc < lim_valid && kc <= lim_causal) ? x : -INFINITY;
-            }
-            s[kt][i] = x;
-            mx = fmaxf(mx, x);
-        }
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kt][i], s[kt][i + 1]));
     }
-    mx = fmaxf(mx, other_half(mx));
+    mx = fmaxf(mx, other_half(mx)) * scale_log2;
     const float m_new = fmaxf(ws.m, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = fast_exp2(ws.m - m_use);
     ws.m = m_new;
-    // ---- P = exp2(S - m), packed to bf16 as the P^T operand
+    // ---- P = exp2(S * scale_log2 - m), packed to bf16 as the P^T operand
     bf16x8 pb[2][2];
     float lsum = 0.f;
 #pragma unroll
@@ -92,8 +109,8 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& ws, const LS_LDS char
             uint32_t w4[4];
 #pragma unroll
             for (int t = 0; t < 4; t++) {
-                const float p0 = fast_exp2(s[kt][8 * u + 2 * t] - m_use);
-                const float p1 = fast_exp2(s[kt][8 * u + 2 * t + 1] - m_use);
+                const float p0 = fast_exp2(__builtin_fmaf(s[kt][8 * u + 2 * t], scale_log2, -m_use));
+                const float p1 = fast_exp2(__builtin_fmaf(s[kt][8 * u + 2 * t + 1], scale_log2, -m_use));
                 lsum += p0 + p1;
                 w4[t] = pack_bf16x2(p0, p1);
             }
@@ -105,22 +122,27 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& ws, const LS_LDS char
 #pragma unroll
         for (int dt = 0; dt < F::DT; dt++) ws.o[dt] *= alpha;
     }
-    // ---- O^T += V^T P^T; rows (keys) 32kt + 16u + 8e + lane row, d tile dt
+    // ---- O^T += V^T P^T.  Step st = (kt, u, dt) with dt fastest, so consecutive MFMAs
+    // accumulate into different tiles; V^T fragments (rows 32kt + 16u + 8e) are read PV
+    // steps ahead.
+    constexpr int NST = 4 * F::DT;
+    constexpr int PV = 4;
+    i16x4 vlo[PV], vhi[PV];
+    auto read_v = [&](int st, i16x4& lo, i16x4& hi) {
+        const int dt = st % F::DT, ku = st / F::DT;
+        const int R = 32 * (ku >> 1) + 16 * (ku & 1);
+        lo = lds_read_tr4(lds_v + (la.v ^ tr_x<D>(dt, R)) + R * 2 * D);
+        hi = lds_read_tr4(lds_v + (la.v ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D);
+    };
 #pragma unroll
-    for (int dt = 0; dt < F::DT; dt++) {
-        const uint32_t x0 = la.v ^ (uint32_t)(((4 * dt) ^ (0 & F::SWZ)) << 4);
-        const uint32_t x1 = la.v ^ (uint32_t)(((4 * dt) ^ (8 & F::SWZ)) << 4);
+    for (int j = 0; j < PV; j++) read_v(j, vlo[j], vhi[j]);
 #pragma unroll
-        for (int kt = 0; kt < 2; kt++) {
-#pragma unroll
-            for (int u = 0; u < 2; u++) {
-                const int row = 32 * kt + 16 * u;
-                const i16x4 lo = lds_read_tr4(lds_v + x0 + row * 2 * D);
-                const i16x4 hi = lds_read_tr4(lds_v + x1 + (row + 8) * 2 * D);
-                const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                ws.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kt][u], ws.o[dt], 0, 0, 0);
-            }
-        }
+    for (int st = 0; st < NST; st++) {
+        const int dt = st % F::DT, ku = st / F::DT;
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[st % PV], vhi[st % PV], 0, 1, 2, 3, 4, 5, 6, 7));
+        if (st + PV < NST) read_v(st + PV, vlo[st % PV], vhi[st % PV]);
+        ws.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ku >> 1][ku & 1], ws.o[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -173,7 +195,10 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
         const int ld_head = kvh * a.g + (int)(ld_row % a.g);
         const bf16_t* qrow = (const bf16_t*)a.q + (ld_tok * a.hq + ld_head) * (int64_t)D + 8 * h;
 #pragma unroll
-        for (int ks = 0; ks < F::KS; ks++) ws.qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * ks));
+        for (int ks = 0; ks < F::KS; ks++) {
+            ws.qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * ks));
+            asm volatile("" : "+a"(ws.qb[ks]));  // read-only MFMA operand: keep it in AGPRs
+        }
 #pragma unroll
         for (int dt = 0; dt < F::DT; dt++) ws.o[dt] = f32x16{};
         ws.m = -INFINITY;

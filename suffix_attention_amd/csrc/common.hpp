@@ -21,18 +21,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kPage = 64;  // tokens per KV page
 
 // ----------------------------------------------------------------------------------------
-// Scalar conversions.  bf16 -> f32 is exact; f32 -> bf16 rounds to nearest-even (NaN kept
-// quiet).
+// Scalar conversions.  bf16 -> f32 is exact; f32 -> bf16 rounds to nearest-even in hardware.
 // ----------------------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(bf16_t x) {
     return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }
 
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<bf16_t>(u >> 16);
+    return __builtin_bit_cast(bf16_t, (__bf16)f);  // v_cvt_pk_bf16_f32: round to nearest even
 }
 
 template <typename T> __device__ __forceinline__ float load_f32(const T* p);
@@ -43,9 +39,12 @@ template <typename T> __device__ __forceinline__ void store_f32(T* p, float v);
 template <> __device__ __forceinline__ void store_f32<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void store_f32<bf16_t>(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
 // Pack two f32 to two bf16 (round to nearest-even) in one 32-bit word, low half first.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v{lo, hi}), bf16x2));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -92,8 +92,9 @@ hipError_t launch_bwd_generic(int dtype, const AttnArgs& a, hipStream_t s);
 // attn_mfma_fwd.hip / attn_mfma_bwd.hip: bf16 matrix-core kernels
 hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t s);
-// bytes the matrix-core backward keeps after the dQ parts: (LSE * log2 e, delta) per group row
-size_t mfma_bwd_extra_bytes(int64_t n_rows, int g, int hkv);
+// bytes the matrix-core backward keeps after the dQ parts: (LSE * log2 e, delta) and the Q
+// and dO rows of every kv head's group, group-major and padded to a multiple of 64 rows
+size_t mfma_bwd_extra_bytes(int64_t n_rows, int g, int hkv, int d);
 
 // Backward workspace layout (float32 elements from the start): delta [n_rows * hq] padded to a
 // multiple of 64, then dq_parts [n_parts, n_rows, hq, d], then the matrix-core extra.

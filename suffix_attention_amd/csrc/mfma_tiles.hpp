@@ -2,8 +2,8 @@
 // matrix-core kernels, and the per-lane LDS addressing of their operands.
 //
 // A tile is 64 rows x D bf16 (one page of one kv head, or 64 consecutive response keys,
-// or 64 query rows).  In LDS, 16-byte chunk c of row r holds logical chunk c ^ (r & SWZ),
-// which spreads the 32 rows read by one MFMA operand over the banks.  Tiles are filled by
+// or 64 query rows).  In LDS, 16-byte chunk c of row r holds logical chunk c ^ swz(r)
+// (below), which spreads both operand read patterns over the banks.  Tiles are filled by
 // direct global->LDS copies (16 bytes per lane, 1 KiB per wave instruction).
 #pragma once
 
@@ -17,9 +17,19 @@ struct TileShape {
     static constexpr int KCH = D / 8;                        // 16-byte chunks per row
     static constexpr int KS = D / 16;                        // k-steps of S over d
     static constexpr int DT = D / 32;                        // 32-wide d tiles of O
-    static constexpr int SWZ = (KCH >= 16 ? 16 : KCH) - 1;   // row -> chunk xor mask
     static constexpr int TILE = kPage * D * 2;               // bytes of one K or V page tile
 };
+
+// LDS swizzle: 16-byte chunk c of tile row r is stored at chunk c ^ swz(r).  swz is a bit
+// permutation of the row's low bits (so swz(a ^ b) = swz(a) ^ swz(b)) chosen so that
+//  - the 16 rows of one half of a natural operand read (32 rows, one chunk) hit 16 distinct
+//    bank groups, and
+//  - a transposed read (4 consecutive rows x 4 consecutive chunks per 32 lanes) hits 16
+//    distinct bank groups.
+template <int D>
+__host__ __device__ constexpr int swz(int r) {
+    return TileShape<D>::KCH >= 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r & 1) << 2) | ((r >> 1) & 3));
+}
 
 struct TileSrc {
     const bf16_t* k;
@@ -60,64 +70,87 @@ __device__ __forceinline__ TileSrc part_tile(const AttnArgs& a, bool resp, int p
     return s;
 }
 
-// Issue the direct-to-LDS copies of one K and one V page tile (all waves together).  Wave
-// w's j-th copy fills 1 KiB block j*NW + w of the tile, i.e. RPK = 512/D whole rows; lane l
-// writes 16-byte slot l of the block, so it fetches the logical chunk that the xor swizzle
-// puts there.  `w` must be wave-uniform.
+// Direct-to-LDS copy of ROWS full rows (D bf16 each, rows `stride` elements apart) from two
+// sources a, b into two LDS tiles, by all NW waves together.  Wave w's j-th copy fills 1 KiB
+// block j*NW + w of a tile, i.e. RPK = 512/D whole rows; lane l writes 16-byte slot l of the
+// block, so it fetches the logical chunk that the swizzle puts there.  `w` must be
+// wave-uniform.
+template <int D, int NW, int ROWS>
+__device__ __forceinline__ void dma_rows(const bf16_t* a, const bf16_t* b, int64_t stride, char* lds_a,
+                                         char* lds_b, int w, int lane) {
+    using F = TileShape<D>;
+    constexpr int RPK = 512 / D;                 // rows per 1 KiB block
+    constexpr int PER_WAVE = ROWS * D * 2 / 1024 / NW;
+    constexpr int JROWS = NW * RPK;              // rows advanced per j (a power of two)
+    static_assert(PER_WAVE * NW * 1024 == ROWS * D * 2, "tile must split evenly over the waves");
+    const int low = w * RPK + lane / F::KCH;     // row inside the j-th group of JROWS rows
+    const int pc = lane % F::KCH;                // 16-byte slot inside the row
+    const int lane_x = pc ^ swz<D>(low);
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; j++) {
+        const int lc = lane_x ^ swz<D>(j * JROWS);
+        const uint32_t off = (uint32_t)(low * (int)stride + lc * 8) * 2u;
+        const int64_t rowj = (int64_t)(j * JROWS) * stride * 2;
+        const int blk = j * NW + w;
+        dma16((const char*)a + rowj + off, (LS_LDS void*)(lds_a + blk * 1024));
+        dma16((const char*)b + rowj + off, (LS_LDS void*)(lds_b + blk * 1024));
+    }
+}
+
+// Issue the direct-to-LDS copies of one K and one V page tile (all waves together).
 template <int D, int NW>
 __device__ __forceinline__ void issue_tile(const TileSrc& s, char* lds_k, char* lds_v, int w,
                                            int lane) {
     using F = TileShape<D>;
-    constexpr int RPK = 512 / D;                 // rows per 1 KiB block
-    constexpr int PER_WAVE = F::TILE / 1024 / NW;
-    constexpr int JROWS = NW * RPK;              // rows advanced per j (a power of two)
-    const int low = w * RPK + lane / F::KCH;     // row inside the j-th group of JROWS rows
-    const int pc = lane % F::KCH;                // 16-byte slot inside the row
-    const int lane_x = pc ^ (low & F::SWZ);
     if (s.valid == kPage) {
+        dma_rows<D, NW, kPage>(s.k, s.v, s.stride, lds_k, lds_v, w, lane);
+        return;
+    }
+    // a partial tile: rows past `valid` repeat the last valid row (finite, masked later)
+    constexpr int RPK = 512 / D;
+    constexpr int PER_WAVE = F::TILE / 1024 / NW;
+    constexpr int JROWS = NW * RPK;
+    const int low = w * RPK + lane / F::KCH;
+    const int pc = lane % F::KCH;
+    const int lane_x = pc ^ swz<D>(low);
 #pragma unroll
-        for (int j = 0; j < PER_WAVE; j++) {
-            const int lc = lane_x ^ ((j * JROWS) & F::SWZ);
-            const uint32_t off = (uint32_t)(low * (int)s.stride + lc * 8) * 2u;
-            const int64_t rowj = (int64_t)(j * JROWS) * s.stride * 2;
-            const char* bk = (const char*)s.k + rowj;
-            const char* bv = (const char*)s.v + rowj;
-            const int blk = j * NW + w;
-            dma16(bk + off, (LS_LDS void*)(lds_k + blk * 1024));
-            dma16(bv + off, (LS_LDS void*)(lds_v + blk * 1024));
-        }
-    } else {
-        // a partial tile: rows past `valid` repeat the last valid row (finite, masked later)
-#pragma unroll
-        for (int j = 0; j < PER_WAVE; j++) {
-            const int r = j * JROWS + low;
-            const int lc = lane_x ^ ((j * JROWS) & F::SWZ);
-            const int rs = r < s.valid ? r : s.valid - 1;
-            const uint32_t off = (uint32_t)(rs * (int)s.stride + lc * 8) * 2u;
-            const int blk = j * NW + w;
-            dma16((const char*)s.k + off, (LS_LDS void*)(lds_k + blk * 1024));
-            dma16((const char*)s.v + off, (LS_LDS void*)(lds_v + blk * 1024));
-        }
+    for (int j = 0; j < PER_WAVE; j++) {
+        const int r = j * JROWS + low;
+        const int lc = lane_x ^ swz<D>(j * JROWS);
+        const int rs = r < s.valid ? r : s.valid - 1;
+        const uint32_t off = (uint32_t)(rs * (int)s.stride + lc * 8) * 2u;
+        const int blk = j * NW + w;
+        dma16((const char*)s.k + off, (LS_LDS void*)(lds_k + blk * 1024));
+        dma16((const char*)s.v + off, (LS_LDS void*)(lds_v + blk * 1024));
     }
 }
 
-// Per-lane LDS byte offsets inside a page tile.  With the xor swizzle, the address of
-// chunk `lc` of row `r` is r*2D + ((lc ^ (r & SWZ)) << 4); splitting r and lc into lane-fixed
-// and step-varying bits turns every operand read into (lane base ^ constant) + constant.
+// Per-lane LDS byte offsets inside a tile.  Splitting the row and chunk of every operand read
+// into lane-fixed and step-varying parts turns its address into (lane base ^ constant) +
+// constant, because swz is linear over xor.
+//  - natural reads (an MFMA operand whose contraction runs along a row): lane reads row
+//    lane%32 (+32kt), chunk 2ks + lane/32:  (k ^ (ks << 5)) + 32kt * 2D;
+//  - transposed reads (ds_read_b64_tr_b16; contraction down the rows): for rows R + 0..7
+//    (R a multiple of 8) and 32-wide d tile dt:  (v ^ tr_x(dt, R)) + R * 2D.
 template <int D>
 struct LaneAddr {
-    uint32_t k;  // K rows lane%32: XOR with (ks << 5) selects chunk 2ks + lane/32
-    uint32_t v;  // V^T transpose reads: XOR with ((4dt ^ (8e & SWZ)) << 4)
+    uint32_t k;
+    uint32_t v;
     __device__ __forceinline__ LaneAddr(int lane) {
-        using F = TileShape<D>;
         const int h = lane >> 5, n = lane & 31;
-        k = n * 2 * D + ((h ^ (n & F::SWZ)) << 4);
+        k = n * 2 * D + ((h ^ swz<D>(n)) << 4);
         const int G = lane >> 4, i16 = lane & 15;
         const int c_lane = 4 * (G >> 1) + (i16 >> 2);          // row within an 8-row group
         const int l_lane = 2 * (G & 1) + ((i16 & 3) >> 1);     // chunk within a 32-wide d tile
         const int half8 = (i16 & 1) * 8;                       // byte inside the 16-byte chunk
-        v = c_lane * 2 * D + half8 + ((l_lane ^ c_lane) << 4);
+        v = c_lane * 2 * D + half8 + ((l_lane ^ swz<D>(c_lane)) << 4);
     }
 };
+
+// xor constant of a transposed read of rows R.. (R % 8 == 0) in d tile dt
+template <int D>
+__host__ __device__ constexpr uint32_t tr_x(int dt, int R) {
+    return (uint32_t)(((4 * dt) ^ swz<D>(R)) << 4);
+}
 
 }  // namespace ls

@@ -74,6 +74,7 @@ def _err():
     (dict(page_table=None), LS_ERR_INVALID, "non-NULL"),
     (dict(prefix_len=-1), LS_ERR_INVALID, "prefix_len"),
     (dict(softmax_scale=float("nan")), LS_ERR_INVALID, "softmax_scale"),
+    (dict(softmax_scale=-0.5), LS_ERR_INVALID, "softmax_scale"),
 ])
 def test_fwd_rejects_bad_prefix(kw, code, msg):
     assert _fwd(_prefix(**kw)) == code
@@ -97,7 +98,8 @@ def test_workspace_size_and_errors():
     assert _fwd(p, ws_bytes=need - 1) == LS_ERR_WORKSPACE
     assert _fwd(p, ws=None) == LS_ERR_WORKSPACE
     nb = lib.ls_bwd_workspace_bytes(C.byref(p), 16)
-    assert nb == 4 * (128 + 3 * 16 * 8 * 256) + 8 * 64 * 2  # delta, dQ parts, (lse2, delta) per group row
+    # delta, dQ parts, then per kv head and padded group row: (lse2, delta) and bf16 Q, dO rows
+    assert nb == 4 * (128 + 3 * 16 * 8 * 256) + (8 + 2 * 2 * 256) * 64 * 2
     assert lib.ls_fwd_workspace_bytes(C.byref(_prefix(hq=7)), 16) == 0
     assert "multiple" in _err()
 
