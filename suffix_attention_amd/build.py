@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "liblongstraw.so")
 SOURCES = ["abi.cpp", "profile.cpp", "capture.hip", "reduce.hip", "attn_generic.hip", "attn_mfma_fwd.hip",
-           "attn_mfma_bwd.hip"]
+           "attn_mfma_bwd.hip", "attn_mfma_dq.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -31,9 +31,12 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
          "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 
-# The forward keeps its output accumulators in VGPRs (they are rescaled on the vector ALUs
-# when the running max grows); the backward kernels keep theirs in AGPRs.
-PER_SOURCE = {"attn_mfma_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Matrix-core accumulators go to VGPRs in the forward (O is rescaled on the vector ALUs when
+# the running max grows) and in the dQ pass (its S / dP tiles feed vector-ALU work every
+# page, its read-only Q / dO operands sit in AGPRs); the dK/dV pass keeps its 256 dK/dV
+# accumulators in AGPRs.
+PER_SOURCE = {"attn_mfma_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "attn_mfma_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src, extra):

@@ -45,6 +45,31 @@ __device__ __forceinline__ int32_t phys_page(const AttnArgs& a, int part, int64_
     return phys < 0 ? 0 : (phys >= a.n_phys ? (int32_t)(a.n_phys - 1) : phys);
 }
 
+// Scalar pieces of tile t of a part starting at logical page lp0 (prompt) or key 0 (response):
+// its physical page, base pointer of K or V, row stride and number of valid rows.
+__device__ __forceinline__ int32_t page_phys(const AttnArgs& a, bool resp, int64_t lp0, int64_t t) {
+    if (resp) return 0;
+    const int32_t phys = a.table[lp0 + t];
+    return phys < 0 ? 0 : (phys >= a.n_phys ? (int32_t)(a.n_phys - 1) : phys);
+}
+
+template <int D>
+__device__ __forceinline__ const bf16_t* tile_ptr(const AttnArgs& a, bool resp, int64_t lp0, int64_t t, int32_t phys,
+                                                  int kvh, bool v) {
+    if (!resp) return (const bf16_t*)(v ? a.v_pages : a.k_pages) + ((int64_t)phys * a.hkv + kvh) * kPage * D;
+    return (const bf16_t*)(v ? a.v_resp : a.k_resp) + (t * kPage * a.hkv + kvh) * D;
+}
+
+template <int D>
+__device__ __forceinline__ int64_t tile_stride(const AttnArgs& a, bool resp) {
+    return resp ? (int64_t)a.hkv * D : D;
+}
+
+__device__ __forceinline__ int tile_valid(const AttnArgs& a, bool resp, int64_t lp0, int64_t t) {
+    const int64_t left = resp ? a.key_end - t * kPage : a.prefix_len - (lp0 + t) * kPage;
+    return left < kPage ? (int)left : kPage;
+}
+
 // Source of tile t of a part; `phys` is its physical page (prompt parts only).
 __device__ __forceinline__ TileSrc part_tile(const AttnArgs& a, bool resp, int part, int kvh,
                                              int64_t t, int32_t phys) {
@@ -94,6 +119,38 @@ __device__ __forceinline__ void dma_rows(const bf16_t* a, const bf16_t* b, int64
         const int blk = j * NW + w;
         dma16((const char*)a + rowj + off, (LS_LDS void*)(lds_a + blk * 1024));
         dma16((const char*)b + rowj + off, (LS_LDS void*)(lds_b + blk * 1024));
+    }
+}
+
+// Copy one 64-row tile from one source (K or V of a page, or 64 response keys) into LDS;
+// rows past `valid` repeat the last valid row (finite, masked later).
+template <int D, int NW>
+__device__ __forceinline__ void issue_one(const bf16_t* src, int64_t stride, int valid, char* lds, int w,
+                                          int lane) {
+    using F = TileShape<D>;
+    constexpr int RPK = 512 / D;
+    constexpr int PER_WAVE = F::TILE / 1024 / NW;
+    constexpr int JROWS = NW * RPK;
+    const int low = w * RPK + lane / F::KCH;
+    const int pc = lane % F::KCH;
+    const int lane_x = pc ^ swz<D>(low);
+    if (valid == kPage) {
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; j++) {
+            const int lc = lane_x ^ swz<D>(j * JROWS);
+            const uint32_t off = (uint32_t)(low * (int)stride + lc * 8) * 2u;
+            const int64_t rowj = (int64_t)(j * JROWS) * stride * 2;
+            dma16((const char*)src + rowj + off, (LS_LDS void*)(lds + (j * NW + w) * 1024));
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; j++) {
+            const int r = j * JROWS + low;
+            const int lc = lane_x ^ swz<D>(j * JROWS);
+            const int rs = r < valid ? r : valid - 1;
+            const uint32_t off = (uint32_t)(rs * (int)stride + lc * 8) * 2u;
+            dma16((const char*)src + off, (LS_LDS void*)(lds + (j * NW + w) * 1024));
+        }
     }
 }
 
