@@ -31,12 +31,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
          "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 
-# Matrix-core accumulators go to VGPRs in the forward (O is rescaled on the vector ALUs when
-# the running max grows) and in the dQ pass (its S / dP tiles feed vector-ALU work every
-# page, its read-only Q / dO operands sit in AGPRs); the dK/dV pass keeps its 256 dK/dV
-# accumulators in AGPRs.
-PER_SOURCE = {"attn_mfma_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-              "attn_mfma_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Matrix-core accumulators go to VGPRs in the dQ pass (its S / dP tiles feed vector-ALU work
+# every page, its read-only Q / dO operands sit in AGPRs); the forward keeps O in AGPRs and
+# the dK/dV pass its 256 dK/dV accumulators.
+PER_SOURCE = {"attn_mfma_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src, extra):

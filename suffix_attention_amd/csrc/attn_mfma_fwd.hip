@@ -1,24 +1,34 @@
 // Split-prefix replay-attention forward on gfx950 bf16 matrix cores.
 //
-// One workgroup handles BM = 32 * NW query rows of one kv head's group against the keys of
-// one part: a prompt shard (a contiguous range of logical pages, walked through the page
-// table) or the response keys the rows see (causal).  It writes the part's normalised
-// output and LSE, the owner-local softmax statistics that the merge composes into the exact
-// result (LongStraw digest, "Method", Qwen implementation; explainer, "Two incompatible
+// One workgroup handles BM = 128 query rows of one kv head's group against the keys of one
+// part: a prompt shard (a contiguous range of logical pages, walked through the page table)
+// or the response keys the rows see (causal).  It writes the part's normalised output and
+// LSE, the owner-local softmax statistics that the merge composes into the exact result
+// (LongStraw digest, "Method", Qwen implementation; explainer, "Two incompatible
 // architectures, same transaction").
 //
-// Per wave (32 rows), per 64-key page:
-//   S^T[64 x 32] = K[64 x D] . Q^T        v_mfma_f32_32x32x16_bf16, K from LDS, Q in VGPRs
-//   online softmax in base 2               each lane owns one row: in-lane max/sum, one
-//                                          cross-half exchange (v_permlane32_swap)
-//   O^T[D x 32] += V^T[D x 64] . P^T       V read transposed from LDS (ds_read_b64_tr_b16),
-//                                          P^T taken straight from the S^T accumulators
+// Eight waves, two per SIMD, in two roles over the same four 32-row groups:
+//   score wave g   S^T(t)[64 x 32] = K(t) . Q^T     v_mfma_f32_32x32x16_bf16, K from LDS,
+//                                                  Q in AGPRs
+//                  online softmax of page t         each lane owns one row; P(t) goes to LDS
+//                                                  already in the layout of an MFMA operand
+//   output wave g  O^T[D x 32] += V(t-1)^T P(t-1)^T V read transposed from LDS
+//                                                  (ds_read_b64_tr_b16), O in AGPRs
+// Every page has two barriers: after the first the score waves multiply while the output
+// waves fetch P; after the second the output waves multiply while the score waves run the
+// softmax.  The two waves of a SIMD thus take turns on its matrix core, and each one's
+// vector work hides under the other's matrix work.  Splitting the roles also halves the
+// registers a wave needs (the 32 x D output tile alone is 128 registers at D = 256), which
+// is what lets two waves share a SIMD.
+//
 // Keys are permuted inside each 16-key MFMA step so that P^T needs no data movement: the
 // order is the same on both operands, so the sum is unchanged.
 //
-// K/V pages (64 x D bf16 each, one contiguous tile per (page, kv head)) are copied into a
-// double-buffered LDS stage by direct global->LDS loads, issued one page ahead.  A 16-byte
-// chunk c of LDS row r holds logical chunk c ^ (r & 15) to spread rows over the banks.
+// The softmax keeps a running reference m for each row and moves it only when the page max
+// exceeds it by more than kLazyLog2 (base 2); probabilities are then at most 2^kLazyLog2,
+// which bf16 and the fp32 sums hold exactly as well as values below 1, and the output
+// rescale is skipped on almost every page.  The result is the same softmax: every term and
+// the sum are taken relative to the same m.
 #include <math.h>
 
 #include "mfma_tiles.hpp"
@@ -26,34 +36,66 @@
 namespace ls {
 namespace {
 
-template <int D>
-struct WaveState {
-    bf16x8 qb[TileShape<D>::KS];   // Q^T operand: row lane%32, d = 16ks + 8(lane/32) .. +8
-    f32x16 o[TileShape<D>::DT];    // O^T accumulators: col = row, rows = d
-    float m;                      // running max (base-2 scaled scores)
-    float l;                      // running sum of this lane's half of the keys
-};
+constexpr float kLazyLog2 = 8.f;
+constexpr int kNW = 8;           // waves per workgroup
+constexpr int kGroups = 4;       // 32-row groups per workgroup
+constexpr int kBM = 32 * kGroups;
 
 template <int D>
-__device__ __forceinline__ void compute_tile(WaveState<D>& ws, const LS_LDS char* lds_k,
-                                             const LS_LDS char* lds_v, LaneAddr<D> la,
-                                             const TileSrc& src, bool resp, bool need_mask,
-                                             int64_t vis_limit, float scale_log2, int lane) {
+struct FwdLds {
+    static constexpr int TILE = TileShape<D>::TILE;
+    static constexpr int P_BYTES = 4 * 64 * 16;   // one group's P^T operands: 4 key steps x 64 lanes x 16 B
+    char kb[2][TILE];
+    char vb[2][TILE];
+    char p[kGroups][P_BYTES];
+    float alpha[kGroups][32];
+    float fin_l[kGroups][32];
+};
+
+// Raw s_barrier after this wave's LDS accesses have completed.  The direct-to-LDS copies in
+// flight are left alone (a workgroup fence would wait for them too).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Copies issued in iteration t by all eight waves: K(t+1) into k_dst and V(t) into v_dst.
+template <int D>
+__device__ __forceinline__ void issue_copies(const AttnArgs& a, bool resp, int64_t lp0, int kvh, int64_t n_tiles,
+                                             int64_t t, int32_t phys_t, int32_t phys_t1, char* k_dst, char* v_dst,
+                                             int w, int lane) {
+    const int64_t stride = tile_stride<D>(a, resp);
+    if (t + 1 < n_tiles)
+        issue_one<D, kNW>(tile_ptr<D>(a, resp, lp0, t + 1, phys_t1, kvh, false), stride,
+                          tile_valid(a, resp, lp0, t + 1), k_dst, w, lane);
+    if (t < n_tiles)
+        issue_one<D, kNW>(tile_ptr<D>(a, resp, lp0, t, phys_t, kvh, true), stride, tile_valid(a, resp, lp0, t),
+                          v_dst, w, lane);
+}
+
+// Where the keys of the workgroup's part come from, and the rows it serves.
+struct PartInfo {
+    bool resp;
+    int kvh;
+    int64_t lp0;        // first logical page (prompt shard)
+    int64_t n_tiles;
+    int64_t tok_min;    // first token of the workgroup's rows
+};
+
+// ---------------------------------------------------------------------------------------
+// score role
+// ---------------------------------------------------------------------------------------
+
+// S^T(t) = K(t) Q^T for the wave's 32 rows: two 32-key tiles, KS k-steps each, K fragments
+// read PD steps ahead.
+template <int D>
+__device__ __forceinline__ void scores(const bf16x8 (&qb)[TileShape<D>::KS], f32x16 (&s)[2], const LS_LDS char* lds_k,
+                                       uint32_t lk) {
     using F = TileShape<D>;
-    const int h = lane >> 5;
-    // keep the per-lane offsets from being hoisted out of the page loop as many registers
-    asm volatile("" : "+v"(la.k), "+v"(la.v));
-    // ---- S^T = K Q^T for the two 32-key halves of the page
-    f32x16 s[2];
+    constexpr int PD = 2;
+    bf16x8 kbuf[PD][2];
     s[0] = f32x16{};
     s[1] = f32x16{};
-    // LDS operands are read PD k-steps ahead of the MFMAs that use them; each sched_barrier
-    // keeps that order.
-    constexpr int PD = 3;
-    bf16x8 kbuf[PD][2];
 #pragma unroll
     for (int j = 0; j < PD; j++) {
-        const LS_LDS char* pk = lds_k + (la.k ^ (uint32_t)(j << 5));
+        const LS_LDS char* pk = lds_k + (lk ^ (uint32_t)(j << 5));
         kbuf[j][0] = *(const LS_LDS bf16x8*)(pk);
         kbuf[j][1] = *(const LS_LDS bf16x8*)(pk + 32 * 2 * D);
     }
@@ -61,78 +103,90 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& ws, const LS_LDS char
     for (int ks = 0; ks < F::KS; ks++) {
         const bf16x8 k0 = kbuf[ks % PD][0], k1 = kbuf[ks % PD][1];
         if (ks + PD < F::KS) {
-            const LS_LDS char* pk = lds_k + (la.k ^ (uint32_t)((ks + PD) << 5));
+            const LS_LDS char* pk = lds_k + (lk ^ (uint32_t)((ks + PD) << 5));
             kbuf[ks % PD][0] = *(const LS_LDS bf16x8*)(pk);
             kbuf[ks % PD][1] = *(const LS_LDS bf16x8*)(pk + 32 * 2 * D);
         }
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ws.qb[ks], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, ws.qb[ks], s[1], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qb[ks], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qb[ks], s[1], 0, 0, 0);
     }
-    // ---- mask and running max on the raw scores (scale_log2 > 0 commutes with max).
-    // Element i of tile kt is key 32kt + 8(i/4) + 4h + i%4 of the page; the mask compares
-    // its lane-free part with two per-lane limits.
-    if (need_mask) {
-        const int lim_valid = src.valid - 4 * h;  // keys < valid exist
-        int lim_causal = 64;                      // response keys <= vis_limit are visible
-        if (resp) {
-            const int64_t c = vis_limit - src.key0 - 4 * h;
-            lim_causal = c < -1 ? -1 : (c > 64 ? 64 : (int)c);
-        }
+}
+
+// Mask page t's scores: element i of tile kt is key 32kt + 8(i/4) + 4h + i%4 of the page; the
+// mask compares its lane-free part with two per-lane limits (valid keys of the page and, for
+// response keys, the causal limit of this lane's row).
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int valid, int64_t key0, bool resp, int64_t vis_limit,
+                                            int h) {
+    const int lim_valid = valid - 4 * h;
+    int lim_causal = 64;
+    if (resp) {
+        const int64_t c = vis_limit - key0 - 4 * h;
+        lim_causal = c < -1 ? -1 : (c > 64 ? 64 : (int)c);
+    }
 #pragma unroll
-        for (int kt = 0; kt < 2; kt++) {
+    for (int kt = 0; kt < 2; kt++) {
 #pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int kc = 32 * kt + 8 * (i >> 2) + (i & 3);
-                s[kt][i] = (kc < lim_valid && kc <= lim_causal) ? s[kt][i] : -INFINITY;
-            }
+        for (int i = 0; i < 16; i++) {
+            const int kc = 32 * kt + 8 * (i >> 2) + (i & 3);
+            s[kt][i] = (kc < lim_valid && kc <= lim_causal) ? s[kt][i] : -INFINITY;
         }
     }
+}
+
+// Online softmax of one page for this lane's row; writes P^T (bf16, MFMA B-operand layout:
+// key step ku = 2kt + u at [ku][lane]) and the row's rescale factor to LDS.
+__device__ __forceinline__ void softmax_page(f32x16 (&s)[2], float& m_ref, float& l, float scale_log2,
+                                             LS_LDS char* p_out, LS_LDS float* alpha_out, int lane) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; kt++) {
+    for (int kt = 0; kt < 2; kt++)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kt][i], s[kt][i + 1]));
-    }
+    // max on raw scores: scale_log2 > 0 commutes with max
     mx = fmaxf(mx, other_half(mx)) * scale_log2;
-    const float m_new = fmaxf(ws.m, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(ws.m - m_use);
-    ws.m = m_new;
-    // ---- P = exp2(S * scale_log2 - m), packed to bf16 as the P^T operand
-    bf16x8 pb[2][2];
+    float alpha = 1.f;
+    if (mx > m_ref + kLazyLog2) {  // false for a fully masked page (mx = -inf)
+        alpha = fast_exp2(m_ref - mx);  // 0 on the first page (m_ref = -inf)
+        m_ref = mx;
+    }
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
     float lsum = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 2; kt++) {
+    for (int ku = 0; ku < 4; ku++) {
+        const int kt = ku >> 1, u = ku & 1;
+        uint32_t wd[4];
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-            uint32_t w4[4];
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                const float p0 = fast_exp2(__builtin_fmaf(s[kt][8 * u + 2 * t], scale_log2, -m_use));
-                const float p1 = fast_exp2(__builtin_fmaf(s[kt][8 * u + 2 * t + 1], scale_log2, -m_use));
-                lsum += p0 + p1;
-                w4[t] = pack_bf16x2(p0, p1);
-            }
-            pb[kt][u] = __builtin_bit_cast(bf16x8, (u32x4{w4[0], w4[1], w4[2], w4[3]}));
+        for (int t = 0; t < 4; t++) {
+            const float p0 = fast_exp2(__builtin_fmaf(s[kt][8 * u + 2 * t], scale_log2, -m_use));
+            const float p1 = fast_exp2(__builtin_fmaf(s[kt][8 * u + 2 * t + 1], scale_log2, -m_use));
+            lsum += p0 + p1;
+            wd[t] = pack_bf16x2(p0, p1);
         }
+        *(LS_LDS u32x4*)(p_out + (ku * 64 + lane) * 16) = u32x4{wd[0], wd[1], wd[2], wd[3]};
     }
-    ws.l = ws.l * alpha + lsum;
-    if (!__all(alpha == 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < F::DT; dt++) ws.o[dt] *= alpha;
-    }
-    // ---- O^T += V^T P^T.  Step st = (kt, u, dt) with dt fastest, so consecutive MFMAs
-    // accumulate into different tiles; V^T fragments (rows 32kt + 16u + 8e) are read PV
-    // steps ahead.
+    l = l * alpha + lsum;
+    if (lane < 32) alpha_out[lane] = alpha;
+}
+
+// ---------------------------------------------------------------------------------------
+// output role
+// ---------------------------------------------------------------------------------------
+
+// O^T += V^T P^T over one page.  Step st = (ku, dt) with dt fastest, so consecutive MFMAs
+// accumulate into different tiles; V^T fragments (rows 32kt + 16u + 8e) are read PV steps
+// ahead.
+template <int D>
+__device__ __forceinline__ void accumulate_pv(f32x16 (&o)[TileShape<D>::DT], const bf16x8 (&pb)[4],
+                                              const LS_LDS char* lds_v, uint32_t lv) {
+    using F = TileShape<D>;
     constexpr int NST = 4 * F::DT;
     constexpr int PV = 4;
     i16x4 vlo[PV], vhi[PV];
     auto read_v = [&](int st, i16x4& lo, i16x4& hi) {
         const int dt = st % F::DT, ku = st / F::DT;
         const int R = 32 * (ku >> 1) + 16 * (ku & 1);
-        lo = lds_read_tr4(lds_v + (la.v ^ tr_x<D>(dt, R)) + R * 2 * D);
-        hi = lds_read_tr4(lds_v + (la.v ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D);
+        lo = lds_read_tr4(lds_v + (lv ^ tr_x<D>(dt, R)) + R * 2 * D);
+        hi = lds_read_tr4(lds_v + (lv ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D);
     };
 #pragma unroll
     for (int j = 0; j < PV; j++) read_v(j, vlo[j], vhi[j]);
@@ -141,33 +195,71 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& ws, const LS_LDS char
         const int dt = st % F::DT, ku = st / F::DT;
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[st % PV], vhi[st % PV], 0, 1, 2, 3, 4, 5, 6, 7));
         if (st + PV < NST) read_v(st + PV, vlo[st % PV], vhi[st % PV]);
-        ws.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ku >> 1][ku & 1], ws.o[dt], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ku], o[dt], 0, 0, 0);
     }
 }
 
-// One pipeline step: start copying the next page into the other LDS stage, then compute on
-// the current one.  The stages are passed as restrict pointers so that, once inlined, the
-// compiler knows the copies cannot alias the reads and does not wait for them.
-template <int D, int NW>
-__device__ __forceinline__ void fwd_step(WaveState<D>& ws, const char* __restrict__ cur,
-                                         char* __restrict__ nxt, bool has_next,
-                                         const TileSrc& next_src, const TileSrc& src,
-                                         LaneAddr<D> la, bool resp, bool need_mask,
-                                         int64_t vis_limit, float scale_log2, int w, int lane) {
-    using F = TileShape<D>;
-    if (has_next) issue_tile<D, NW>(next_src, nxt, nxt + F::TILE, w, lane);
-    compute_tile<D>(ws, (const LS_LDS char*)cur, (const LS_LDS char*)(cur + F::TILE), la, src, resp,
-                    need_mask, vis_limit, scale_log2, lane);
+// One iteration of each role.  Every pointer to LDS is restrict-qualified so that, once
+// inlined, the compiler knows the copies just issued cannot alias the tiles being read and
+// does not wait for them before each read.
+
+// Score role, iteration t: S(t) while the output waves fetch P(t-1); then the softmax of
+// page t while they multiply.
+template <int D>
+__device__ __forceinline__ void score_iter(const AttnArgs& a, const PartInfo& pi, int64_t t, int32_t phys_t,
+                                           int32_t phys_t1, char* __restrict__ k_dst, char* __restrict__ v_dst,
+                                           const char* __restrict__ k_cur, char* __restrict__ p_out,
+                                           float* __restrict__ alpha_out, const bf16x8 (&qb)[TileShape<D>::KS],
+                                           float& m_ref, float& l, int64_t vis_limit, uint32_t lk, int w, int lane) {
+    wait_vm_all();
+    lds_barrier();
+    issue_copies<D>(a, pi.resp, pi.lp0, pi.kvh, pi.n_tiles, t, phys_t, phys_t1, k_dst, v_dst, w, lane);
+    f32x16 s[2];
+    const bool live = t < pi.n_tiles;
+    if (live) scores<D>(qb, s, (const LS_LDS char*)k_cur, lk);
+    lds_barrier();
+    if (live) {
+        const int valid = tile_valid(a, pi.resp, pi.lp0, t);
+        const int64_t key0 = (pi.lp0 + t) * kPage;
+        if (valid < kPage || (pi.resp && key0 + kPage - 1 > a.q_start + pi.tok_min))
+            mask_scores(s, valid, key0, pi.resp, vis_limit, lane >> 5);
+        softmax_page(s, m_ref, l, a.scale_log2, (LS_LDS char*)p_out, (LS_LDS float*)alpha_out, lane);
+    }
 }
 
-template <int D, int NW>
-__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(1, 1)))
+// Output role, iteration t >= 1: fetch P(t-1) while the score waves multiply; then rescale O
+// if a row's reference moved and accumulate V(t-1) P(t-1).
+template <int D>
+__device__ __forceinline__ void output_iter(const AttnArgs& a, const PartInfo& pi, int64_t t, int32_t phys_t,
+                                            int32_t phys_t1, char* __restrict__ k_dst, char* __restrict__ v_dst,
+                                            const char* __restrict__ v_prev, const char* __restrict__ p_in,
+                                            const float* __restrict__ alpha_in, f32x16 (&o)[TileShape<D>::DT],
+                                            uint32_t lv, int w, int lane) {
+    using F = TileShape<D>;
+    wait_vm_all();
+    lds_barrier();
+    issue_copies<D>(a, pi.resp, pi.lp0, pi.kvh, pi.n_tiles, t, phys_t, phys_t1, k_dst, v_dst, w, lane);
+    bf16x8 pb[4];
+#pragma unroll
+    for (int ku = 0; ku < 4; ku++) pb[ku] = *(const LS_LDS bf16x8*)((const LS_LDS char*)p_in + (ku * 64 + lane) * 16);
+    const float alpha = ((const LS_LDS float*)alpha_in)[lane & 31];
+    lds_barrier();
+    if (!__all(alpha == 1.f)) {
+        mfma_drain();
+#pragma unroll
+        for (int dt = 0; dt < F::DT; dt++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) o[dt][i] = agpr_scaled(o[dt][i], alpha);
+        agpr_write_gap();
+    }
+    accumulate_pv<D>(o, pb, (const LS_LDS char*)v_prev, lv);
+}
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kNW * 64, kNW * 64), amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
     using F = TileShape<D>;
-    constexpr int BM = 32 * NW;
-    __shared__ __attribute__((aligned(1024))) char st0[2 * F::TILE];
-    __shared__ __attribute__((aligned(1024))) char st1[2 * F::TILE];
+    __shared__ __attribute__((aligned(1024))) FwdLds<D> L;
 
     const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
     if (lb >= n_blocks) return;
@@ -178,96 +270,140 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
+    const int g = w & (kGroups - 1);
+    const bool score_role = w < kGroups;
     const int h = lane >> 5;
     const int n = lane & 31;
     const int64_t rows_total = a.n_rows * a.g;
-    const int64_t r0 = (int64_t)qtile * BM;
-    const int64_t my_row = r0 + 32 * w + n;
+    const int64_t r0 = (int64_t)qtile * kBM;
+    const int64_t my_row = r0 + 32 * g + n;
     const bool row_ok = my_row < rows_total;
     const int64_t my_tok = my_row / a.g;
     const int my_head = kvh * a.g + (int)(my_row % a.g);
 
-    WaveState<D> ws;
-    {
-        // rows past the block (a partial last tile) read a valid row and are never stored
-        const int64_t ld_row = row_ok ? my_row : rows_total - 1;
-        const int64_t ld_tok = ld_row / a.g;
-        const int ld_head = kvh * a.g + (int)(ld_row % a.g);
-        const bf16_t* qrow = (const bf16_t*)a.q + (ld_tok * a.hq + ld_head) * (int64_t)D + 8 * h;
-#pragma unroll
-        for (int ks = 0; ks < F::KS; ks++) {
-            ws.qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * ks));
-            asm volatile("" : "+a"(ws.qb[ks]));  // read-only MFMA operand: keep it in AGPRs
-        }
-#pragma unroll
-        for (int dt = 0; dt < F::DT; dt++) ws.o[dt] = f32x16{};
-        ws.m = -INFINITY;
-        ws.l = 0.f;
-    }
-    const LaneAddr<D> la(lane);
-
-    // number of key tiles of this part for this query tile
+    // keys of this part
+    const int64_t lp0 = resp ? 0 : a.shard_lo[part];
     int64_t n_tiles;
-    const int64_t tok_min = r0 / a.g;
     if (!resp) {
         n_tiles = a.shard_lo[part + 1] - a.shard_lo[part];
     } else {
-        int64_t tok_max = (r0 + BM - 1) / a.g;
+        int64_t tok_max = (r0 + kBM - 1) / a.g;
         if (tok_max > a.n_rows - 1) tok_max = a.n_rows - 1;
         n_tiles = (a.q_start + tok_max + 1 + kPage - 1) / kPage;
     }
-    const int64_t vis_limit = a.q_start + my_tok;  // last response key this row sees
-    // Page-table entries are read one tile ahead of their copy, so the lookup latency hides
-    // behind the current tile's compute.
-    int32_t phys_cur = (!resp && n_tiles > 0) ? phys_page(a, part, 0) : 0;
-    int32_t phys_next = (!resp && n_tiles > 1) ? phys_page(a, part, 1) : 0;
-    TileSrc src = part_tile(a, resp, part, kvh, 0, __builtin_amdgcn_readfirstlane(phys_cur));
-    if (n_tiles > 0) issue_tile<D, NW>(src, st0, st0 + F::TILE, w, lane);
-    for (int64_t t = 0; t < n_tiles; t++) {
-        wait_vm_all();
-        __syncthreads();
-        const bool has_next = t + 1 < n_tiles;
-        const TileSrc next_src =
-            part_tile(a, resp, part, kvh, has_next ? t + 1 : t, __builtin_amdgcn_readfirstlane(phys_next));
-        if (!resp && t + 2 < n_tiles) phys_next = phys_page(a, part, t + 2);
-        const bool need_mask = src.valid < kPage || (resp && src.key0 + kPage - 1 > a.q_start + tok_min);
-        char* cur = (t & 1) ? st1 : st0;
-        char* nxt = (t & 1) ? st0 : st1;
-        fwd_step<D, NW>(ws, cur, nxt, has_next, next_src, src, la, resp, need_mask, vis_limit, a.scale_log2, w,
-                        lane);
-        src = next_src;
-    }
 
-    // ---- normalise and write this part's output and LSE
-    const float l = ws.l + other_half(ws.l);
-    if (!row_ok) return;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    float* dst = a.o_parts + (((int64_t)part * a.n_rows + my_tok) * a.hq + my_head) * (int64_t)D;
+    // prologue: K(0) in flight; physical pages of tiles 0 and 1 known
+    int32_t phys_t = n_tiles > 0 ? page_phys(a, resp, lp0, 0) : 0;
+    int32_t phys_t1 = n_tiles > 1 ? page_phys(a, resp, lp0, 1) : 0;
+    if (n_tiles > 0)
+        issue_one<D, kNW>(tile_ptr<D>(a, resp, lp0, 0, phys_t, kvh, false), tile_stride<D>(a, resp),
+                          tile_valid(a, resp, lp0, 0), L.kb[0], w, lane);
+
+    PartInfo pi;
+    pi.resp = resp;
+    pi.kvh = kvh;
+    pi.lp0 = lp0;
+    pi.n_tiles = n_tiles;
+    pi.tok_min = r0 / a.g;
+    char* p_grp = L.p[g];
+    float* alpha_grp = L.alpha[g];
+    LS_LDS float* fin_grp = (LS_LDS float*)L.fin_l[g];
+    const LaneAddr<D> la(lane);
+
+    // Iteration t (0 .. n_tiles): score waves handle page t, output waves page t - 1.  The
+    // lane's base offsets are re-materialised opaquely each iteration so that their xor
+    // variants are formed next to their reads instead of all being held across the loop.
+    if (score_role) {
+        bf16x8 qb[F::KS];
+        {
+            // rows past the block (a partial last tile) read a valid row; their output is never stored
+            const int64_t ld_row = row_ok ? my_row : rows_total - 1;
+            const int64_t ld_tok = ld_row / a.g;
+            const int ld_head = kvh * a.g + (int)(ld_row % a.g);
+            const bf16_t* qrow = (const bf16_t*)a.q + (ld_tok * a.hq + ld_head) * (int64_t)D + 8 * h;
 #pragma unroll
-    for (int dt = 0; dt < F::DT; dt++) {
+            for (int ks = 0; ks < F::KS; ks++) qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * ks));
+            // read-only MFMA operand: keep it in AGPRs (after all loads are in flight)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; q4++) {
-            const int dd = dt * 32 + 8 * q4 + 4 * h;
-            float4 v = make_float4(ws.o[dt][4 * q4] * inv, ws.o[dt][4 * q4 + 1] * inv,
-                                   ws.o[dt][4 * q4 + 2] * inv, ws.o[dt][4 * q4 + 3] * inv);
-            *(float4*)(dst + dd) = v;
+            for (int ks = 0; ks < F::KS; ks++) asm volatile("" : "+a"(qb[ks]));
+        }
+        const int64_t vis_limit = a.q_start + my_tok;  // last response key this row sees
+        float m_ref = -INFINITY, l = 0.f;
+        for (int64_t t = 0; t <= n_tiles; t++) {
+            const int32_t phys_t2 = t + 2 < n_tiles ? page_phys(a, resp, lp0, t + 2) : 0;
+            uint32_t lk = la.k;
+            asm volatile("" : "+v"(lk));
+            score_iter<D>(a, pi, t, __builtin_amdgcn_readfirstlane(phys_t), __builtin_amdgcn_readfirstlane(phys_t1),
+                          L.kb[(t + 1) & 1], L.vb[t & 1], L.kb[t & 1], p_grp, alpha_grp, qb, m_ref, l, vis_limit, lk,
+                          w, lane);
+            phys_t = phys_t1;
+            phys_t1 = phys_t2;
+        }
+        // final statistics for the output waves, and this part's LSE
+        const float l_tot = l + other_half(l);
+        if (lane < 32) fin_grp[lane] = l_tot;
+        lds_barrier();
+        if (row_ok && h == 0)
+            a.lse_parts[((int64_t)part * a.n_rows + my_tok) * a.hq + my_head] =
+                l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    } else {
+        f32x16 o[F::DT];
+#pragma unroll
+        for (int dt = 0; dt < F::DT; dt++) {
+            o[dt] = f32x16{};
+            asm volatile("" : "+a"(o[dt]));
+        }
+        agpr_write_gap();
+        // iteration 0: only the copies (no page has been scored yet)
+        {
+            const int32_t phys_t2 = 2 < n_tiles ? page_phys(a, resp, lp0, 2) : 0;
+            wait_vm_all();
+            lds_barrier();
+            issue_copies<D>(a, resp, lp0, kvh, n_tiles, 0, __builtin_amdgcn_readfirstlane(phys_t),
+                            __builtin_amdgcn_readfirstlane(phys_t1), L.kb[1], L.vb[0], w, lane);
+            lds_barrier();
+            phys_t = phys_t1;
+            phys_t1 = phys_t2;
+        }
+        for (int64_t t = 1; t <= n_tiles; t++) {
+            const int32_t phys_t2 = t + 2 < n_tiles ? page_phys(a, resp, lp0, t + 2) : 0;
+            uint32_t lv = la.v;
+            asm volatile("" : "+v"(lv));
+            output_iter<D>(a, pi, t, __builtin_amdgcn_readfirstlane(phys_t), __builtin_amdgcn_readfirstlane(phys_t1),
+                           L.kb[(t + 1) & 1], L.vb[t & 1], L.vb[(t - 1) & 1], p_grp, alpha_grp, o, lv, w, lane);
+            phys_t = phys_t1;
+            phys_t1 = phys_t2;
+        }
+        lds_barrier();
+        const float l_tot = fin_grp[n];
+        mfma_drain();
+        if (row_ok) {
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            float* dst = a.o_parts + (((int64_t)part * a.n_rows + my_tok) * a.hq + my_head) * (int64_t)D;
+#pragma unroll
+            for (int dt = 0; dt < F::DT; dt++) {
+                // normalise in place in the AGPRs; the stores read them from there
+#pragma unroll
+                for (int i = 0; i < 16; i++) o[dt][i] = agpr_scaled(o[dt][i], inv);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; q4++) {
+                    const int dd = dt * 32 + 8 * q4 + 4 * h;
+                    *(float4*)(dst + dd) = make_float4(o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2],
+                                                       o[dt][4 * q4 + 3]);
+                }
+            }
         }
     }
-    if (h == 0)
-        a.lse_parts[((int64_t)part * a.n_rows + my_tok) * a.hq + my_head] =
-            l > 0.f ? (ws.m + fast_log2(l)) * kLn2 : -INFINITY;
 }
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
-    constexpr int NW = 4;
-    constexpr int BM = 32 * NW;
-    const int64_t n_qtiles = (a.n_rows * a.g + BM - 1) / BM;
+    const int64_t n_qtiles = (a.n_rows * a.g + kBM - 1) / kBM;
     const int64_t n_blocks = n_qtiles * a.n_parts * a.hkv;
     if (n_blocks == 0) return hipSuccess;
     const int grid = pad_grid((int)n_blocks);
     KernelTimer kt("fwd_mfma", s);
-    fwd_mfma_kernel<D, NW><<<grid, NW * 64, 0, s>>>(a, (int)n_qtiles, (int)n_blocks);
+    fwd_mfma_kernel<D><<<grid, kNW * 64, 0, s>>>(a, (int)n_qtiles, (int)n_blocks);
     return hipGetLastError();
 }
 

@@ -88,4 +88,25 @@ __device__ __forceinline__ i16x4 lds_read_tr4(const LS_LDS void* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LS_LDS i16x4*)(p));
 }
 
+// Enough wait states for any matrix instruction in flight to retire before its result is read
+// by inline assembly, which the compiler's hazard tracking does not see (the longest,
+// 32x32x16, needs fewer than 20).
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+// x * f for an accumulator element held in an AGPR, computed in place (through one scratch VGPR), so
+// that the accumulator never has to leave the AGPRs.  Call mfma_drain() before the first one
+// if a matrix instruction may still be writing x, and agpr_write_gap() before the next matrix
+// instruction reads it.
+__device__ __forceinline__ float agpr_scaled(float x, float f) {
+    float tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(tmp)
+                 : "v"(f));
+    return x;
+}
+
+// Wait states between a v_accvgpr_write made in inline assembly (which the compiler's hazard
+// tracking does not see) and a matrix instruction reading that accumulator.
+__device__ __forceinline__ void agpr_write_gap() { asm volatile("s_nop 7" ::: "memory"); }
+
 }  // namespace ls
