@@ -17,6 +17,9 @@ recompute of the two-pass backward are not counted.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -38,6 +41,94 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # Algorithmic matrix work per visible (row, key) pair and query head, in units of 2*d flops
 # (one multiply-add GEMM over the head dimension), for each kernel that does it.
 KERNEL_UNITS = {"fwd_mfma": 2, "dkdv_mfma": 4, "dq_mfma": 3}
+
+# Measured HBM traffic of the dominant kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch,
+# scaled by the same counters on a copy of known size), written by --ingest-counters.  It is
+# reported only while the kernel sources still hash to the digest it was measured on.
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "suffix_attention_amd", "csrc")
+COPY_BYTES = 1 << 30  # --calibrate-copy: bytes read and bytes written per copy launch
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp"))
+                    + glob.glob(os.path.join(CSRC, "*.cpp"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_file(cfg_name: str) -> str:
+    return os.path.join(PROFILES, f"hbm_traffic_{cfg_name}.json")
+
+
+def measured_traffic(cfg_name: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None if absent or
+    taken on other kernel sources."""
+    path = traffic_file(cfg_name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("kernel") != kernel or t.get("source_sha256") != source_digest():
+        return None
+    return t["hbm_bytes_per_launch"]
+
+
+def _counter_sums(d: str, counter: str) -> dict:
+    """{kernel name: [per-dispatch values]} from a rocprofv3 --pmc csv directory."""
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        per = {}
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id", "")))
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (name, _), v in per.items():
+            out.setdefault(name, []).append(v)
+    return out
+
+
+def ingest_counters(cfg_name: str, kernel: str, fetch_dir: str, write_dir: str, cal_fetch: str, cal_write: str):
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE on the benchmark and on
+    --calibrate-copy) into the traffic summary that the benchmark reports."""
+    def per_launch(d, counter, match):
+        sums = _counter_sums(d, counter)
+        vals = [v for name, vs in sums.items() if match(name) for v in vs]
+        assert vals, (d, counter)
+        return sum(vals) / len(vals), len(vals)
+
+    def biggest(d, counter):
+        sums = _counter_sums(d, counter)
+        name = max(sums, key=lambda k: max(sums[k]))
+        return max(sums[name])
+
+    fetch_kib, n_f = per_launch(fetch_dir, "FETCH_SIZE", lambda n: kernel in n)
+    write_kib, n_w = per_launch(write_dir, "WRITE_SIZE", lambda n: kernel in n)
+    cal_f = COPY_BYTES / (biggest(cal_fetch, "FETCH_SIZE") * 1024)   # true bytes per counted byte
+    cal_w = COPY_BYTES / (biggest(cal_write, "WRITE_SIZE") * 1024)
+    out = {"kernel": kernel, "config": cfg_name, "source_sha256": source_digest(),
+           "fetch_kib_per_launch": fetch_kib, "write_kib_per_launch": write_kib, "launches": [n_f, n_w],
+           "copy_calibration": {"bytes": COPY_BYTES, "fetch_factor": cal_f, "write_factor": cal_w},
+           "hbm_bytes_per_launch": fetch_kib * 1024 * cal_f + write_kib * 1024 * cal_w}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_file(cfg_name), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
+def calibrate_copy():
+    """A plain device copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES), three launches."""
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": COPY_BYTES, "launches": 3}))
 
 
 def log(msg):
@@ -73,7 +164,7 @@ def run_steps(prefix, members, cfg, n):
     return last
 
 
-def cpu_baseline(cfg, kp, vp, member, n_tok=16):
+def cpu_baseline(cfg, kp, vp, member, n_tok=64):
     """The oracle, untuned, on a bounded sample: the last n_tok response rows of member 0
     (all heads) against prompt shard 0 and the response keys those rows see."""
     from oracle import attention as orc  # test infrastructure; used only for this baseline leg
@@ -105,7 +196,15 @@ def main():
     ap.add_argument("--config", default="c2m", choices=sorted(configs.CONFIGS))
     ap.add_argument("--G", type=int, default=None, help="override the group size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a device copy of known size (for HBM counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                    help="write the dominant kernel's HBM traffic summary from rocprofv3 --pmc output")
+    ap.add_argument("--kernel", default="dkdv_mfma", help="kernel for --ingest-counters")
     ns = ap.parse_args()
+    if ns.ingest_counters:
+        ingest_counters(ns.config, ns.kernel, *ns.ingest_counters)
+        return
     if ns.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (--gpus {ns.gpus} requested)",
               file=sys.stderr)
@@ -113,6 +212,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if ns.calibrate_copy:
+        calibrate_copy()
+        return
     cfg = configs.CONFIGS[ns.config]
     if ns.G:
         cfg = cfg.with_(G=ns.G)
@@ -186,7 +288,8 @@ def main():
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "counted_tflop_per_step": round(flops_step / 1e12, 3),
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(cfg.name, dom),
                      "flops_per_unit": f"{2 * KERNEL_UNITS[dom]}*d per visible (row, key) pair and query head",
                      "mean_launch_ms": kern[dom]["mean_ms"]},
         "kernels": kern,
