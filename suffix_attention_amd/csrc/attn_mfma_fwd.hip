@@ -133,6 +133,11 @@ __device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int valid, int64_t k
     }
 }
 
+// IEEE maximum (NaN-propagating): maps to v_maximum3_f32 without operand canonicalisation.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
+}
+
 // Online softmax of one page for this lane's row; writes P^T (bf16, MFMA B-operand layout:
 // key step ku = 2kt + u at [ku][lane]) and the row's rescale factor to LDS.
 __device__ __forceinline__ void softmax_page(f32x16 (&s)[2], float& m_ref, float& l, float scale_log2,
@@ -141,9 +146,9 @@ __device__ __forceinline__ void softmax_page(f32x16 (&s)[2], float& m_ref, float
 #pragma unroll
     for (int kt = 0; kt < 2; kt++)
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kt][i], s[kt][i + 1]));
+        for (int i = 0; i < 16; i += 2) mx = max3f(mx, s[kt][i], s[kt][i + 1]);
     // max on raw scores: scale_log2 > 0 commutes with max
-    mx = fmaxf(mx, other_half(mx)) * scale_log2;
+    mx = __builtin_elementwise_maximum(mx, other_half(mx)) * scale_log2;
     float alpha = 1.f;
     if (mx > m_ref + kLazyLog2) {  // false for a fully masked page (mx = -inf)
         alpha = fast_exp2(m_ref - mx);  // 0 on the first page (m_ref = -inf)
@@ -293,8 +298,10 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
     }
 
     // prologue: K(0) in flight; physical pages of tiles 0 and 1 known
-    int32_t phys_t = n_tiles > 0 ? page_phys(a, resp, lp0, 0) : 0;
-    int32_t phys_t1 = n_tiles > 1 ? page_phys(a, resp, lp0, 1) : 0;
+    // page-table entries, read through the scalar cache one iteration before their copies
+    // and clamped where they are used
+    int32_t phys_t = n_tiles > 0 ? clamp_phys(a, page_entry(a, resp, lp0, 0)) : 0;
+    int32_t phys_t1 = n_tiles > 1 ? page_entry(a, resp, lp0, 1) : 0;
     if (n_tiles > 0)
         issue_one<D, kNW>(tile_ptr<D>(a, resp, lp0, 0, phys_t, kvh, false), tile_stride<D>(a, resp),
                           tile_valid(a, resp, lp0, 0), L.kb[0], w, lane);
@@ -330,10 +337,10 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
         const int64_t vis_limit = a.q_start + my_tok;  // last response key this row sees
         float m_ref = -INFINITY, l = 0.f;
         for (int64_t t = 0; t <= n_tiles; t++) {
-            const int32_t phys_t2 = t + 2 < n_tiles ? page_phys(a, resp, lp0, t + 2) : 0;
+            const int32_t phys_t2 = t + 2 < n_tiles ? page_entry(a, resp, lp0, t + 2) : 0;
             uint32_t lk = la.k;
             asm volatile("" : "+v"(lk));
-            score_iter<D>(a, pi, t, __builtin_amdgcn_readfirstlane(phys_t), __builtin_amdgcn_readfirstlane(phys_t1),
+            score_iter<D>(a, pi, t, clamp_phys(a, phys_t), clamp_phys(a, phys_t1),
                           L.kb[(t + 1) & 1], L.vb[t & 1], L.kb[t & 1], p_grp, alpha_grp, qb, m_ref, l, vis_limit, lk,
                           w, lane);
             phys_t = phys_t1;
@@ -356,20 +363,20 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
         agpr_write_gap();
         // iteration 0: only the copies (no page has been scored yet)
         {
-            const int32_t phys_t2 = 2 < n_tiles ? page_phys(a, resp, lp0, 2) : 0;
+            const int32_t phys_t2 = 2 < n_tiles ? page_entry(a, resp, lp0, 2) : 0;
             wait_vm_all();
             lds_barrier();
-            issue_copies<D>(a, resp, lp0, kvh, n_tiles, 0, __builtin_amdgcn_readfirstlane(phys_t),
-                            __builtin_amdgcn_readfirstlane(phys_t1), L.kb[1], L.vb[0], w, lane);
+            issue_copies<D>(a, resp, lp0, kvh, n_tiles, 0, clamp_phys(a, phys_t),
+                            clamp_phys(a, phys_t1), L.kb[1], L.vb[0], w, lane);
             lds_barrier();
             phys_t = phys_t1;
             phys_t1 = phys_t2;
         }
         for (int64_t t = 1; t <= n_tiles; t++) {
-            const int32_t phys_t2 = t + 2 < n_tiles ? page_phys(a, resp, lp0, t + 2) : 0;
+            const int32_t phys_t2 = t + 2 < n_tiles ? page_entry(a, resp, lp0, t + 2) : 0;
             uint32_t lv = la.v;
             asm volatile("" : "+v"(lv));
-            output_iter<D>(a, pi, t, __builtin_amdgcn_readfirstlane(phys_t), __builtin_amdgcn_readfirstlane(phys_t1),
+            output_iter<D>(a, pi, t, clamp_phys(a, phys_t), clamp_phys(a, phys_t1),
                            L.kb[(t + 1) & 1], L.vb[t & 1], L.vb[(t - 1) & 1], p_grp, alpha_grp, o, lv, w, lane);
             phys_t = phys_t1;
             phys_t1 = phys_t2;

@@ -53,6 +53,20 @@ __device__ __forceinline__ int32_t page_phys(const AttnArgs& a, bool resp, int64
     return phys < 0 ? 0 : (phys >= a.n_phys ? (int32_t)(a.n_phys - 1) : phys);
 }
 
+// Raw page-table entry of tile t of a prompt part (0 for response tiles), read through the
+// scalar cache: the table is never written while a kernel runs.  Clamp it with clamp_phys()
+// where it is used, so that the load's latency is not waited for where it is issued.
+__device__ __forceinline__ int32_t page_entry(const AttnArgs& a, bool resp, int64_t lp0, int64_t t) {
+    if (resp) return 0;
+    const __attribute__((address_space(4))) int32_t* tab = (const __attribute__((address_space(4))) int32_t*)a.table;
+    return tab[lp0 + t];
+}
+
+// A physical page index that is always inside the pool (a bad table cannot fault).
+__device__ __forceinline__ int32_t clamp_phys(const AttnArgs& a, int32_t phys) {
+    return phys < 0 ? 0 : (phys >= a.n_phys ? (int32_t)(a.n_phys - 1) : phys);
+}
+
 template <int D>
 __device__ __forceinline__ const bf16_t* tile_ptr(const AttnArgs& a, bool resp, int64_t lp0, int64_t t, int32_t phys,
                                                   int kvh, bool v) {
