@@ -12,5 +12,6 @@ from .attention import (  # noqa: F401
     forward_parts,
     gather_pages,
     lse_merge,
+    round_bf16,
     shard_token_bounds,
 )

@@ -254,6 +254,21 @@ def lse_merge(o_parts, lse_parts):
 
 
 # ---------------------------------------------------------------------------------------
+# Output rounding (the replayed block's output is a tensor of the model's dtype, bf16 on the
+# pages' runs: digest "Method", Qwen implementation; the backward's delta is formed from that
+# stored output)
+# ---------------------------------------------------------------------------------------
+
+def round_bf16(x):
+    """x rounded to the nearest bfloat16 value (8 significant bits, ties to even), returned
+    as float64.  Written from the definition of the format; values below the bf16 normal
+    range keep 8 significant bits (none occur in the tests' data)."""
+    x = _f64(x)
+    m, e = np.frexp(x)                     # x = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+# ---------------------------------------------------------------------------------------
 # Backward (gradient of L = sum(O * dO) w.r.t. q, prompt k/v and response k/v)
 # ---------------------------------------------------------------------------------------
 

@@ -112,6 +112,10 @@ class Case:
         tab = self.table.numpy()
         return pg[tab[t // 64], :, t % 64, :]
 
+    def stored(self, o):
+        """The oracle's output as the library stores it: rounded to the input dtype."""
+        return orc.round_bf16(o) if self.dtype == torch.bfloat16 else np.asarray(o, np.float32).astype(np.float64)
+
     def oracle(self, q_start, n_rows, o_used=None):
         q = np32(self.q[q_start:q_start + n_rows])
         do = np32(self.do[q_start:q_start + n_rows])
@@ -130,10 +134,10 @@ def check_against_oracle(case: Case, q_start: int, n_rows: int, res=None, parts=
     """atol: optional per-tensor max-abs bounds (for inputs scaled away from N(0, 1))."""
     atol = atol or {}
     res = res or case.gpu(q_start, n_rows)
-    # delta is formed from the O the forward returned (rounded to the input dtype), as the
-    # GPU path does; the oracle takes the same O.
-    ref = case.oracle(q_start, n_rows, o_used=np32(res["o"]))
+    # The backward's delta is formed from the stored output, which has the input dtype; the
+    # oracle's reference backward takes its own output rounded the same way.
     ref_exact = case.oracle(q_start, n_rows)
+    ref = case.oracle(q_start, n_rows, o_used=case.stored(ref_exact["o"]))
     assert_close("O", np32(res["o"]), ref_exact["o"])
     assert_close("LSE", np32(res["lse"]), ref_exact["lse"])
     assert_close("dQ", np32(res["dq"]), ref["dq"], atol=atol.get("dQ", ATOL))

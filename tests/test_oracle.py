@@ -350,3 +350,20 @@ def test_pins_catch_planted(monkeypatch):
     monkeypatch.setattr(orc, "_group_rows", orig_group)
     O, L = fwd()
     assert np.allclose(O, Ob, atol=1e-12) and np.allclose(L, Lb, atol=1e-12)
+
+
+def test_round_bf16_matches_torch_rne_and_is_idempotent():
+    """round_bf16 against torch's CPU float32 -> bfloat16 conversion (round to nearest even)
+    on float32-representable values, including exact ties, signs, zeros and powers of two."""
+    import torch
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(200_000).astype(np.float32) * np.float32(10.0) ** rng.integers(-6, 6, 200_000)
+    # exact ties: bf16 values plus half an ulp (bit 15 set, lower bits clear)
+    ties = (rng.integers(0, 1 << 16, 5000, dtype=np.uint32) << 16 | 0x8000).astype(np.uint32)
+    exp_field = ties & 0x7F800000
+    ties = ties[(exp_field != 0x7F800000) & (exp_field != 0)].view(np.float32)  # normal numbers
+    x = np.concatenate([x, ties, np.array([0.0, -0.0, 1.0, -2.0, 0.5, 3.0], np.float32)])
+    got = orc.round_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, ref)
+    assert np.array_equal(orc.round_bf16(got), got)
