@@ -26,7 +26,7 @@ struct DqState {
 
 template <int D>
 __device__ __forceinline__ void dq_tile(DqState<D>& st, const LS_LDS char* lds_k, const LS_LDS char* lds_v,
-                                        LaneAddr<D> la, const TileSrc& src, bool resp, bool need_mask,
+                                        LaneAddr<D> la, int valid, int64_t key0, bool resp, bool need_mask,
                                         int64_t vis_limit, float scale_log2, int lane) {
     using F = TileShape<D>;
     const int h = lane >> 5;
@@ -55,10 +55,10 @@ __device__ __forceinline__ void dq_tile(DqState<D>& st, const LS_LDS char* lds_k
         dp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, st.dob[ks], dp[1], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
-    int lim_valid = src.valid - 4 * h;
+    int lim_valid = valid - 4 * h;
     int lim_causal = 64;
     if (resp) {
-        const int64_t c = vis_limit - src.key0 - 4 * h;
+        const int64_t c = vis_limit - key0 - 4 * h;
         lim_causal = c < -1 ? -1 : (c > 64 ? 64 : (int)c);
     }
     bf16x8 db[2][2];
@@ -107,14 +107,21 @@ __device__ __forceinline__ void dq_tile(DqState<D>& st, const LS_LDS char* lds_k
     }
 }
 
+// One page: issue the copies of page t+1 (K and V into nxt), then the tile on cur.  The two
+// stages are restrict pointers so that, once inlined, the compiler knows the copies in flight
+// cannot alias the tile being read and does not wait for them.
 template <int D, int NW>
 __device__ __forceinline__ void dq_step(DqState<D>& st, const char* __restrict__ cur, char* __restrict__ nxt,
-                                        bool has_next, const TileSrc& next_src, const TileSrc& src, LaneAddr<D> la,
-                                        bool resp, bool need_mask, int64_t vis_limit, float scale_log2, int w,
-                                        int lane) {
+                                        const KeyTiles<D, NW>& kt, bool has_next, int32_t e_next, int64_t t,
+                                        int valid, int64_t key0, LaneAddr<D> la, bool resp, bool need_mask,
+                                        int64_t vis_limit, float scale_log2, int w, int lane) {
     using F = TileShape<D>;
-    if (has_next) issue_tile<D, NW>(next_src, nxt, nxt + F::TILE, w, lane);
-    dq_tile<D>(st, (const LS_LDS char*)cur, (const LS_LDS char*)(cur + F::TILE), la, src, resp, need_mask,
+    if (has_next) {
+        const int vn = kt.valid(t + 1);
+        kt.copy(kt.tile(e_next, t + 1, false), vn, nxt, w);
+        kt.copy(kt.tile(e_next, t + 1, true), vn, nxt + F::TILE, w);
+    }
+    dq_tile<D>(st, (const LS_LDS char*)cur, (const LS_LDS char*)(cur + F::TILE), la, valid, key0, resp, need_mask,
                vis_limit, scale_log2, lane);
 }
 
@@ -174,23 +181,28 @@ void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
     }
     const int64_t vis_limit = a.q_start + my_tok;
 
-    int32_t phys_cur = (!resp && n_tiles > 0) ? phys_page(a, part, 0) : 0;
-    int32_t phys_next = (!resp && n_tiles > 1) ? phys_page(a, part, 1) : 0;
-    TileSrc src = part_tile(a, resp, part, kvh, 0, __builtin_amdgcn_readfirstlane(phys_cur));
-    if (n_tiles > 0) issue_tile<D, NW>(src, st0, st0 + F::TILE, w, lane);
+    const int64_t lp0 = resp ? 0 : a.shard_lo[part];
+    const KeyTiles<D, NW> kt(a, resp, lp0, kvh, w, lane);
+    // page-table entries are read through the scalar cache one page before their copies and
+    // clamped where they are used
+    int32_t e_next = n_tiles > 1 ? kt.entry(1) : 0;
+    if (n_tiles > 0) {
+        const int32_t e0 = kt.entry(0);
+        kt.copy(kt.tile(e0, 0, false), kt.valid(0), st0, w);
+        kt.copy(kt.tile(e0, 0, true), kt.valid(0), st0 + F::TILE, w);
+    }
     for (int64_t t = 0; t < n_tiles; t++) {
+        const int32_t e_after = t + 2 < n_tiles ? kt.entry(t + 2) : 0;
         wait_vm_all();
         __syncthreads();
-        const bool has_next = t + 1 < n_tiles;
-        const TileSrc next_src =
-            part_tile(a, resp, part, kvh, has_next ? t + 1 : t, __builtin_amdgcn_readfirstlane(phys_next));
-        if (!resp && t + 2 < n_tiles) phys_next = phys_page(a, part, t + 2);
-        const bool need_mask = src.valid < kPage || (resp && src.key0 + kPage - 1 > a.q_start + tok_min);
+        const int valid = kt.valid(t);
+        const int64_t key0 = (lp0 + t) * kPage;
+        const bool need_mask = valid < kPage || (resp && key0 + kPage - 1 > a.q_start + tok_min);
         char* cur = (t & 1) ? st1 : st0;
         char* nxt = (t & 1) ? st0 : st1;
-        dq_step<D, NW>(st, cur, nxt, has_next, next_src, src, la, resp, need_mask, vis_limit, a.scale_log2, w,
-                       lane);
-        src = next_src;
+        dq_step<D, NW>(st, cur, nxt, kt, t + 1 < n_tiles, e_next, t, valid, key0, la, resp, need_mask, vis_limit,
+                       a.scale_log2, w, lane);
+        e_next = e_after;
     }
     if (!row_ok) return;
     float* dst = a.dq_parts + (((int64_t)part * a.n_rows + my_tok) * a.hq + my_head) * (int64_t)D;

@@ -56,24 +56,20 @@ struct FwdLds {
 // flight are left alone (a workgroup fence would wait for them too).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Copies issued in iteration t by all eight waves: K(t+1) into k_dst and V(t) into v_dst.
+// Copies issued in iteration t by all eight waves: K(t+1) into k_dst and V(t) into v_dst;
+// e_t / e_t1 are the raw page-table entries of tiles t and t+1.
 template <int D>
-__device__ __forceinline__ void issue_copies(const AttnArgs& a, bool resp, int64_t lp0, int kvh, int64_t n_tiles,
-                                             int64_t t, int32_t phys_t, int32_t phys_t1, char* k_dst, char* v_dst,
-                                             int w, int lane) {
-    const int64_t stride = tile_stride<D>(a, resp);
-    if (t + 1 < n_tiles)
-        issue_one<D, kNW>(tile_ptr<D>(a, resp, lp0, t + 1, phys_t1, kvh, false), stride,
-                          tile_valid(a, resp, lp0, t + 1), k_dst, w, lane);
-    if (t < n_tiles)
-        issue_one<D, kNW>(tile_ptr<D>(a, resp, lp0, t, phys_t, kvh, true), stride, tile_valid(a, resp, lp0, t),
-                          v_dst, w, lane);
+__device__ __forceinline__ void issue_copies(const KeyTiles<D, kNW>& kt, int64_t n_tiles, int64_t t, int32_t e_t,
+                                             int32_t e_t1, char* k_dst, char* v_dst, int w) {
+    if (t + 1 < n_tiles) kt.copy(kt.tile(e_t1, t + 1, false), kt.valid(t + 1), k_dst, w);
+    if (t < n_tiles) kt.copy(kt.tile(e_t, t, true), kt.valid(t), v_dst, w);
 }
 
 // Where the keys of the workgroup's part come from, and the rows it serves.
+template <int D>
 struct PartInfo {
+    KeyTiles<D, kNW> kt;
     bool resp;
-    int kvh;
     int64_t lp0;        // first logical page (prompt shard)
     int64_t n_tiles;
     int64_t tok_min;    // first token of the workgroup's rows
@@ -211,20 +207,20 @@ __device__ __forceinline__ void accumulate_pv(f32x16 (&o)[TileShape<D>::DT], con
 // Score role, iteration t: S(t) while the output waves fetch P(t-1); then the softmax of
 // page t while they multiply.
 template <int D>
-__device__ __forceinline__ void score_iter(const AttnArgs& a, const PartInfo& pi, int64_t t, int32_t phys_t,
+__device__ __forceinline__ void score_iter(const AttnArgs& a, const PartInfo<D>& pi, int64_t t, int32_t phys_t,
                                            int32_t phys_t1, char* __restrict__ k_dst, char* __restrict__ v_dst,
                                            const char* __restrict__ k_cur, char* __restrict__ p_out,
                                            float* __restrict__ alpha_out, const bf16x8 (&qb)[TileShape<D>::KS],
                                            float& m_ref, float& l, int64_t vis_limit, uint32_t lk, int w, int lane) {
     wait_vm_all();
     lds_barrier();
-    issue_copies<D>(a, pi.resp, pi.lp0, pi.kvh, pi.n_tiles, t, phys_t, phys_t1, k_dst, v_dst, w, lane);
+    issue_copies<D>(pi.kt, pi.n_tiles, t, phys_t, phys_t1, k_dst, v_dst, w);
     f32x16 s[2];
     const bool live = t < pi.n_tiles;
     if (live) scores<D>(qb, s, (const LS_LDS char*)k_cur, lk);
     lds_barrier();
     if (live) {
-        const int valid = tile_valid(a, pi.resp, pi.lp0, t);
+        const int valid = pi.kt.valid(t);
         const int64_t key0 = (pi.lp0 + t) * kPage;
         if (valid < kPage || (pi.resp && key0 + kPage - 1 > a.q_start + pi.tok_min))
             mask_scores(s, valid, key0, pi.resp, vis_limit, lane >> 5);
@@ -235,7 +231,7 @@ __device__ __forceinline__ void score_iter(const AttnArgs& a, const PartInfo& pi
 // Output role, iteration t >= 1: fetch P(t-1) while the score waves multiply; then rescale O
 // if a row's reference moved and accumulate V(t-1) P(t-1).
 template <int D>
-__device__ __forceinline__ void output_iter(const AttnArgs& a, const PartInfo& pi, int64_t t, int32_t phys_t,
+__device__ __forceinline__ void output_iter(const AttnArgs& a, const PartInfo<D>& pi, int64_t t, int32_t phys_t,
                                             int32_t phys_t1, char* __restrict__ k_dst, char* __restrict__ v_dst,
                                             const char* __restrict__ v_prev, const char* __restrict__ p_in,
                                             const float* __restrict__ alpha_in, f32x16 (&o)[TileShape<D>::DT],
@@ -243,7 +239,7 @@ __device__ __forceinline__ void output_iter(const AttnArgs& a, const PartInfo& p
     using F = TileShape<D>;
     wait_vm_all();
     lds_barrier();
-    issue_copies<D>(a, pi.resp, pi.lp0, pi.kvh, pi.n_tiles, t, phys_t, phys_t1, k_dst, v_dst, w, lane);
+    issue_copies<D>(pi.kt, pi.n_tiles, t, phys_t, phys_t1, k_dst, v_dst, w);
     bf16x8 pb[4];
 #pragma unroll
     for (int ku = 0; ku < 4; ku++) pb[ku] = *(const LS_LDS bf16x8*)((const LS_LDS char*)p_in + (ku * 64 + lane) * 16);
@@ -297,21 +293,18 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
         n_tiles = (a.q_start + tok_max + 1 + kPage - 1) / kPage;
     }
 
-    // prologue: K(0) in flight; physical pages of tiles 0 and 1 known
-    // page-table entries, read through the scalar cache one iteration before their copies
-    // and clamped where they are used
-    int32_t phys_t = n_tiles > 0 ? clamp_phys(a, page_entry(a, resp, lp0, 0)) : 0;
-    int32_t phys_t1 = n_tiles > 1 ? page_entry(a, resp, lp0, 1) : 0;
-    if (n_tiles > 0)
-        issue_one<D, kNW>(tile_ptr<D>(a, resp, lp0, 0, phys_t, kvh, false), tile_stride<D>(a, resp),
-                          tile_valid(a, resp, lp0, 0), L.kb[0], w, lane);
-
-    PartInfo pi;
+    PartInfo<D> pi{KeyTiles<D, kNW>(a, resp, lp0, kvh, w, lane)};
+    const KeyTiles<D, kNW>& kt = pi.kt;
     pi.resp = resp;
-    pi.kvh = kvh;
     pi.lp0 = lp0;
     pi.n_tiles = n_tiles;
     pi.tok_min = r0 / a.g;
+
+    // prologue: K(0) in flight.  Page-table entries are read through the scalar cache one
+    // iteration before their copies and clamped where they are used.
+    int32_t phys_t = n_tiles > 0 ? kt.entry(0) : 0;
+    int32_t phys_t1 = n_tiles > 1 ? kt.entry(1) : 0;
+    if (n_tiles > 0) kt.copy(kt.tile(phys_t, 0, false), kt.valid(0), L.kb[0], w);
     char* p_grp = L.p[g];
     float* alpha_grp = L.alpha[g];
     LS_LDS float* fin_grp = (LS_LDS float*)L.fin_l[g];
@@ -337,10 +330,10 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
         const int64_t vis_limit = a.q_start + my_tok;  // last response key this row sees
         float m_ref = -INFINITY, l = 0.f;
         for (int64_t t = 0; t <= n_tiles; t++) {
-            const int32_t phys_t2 = t + 2 < n_tiles ? page_entry(a, resp, lp0, t + 2) : 0;
+            const int32_t phys_t2 = t + 2 < n_tiles ? kt.entry(t + 2) : 0;
             uint32_t lk = la.k;
             asm volatile("" : "+v"(lk));
-            score_iter<D>(a, pi, t, clamp_phys(a, phys_t), clamp_phys(a, phys_t1),
+            score_iter<D>(a, pi, t, phys_t, phys_t1,
                           L.kb[(t + 1) & 1], L.vb[t & 1], L.kb[t & 1], p_grp, alpha_grp, qb, m_ref, l, vis_limit, lk,
                           w, lane);
             phys_t = phys_t1;
@@ -363,20 +356,19 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
         agpr_write_gap();
         // iteration 0: only the copies (no page has been scored yet)
         {
-            const int32_t phys_t2 = 2 < n_tiles ? page_entry(a, resp, lp0, 2) : 0;
+            const int32_t phys_t2 = 2 < n_tiles ? kt.entry(2) : 0;
             wait_vm_all();
             lds_barrier();
-            issue_copies<D>(a, resp, lp0, kvh, n_tiles, 0, clamp_phys(a, phys_t),
-                            clamp_phys(a, phys_t1), L.kb[1], L.vb[0], w, lane);
+            issue_copies<D>(kt, n_tiles, 0, phys_t, phys_t1, L.kb[1], L.vb[0], w);
             lds_barrier();
             phys_t = phys_t1;
             phys_t1 = phys_t2;
         }
         for (int64_t t = 1; t <= n_tiles; t++) {
-            const int32_t phys_t2 = t + 2 < n_tiles ? page_entry(a, resp, lp0, t + 2) : 0;
+            const int32_t phys_t2 = t + 2 < n_tiles ? kt.entry(t + 2) : 0;
             uint32_t lv = la.v;
             asm volatile("" : "+v"(lv));
-            output_iter<D>(a, pi, t, clamp_phys(a, phys_t), clamp_phys(a, phys_t1),
+            output_iter<D>(a, pi, t, phys_t, phys_t1,
                            L.kb[(t + 1) & 1], L.vb[t & 1], L.vb[(t - 1) & 1], p_grp, alpha_grp, o, lv, w, lane);
             phys_t = phys_t1;
             phys_t1 = phys_t2;

@@ -31,83 +31,93 @@ __host__ __device__ constexpr int swz(int r) {
     return TileShape<D>::KCH >= 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r & 1) << 2) | ((r >> 1) & 3));
 }
 
-struct TileSrc {
-    const bf16_t* k;
-    const bf16_t* v;
-    int64_t stride;  // elements between consecutive key rows
-    int valid;       // rows [0, valid) hold keys; the rest repeat the last valid row
-    int64_t key0;    // first key: logical prompt token, or response position
-};
+// The key tiles of one part (a prompt shard: logical pages lp0.., walked through the page
+// table; or the response keys as 64-key "virtual pages"), with everything that does not change
+// from page to page computed once per workgroup, so that a page costs one page-table entry,
+// one scalar multiply-add and PER_WAVE direct-to-LDS copies per tile.
+//
+// Wave w's j-th copy fills 1 KiB block j*NW + w of an LDS tile, i.e. RPK = 512/D whole rows
+// starting at row j*JROWS + low; lane l writes 16-byte slot l of the block, so it fetches the
+// logical chunk that the swizzle puts there (swz is linear over xor and low < JROWS, a power
+// of two, so the chunk index splits into a lane part and a j part).
+template <int D, int NW>
+struct KeyTiles {
+    using F = TileShape<D>;
+    static constexpr int RPK = 512 / D;
+    static constexpr int PER_WAVE = F::TILE / 1024 / NW;
+    static constexpr int JROWS = NW * RPK;
+    static_assert(PER_WAVE * NW * 1024 == F::TILE, "a tile must split evenly over the waves");
 
-// Physical page of tile t of a prompt part (clamped so that a bad table cannot fault).
-__device__ __forceinline__ int32_t phys_page(const AttnArgs& a, int part, int64_t t) {
-    int32_t phys = a.table[a.shard_lo[part] + t];
-    return phys < 0 ? 0 : (phys >= a.n_phys ? (int32_t)(a.n_phys - 1) : phys);
-}
+    const char* kbase;      // K of this kv head: physical page 0 (prompt) or response key 0
+    const char* vbase;
+    int64_t tile_bytes;     // bytes between physical pages (prompt) or 64-key tiles (response)
+    const __attribute__((address_space(4))) int32_t* table;  // entries from logical page lp0 on
+    int64_t keys;           // keys of the part counted from tile 0
+    int32_t n_phys;
+    uint32_t row_bytes;     // bytes between key rows inside a tile
+    bool resp;
+    int low;                // first row of this lane's copies (plus j * JROWS)
+    int lane_x;             // this lane's chunk before the j part of the swizzle
+    uint32_t off[PER_WAVE]; // this lane's byte offset in a full tile, copy j
 
-// Scalar pieces of tile t of a part starting at logical page lp0 (prompt) or key 0 (response):
-// its physical page, base pointer of K or V, row stride and number of valid rows.
-__device__ __forceinline__ int32_t page_phys(const AttnArgs& a, bool resp, int64_t lp0, int64_t t) {
-    if (resp) return 0;
-    const int32_t phys = a.table[lp0 + t];
-    return phys < 0 ? 0 : (phys >= a.n_phys ? (int32_t)(a.n_phys - 1) : phys);
-}
-
-// Raw page-table entry of tile t of a prompt part (0 for response tiles), read through the
-// scalar cache: the table is never written while a kernel runs.  Clamp it with clamp_phys()
-// where it is used, so that the load's latency is not waited for where it is issued.
-__device__ __forceinline__ int32_t page_entry(const AttnArgs& a, bool resp, int64_t lp0, int64_t t) {
-    if (resp) return 0;
-    const __attribute__((address_space(4))) int32_t* tab = (const __attribute__((address_space(4))) int32_t*)a.table;
-    return tab[lp0 + t];
-}
-
-// A physical page index that is always inside the pool (a bad table cannot fault).
-__device__ __forceinline__ int32_t clamp_phys(const AttnArgs& a, int32_t phys) {
-    return phys < 0 ? 0 : (phys >= a.n_phys ? (int32_t)(a.n_phys - 1) : phys);
-}
-
-template <int D>
-__device__ __forceinline__ const bf16_t* tile_ptr(const AttnArgs& a, bool resp, int64_t lp0, int64_t t, int32_t phys,
-                                                  int kvh, bool v) {
-    if (!resp) return (const bf16_t*)(v ? a.v_pages : a.k_pages) + ((int64_t)phys * a.hkv + kvh) * kPage * D;
-    return (const bf16_t*)(v ? a.v_resp : a.k_resp) + (t * kPage * a.hkv + kvh) * D;
-}
-
-template <int D>
-__device__ __forceinline__ int64_t tile_stride(const AttnArgs& a, bool resp) {
-    return resp ? (int64_t)a.hkv * D : D;
-}
-
-__device__ __forceinline__ int tile_valid(const AttnArgs& a, bool resp, int64_t lp0, int64_t t) {
-    const int64_t left = resp ? a.key_end - t * kPage : a.prefix_len - (lp0 + t) * kPage;
-    return left < kPage ? (int)left : kPage;
-}
-
-// Source of tile t of a part; `phys` is its physical page (prompt parts only).
-__device__ __forceinline__ TileSrc part_tile(const AttnArgs& a, bool resp, int part, int kvh,
-                                             int64_t t, int32_t phys) {
-    TileSrc s;
-    if (!resp) {
-        const int64_t lp = a.shard_lo[part] + t;
-        const int64_t off = ((int64_t)phys * a.hkv + kvh) * kPage * a.d;
-        s.k = (const bf16_t*)a.k_pages + off;
-        s.v = (const bf16_t*)a.v_pages + off;
-        s.stride = a.d;
-        s.key0 = lp * kPage;
-        const int64_t left = a.prefix_len - s.key0;
-        s.valid = left < kPage ? (int)left : kPage;
-    } else {
-        s.key0 = t * kPage;
-        const int64_t off = (s.key0 * a.hkv + kvh) * a.d;
-        s.k = (const bf16_t*)a.k_resp + off;
-        s.v = (const bf16_t*)a.v_resp + off;
-        s.stride = (int64_t)a.hkv * a.d;
-        const int64_t left = a.key_end - s.key0;
-        s.valid = left < kPage ? (int)left : kPage;
+    __device__ __forceinline__ KeyTiles(const AttnArgs& a, bool resp_, int64_t lp0, int kvh, int w, int lane) {
+        resp = resp_;
+        n_phys = (int32_t)a.n_phys;
+        if (!resp) {
+            kbase = (const char*)a.k_pages + (int64_t)kvh * kPage * D * 2;
+            vbase = (const char*)a.v_pages + (int64_t)kvh * kPage * D * 2;
+            tile_bytes = (int64_t)a.hkv * kPage * D * 2;
+            row_bytes = D * 2;
+            keys = a.prefix_len - lp0 * kPage;
+        } else {
+            kbase = (const char*)a.k_resp + (int64_t)kvh * D * 2;
+            vbase = (const char*)a.v_resp + (int64_t)kvh * D * 2;
+            tile_bytes = (int64_t)kPage * a.hkv * D * 2;
+            row_bytes = (uint32_t)a.hkv * D * 2;
+            keys = a.key_end;
+        }
+        table = (const __attribute__((address_space(4))) int32_t*)a.table + (resp ? 0 : lp0);
+        low = w * RPK + lane / F::KCH;
+        lane_x = (lane % F::KCH) ^ swz<D>(low);
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; j++)
+            off[j] = (uint32_t)(j * JROWS + low) * row_bytes + (uint32_t)((lane_x ^ swz<D>(j * JROWS)) << 4);
     }
-    return s;
-}
+
+    // Raw page-table entry of tile t (scalar load; 0 for the response).  Clamp it with tile()
+    // where it is used, so that the load's latency is not waited for where it is issued.
+    __device__ __forceinline__ int32_t entry(int64_t t) const { return resp ? 0 : table[t]; }
+
+    // Base of tile t of K (v = false) or V; `raw` is entry(t).  A bad table entry is clamped
+    // into the pool, so it cannot fault.
+    __device__ __forceinline__ const char* tile(int32_t raw, int64_t t, bool v) const {
+        const int32_t phys = raw < 0 ? 0 : (raw >= n_phys ? n_phys - 1 : raw);
+        return (v ? vbase : kbase) + (resp ? t : (int64_t)phys) * tile_bytes;
+    }
+
+    // Rows of tile t that hold keys of the part.
+    __device__ __forceinline__ int valid(int64_t t) const {
+        const int64_t left = keys - t * kPage;
+        return left < kPage ? (int)left : kPage;
+    }
+
+    // Copy one tile into LDS (all NW waves together); rows past `valid` repeat the last valid
+    // row (finite, masked by the caller).
+    __device__ __forceinline__ void copy(const char* src, int valid_rows, char* lds, int w) const {
+        if (valid_rows == kPage) {
+#pragma unroll
+            for (int j = 0; j < PER_WAVE; j++) dma16(src + off[j], (LS_LDS void*)(lds + (j * NW + w) * 1024));
+        } else {
+#pragma unroll
+            for (int j = 0; j < PER_WAVE; j++) {
+                const int r = j * JROWS + low;
+                const int rs = r < valid_rows ? r : valid_rows - 1;
+                const uint32_t o = (uint32_t)rs * row_bytes + (uint32_t)((lane_x ^ swz<D>(j * JROWS)) << 4);
+                dma16(src + o, (LS_LDS void*)(lds + (j * NW + w) * 1024));
+            }
+        }
+    }
+};
 
 // Direct-to-LDS copy of ROWS full rows (D bf16 each, rows `stride` elements apart) from two
 // sources a, b into two LDS tiles, by all NW waves together.  Wave w's j-th copy fills 1 KiB
@@ -133,66 +143,6 @@ __device__ __forceinline__ void dma_rows(const bf16_t* a, const bf16_t* b, int64
         const int blk = j * NW + w;
         dma16((const char*)a + rowj + off, (LS_LDS void*)(lds_a + blk * 1024));
         dma16((const char*)b + rowj + off, (LS_LDS void*)(lds_b + blk * 1024));
-    }
-}
-
-// Copy one 64-row tile from one source (K or V of a page, or 64 response keys) into LDS;
-// rows past `valid` repeat the last valid row (finite, masked later).
-template <int D, int NW>
-__device__ __forceinline__ void issue_one(const bf16_t* src, int64_t stride, int valid, char* lds, int w,
-                                          int lane) {
-    using F = TileShape<D>;
-    constexpr int RPK = 512 / D;
-    constexpr int PER_WAVE = F::TILE / 1024 / NW;
-    constexpr int JROWS = NW * RPK;
-    const int low = w * RPK + lane / F::KCH;
-    const int pc = lane % F::KCH;
-    const int lane_x = pc ^ swz<D>(low);
-    if (valid == kPage) {
-#pragma unroll
-        for (int j = 0; j < PER_WAVE; j++) {
-            const int lc = lane_x ^ swz<D>(j * JROWS);
-            const uint32_t off = (uint32_t)(low * (int)stride + lc * 8) * 2u;
-            const int64_t rowj = (int64_t)(j * JROWS) * stride * 2;
-            dma16((const char*)src + rowj + off, (LS_LDS void*)(lds + (j * NW + w) * 1024));
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < PER_WAVE; j++) {
-            const int r = j * JROWS + low;
-            const int lc = lane_x ^ swz<D>(j * JROWS);
-            const int rs = r < valid ? r : valid - 1;
-            const uint32_t off = (uint32_t)(rs * (int)stride + lc * 8) * 2u;
-            dma16((const char*)src + off, (LS_LDS void*)(lds + (j * NW + w) * 1024));
-        }
-    }
-}
-
-// Issue the direct-to-LDS copies of one K and one V page tile (all waves together).
-template <int D, int NW>
-__device__ __forceinline__ void issue_tile(const TileSrc& s, char* lds_k, char* lds_v, int w,
-                                           int lane) {
-    using F = TileShape<D>;
-    if (s.valid == kPage) {
-        dma_rows<D, NW, kPage>(s.k, s.v, s.stride, lds_k, lds_v, w, lane);
-        return;
-    }
-    // a partial tile: rows past `valid` repeat the last valid row (finite, masked later)
-    constexpr int RPK = 512 / D;
-    constexpr int PER_WAVE = F::TILE / 1024 / NW;
-    constexpr int JROWS = NW * RPK;
-    const int low = w * RPK + lane / F::KCH;
-    const int pc = lane % F::KCH;
-    const int lane_x = pc ^ swz<D>(low);
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; j++) {
-        const int r = j * JROWS + low;
-        const int lc = lane_x ^ swz<D>(j * JROWS);
-        const int rs = r < s.valid ? r : s.valid - 1;
-        const uint32_t off = (uint32_t)(rs * (int)s.stride + lc * 8) * 2u;
-        const int blk = j * NW + w;
-        dma16((const char*)s.k + off, (LS_LDS void*)(lds_k + blk * 1024));
-        dma16((const char*)s.v + off, (LS_LDS void*)(lds_v + blk * 1024));
     }
 }
 
