@@ -32,9 +32,11 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
 
 
 # Matrix-core accumulators go to VGPRs in the dQ pass (its S / dP tiles feed vector-ALU work
-# every page, its read-only Q / dO operands sit in AGPRs); the forward keeps O in AGPRs and
-# the dK/dV pass its 256 dK/dV accumulators.
-PER_SOURCE = {"attn_mfma_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# every page, its read-only Q / dO operands sit in AGPRs) and in the dK/dV pass (its S / dP
+# tiles likewise; its 256 dK / dV accumulators are kept in AGPRs by explicit AGPR-form matrix
+# instructions); the forward keeps O in AGPRs in the default form.
+PER_SOURCE = {"attn_mfma_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "attn_mfma_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src, extra):

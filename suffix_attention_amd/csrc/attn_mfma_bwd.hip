@@ -99,22 +99,21 @@ struct DkvState {
     f32x16 dv[TileShape<D>::DT];
 };
 
+// Phase 1 of a row tile: S = Q K^T and dP = dO V^T for 32 rows x 32 keys (element i is row
+// 8(i/4) + 4h + i%4 of the tile, key lane%32).  Q and dO fragments are read PD k-steps ahead.
 template <int D>
-__device__ __forceinline__ void dkdv_rows(DkvState<D>& st, const LS_LDS char* stage, LaneAddr<D> la,
-                                          bool need_mask, int rmin, float scale_log2, int lane) {
+__device__ __forceinline__ void tile_scores(const DkvState<D>& st, const LS_LDS char* stage, uint32_t lk, f32x16& s,
+                                            f32x16& dp) {
     using F = TileShape<D>;
-    const int h = lane >> 5;
-    asm volatile("" : "+v"(la.k), "+v"(la.v));
     const LS_LDS char* lq = stage;
     const LS_LDS char* ldo = stage + RowStage<D>::QBYTES;
-    const LS_LDS f32x2* lsd = (const LS_LDS f32x2*)(stage + 2 * RowStage<D>::QBYTES);
-    // S = Q K^T, dP = dO V^T for 32 rows x 32 keys; Q and dO fragments read PD k-steps ahead
-    f32x16 s = f32x16{}, dp = f32x16{};
+    s = f32x16{};
+    dp = f32x16{};
     constexpr int PD = 3;
     bf16x8 qd[PD][2];
 #pragma unroll
     for (int j = 0; j < PD; j++) {
-        const uint32_t o = la.k ^ (uint32_t)(j << 5);
+        const uint32_t o = lk ^ (uint32_t)(j << 5);
         qd[j][0] = *(const LS_LDS bf16x8*)(lq + o);
         qd[j][1] = *(const LS_LDS bf16x8*)(ldo + o);
     }
@@ -122,7 +121,7 @@ __device__ __forceinline__ void dkdv_rows(DkvState<D>& st, const LS_LDS char* st
     for (int ks = 0; ks < F::KS; ks++) {
         const bf16x8 qa = qd[ks % PD][0], da = qd[ks % PD][1];
         if (ks + PD < F::KS) {
-            const uint32_t o = la.k ^ (uint32_t)((ks + PD) << 5);
+            const uint32_t o = lk ^ (uint32_t)((ks + PD) << 5);
             qd[ks % PD][0] = *(const LS_LDS bf16x8*)(lq + o);
             qd[ks % PD][1] = *(const LS_LDS bf16x8*)(ldo + o);
         }
@@ -130,46 +129,65 @@ __device__ __forceinline__ void dkdv_rows(DkvState<D>& st, const LS_LDS char* st
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, st.vb[ks], dp, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
-    // element i is row 8(i/4) + 4h + i%4 of the stage, key lane%32
-    const int rmh = rmin - 4 * h;  // rows (without the 4h of this half) that precede the key
+}
+
+// Phase 2, one unit (u, hb) of four elements: P = exp2(S log2e/sqrt(d) - LSE log2e) (0 for
+// rows that precede the key when masked) and dS = P (dP - delta), packed as bf16 operand
+// words 2hb, 2hb+1 of key step u.
+struct Prob {
+    uint32_t wp[2][4], wd[2][4];  // [u][word]
+};
+
+__device__ __forceinline__ void prob_unit(int unit, const f32x16& s, const f32x16& dp, const LS_LDS f32x2* lsd,
+                                          bool need_mask, int rmh, float scale_log2, int h, Prob& pr) {
+    const int u = unit >> 1, hb = unit & 1;
+    const int rbase = 16 * u + 8 * hb + 4 * h;
+    const f32x4 l01 = *(const LS_LDS f32x4*)(lsd + rbase);       // rows rbase, rbase+1: (lse2, delta)
+    const f32x4 l23 = *(const LS_LDS f32x4*)(lsd + rbase + 2);   // rows rbase+2, rbase+3
+    float pv[4], dv[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const float l2 = j < 2 ? l01[2 * j] : l23[2 * (j - 2)];
+        const float dl = j < 2 ? l01[2 * j + 1] : l23[2 * (j - 2) + 1];
+        const int i = 8 * u + 4 * hb + j;
+        float p = fast_exp2(__builtin_fmaf(s[i], scale_log2, -l2));
+        if (need_mask) p = (16 * u + 8 * hb + j) >= rmh ? p : 0.f;
+        pv[j] = p;
+        dv[j] = p * (dp[i] - dl);
+    }
+    pr.wp[u][2 * hb] = pack_bf16x2(pv[0], pv[1]);
+    pr.wp[u][2 * hb + 1] = pack_bf16x2(pv[2], pv[3]);
+    pr.wd[u][2 * hb] = pack_bf16x2(dv[0], dv[1]);
+    pr.wd[u][2 * hb + 1] = pack_bf16x2(dv[2], dv[3]);
+}
+
+// Phase 3 of row tile t: dV += P^T dO, dK += dS^T Q (dO, Q read transposed: rows are the
+// contraction), with phase 2 of row tile t+1 (its S, dP already computed) spread over the
+// steps so that its vector work runs while the matrix core is busy.  Step st = (u, dt), dt
+// fastest; fragments read PT steps ahead.
+template <int D>
+__device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur, const LS_LDS char* stage,
+                                                uint32_t lv, const f32x16& s_n, const f32x16& dp_n,
+                                                const LS_LDS f32x2* lsd_n, bool mask_n, int rmh_n,
+                                                float scale_log2, int h, Prob& nxt) {
+    using F = TileShape<D>;
+    const LS_LDS char* lq = stage;
+    const LS_LDS char* ldo = stage + RowStage<D>::QBYTES;
     bf16x8 pa[2], sa[2];
 #pragma unroll
     for (int u = 0; u < 2; u++) {
-        uint32_t wp[4], wd[4];
-#pragma unroll
-        for (int hb = 0; hb < 2; hb++) {
-            const int rbase = 16 * u + 8 * hb + 4 * h;
-            const f32x4 l01 = *(const LS_LDS f32x4*)(lsd + rbase);       // rows rbase, rbase+1
-            const f32x4 l23 = *(const LS_LDS f32x4*)(lsd + rbase + 2);   // rows rbase+2, rbase+3
-            float pv[4], dv[4];
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const float l2 = j < 2 ? l01[2 * j] : l23[2 * (j - 2)];
-                const float dl = j < 2 ? l01[2 * j + 1] : l23[2 * (j - 2) + 1];
-                const int i = 8 * u + 4 * hb + j;
-                float p = fast_exp2(__builtin_fmaf(s[i], scale_log2, -l2));
-                if (need_mask) p = (16 * u + 8 * hb + j) >= rmh ? p : 0.f;
-                pv[j] = p;
-                dv[j] = p * (dp[i] - dl);
-            }
-            wp[2 * hb] = pack_bf16x2(pv[0], pv[1]);
-            wp[2 * hb + 1] = pack_bf16x2(pv[2], pv[3]);
-            wd[2 * hb] = pack_bf16x2(dv[0], dv[1]);
-            wd[2 * hb + 1] = pack_bf16x2(dv[2], dv[3]);
-        }
-        pa[u] = __builtin_bit_cast(bf16x8, (u32x4{wp[0], wp[1], wp[2], wp[3]}));
-        sa[u] = __builtin_bit_cast(bf16x8, (u32x4{wd[0], wd[1], wd[2], wd[3]}));
+        pa[u] = __builtin_bit_cast(bf16x8, (u32x4{cur.wp[u][0], cur.wp[u][1], cur.wp[u][2], cur.wp[u][3]}));
+        sa[u] = __builtin_bit_cast(bf16x8, (u32x4{cur.wd[u][0], cur.wd[u][1], cur.wd[u][2], cur.wd[u][3]}));
     }
-    // dV += P^T dO, dK += dS^T Q (dO, Q read transposed: rows are the contraction).  Step
-    // st = (u, dt), dt fastest; fragments read PT steps ahead.
     constexpr int NST = 2 * F::DT;
     constexpr int PT = 2;
+    constexpr int NU = 4;  // phase-2 units of the next tile
     i16x4 fr[PT][4];
     auto read_t = [&](int st_, i16x4* f) {
         const int dt = st_ % F::DT, u = st_ / F::DT;
         const int R = 16 * u;
-        const uint32_t a0 = (la.v ^ tr_x<D>(dt, R)) + R * 2 * D;
-        const uint32_t a1 = (la.v ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D;
+        const uint32_t a0 = (lv ^ tr_x<D>(dt, R)) + R * 2 * D;
+        const uint32_t a1 = (lv ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D;
         f[0] = lds_read_tr4(ldo + a0);
         f[1] = lds_read_tr4(ldo + a1);
         f[2] = lds_read_tr4(lq + a0);
@@ -184,19 +202,36 @@ __device__ __forceinline__ void dkdv_rows(DkvState<D>& st, const LS_LDS char* st
         const bf16x8 dob = __builtin_bit_cast(bf16x8, __builtin_shufflevector(f[0], f[1], 0, 1, 2, 3, 4, 5, 6, 7));
         const bf16x8 qbt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(f[2], f[3], 0, 1, 2, 3, 4, 5, 6, 7));
         if (st_ + PT < NST) read_t(st_ + PT, f);
-        st.dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[u], dob, st.dv[dt], 0, 0, 0);
-        st.dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[u], qbt, st.dk[dt], 0, 0, 0);
+        mfma32_agpr(st.dv[dt], pa[u], dob);
+        mfma32_agpr(st.dk[dt], sa[u], qbt);
+        // units [st*NU/NST, (st+1)*NU/NST) of the next tile's phase 2 run beside this step;
+        // constant loop bounds so that every unit index is a constant after unrolling
+#pragma unroll
+        for (int un = 0; un < NU; un++)
+            if (un >= st_ * NU / NST && un < (st_ + 1) * NU / NST)
+                prob_unit(un, s_n, dp_n, lsd_n, mask_n, rmh_n, scale_log2, h, nxt);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
+// Row tile t of the pipeline: phase 1 of tile t+1, then phase 3 of tile t with phase 2 of
+// tile t+1 beside it.  The LDS stages are restrict pointers so that, once inlined, the
+// compiler knows the copy in flight (into `dst`) cannot alias the stages being read and does
+// not wait for it.
 template <int D>
-__device__ __forceinline__ void dkdv_step(DkvState<D>& st, const char* __restrict__ cur, char* __restrict__ nxt,
-                                          bool has_next, const AttnArgs& a, const GroupRows& gr, int kvh,
-                                          int64_t next_r0, LaneAddr<D> la, bool need_mask, int rmin, int w,
+__device__ __forceinline__ void dkdv_step(DkvState<D>& st, const char* __restrict__ stage_t,
+                                          const char* __restrict__ stage_n, char* __restrict__ dst, bool copy,
+                                          const GroupRows& gr, int kvh, int64_t copy_r0, const Prob& cur, Prob& nxt,
+                                          LaneAddr<D> la, bool mask_n, int rmh_n, float scale_log2, int w,
                                           int lane) {
-    if (has_next) issue_rows<D>(gr, kvh, next_r0, nxt, w, lane);
-    dkdv_rows<D>(st, (const LS_LDS char*)cur, la, need_mask, rmin, a.scale_log2, lane);
+    if (copy) issue_rows<D>(gr, kvh, copy_r0, dst, w, lane);
+    uint32_t lk = la.k, lv = la.v;
+    asm volatile("" : "+v"(lk), "+v"(lv));
+    f32x16 s_n, dp_n;
+    tile_scores<D>(st, (const LS_LDS char*)stage_n, lk, s_n, dp_n);
+    tile_accumulate<D>(st, cur, (const LS_LDS char*)stage_t, lv, s_n, dp_n,
+                       (const LS_LDS f32x2*)((const LS_LDS char*)stage_n + 2 * RowStage<D>::QBYTES), mask_n, rmh_n,
+                       scale_log2, lane >> 5, nxt);
 }
 
 // One workgroup: 4 waves over two consecutive 64-key pages (wave w: page w/2, keys
@@ -205,8 +240,7 @@ template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks) {
     using F = TileShape<D>;
-    __shared__ __attribute__((aligned(1024))) char st0[RowStage<D>::BYTES];
-    __shared__ __attribute__((aligned(1024))) char st1[RowStage<D>::BYTES];
+    __shared__ __attribute__((aligned(1024))) char stg[3][(RowStage<D>::BYTES + 1023) / 1024 * 1024];
 
     const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
     if (lb >= n_blocks) return;
@@ -259,7 +293,11 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks
             st.vb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(vrow + 16 * ks));
         }
 #pragma unroll
-        for (int dt = 0; dt < F::DT; dt++) st.dk[dt] = st.dv[dt] = f32x16{};
+        for (int dt = 0; dt < F::DT; dt++) {
+            st.dk[dt] = st.dv[dt] = f32x16{};
+            asm volatile("" : "+a"(st.dk[dt]), "+a"(st.dv[dt]));  // accumulators live in AGPRs
+        }
+        agpr_write_gap();
     }
 
     // ---- rows that see these keys: all rows for the prompt; for response keys the rows
@@ -272,23 +310,52 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks
     const int64_t my_key = page * kPage + 32 * kh + n;
     const int64_t row_min = resp ? (my_key - a.q_start) * a.g : 0;
 
+    // Row tile t needs the causal mask if some row in it precedes some key of the pair; rmh is
+    // the number of its rows (without the 4h of this lane's half) that precede this lane's key.
+    auto mask_of = [&](int64_t t, bool& need_mask, int& rmh) {
+        const int64_t r0 = r_begin + t * kRows;
+        need_mask = resp && r0 < (key0_pair + 2 * kPage - 1 - a.q_start) * a.g;
+        const int64_t rm = row_min - r0;
+        rmh = (rm < 0 ? 0 : (rm > kRows ? kRows : (int)rm)) - 4 * h;
+    };
+
+    // Pipeline over row tiles (three LDS stages): iteration t copies tile t+2, computes
+    // S and dP of tile t+1, and accumulates tile t with tile t+1's P and dS formed beside it.
     const LaneAddr<D> la(lane);
-    if (n_stages > 0) issue_rows<D>(gr, kvh, r_begin, st0, w, lane);
-    for (int64_t t = 0; t < n_stages; t++) {
+    if (n_stages > 0) {
+        issue_rows<D>(gr, kvh, r_begin, stg[0], w, lane);
+        if (n_stages > 1) issue_rows<D>(gr, kvh, r_begin + kRows, stg[1], w, lane);
         wait_vm_all();
         __syncthreads();
-        const int64_t r0 = r_begin + t * kRows;
-        const bool has_next = t + 1 < n_stages;
-        // this stage needs the causal mask if some row in it precedes some key of the pair
-        const bool need_mask = resp && r0 < (key0_pair + 2 * kPage - 1 - a.q_start) * a.g;
-        int64_t rm = row_min - r0;
-        const int rmin = rm < 0 ? 0 : (rm > kRows ? kRows : (int)rm);
-        char* cur = (t & 1) ? st1 : st0;
-        char* nxt = (t & 1) ? st0 : st1;
-        dkdv_step<D>(st, cur, nxt, has_next, a, gr, kvh, r0 + kRows, la, need_mask, rmin, w, lane);
+        Prob cur;
+        {
+            f32x16 s0, dp0;
+            tile_scores<D>(st, (const LS_LDS char*)stg[0], la.k, s0, dp0);
+            bool m0;
+            int rmh0;
+            mask_of(0, m0, rmh0);
+            const LS_LDS f32x2* lsd0 = (const LS_LDS f32x2*)((const LS_LDS char*)stg[0] + 2 * RowStage<D>::QBYTES);
+#pragma unroll
+            for (int un = 0; un < 4; un++) prob_unit(un, s0, dp0, lsd0, m0, rmh0, a.scale_log2, h, cur);
+        }
+        for (int64_t t = 0; t < n_stages; t++) {
+            // tile t+1 has landed; stage (t+2) % 3 was last read in iteration t-1
+            wait_vm_all();
+            __syncthreads();
+            // the last iteration runs phases 1-2 on a stale stage; that result is never used
+            bool mn;
+            int rmhn;
+            mask_of(t + 1, mn, rmhn);
+            Prob nxt;
+            const int it = (int)(t % 3);
+            dkdv_step<D>(st, stg[it], stg[it == 2 ? 0 : it + 1], stg[it == 0 ? 2 : it - 1], t + 2 < n_stages, gr,
+                         kvh, r_begin + (t + 2) * kRows, cur, nxt, la, mn, rmhn, a.scale_log2, w, lane);
+            cur = nxt;
+        }
     }
 
     // ---- write this wave's keys: dK (scaled) and dV, element i is key 8(i/4) + 4h + i%4
+    mfma_drain();
     if (!page_ok) return;
     bool first;
     float *gk, *gv;
@@ -308,23 +375,40 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks
         gv = a.dv_resp + off;
         key_stride = (int64_t)a.hkv * D;
     }
+    // Four key rows at a time: all their old values are loaded before any is used, so the
+    // read-modify-writes of an accumulating pass overlap instead of waiting one by one.  Keys
+    // past the block are skipped, except that a first touch writes the padding rows of a prompt
+    // page as 0; their loads read row 0 (always a key) and are discarded.
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-        const int kr = 32 * kh + 8 * (i >> 2) + 4 * h + (i & 3);  // key row within the page
-        const bool key_ok = kr < valid;
-        if (!key_ok && (resp || !first)) continue;  // response keys past the block / kept padding
-        float* pk = gk + kr * key_stride + n;
-        float* pv = gv + kr * key_stride + n;
+    for (int ib = 0; ib < 16; ib += 4) {
+        float old_k[4][F::DT], old_v[4][F::DT];
+        if (!first) {
 #pragma unroll
-        for (int dt = 0; dt < F::DT; dt++) {
-            const float vk = key_ok ? a.scale * st.dk[dt][i] : 0.f;
-            const float vv = key_ok ? st.dv[dt][i] : 0.f;
-            if (first) {
-                pk[32 * dt] = vk;
-                pv[32 * dt] = vv;
-            } else {
-                pk[32 * dt] += vk;
-                pv[32 * dt] += vv;
+            for (int ii = 0; ii < 4; ii++) {
+                const int i = ib + ii;
+                const int kr = 32 * kh + 8 * (i >> 2) + 4 * h + (i & 3);
+                const int rr = kr < valid ? kr : 0;
+#pragma unroll
+                for (int dt = 0; dt < F::DT; dt++) {
+                    old_k[ii][dt] = gk[rr * key_stride + n + 32 * dt];
+                    old_v[ii][dt] = gv[rr * key_stride + n + 32 * dt];
+                }
+            }
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ii++) {
+            const int i = ib + ii;
+            const int kr = 32 * kh + 8 * (i >> 2) + 4 * h + (i & 3);  // key row within the page
+            const bool key_ok = kr < valid;
+            if (!key_ok && (resp || !first)) continue;  // response keys past the block / kept padding
+            float* pk = gk + kr * key_stride + n;
+            float* pv = gv + kr * key_stride + n;
+#pragma unroll
+            for (int dt = 0; dt < F::DT; dt++) {
+                const float vk = key_ok ? a.scale * st.dk[dt][i] : 0.f;
+                const float vv = key_ok ? st.dv[dt][i] : 0.f;
+                pk[32 * dt] = first ? vk : old_k[ii][dt] + vk;
+                pv[32 * dt] = first ? vv : old_v[ii][dt] + vv;
             }
         }
     }

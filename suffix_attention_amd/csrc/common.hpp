@@ -88,6 +88,18 @@ __device__ __forceinline__ i16x4 lds_read_tr4(const LS_LDS void* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LS_LDS i16x4*)(p));
 }
 
+// Matrix-core multiply-add with the accumulator held in AGPRs, for kernels built with
+// VGPR-form matrix instructions (whose other accumulators feed vector-ALU work):
+//   acc[32 x 32] += A[32 x 16] . B[16 x 32]   (v_mfma_f32_32x32x16_bf16)
+// The compiler does not see this as a matrix instruction, so it does not model its hazards:
+// the two wait states ahead of it cover a vector-ALU write of A or B just before it; a chain
+// of these on one accumulator needs none (same-size back-to-back accumulation); the caller
+// runs mfma_drain() before anything reads the accumulator, and keeps the accumulator out of
+// vector-ALU code so that the compiler never moves it between these instructions.
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 // Enough wait states for any matrix instruction in flight to retire before its result is read
 // by inline assembly, which the compiler's hazard tracking does not see (the longest,
 // 32x32x16, needs fewer than 20).
