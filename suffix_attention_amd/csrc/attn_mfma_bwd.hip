@@ -131,34 +131,31 @@ __device__ __forceinline__ void tile_scores(const DkvState<D>& st, const LS_LDS 
     }
 }
 
-// Phase 2, one unit (u, hb) of four elements: P = exp2(S log2e/sqrt(d) - LSE log2e) (0 for
+// Phase 2, one unit (u, hb, j2) of two elements: P = exp2(S log2e/sqrt(d) - LSE log2e) (0 for
 // rows that precede the key when masked) and dS = P (dP - delta), packed as bf16 operand
-// words 2hb, 2hb+1 of key step u.
+// word 2hb + j2 of key step u.  Units are small so that they fit between consecutive matrix
+// instructions.
 struct Prob {
     uint32_t wp[2][4], wd[2][4];  // [u][word]
 };
 
 __device__ __forceinline__ void prob_unit(int unit, const f32x16& s, const f32x16& dp, const LS_LDS f32x2* lsd,
                                           bool need_mask, int rmh, float scale_log2, int h, Prob& pr) {
-    const int u = unit >> 1, hb = unit & 1;
-    const int rbase = 16 * u + 8 * hb + 4 * h;
-    const f32x4 l01 = *(const LS_LDS f32x4*)(lsd + rbase);       // rows rbase, rbase+1: (lse2, delta)
-    const f32x4 l23 = *(const LS_LDS f32x4*)(lsd + rbase + 2);   // rows rbase+2, rbase+3
-    float pv[4], dv[4];
+    const int u = unit >> 2, hb = (unit >> 1) & 1, j2 = unit & 1;
+    const int rbase = 16 * u + 8 * hb + 4 * h + 2 * j2;
+    const f32x4 l = *(const LS_LDS f32x4*)(lsd + rbase);  // rows rbase, rbase+1: (lse2, delta)
+    float pv[2], dv[2];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const float l2 = j < 2 ? l01[2 * j] : l23[2 * (j - 2)];
-        const float dl = j < 2 ? l01[2 * j + 1] : l23[2 * (j - 2) + 1];
+    for (int e = 0; e < 2; e++) {
+        const int j = 2 * j2 + e;
         const int i = 8 * u + 4 * hb + j;
-        float p = fast_exp2(__builtin_fmaf(s[i], scale_log2, -l2));
+        float p = fast_exp2(__builtin_fmaf(s[i], scale_log2, -l[2 * e]));
         if (need_mask) p = (16 * u + 8 * hb + j) >= rmh ? p : 0.f;
-        pv[j] = p;
-        dv[j] = p * (dp[i] - dl);
+        pv[e] = p;
+        dv[e] = p * (dp[i] - l[2 * e + 1]);
     }
-    pr.wp[u][2 * hb] = pack_bf16x2(pv[0], pv[1]);
-    pr.wp[u][2 * hb + 1] = pack_bf16x2(pv[2], pv[3]);
-    pr.wd[u][2 * hb] = pack_bf16x2(dv[0], dv[1]);
-    pr.wd[u][2 * hb + 1] = pack_bf16x2(dv[2], dv[3]);
+    pr.wp[u][2 * hb + j2] = pack_bf16x2(pv[0], pv[1]);
+    pr.wd[u][2 * hb + j2] = pack_bf16x2(dv[0], dv[1]);
 }
 
 // Phase 3 of row tile t: dV += P^T dO, dK += dS^T Q (dO, Q read transposed: rows are the
@@ -181,7 +178,7 @@ __device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur
     }
     constexpr int NST = 2 * F::DT;
     constexpr int PT = 2;
-    constexpr int NU = 4;  // phase-2 units of the next tile
+    constexpr int NU = 8;  // phase-2 units of the next tile
     i16x4 fr[PT][4];
     auto read_t = [&](int st_, i16x4* f) {
         const int dt = st_ % F::DT, u = st_ / F::DT;
@@ -336,7 +333,7 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks
             mask_of(0, m0, rmh0);
             const LS_LDS f32x2* lsd0 = (const LS_LDS f32x2*)((const LS_LDS char*)stg[0] + 2 * RowStage<D>::QBYTES);
 #pragma unroll
-            for (int un = 0; un < 4; un++) prob_unit(un, s0, dp0, lsd0, m0, rmh0, a.scale_log2, h, cur);
+            for (int un = 0; un < 8; un++) prob_unit(un, s0, dp0, lsd0, m0, rmh0, a.scale_log2, h, cur);
         }
         for (int64_t t = 0; t < n_stages; t++) {
             // tile t+1 has landed; stage (t+2) % 3 was last read in iteration t-1

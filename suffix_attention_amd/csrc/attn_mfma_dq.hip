@@ -3,8 +3,14 @@
 // (query tile, part, kv head), like the forward: per 64-key page, S^T = K Q^T and
 // dP^T = V dO^T (Q, dO in AGPRs as the B operands, K, V from LDS), dS^T = P^T (dP^T - delta)
 // with P recomputed from the forward's LSE, dQ^T += K^T dS^T (K read transposed).  Writes
-// one dQ part per key part; the parts are summed afterwards.  Built with its accumulators in
-// VGPRs: the S and dP tiles feed vector-ALU work every page.
+// one dQ part per key part; the parts are summed afterwards.
+//
+// Software pipeline over pages: iteration t computes S and dP of page t+1 on the matrix core,
+// then accumulates dQ for page t while page t+1's P and dS are formed on the vector ALU
+// between its matrix instructions.  That needs K of three pages (t for dQ, t+1 for S, t+2 in
+// flight) and V of two in LDS: 5 x 32 KiB at d = 256.  Built with VGPR-form matrix
+// instructions (the S and dP tiles feed vector-ALU work); the dQ accumulators stay in AGPRs
+// through explicit AGPR-form instructions.
 #include <math.h>
 
 #include "mfma_bwd.hpp"
@@ -12,32 +18,26 @@
 namespace ls {
 namespace {
 
-// ---------------------------------------------------------------------------------------
-// dQ pass
-// ---------------------------------------------------------------------------------------
 template <int D>
 struct DqState {
     bf16x8 qb[TileShape<D>::KS];    // Q^T operand (row lane%32)
     bf16x8 dob[TileShape<D>::KS];   // dO^T operand
-    f32x16 dq[TileShape<D>::DT];    // dQ^T accumulators: col = row, rows = d
+    f32x16 dq[TileShape<D>::DT];    // dQ^T accumulators (AGPRs): col = row, rows = d
     float lse2;                     // LSE * log2 e of this lane's row
     float dlt;                      // delta of this lane's row
 };
 
-template <int D>
-__device__ __forceinline__ void dq_tile(DqState<D>& st, const LS_LDS char* lds_k, const LS_LDS char* lds_v,
-                                        LaneAddr<D> la, int valid, int64_t key0, bool resp, bool need_mask,
-                                        int64_t vis_limit, float scale_log2, int lane) {
+// Phase 1 of page t: S^T = K Q^T and dP^T = V dO^T (two 32-key tiles each); K and V
+// fragments are read PD k-steps ahead.
+template <int D, typename Copy>
+__device__ __forceinline__ void page_scores(const DqState<D>& st, const LS_LDS char* lds_k, const LS_LDS char* lds_v,
+                                            uint32_t lk, f32x16 (&s)[2], f32x16 (&dp)[2], Copy&& copy_step) {
     using F = TileShape<D>;
-    const int h = lane >> 5;
-    asm volatile("" : "+v"(la.k), "+v"(la.v));
-    f32x16 s[2], dp[2];
     s[0] = s[1] = dp[0] = dp[1] = f32x16{};
-    // K and V fragments are read PD k-steps ahead of their MFMAs
     constexpr int PD = 2;
     bf16x8 kb[PD][4];
     auto read_kv = [&](int ks, bf16x8* b) {
-        const uint32_t o = la.k ^ (uint32_t)(ks << 5);
+        const uint32_t o = lk ^ (uint32_t)(ks << 5);
         b[0] = *(const LS_LDS bf16x8*)(lds_k + o);
         b[1] = *(const LS_LDS bf16x8*)(lds_k + o + 32 * 2 * D);
         b[2] = *(const LS_LDS bf16x8*)(lds_v + o);
@@ -53,47 +53,78 @@ __device__ __forceinline__ void dq_tile(DqState<D>& st, const LS_LDS char* lds_k
         s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, st.qb[ks], s[1], 0, 0, 0);
         dp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, st.dob[ks], dp[0], 0, 0, 0);
         dp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, st.dob[ks], dp[1], 0, 0, 0);
+        copy_step(ks);  // this step's share of the next pages' copies, beside the matrix work
         __builtin_amdgcn_sched_barrier(0);
     }
-    int lim_valid = valid - 4 * h;
-    int lim_causal = 64;
+}
+
+// Masking limits of one page for this lane's row: element i of tile kt is key
+// 32kt + 8(i/4) + 4h + i%4 of the page; keys at or past lim_valid, or past lim_causal (response
+// keys after the row), get P = 0.
+struct PageMask {
+    bool on;
+    int lim_valid, lim_causal;
+};
+
+__device__ __forceinline__ PageMask page_mask(bool need_mask, int valid, int64_t key0, bool resp, int64_t vis_limit,
+                                              int h) {
+    PageMask m;
+    m.on = need_mask;
+    m.lim_valid = valid - 4 * h;
+    m.lim_causal = 64;
     if (resp) {
         const int64_t c = vis_limit - key0 - 4 * h;
-        lim_causal = c < -1 ? -1 : (c > 64 ? 64 : (int)c);
+        m.lim_causal = c < -1 ? -1 : (c > 64 ? 64 : (int)c);
     }
-    bf16x8 db[2][2];
+    return m;
+}
+
+// Phase 2, one unit (ku, t) of two elements (ku = (kt, u) a 16-key step): P = exp2(S scale
+// log2e - LSE log2e), dS = P (dP - delta), packed as word t of the bf16 dS^T operand of key
+// step ku.  Units are small so that they fit between consecutive matrix instructions.
+struct DsWords {
+    uint32_t w[4][4];  // [ku][word]
+};
+
+template <int D>
+__device__ __forceinline__ void ds_unit(int unit, const f32x16 (&s)[2], const f32x16 (&dp)[2], const PageMask& m,
+                                        const DqState<D>& st, float scale_log2, DsWords& out) {
+    const int ku = unit >> 2, t = unit & 3;
+    const int kt = ku >> 1, u = ku & 1;
+    float d2[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; kt++) {
-#pragma unroll
-        for (int u = 0; u < 2; u++) {
-            uint32_t w4[4];
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                float d2[2];
-#pragma unroll
-                for (int e = 0; e < 2; e++) {
-                    const int i = 8 * u + 2 * t + e;
-                    float p = fast_exp2(__builtin_fmaf(s[kt][i], scale_log2, -st.lse2));
-                    if (need_mask) {
-                        const int kc = 32 * kt + 8 * (i >> 2) + (i & 3);
-                        p = (kc < lim_valid && kc <= lim_causal) ? p : 0.f;
-                    }
-                    d2[e] = p * (dp[kt][i] - st.dlt);
-                }
-                w4[t] = pack_bf16x2(d2[0], d2[1]);
-            }
-            db[kt][u] = __builtin_bit_cast(bf16x8, (u32x4{w4[0], w4[1], w4[2], w4[3]}));
+    for (int e = 0; e < 2; e++) {
+        const int i = 8 * u + 2 * t + e;
+        float p = fast_exp2(__builtin_fmaf(s[kt][i], scale_log2, -st.lse2));
+        if (m.on) {
+            const int kc = 32 * kt + 8 * (i >> 2) + (i & 3);
+            p = (kc < m.lim_valid && kc <= m.lim_causal) ? p : 0.f;
         }
+        d2[e] = p * (dp[kt][i] - st.dlt);
     }
-    // dQ^T += K^T dS^T.  Step st = (kt, u, dt), dt fastest; K^T fragments read PV steps ahead.
+    out.w[ku][t] = pack_bf16x2(d2[0], d2[1]);
+}
+
+// Phase 3 of page t: dQ^T += K^T dS^T (K read transposed), with phase 2 of page t+1 spread
+// over the steps.  Step st = (ku, dt), dt fastest; K^T fragments read PV steps ahead.
+template <int D>
+__device__ __forceinline__ void page_accumulate(DqState<D>& st, const DsWords& cur, const LS_LDS char* lds_k,
+                                                uint32_t lv, const f32x16 (&s_n)[2], const f32x16 (&dp_n)[2],
+                                                const PageMask& m_n, float scale_log2, DsWords& nxt) {
+    using F = TileShape<D>;
+    bf16x8 db[4];
+#pragma unroll
+    for (int ku = 0; ku < 4; ku++)
+        db[ku] = __builtin_bit_cast(bf16x8, (u32x4{cur.w[ku][0], cur.w[ku][1], cur.w[ku][2], cur.w[ku][3]}));
     constexpr int NST = 4 * F::DT;
     constexpr int PV = 4;
+    constexpr int NU = 16;  // phase-2 units of the next page
     i16x4 tlo[PV], thi[PV];
     auto read_kt = [&](int st_, i16x4& lo, i16x4& hi) {
         const int dt = st_ % F::DT, ku = st_ / F::DT;
         const int R = 32 * (ku >> 1) + 16 * (ku & 1);
-        lo = lds_read_tr4(lds_k + (la.v ^ tr_x<D>(dt, R)) + R * 2 * D);
-        hi = lds_read_tr4(lds_k + (la.v ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D);
+        lo = lds_read_tr4(lds_k + (lv ^ tr_x<D>(dt, R)) + R * 2 * D);
+        hi = lds_read_tr4(lds_k + (lv ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D);
     };
 #pragma unroll
     for (int j = 0; j < PV; j++) read_kt(j, tlo[j], thi[j]);
@@ -102,27 +133,44 @@ __device__ __forceinline__ void dq_tile(DqState<D>& st, const LS_LDS char* lds_k
         const int dt = st_ % F::DT, ku = st_ / F::DT;
         const bf16x8 ka = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tlo[st_ % PV], thi[st_ % PV], 0, 1, 2, 3, 4, 5, 6, 7));
         if (st_ + PV < NST) read_kt(st_ + PV, tlo[st_ % PV], thi[st_ % PV]);
-        st.dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, db[ku >> 1][ku & 1], st.dq[dt], 0, 0, 0);
+        mfma32_agpr(st.dq[dt], ka, db[ku]);
+#pragma unroll
+        for (int un = 0; un < NU; un++)
+            if (un >= st_ * NU / NST && un < (st_ + 1) * NU / NST) ds_unit<D>(un, s_n, dp_n, m_n, st, scale_log2, nxt);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// One page: issue the copies of page t+1 (K and V into nxt), then the tile on cur.  The two
-// stages are restrict pointers so that, once inlined, the compiler knows the copies in flight
-// cannot alias the tile being read and does not wait for them.
+// Iteration t: copy K(t+2) and V(t+2), phase 1 of page t+1, then phase 3 of page t with
+// phase 2 of page t+1 beside it.  The LDS tiles are restrict pointers so that, once inlined,
+// the compiler knows the copies in flight cannot alias the tiles being read.
 template <int D, int NW>
-__device__ __forceinline__ void dq_step(DqState<D>& st, const char* __restrict__ cur, char* __restrict__ nxt,
-                                        const KeyTiles<D, NW>& kt, bool has_next, int32_t e_next, int64_t t,
-                                        int valid, int64_t key0, LaneAddr<D> la, bool resp, bool need_mask,
-                                        int64_t vis_limit, float scale_log2, int w, int lane) {
-    using F = TileShape<D>;
-    if (has_next) {
-        const int vn = kt.valid(t + 1);
-        kt.copy(kt.tile(e_next, t + 1, false), vn, nxt, w);
-        kt.copy(kt.tile(e_next, t + 1, true), vn, nxt + F::TILE, w);
-    }
-    dq_tile<D>(st, (const LS_LDS char*)cur, (const LS_LDS char*)(cur + F::TILE), la, valid, key0, resp, need_mask,
-               vis_limit, scale_log2, lane);
+__device__ __forceinline__ void dq_iter(DqState<D>& st, const KeyTiles<D, NW>& kt, int64_t t, bool copy, int32_t e2,
+                                        char* __restrict__ k_dst, char* __restrict__ v_dst,
+                                        const char* __restrict__ k_n, const char* __restrict__ v_n,
+                                        const char* __restrict__ k_t, const DsWords& cur, DsWords& nxt,
+                                        const PageMask& m_n, LaneAddr<D> la, float scale_log2, int w) {
+    // the copies of page t+2 are spread over the S / dP steps, so that issuing them never
+    // stalls the wave for long and they overlap the matrix work
+    constexpr int PW = KeyTiles<D, NW>::PER_WAVE;
+    constexpr int KS = TileShape<D>::KS;
+    const int vn = kt.valid(t + 2);
+    const char* ksrc = kt.tile(e2, t + 2, false);
+    const char* vsrc = kt.tile(e2, t + 2, true);
+    auto copy_step = [&](int ks) {
+        if (!copy) return;
+#pragma unroll
+        for (int p = 0; p < 2 * PW; p++)
+            if (p * KS / (2 * PW) == ks) {
+                if (p < PW) kt.copy_piece(ksrc, vn, k_dst, w, p);
+                else kt.copy_piece(vsrc, vn, v_dst, w, p - PW);
+            }
+    };
+    uint32_t lk = la.k, lv = la.v;
+    asm volatile("" : "+v"(lk), "+v"(lv));
+    f32x16 s_n[2], dp_n[2];
+    page_scores<D>(st, (const LS_LDS char*)k_n, (const LS_LDS char*)v_n, lk, s_n, dp_n, copy_step);
+    page_accumulate<D>(st, cur, (const LS_LDS char*)k_t, lv, s_n, dp_n, m_n, scale_log2, nxt);
 }
 
 template <int D, int NW>
@@ -130,8 +178,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_
 void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
     using F = TileShape<D>;
     constexpr int BM = 32 * NW;
-    __shared__ __attribute__((aligned(1024))) char st0[2 * F::TILE];
-    __shared__ __attribute__((aligned(1024))) char st1[2 * F::TILE];
+    __shared__ __attribute__((aligned(1024))) char kbuf[3][F::TILE];
+    __shared__ __attribute__((aligned(1024))) char vbuf[2][F::TILE];
 
     const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
     if (lb >= n_blocks) return;
@@ -161,10 +209,16 @@ void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
         for (int ks = 0; ks < F::KS; ks++) {
             st.qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * ks));
             st.dob[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(drow + 16 * ks));
-            asm volatile("" : "+a"(st.qb[ks]), "+a"(st.dob[ks]));  // read-only MFMA operands
         }
+        // read-only MFMA operands (after all loads are in flight), and the accumulators: AGPRs
 #pragma unroll
-        for (int dt = 0; dt < F::DT; dt++) st.dq[dt] = f32x16{};
+        for (int ks = 0; ks < F::KS; ks++) asm volatile("" : "+a"(st.qb[ks]), "+a"(st.dob[ks]));
+#pragma unroll
+        for (int dt = 0; dt < F::DT; dt++) {
+            st.dq[dt] = f32x16{};
+            asm volatile("" : "+a"(st.dq[dt]));
+        }
+        agpr_write_gap();
         const f32x2 ld = gr.lsed[kvh * gr.rows_pad + (row_ok ? my_row : rows_total - 1)];
         st.lse2 = ld[0];
         st.dlt = ld[1];
@@ -183,36 +237,66 @@ void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
 
     const int64_t lp0 = resp ? 0 : a.shard_lo[part];
     const KeyTiles<D, NW> kt(a, resp, lp0, kvh, w, lane);
-    // page-table entries are read through the scalar cache one page before their copies and
-    // clamped where they are used
-    int32_t e_next = n_tiles > 1 ? kt.entry(1) : 0;
-    if (n_tiles > 0) {
-        const int32_t e0 = kt.entry(0);
-        kt.copy(kt.tile(e0, 0, false), kt.valid(0), st0, w);
-        kt.copy(kt.tile(e0, 0, true), kt.valid(0), st0 + F::TILE, w);
-    }
-    for (int64_t t = 0; t < n_tiles; t++) {
-        const int32_t e_after = t + 2 < n_tiles ? kt.entry(t + 2) : 0;
-        wait_vm_all();
-        __syncthreads();
+    auto mask_of = [&](int64_t t) {
         const int valid = kt.valid(t);
         const int64_t key0 = (lp0 + t) * kPage;
-        const bool need_mask = valid < kPage || (resp && key0 + kPage - 1 > a.q_start + tok_min);
-        char* cur = (t & 1) ? st1 : st0;
-        char* nxt = (t & 1) ? st0 : st1;
-        dq_step<D, NW>(st, cur, nxt, kt, t + 1 < n_tiles, e_next, t, valid, key0, la, resp, need_mask, vis_limit,
-                       a.scale_log2, w, lane);
-        e_next = e_after;
+        const bool need = valid < kPage || (resp && key0 + kPage - 1 > a.q_start + tok_min);
+        return page_mask(need, valid, key0, resp, vis_limit, h);
+    };
+
+    if (n_tiles > 0) {
+        // prologue: pages 0 and 1 in LDS, phases 1-2 of page 0
+        const int32_t e0 = kt.entry(0);
+        kt.copy(kt.tile(e0, 0, false), kt.valid(0), kbuf[0], w);
+        kt.copy(kt.tile(e0, 0, true), kt.valid(0), vbuf[0], w);
+        if (n_tiles > 1) {
+            const int32_t e1 = kt.entry(1);
+            kt.copy(kt.tile(e1, 1, false), kt.valid(1), kbuf[1], w);
+            kt.copy(kt.tile(e1, 1, true), kt.valid(1), vbuf[1], w);
+        }
+        // page-table entries are read through the scalar cache one iteration before their
+        // copies and clamped where they are used
+        int32_t e2 = n_tiles > 2 ? kt.entry(2) : 0;
+        wait_vm_all();
+        __syncthreads();
+        DsWords cur;
+        {
+            f32x16 s0[2], dp0[2];
+            page_scores<D>(st, (const LS_LDS char*)kbuf[0], (const LS_LDS char*)vbuf[0], la.k, s0, dp0, [](int) {});
+            const PageMask m0 = mask_of(0);
+#pragma unroll
+            for (int un = 0; un < 16; un++) ds_unit<D>(un, s0, dp0, m0, st, a.scale_log2, cur);
+        }
+        for (int64_t t = 0; t < n_tiles; t++) {
+            // K(t+1), V(t+1) have landed; K buffer (t+2) % 3 and V buffer t % 2 were last read
+            // in iteration t-1.  The last iteration runs phases 1-2 on stale tiles; that
+            // result is never used.
+            const int32_t e3 = t + 3 < n_tiles ? kt.entry(t + 3) : 0;
+            wait_vm_all();
+            __syncthreads();
+            const int k0 = (int)(t % 3), k1 = k0 == 2 ? 0 : k0 + 1, k2 = k0 == 0 ? 2 : k0 - 1;
+            const int v0 = (int)(t & 1), v1 = v0 ^ 1;
+            const PageMask m_n = mask_of(t + 1);
+            DsWords nxt;
+            dq_iter<D, NW>(st, kt, t, t + 2 < n_tiles, e2, kbuf[k2], vbuf[v0], kbuf[k1], vbuf[v1], kbuf[k0], cur, nxt,
+                           m_n, la, a.scale_log2, w);
+            cur = nxt;
+            e2 = e3;
+        }
     }
+    mfma_drain();
     if (!row_ok) return;
     float* dst = a.dq_parts + (((int64_t)part * a.n_rows + my_tok) * a.hq + my_head) * (int64_t)D;
 #pragma unroll
     for (int dt = 0; dt < F::DT; dt++) {
+        // scale in place in the AGPRs; the stores read them from there
+#pragma unroll
+        for (int i = 0; i < 16; i++) st.dq[dt][i] = agpr_scaled(st.dq[dt][i], a.scale);
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++) {
             const int dd = dt * 32 + 8 * q4 + 4 * h;
-            *(float4*)(dst + dd) = make_float4(a.scale * st.dq[dt][4 * q4], a.scale * st.dq[dt][4 * q4 + 1],
-                                               a.scale * st.dq[dt][4 * q4 + 2], a.scale * st.dq[dt][4 * q4 + 3]);
+            *(float4*)(dst + dd) = make_float4(st.dq[dt][4 * q4], st.dq[dt][4 * q4 + 1], st.dq[dt][4 * q4 + 2],
+                                               st.dq[dt][4 * q4 + 3]);
         }
     }
 }

@@ -101,6 +101,18 @@ struct KeyTiles {
         return left < kPage ? (int)left : kPage;
     }
 
+    // Copy j (0 <= j < PER_WAVE) of this wave's share of one tile, so that a caller can spread
+    // a tile's copies over its compute steps; rows past `valid` repeat the last valid row.
+    __device__ __forceinline__ void copy_piece(const char* src, int valid_rows, char* lds, int w, int j) const {
+        uint32_t o = off[j];
+        if (valid_rows < kPage) {
+            const int r = j * JROWS + low;
+            const int rs = r < valid_rows ? r : valid_rows - 1;
+            o = (uint32_t)rs * row_bytes + (uint32_t)((lane_x ^ swz<D>(j * JROWS)) << 4);
+        }
+        dma16(src + o, (LS_LDS void*)(lds + (j * NW + w) * 1024));
+    }
+
     // Copy one tile into LDS (all NW waves together); rows past `valid` repeat the last valid
     // row (finite, masked by the caller).
     __device__ __forceinline__ void copy(const char* src, int valid_rows, char* lds, int w) const {
