@@ -91,6 +91,39 @@ __device__ __forceinline__ void issue_rows(const GroupRows& gr, int kvh, int64_t
               (LS_LDS void*)(stage + 2 * RowStage<D>::QBYTES));
 }
 
+// The same copy in pieces, so that a caller can spread it over its compute steps: piece p of
+// 2 * PER_WAVE copies block p % PER_WAVE of Q (p < PER_WAVE) or dO; piece 0 also carries the
+// (lse2, delta) pairs (wave 0).
+template <int D>
+struct RowCopy {
+    static constexpr int RPK = 512 / D;
+    static constexpr int PER_WAVE = kRows * D * 2 / 1024 / 4;
+    static constexpr int JROWS = 4 * RPK;
+    static constexpr int PIECES = 2 * PER_WAVE;
+    uint32_t off[PER_WAVE];  // this lane's byte offset inside the Q (or dO) row tile, copy j
+
+    __device__ __forceinline__ RowCopy(int w, int lane) {
+        using F = TileShape<D>;
+        const int low = w * RPK + lane / F::KCH;
+        const int lane_x = (lane % F::KCH) ^ swz<D>(low);
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; j++)
+            off[j] = (uint32_t)(j * JROWS + low) * (D * 2) + (uint32_t)((lane_x ^ swz<D>(j * JROWS)) << 4);
+    }
+
+    __device__ __forceinline__ void piece(const GroupRows& gr, int kvh, int64_t r0, char* stage, int w, int lane,
+                                          int p) const {
+        const int64_t base = ((int64_t)kvh * gr.rows_pad + r0) * D * 2;
+        const int j = p % PER_WAVE;
+        const char* src = (const char*)(p < PER_WAVE ? gr.q : gr.dout) + base;
+        char* dst = stage + (p < PER_WAVE ? 0 : RowStage<D>::QBYTES);
+        dma16(src + off[j], (LS_LDS void*)(dst + (j * 4 + w) * 1024));
+        if (p == 0 && w == 0 && lane < kRows * 8 / 16)
+            dma16((const char*)(gr.lsed + kvh * gr.rows_pad + r0) + lane * 16,
+                  (LS_LDS void*)(stage + 2 * RowStage<D>::QBYTES));
+    }
+};
+
 template <int D>
 struct DkvState {
     bf16x8 kb[TileShape<D>::KS];   // K^T operand: key lane%32, d = 16ks + 8(lane/32) .. +8
@@ -101,9 +134,9 @@ struct DkvState {
 
 // Phase 1 of a row tile: S = Q K^T and dP = dO V^T for 32 rows x 32 keys (element i is row
 // 8(i/4) + 4h + i%4 of the tile, key lane%32).  Q and dO fragments are read PD k-steps ahead.
-template <int D>
+template <int D, typename Copy>
 __device__ __forceinline__ void tile_scores(const DkvState<D>& st, const LS_LDS char* stage, uint32_t lk, f32x16& s,
-                                            f32x16& dp) {
+                                            f32x16& dp, Copy&& copy_step) {
     using F = TileShape<D>;
     const LS_LDS char* lq = stage;
     const LS_LDS char* ldo = stage + RowStage<D>::QBYTES;
@@ -127,6 +160,7 @@ __device__ __forceinline__ void tile_scores(const DkvState<D>& st, const LS_LDS 
         }
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, st.kb[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, st.vb[ks], dp, 0, 0, 0);
+        copy_step(ks);  // this step's share of a later tile's copies, beside the matrix work
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -218,14 +252,22 @@ __device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur
 template <int D>
 __device__ __forceinline__ void dkdv_step(DkvState<D>& st, const char* __restrict__ stage_t,
                                           const char* __restrict__ stage_n, char* __restrict__ dst, bool copy,
-                                          const GroupRows& gr, int kvh, int64_t copy_r0, const Prob& cur, Prob& nxt,
+                                          const GroupRows& gr, const RowCopy<D>& rc, int kvh, int64_t copy_r0,
+                                          const Prob& cur, Prob& nxt,
                                           LaneAddr<D> la, bool mask_n, int rmh_n, float scale_log2, int w,
                                           int lane) {
-    if (copy) issue_rows<D>(gr, kvh, copy_r0, dst, w, lane);
+    // the copies of the tile two ahead are spread over the S / dP steps, so that issuing them
+    // never stalls the wave for long and they overlap the matrix work
+    auto copy_step = [&](int ks) {
+        if (!copy) return;
+#pragma unroll
+        for (int p = 0; p < RowCopy<D>::PIECES; p++)
+            if (p * TileShape<D>::KS / RowCopy<D>::PIECES == ks) rc.piece(gr, kvh, copy_r0, dst, w, lane, p);
+    };
     uint32_t lk = la.k, lv = la.v;
     asm volatile("" : "+v"(lk), "+v"(lv));
     f32x16 s_n, dp_n;
-    tile_scores<D>(st, (const LS_LDS char*)stage_n, lk, s_n, dp_n);
+    tile_scores<D>(st, (const LS_LDS char*)stage_n, lk, s_n, dp_n, copy_step);
     tile_accumulate<D>(st, cur, (const LS_LDS char*)stage_t, lv, s_n, dp_n,
                        (const LS_LDS f32x2*)((const LS_LDS char*)stage_n + 2 * RowStage<D>::QBYTES), mask_n, rmh_n,
                        scale_log2, lane >> 5, nxt);
@@ -319,6 +361,7 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks
     // Pipeline over row tiles (three LDS stages): iteration t copies tile t+2, computes
     // S and dP of tile t+1, and accumulates tile t with tile t+1's P and dS formed beside it.
     const LaneAddr<D> la(lane);
+    const RowCopy<D> rc(w, lane);
     if (n_stages > 0) {
         issue_rows<D>(gr, kvh, r_begin, stg[0], w, lane);
         if (n_stages > 1) issue_rows<D>(gr, kvh, r_begin + kRows, stg[1], w, lane);
@@ -327,7 +370,7 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks
         Prob cur;
         {
             f32x16 s0, dp0;
-            tile_scores<D>(st, (const LS_LDS char*)stg[0], la.k, s0, dp0);
+            tile_scores<D>(st, (const LS_LDS char*)stg[0], la.k, s0, dp0, [](int) {});
             bool m0;
             int rmh0;
             mask_of(0, m0, rmh0);
@@ -346,7 +389,7 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks
             Prob nxt;
             const int it = (int)(t % 3);
             dkdv_step<D>(st, stg[it], stg[it == 2 ? 0 : it + 1], stg[it == 0 ? 2 : it - 1], t + 2 < n_stages, gr,
-                         kvh, r_begin + (t + 2) * kRows, cur, nxt, la, mn, rmhn, a.scale_log2, w, lane);
+                         rc, kvh, r_begin + (t + 2) * kRows, cur, nxt, la, mn, rmhn, a.scale_log2, w, lane);
             cur = nxt;
         }
     }

@@ -81,9 +81,9 @@ struct PartInfo {
 
 // S^T(t) = K(t) Q^T for the wave's 32 rows: two 32-key tiles, KS k-steps each, K fragments
 // read PD steps ahead.
-template <int D>
+template <int D, typename Copy>
 __device__ __forceinline__ void scores(const bf16x8 (&qb)[TileShape<D>::KS], f32x16 (&s)[2], const LS_LDS char* lds_k,
-                                       uint32_t lk) {
+                                       uint32_t lk, Copy&& copy_step) {
     using F = TileShape<D>;
     constexpr int PD = 2;
     bf16x8 kbuf[PD][2];
@@ -105,6 +105,7 @@ __device__ __forceinline__ void scores(const bf16x8 (&qb)[TileShape<D>::KS], f32
         }
         s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qb[ks], s[0], 0, 0, 0);
         s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qb[ks], s[1], 0, 0, 0);
+        copy_step(ks);  // this step's share of the copies, beside the matrix work
     }
 }
 
@@ -214,10 +215,29 @@ __device__ __forceinline__ void score_iter(const AttnArgs& a, const PartInfo<D>&
                                            float& m_ref, float& l, int64_t vis_limit, uint32_t lk, int w, int lane) {
     wait_vm_all();
     lds_barrier();
-    issue_copies<D>(pi.kt, pi.n_tiles, t, phys_t, phys_t1, k_dst, v_dst, w);
+    // this wave's copies of K(t+1) and V(t) are spread over the score steps, so that issuing
+    // them never stalls the wave for long and they overlap the matrix work
+    constexpr int PW = KeyTiles<D, kNW>::PER_WAVE;
+    constexpr int KS = TileShape<D>::KS;
+    const bool ck = t + 1 < pi.n_tiles, cv = t < pi.n_tiles;
+    const int vk = pi.kt.valid(t + 1), vv = pi.kt.valid(t);
+    const char* ksrc = pi.kt.tile(phys_t1, t + 1, false);
+    const char* vsrc = pi.kt.tile(phys_t, t, true);
+    auto copy_step = [&](int ks) {
+#pragma unroll
+        for (int p = 0; p < 2 * PW; p++)
+            if (p * KS / (2 * PW) == ks) {
+                if (p < PW) {
+                    if (ck) pi.kt.copy_piece(ksrc, vk, k_dst, w, p);
+                } else if (cv) {
+                    pi.kt.copy_piece(vsrc, vv, v_dst, w, p - PW);
+                }
+            }
+    };
     f32x16 s[2];
     const bool live = t < pi.n_tiles;
-    if (live) scores<D>(qb, s, (const LS_LDS char*)k_cur, lk);
+    if (live) scores<D>(qb, s, (const LS_LDS char*)k_cur, lk, copy_step);
+    else issue_copies<D>(pi.kt, pi.n_tiles, t, phys_t, phys_t1, k_dst, v_dst, w);
     lds_barrier();
     if (live) {
         const int valid = pi.kt.valid(t);
