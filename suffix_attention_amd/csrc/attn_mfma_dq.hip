@@ -5,10 +5,11 @@
 // with P recomputed from the forward's LSE, dQ^T += K^T dS^T (K read transposed).  Writes
 // one dQ part per key part; the parts are summed afterwards.
 //
-// Software pipeline over pages: iteration t computes S and dP of page t+1 on the matrix core,
-// then accumulates dQ for page t while page t+1's P and dS are formed on the vector ALU
-// between its matrix instructions.  That needs K of three pages (t for dQ, t+1 for S, t+2 in
-// flight) and V of two in LDS: 5 x 32 KiB at d = 256.  Built with VGPR-form matrix
+// Software pipeline over pages, so that the vector work (P and dS) of one tile runs between the
+// matrix instructions of another: iteration t computes S and dP of page t+1 and accumulates dQ
+// for page t, with dS of page t's second key tile and page t+1's first formed beside them.  That
+// needs K of three pages (t for dQ, t+1 for S, t+2 in flight) and V of two in LDS: 5 x 32 KiB
+// at d = 256.  Built with VGPR-form matrix
 // instructions (the S and dP tiles feed vector-ALU work); the dQ accumulators stay in AGPRs
 // through explicit AGPR-form instructions.
 #include <math.h>
@@ -27,98 +28,93 @@ struct DqState {
     float dlt;                      // delta of this lane's row
 };
 
-// Phase 1 of page t: S^T = K Q^T and dP^T = V dO^T (two 32-key tiles each); K and V
-// fragments are read PD k-steps ahead.
-template <int D, typename Copy>
-__device__ __forceinline__ void page_scores(const DqState<D>& st, const LS_LDS char* lds_k, const LS_LDS char* lds_v,
-                                            uint32_t lk, f32x16 (&s)[2], f32x16 (&dp)[2], Copy&& copy_step) {
+// Phase 1 of one 32-key tile of a page: S^T = K Q^T and dP^T = V dO^T (lds_k, lds_v point at
+// the tile's first key row), 16 k-steps of two matrix instructions; K and V fragments are read
+// PD steps ahead.  beside(ks) runs after step ks's matrix instructions: vector work or copies
+// that overlap them.
+template <int D, typename Beside>
+__device__ __forceinline__ void tile_scores(const DqState<D>& st, const LS_LDS char* lds_k, const LS_LDS char* lds_v,
+                                            uint32_t lk, f32x16& s, f32x16& dp, Beside&& beside) {
     using F = TileShape<D>;
-    s[0] = s[1] = dp[0] = dp[1] = f32x16{};
-    constexpr int PD = 2;
-    bf16x8 kb[PD][4];
+    s = dp = f32x16{};
+    constexpr int PD = 3;
+    bf16x8 kb[PD][2];
     auto read_kv = [&](int ks, bf16x8* b) {
         const uint32_t o = lk ^ (uint32_t)(ks << 5);
         b[0] = *(const LS_LDS bf16x8*)(lds_k + o);
-        b[1] = *(const LS_LDS bf16x8*)(lds_k + o + 32 * 2 * D);
-        b[2] = *(const LS_LDS bf16x8*)(lds_v + o);
-        b[3] = *(const LS_LDS bf16x8*)(lds_v + o + 32 * 2 * D);
+        b[1] = *(const LS_LDS bf16x8*)(lds_v + o);
     };
 #pragma unroll
-    for (int j = 0; j < PD; j++) read_kv(j, kb[j]);
+    for (int j = 0; j < PD; j++)
+        if (j < F::KS) read_kv(j, kb[j]);
 #pragma unroll
     for (int ks = 0; ks < F::KS; ks++) {
-        const bf16x8 k0 = kb[ks % PD][0], k1 = kb[ks % PD][1], v0 = kb[ks % PD][2], v1 = kb[ks % PD][3];
+        const bf16x8 k0 = kb[ks % PD][0], v0 = kb[ks % PD][1];
         if (ks + PD < F::KS) read_kv(ks + PD, kb[ks % PD]);
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, st.qb[ks], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, st.qb[ks], s[1], 0, 0, 0);
-        dp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, st.dob[ks], dp[0], 0, 0, 0);
-        dp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, st.dob[ks], dp[1], 0, 0, 0);
-        copy_step(ks);  // this step's share of the next pages' copies, beside the matrix work
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, st.qb[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, st.dob[ks], dp, 0, 0, 0);
+        beside(ks);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// Masking limits of one page for this lane's row: element i of tile kt is key
-// 32kt + 8(i/4) + 4h + i%4 of the page; keys at or past lim_valid, or past lim_causal (response
-// keys after the row), get P = 0.
+// Masking limit of one page for this lane's row: element i of key tile kt is key
+// 32kt + 8(i/4) + 4h + i%4 of the page, and gets P = 0 unless that key is below the page's
+// valid keys and, for response keys, at most the row's own position.  Both conditions fold into
+// one bound on 32kt + 8(i/4) + i%4 (the lane's 4h is taken out of it).  `on` is false when no
+// key of the page is masked for any row of the workgroup.
 struct PageMask {
     bool on;
-    int lim_valid, lim_causal;
+    int lim;
 };
 
 __device__ __forceinline__ PageMask page_mask(bool need_mask, int valid, int64_t key0, bool resp, int64_t vis_limit,
                                               int h) {
     PageMask m;
     m.on = need_mask;
-    m.lim_valid = valid - 4 * h;
-    m.lim_causal = 64;
+    m.lim = valid - 4 * h;
     if (resp) {
-        const int64_t c = vis_limit - key0 - 4 * h;
-        m.lim_causal = c < -1 ? -1 : (c > 64 ? 64 : (int)c);
+        const int64_t c = vis_limit - key0 - 4 * h + 1;
+        const int lc = c < 0 ? 0 : (c > 65 ? 65 : (int)c);
+        m.lim = lc < m.lim ? lc : m.lim;
     }
     return m;
 }
 
-// Phase 2, one unit (ku, t) of two elements (ku = (kt, u) a 16-key step): P = exp2(S scale
-// log2e - LSE log2e), dS = P (dP - delta), packed as word t of the bf16 dS^T operand of key
-// step ku.  Units are small so that they fit between consecutive matrix instructions.
-struct DsWords {
-    uint32_t w[4][4];  // [ku][word]
-};
-
-template <int D>
-__device__ __forceinline__ void ds_unit(int unit, const f32x16 (&s)[2], const f32x16 (&dp)[2], const PageMask& m,
-                                        const DqState<D>& st, float scale_log2, DsWords& out) {
-    const int ku = unit >> 2, t = unit & 3;
-    const int kt = ku >> 1, u = ku & 1;
+// Phase 2, one unit (u, t) of two elements of key tile kt: P = exp2(S scale log2e - LSE log2e),
+// dS = P (dP - delta), packed as word t of the bf16 dS^T operand of key step 2kt + u.  Units are
+// small so that they fit between consecutive matrix instructions; the masked form is only
+// instantiated for pages that need it.
+template <bool MASK, int D>
+__device__ __forceinline__ void ds_unit(int unit, int kt, const f32x16& s, const f32x16& dp, int lim,
+                                        const DqState<D>& st, float scale_log2, u32x4 (&out)[4]) {
+    const int u = unit >> 2, t = unit & 3;
     float d2[2];
 #pragma unroll
     for (int e = 0; e < 2; e++) {
         const int i = 8 * u + 2 * t + e;
-        float p = fast_exp2(__builtin_fmaf(s[kt][i], scale_log2, -st.lse2));
-        if (m.on) {
-            const int kc = 32 * kt + 8 * (i >> 2) + (i & 3);
-            p = (kc < m.lim_valid && kc <= m.lim_causal) ? p : 0.f;
-        }
-        d2[e] = p * (dp[kt][i] - st.dlt);
+        float p = fast_exp2(__builtin_fmaf(s[i], scale_log2, -st.lse2));
+        if (MASK) p = (32 * kt + 8 * (i >> 2) + (i & 3)) < lim ? p : 0.f;
+        d2[e] = p * (dp[i] - st.dlt);
     }
-    out.w[ku][t] = pack_bf16x2(d2[0], d2[1]);
+    uint32_t word = pack_bf16x2(d2[0], d2[1]);
+    // pinned here: otherwise the compiler sinks the unit past the branches of the copies that
+    // share its stretch, next to its use, where no matrix work is left to hide it
+    asm volatile("" : "+v"(word));
+    out[2 * kt + u][t] = word;
 }
 
-// Phase 3 of page t: dQ^T += K^T dS^T (K read transposed), with phase 2 of page t+1 spread
-// over the steps.  Step st = (ku, dt), dt fastest; K^T fragments read PV steps ahead.
-template <int D>
-__device__ __forceinline__ void page_accumulate(DqState<D>& st, const DsWords& cur, const LS_LDS char* lds_k,
-                                                uint32_t lv, const f32x16 (&s_n)[2], const f32x16 (&dp_n)[2],
-                                                const PageMask& m_n, float scale_log2, DsWords& nxt) {
+// Phase 3 of page t: dQ^T += K^T dS^T (K read transposed).  Step st = (ku, dt), dt fastest;
+// K^T fragments read PV steps ahead; beside(st) runs after each step's matrix instruction.
+template <int D, typename Beside>
+__device__ __forceinline__ void page_accumulate(DqState<D>& st, const u32x4 (&ds)[4], const LS_LDS char* lds_k,
+                                                uint32_t lv, Beside&& beside) {
     using F = TileShape<D>;
     bf16x8 db[4];
 #pragma unroll
-    for (int ku = 0; ku < 4; ku++)
-        db[ku] = __builtin_bit_cast(bf16x8, (u32x4{cur.w[ku][0], cur.w[ku][1], cur.w[ku][2], cur.w[ku][3]}));
+    for (int ku = 0; ku < 4; ku++) db[ku] = __builtin_bit_cast(bf16x8, ds[ku]);
     constexpr int NST = 4 * F::DT;
     constexpr int PV = 4;
-    constexpr int NU = 16;  // phase-2 units of the next page
     i16x4 tlo[PV], thi[PV];
     auto read_kt = [&](int st_, i16x4& lo, i16x4& hi) {
         const int dt = st_ % F::DT, ku = st_ / F::DT;
@@ -134,43 +130,60 @@ __device__ __forceinline__ void page_accumulate(DqState<D>& st, const DsWords& c
         const bf16x8 ka = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tlo[st_ % PV], thi[st_ % PV], 0, 1, 2, 3, 4, 5, 6, 7));
         if (st_ + PV < NST) read_kt(st_ + PV, tlo[st_ % PV], thi[st_ % PV]);
         mfma32_agpr(st.dq[dt], ka, db[ku]);
-#pragma unroll
-        for (int un = 0; un < NU; un++)
-            if (un >= st_ * NU / NST && un < (st_ + 1) * NU / NST) ds_unit<D>(un, s_n, dp_n, m_n, st, scale_log2, nxt);
+        beside(st_);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// Iteration t: copy K(t+2) and V(t+2), phase 1 of page t+1, then phase 3 of page t with
-// phase 2 of page t+1 beside it.  The LDS tiles are restrict pointers so that, once inlined,
-// the compiler knows the copies in flight cannot alias the tiles being read.
-template <int D, int NW>
+// Run the units [n * k / steps, n * (k + 1) / steps) of n at step k, with constant loop bounds so
+// that every unit index is a constant after unrolling.
+template <int N, int STEPS, typename F>
+__device__ __forceinline__ void units_at(int k, F&& f) {
+#pragma unroll
+    for (int un = 0; un < N; un++)
+        if (un >= k * N / STEPS && un < (k + 1) * N / STEPS) f(un);
+}
+
+// Iteration t, three stretches of matrix work, each with vector work beside it:
+//   1. S, dP of key tile 0 of page t+1, beside dS of key tile 1 of page t and the copies of
+//      page t+2;
+//   2. dQ += K^T dS^T of page t, beside dS of key tile 0 of page t+1;
+//   3. S, dP of key tile 1 of page t+1.
+// ds holds page t's dS operand words (key tile 0 on entry, both on leaving stretch 1) and page
+// t+1's key tile 0 on return; s1, dp1 hold key tile 1 of page t on entry and of page t+1 on
+// return.  The LDS tiles are restrict pointers so that, once inlined, the compiler knows the
+// copies in flight cannot alias the tiles being read.
+template <bool MASK, int D, int NW>
 __device__ __forceinline__ void dq_iter(DqState<D>& st, const KeyTiles<D, NW>& kt, int64_t t, bool copy, int32_t e2,
                                         char* __restrict__ k_dst, char* __restrict__ v_dst,
                                         const char* __restrict__ k_n, const char* __restrict__ v_n,
-                                        const char* __restrict__ k_t, const DsWords& cur, DsWords& nxt,
-                                        const PageMask& m_n, LaneAddr<D> la, float scale_log2, int w) {
-    // the copies of page t+2 are spread over the S / dP steps, so that issuing them never
-    // stalls the wave for long and they overlap the matrix work
+                                        const char* __restrict__ k_t, u32x4 (&ds)[4], f32x16& s1, f32x16& dp1,
+                                        int lim_t, int lim_n, LaneAddr<D> la, float scale_log2, int w) {
     constexpr int PW = KeyTiles<D, NW>::PER_WAVE;
     constexpr int KS = TileShape<D>::KS;
+    constexpr int NST = 4 * TileShape<D>::DT;
     const int vn = kt.valid(t + 2);
     const char* ksrc = kt.tile(e2, t + 2, false);
     const char* vsrc = kt.tile(e2, t + 2, true);
-    auto copy_step = [&](int ks) {
-        if (!copy) return;
-#pragma unroll
-        for (int p = 0; p < 2 * PW; p++)
-            if (p * KS / (2 * PW) == ks) {
-                if (p < PW) kt.copy_piece(ksrc, vn, k_dst, w, p);
-                else kt.copy_piece(vsrc, vn, v_dst, w, p - PW);
-            }
-    };
     uint32_t lk = la.k, lv = la.v;
     asm volatile("" : "+v"(lk), "+v"(lv));
-    f32x16 s_n[2], dp_n[2];
-    page_scores<D>(st, (const LS_LDS char*)k_n, (const LS_LDS char*)v_n, lk, s_n, dp_n, copy_step);
-    page_accumulate<D>(st, cur, (const LS_LDS char*)k_t, lv, s_n, dp_n, m_n, scale_log2, nxt);
+    f32x16 s0, dp0;
+    tile_scores<D>(st, (const LS_LDS char*)k_n, (const LS_LDS char*)v_n, lk, s0, dp0, [&](int ks) {
+        units_at<8, KS>(ks, [&](int un) { ds_unit<MASK>(un, 1, s1, dp1, lim_t, st, scale_log2, ds); });
+        if (copy)
+            units_at<2 * PW, KS>(ks, [&](int p) {
+                if (p < PW) kt.copy_piece(ksrc, vn, k_dst, w, p);
+                else kt.copy_piece(vsrc, vn, v_dst, w, p - PW);
+            });
+    });
+    u32x4 nxt[4];
+    page_accumulate<D>(st, ds, (const LS_LDS char*)k_t, lv, [&](int k) {
+        units_at<8, NST>(k, [&](int un) { ds_unit<MASK>(un, 0, s0, dp0, lim_n, st, scale_log2, nxt); });
+    });
+    tile_scores<D>(st, (const LS_LDS char*)k_n + 32 * 2 * D, (const LS_LDS char*)v_n + 32 * 2 * D, lk, s1, dp1,
+                   [](int) {});
+    ds[0] = nxt[0];
+    ds[1] = nxt[1];
 }
 
 template <int D, int NW>
@@ -245,7 +258,7 @@ void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
     };
 
     if (n_tiles > 0) {
-        // prologue: pages 0 and 1 in LDS, phases 1-2 of page 0
+        // prologue: pages 0 and 1 in LDS; S, dP of page 0 and dS of its key tile 0
         const int32_t e0 = kt.entry(0);
         kt.copy(kt.tile(e0, 0, false), kt.valid(0), kbuf[0], w);
         kt.copy(kt.tile(e0, 0, true), kt.valid(0), vbuf[0], w);
@@ -259,28 +272,32 @@ void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
         int32_t e2 = n_tiles > 2 ? kt.entry(2) : 0;
         wait_vm_all();
         __syncthreads();
-        DsWords cur;
+        u32x4 ds[4];
+        f32x16 s1, dp1;
+        PageMask m_t = mask_of(0);
         {
-            f32x16 s0[2], dp0[2];
-            page_scores<D>(st, (const LS_LDS char*)kbuf[0], (const LS_LDS char*)vbuf[0], la.k, s0, dp0, [](int) {});
-            const PageMask m0 = mask_of(0);
-#pragma unroll
-            for (int un = 0; un < 16; un++) ds_unit<D>(un, s0, dp0, m0, st, a.scale_log2, cur);
+            f32x16 s0, dp0;
+            tile_scores<D>(st, (const LS_LDS char*)kbuf[0], (const LS_LDS char*)vbuf[0], la.k, s0, dp0, [](int) {});
+            tile_scores<D>(st, (const LS_LDS char*)kbuf[0] + 32 * 2 * D, (const LS_LDS char*)vbuf[0] + 32 * 2 * D, la.k,
+                           s1, dp1, [&](int ks) {
+                               units_at<8, F::KS>(ks, [&](int un) {
+                                   ds_unit<true>(un, 0, s0, dp0, m_t.lim, st, a.scale_log2, ds);
+                               });
+                           });
         }
         for (int64_t t = 0; t < n_tiles; t++) {
             // K(t+1), V(t+1) have landed; K buffer (t+2) % 3 and V buffer t % 2 were last read
-            // in iteration t-1.  The last iteration runs phases 1-2 on stale tiles; that
-            // result is never used.
+            // in iteration t-1.  The last iteration runs phase 1 on stale tiles; that result is
+            // never used.
             const int32_t e3 = t + 3 < n_tiles ? kt.entry(t + 3) : 0;
             wait_vm_all();
             __syncthreads();
             const int k0 = (int)(t % 3), k1 = k0 == 2 ? 0 : k0 + 1, k2 = k0 == 0 ? 2 : k0 - 1;
             const int v0 = (int)(t & 1), v1 = v0 ^ 1;
             const PageMask m_n = mask_of(t + 1);
-            DsWords nxt;
-            dq_iter<D, NW>(st, kt, t, t + 2 < n_tiles, e2, kbuf[k2], vbuf[v0], kbuf[k1], vbuf[v1], kbuf[k0], cur, nxt,
-                           m_n, la, a.scale_log2, w);
-            cur = nxt;
+            dq_iter<true, D, NW>(st, kt, t, t + 2 < n_tiles, e2, kbuf[k2], vbuf[v0], kbuf[k1], vbuf[v1], kbuf[k0], ds,
+                                 s1, dp1, m_t.lim, m_n.lim, la, a.scale_log2, w);
+            m_t = m_n;
             e2 = e3;
         }
     }
