@@ -87,8 +87,7 @@ __device__ __forceinline__ void issue_rows(const GroupRows& gr, int kvh, int64_t
     const int64_t base = ((int64_t)kvh * gr.rows_pad + r0) * D;
     dma_rows<D, 4, kRows>(gr.q + base, gr.dout + base, D, stage, stage + RowStage<D>::QBYTES, w, lane);
     if (w == 0 && lane < kRows * 8 / 16)
-        dma16((const char*)(gr.lsed + kvh * gr.rows_pad + r0) + lane * 16,
-              (LS_LDS void*)(stage + 2 * RowStage<D>::QBYTES));
+        dma16(gr.lsed + kvh * gr.rows_pad + r0, kRows * 8, lane * 16, (LS_LDS void*)(stage + 2 * RowStage<D>::QBYTES));
 }
 
 // The same copy in pieces, so that a caller can spread it over its compute steps: piece p of
@@ -117,10 +116,9 @@ struct RowCopy {
         const int j = p % PER_WAVE;
         const char* src = (const char*)(p < PER_WAVE ? gr.q : gr.dout) + base;
         char* dst = stage + (p < PER_WAVE ? 0 : RowStage<D>::QBYTES);
-        dma16(src + off[j], (LS_LDS void*)(dst + (j * 4 + w) * 1024));
+        dma16(src, RowStage<D>::QBYTES, off[j], (LS_LDS void*)(dst + (j * 4 + w) * 1024));
         if (p == 0 && w == 0 && lane < kRows * 8 / 16)
-            dma16((const char*)(gr.lsed + kvh * gr.rows_pad + r0) + lane * 16,
-                  (LS_LDS void*)(stage + 2 * RowStage<D>::QBYTES));
+            dma16(gr.lsed + kvh * gr.rows_pad + r0, kRows * 8, lane * 16, (LS_LDS void*)(stage + 2 * RowStage<D>::QBYTES));
     }
 };
 
@@ -173,11 +171,9 @@ struct Prob {
     uint32_t wp[2][4], wd[2][4];  // [u][word]
 };
 
-__device__ __forceinline__ void prob_unit(int unit, const f32x16& s, const f32x16& dp, const LS_LDS f32x2* lsd,
-                                          bool need_mask, int rmh, float scale_log2, int h, Prob& pr) {
+__device__ __forceinline__ void prob_unit(int unit, const f32x16& s, const f32x16& dp, f32x4 l, bool need_mask,
+                                          int rmh, float scale_log2, Prob& pr) {
     const int u = unit >> 2, hb = (unit >> 1) & 1, j2 = unit & 1;
-    const int rbase = 16 * u + 8 * hb + 4 * h + 2 * j2;
-    const f32x4 l = *(const LS_LDS f32x4*)(lsd + rbase);  // rows rbase, rbase+1: (lse2, delta)
     float pv[2], dv[2];
 #pragma unroll
     for (int e = 0; e < 2; e++) {
@@ -190,6 +186,12 @@ __device__ __forceinline__ void prob_unit(int unit, const f32x16& s, const f32x1
     }
     pr.wp[u][2 * hb + j2] = pack_bf16x2(pv[0], pv[1]);
     pr.wd[u][2 * hb + j2] = pack_bf16x2(dv[0], dv[1]);
+}
+
+// (LSE log2e, delta) of the two rows of unit `unit` (rows 16u + 8hb + 4h + 2j2, +1)
+__device__ __forceinline__ f32x4 unit_lsd(int unit, const LS_LDS f32x2* lsd, int h) {
+    const int u = unit >> 2, hb = (unit >> 1) & 1, j2 = unit & 1;
+    return *(const LS_LDS f32x4*)(lsd + 16 * u + 8 * hb + 4 * h + 2 * j2);
 }
 
 // Phase 3 of row tile t: dV += P^T dO, dK += dS^T Q (dO, Q read transposed: rows are the
@@ -224,6 +226,10 @@ __device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur
         f[2] = lds_read_tr4(lq + a0);
         f[3] = lds_read_tr4(lq + a1);
     };
+    // each unit's (LSE, delta) pair is read one unit ahead: a read issued just before its use
+    // would make the wait for it (LDS returns in order) drain the prefetched operand reads too
+    f32x4 lb[2];
+    lb[0] = unit_lsd(0, lsd_n, h);
 #pragma unroll
     for (int j = 0; j < PT; j++) read_t(j, fr[j]);
 #pragma unroll
@@ -239,8 +245,10 @@ __device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur
         // constant loop bounds so that every unit index is a constant after unrolling
 #pragma unroll
         for (int un = 0; un < NU; un++)
-            if (un >= st_ * NU / NST && un < (st_ + 1) * NU / NST)
-                prob_unit(un, s_n, dp_n, lsd_n, mask_n, rmh_n, scale_log2, h, nxt);
+            if (un >= st_ * NU / NST && un < (st_ + 1) * NU / NST) {
+                if (un + 1 < NU) lb[(un + 1) & 1] = unit_lsd(un + 1, lsd_n, h);
+                prob_unit(un, s_n, dp_n, lb[un & 1], mask_n, rmh_n, scale_log2, nxt);
+            }
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -376,7 +384,7 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks
             mask_of(0, m0, rmh0);
             const LS_LDS f32x2* lsd0 = (const LS_LDS f32x2*)((const LS_LDS char*)stg[0] + 2 * RowStage<D>::QBYTES);
 #pragma unroll
-            for (int un = 0; un < 8; un++) prob_unit(un, s0, dp0, lsd0, m0, rmh0, a.scale_log2, h, cur);
+            for (int un = 0; un < 8; un++) prob_unit(un, s0, dp0, unit_lsd(un, lsd0, h), m0, rmh0, a.scale_log2, cur);
         }
         for (int64_t t = 0; t < n_stages; t++) {
             // tile t+1 has landed; stage (t+2) % 3 was last read in iteration t-1

@@ -71,11 +71,18 @@ __device__ __forceinline__ int xcd_logical_block(int b, int n) {
 inline int pad_grid(int n) { return (n + kXcds - 1) / kXcds * kXcds; }
 
 // ----------------------------------------------------------------------------------------
-// Direct global -> LDS copy of 16 bytes per lane.  Lane l's bytes land at
-// lds_wave_base + 16 * l (lds_wave_base must be uniform across the wave).
+// Direct global -> LDS copy of 16 bytes per lane, through a buffer resource over
+// [base, base + bytes): lane l reads base + off and its bytes land at lds_wave_base + 16 * l
+// (base, bytes and lds_wave_base uniform across the wave).  Offsets past `bytes` read as 0.
+// The buffer (MUBUF) form is used because it counts only in vmcnt: the global form also
+// counts as an LDS access, so while one is in flight the compiler can only wait for LDS reads
+// with lgkmcnt(0), which drains every operand prefetch of the matrix loops.
 // ----------------------------------------------------------------------------------------
-__device__ __forceinline__ void dma16(const void* src, LS_LDS void* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
+constexpr int kRawBufferWord3 = 0x00020000;  // 32-bit data format, no swizzle, no index
+__device__ __forceinline__ void dma16(const void* base, uint32_t bytes, uint32_t off, LS_LDS void* lds_wave_base) {
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes,
+                                                                 kRawBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, off, 0, 0, 0);
 }
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -55,6 +55,7 @@ struct KeyTiles {
     int64_t keys;           // keys of the part counted from tile 0
     int32_t n_phys;
     uint32_t row_bytes;     // bytes between key rows inside a tile
+    uint32_t span;          // bytes from a tile's first row to the end of its last
     bool resp;
     int low;                // first row of this lane's copies (plus j * JROWS)
     int lane_x;             // this lane's chunk before the j part of the swizzle
@@ -76,6 +77,7 @@ struct KeyTiles {
             row_bytes = (uint32_t)a.hkv * D * 2;
             keys = a.key_end;
         }
+        span = (kPage - 1) * row_bytes + D * 2;
         table = (const __attribute__((address_space(4))) int32_t*)a.table + (resp ? 0 : lp0);
         low = w * RPK + lane / F::KCH;
         lane_x = (lane % F::KCH) ^ swz<D>(low);
@@ -110,7 +112,7 @@ struct KeyTiles {
             const int rs = r < valid_rows ? r : valid_rows - 1;
             o = (uint32_t)rs * row_bytes + (uint32_t)((lane_x ^ swz<D>(j * JROWS)) << 4);
         }
-        dma16(src + o, (LS_LDS void*)(lds + (j * NW + w) * 1024));
+        dma16(src, span, o, (LS_LDS void*)(lds + (j * NW + w) * 1024));
     }
 
     // Copy one tile into LDS (all NW waves together); rows past `valid` repeat the last valid
@@ -118,14 +120,14 @@ struct KeyTiles {
     __device__ __forceinline__ void copy(const char* src, int valid_rows, char* lds, int w) const {
         if (valid_rows == kPage) {
 #pragma unroll
-            for (int j = 0; j < PER_WAVE; j++) dma16(src + off[j], (LS_LDS void*)(lds + (j * NW + w) * 1024));
+            for (int j = 0; j < PER_WAVE; j++) dma16(src, span, off[j], (LS_LDS void*)(lds + (j * NW + w) * 1024));
         } else {
 #pragma unroll
             for (int j = 0; j < PER_WAVE; j++) {
                 const int r = j * JROWS + low;
                 const int rs = r < valid_rows ? r : valid_rows - 1;
                 const uint32_t o = (uint32_t)rs * row_bytes + (uint32_t)((lane_x ^ swz<D>(j * JROWS)) << 4);
-                dma16(src + o, (LS_LDS void*)(lds + (j * NW + w) * 1024));
+                dma16(src, span, o, (LS_LDS void*)(lds + (j * NW + w) * 1024));
             }
         }
     }
@@ -150,11 +152,11 @@ __device__ __forceinline__ void dma_rows(const bf16_t* a, const bf16_t* b, int64
 #pragma unroll
     for (int j = 0; j < PER_WAVE; j++) {
         const int lc = lane_x ^ swz<D>(j * JROWS);
-        const uint32_t off = (uint32_t)(low * (int)stride + lc * 8) * 2u;
-        const int64_t rowj = (int64_t)(j * JROWS) * stride * 2;
+        const uint32_t off = (uint32_t)((j * JROWS + low) * (int)stride + lc * 8) * 2u;
+        const uint32_t bytes = (uint32_t)((ROWS - 1) * stride + D) * 2u;
         const int blk = j * NW + w;
-        dma16((const char*)a + rowj + off, (LS_LDS void*)(lds_a + blk * 1024));
-        dma16((const char*)b + rowj + off, (LS_LDS void*)(lds_b + blk * 1024));
+        dma16(a, bytes, off, (LS_LDS void*)(lds_a + blk * 1024));
+        dma16(b, bytes, off, (LS_LDS void*)(lds_b + blk * 1024));
     }
 }
 
