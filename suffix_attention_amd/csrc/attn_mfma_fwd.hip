@@ -15,8 +15,10 @@
 //   output wave g  O^T[D x 32] += V(t-1)^T P(t-1)^T V read transposed from LDS
 //                                                  (ds_read_b64_tr_b16), O in AGPRs
 // Every page has two barriers: after the first the score waves multiply while the output
-// waves fetch P; after the second the output waves multiply while the score waves run the
-// softmax.  The two waves of a SIMD thus take turns on its matrix core, and each one's
+// waves fetch P and issue all of the page's copies; after the second the output waves
+// multiply while the score waves run the softmax.  The copies sit with the output waves
+// because a wave issues at most about one instruction per four cycles: the score wave's
+// stream (scores, softmax) is the long one, and its length sets the pace of the page.  The two waves of a SIMD thus take turns on its matrix core, and each one's
 // vector work hides under the other's matrix work.  Splitting the roles also halves the
 // registers a wave needs (the 32 x D output tile alone is 128 registers at D = 256), which
 // is what lets two waves share a SIMD.
@@ -56,10 +58,14 @@ struct FwdLds {
 // flight are left alone (a workgroup fence would wait for them too).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Copies issued in iteration t by all eight waves: K(t+1) into k_dst and V(t) into v_dst;
-// e_t / e_t1 are the raw page-table entries of tiles t and t+1.
+// Copies issued in iteration t by the four output waves: K(t+1) into k_dst and V(t) into
+// v_dst; e_t / e_t1 are the raw page-table entries of tiles t and t+1.  The output waves do all
+// the copying: the score waves' instruction stream (scores, softmax) is the longer one.
 template <int D>
-__device__ __forceinline__ void issue_copies(const KeyTiles<D, kNW>& kt, int64_t n_tiles, int64_t t, int32_t e_t,
+using OutTiles = KeyTiles<D, kGroups>;
+
+template <int D>
+__device__ __forceinline__ void issue_copies(const OutTiles<D>& kt, int64_t n_tiles, int64_t t, int32_t e_t,
                                              int32_t e_t1, char* k_dst, char* v_dst, int w) {
     if (t + 1 < n_tiles) kt.copy(kt.tile(e_t1, t + 1, false), kt.valid(t + 1), k_dst, w);
     if (t < n_tiles) kt.copy(kt.tile(e_t, t, true), kt.valid(t), v_dst, w);
@@ -68,7 +74,7 @@ __device__ __forceinline__ void issue_copies(const KeyTiles<D, kNW>& kt, int64_t
 // Where the keys of the workgroup's part come from, and the rows it serves.
 template <int D>
 struct PartInfo {
-    KeyTiles<D, kNW> kt;
+    OutTiles<D> kt;     // copy addressing of the output waves (valid() serves both roles)
     bool resp;
     int64_t lp0;        // first logical page (prompt shard)
     int64_t n_tiles;
@@ -81,9 +87,9 @@ struct PartInfo {
 
 // S^T(t) = K(t) Q^T for the wave's 32 rows: two 32-key tiles, KS k-steps each, K fragments
 // read PD steps ahead.
-template <int D, typename Copy>
+template <int D>
 __device__ __forceinline__ void scores(const bf16x8 (&qb)[TileShape<D>::KS], f32x16 (&s)[2], const LS_LDS char* lds_k,
-                                       uint32_t lk, Copy&& copy_step) {
+                                       uint32_t lk) {
     using F = TileShape<D>;
     constexpr int PD = 2;
     bf16x8 kbuf[PD][2];
@@ -105,7 +111,6 @@ __device__ __forceinline__ void scores(const bf16x8 (&qb)[TileShape<D>::KS], f32
         }
         s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qb[ks], s[0], 0, 0, 0);
         s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qb[ks], s[1], 0, 0, 0);
-        copy_step(ks);  // this step's share of the copies, beside the matrix work
     }
 }
 
@@ -205,47 +210,23 @@ __device__ __forceinline__ void accumulate_pv(f32x16 (&o)[TileShape<D>::DT], con
 // inlined, the compiler knows the copies just issued cannot alias the tiles being read and
 // does not wait for them before each read.
 
-// Score role, iteration t: S(t) while the output waves fetch P(t-1); then the softmax of
-// page t while they multiply.
+// Score role, iteration t < n_tiles: S(t) while the output waves fetch P(t-1) and issue the
+// copies; then the softmax of page t while they multiply.
 template <int D>
-__device__ __forceinline__ void score_iter(const AttnArgs& a, const PartInfo<D>& pi, int64_t t, int32_t phys_t,
-                                           int32_t phys_t1, char* __restrict__ k_dst, char* __restrict__ v_dst,
+__device__ __forceinline__ void score_iter(const AttnArgs& a, const PartInfo<D>& pi, int64_t t,
                                            const char* __restrict__ k_cur, char* __restrict__ p_out,
                                            float* __restrict__ alpha_out, const bf16x8 (&qb)[TileShape<D>::KS],
-                                           float& m_ref, float& l, int64_t vis_limit, uint32_t lk, int w, int lane) {
+                                           float& m_ref, float& l, int64_t vis_limit, uint32_t lk, int lane) {
     wait_vm_all();
     lds_barrier();
-    // this wave's copies of K(t+1) and V(t) are spread over the score steps, so that issuing
-    // them never stalls the wave for long and they overlap the matrix work
-    constexpr int PW = KeyTiles<D, kNW>::PER_WAVE;
-    constexpr int KS = TileShape<D>::KS;
-    const bool ck = t + 1 < pi.n_tiles, cv = t < pi.n_tiles;
-    const int vk = pi.kt.valid(t + 1), vv = pi.kt.valid(t);
-    const char* ksrc = pi.kt.tile(phys_t1, t + 1, false);
-    const char* vsrc = pi.kt.tile(phys_t, t, true);
-    auto copy_step = [&](int ks) {
-#pragma unroll
-        for (int p = 0; p < 2 * PW; p++)
-            if (p * KS / (2 * PW) == ks) {
-                if (p < PW) {
-                    if (ck) pi.kt.copy_piece(ksrc, vk, k_dst, w, p);
-                } else if (cv) {
-                    pi.kt.copy_piece(vsrc, vv, v_dst, w, p - PW);
-                }
-            }
-    };
     f32x16 s[2];
-    const bool live = t < pi.n_tiles;
-    if (live) scores<D>(qb, s, (const LS_LDS char*)k_cur, lk, copy_step);
-    else issue_copies<D>(pi.kt, pi.n_tiles, t, phys_t, phys_t1, k_dst, v_dst, w);
+    scores<D>(qb, s, (const LS_LDS char*)k_cur, lk);
     lds_barrier();
-    if (live) {
-        const int valid = pi.kt.valid(t);
-        const int64_t key0 = (pi.lp0 + t) * kPage;
-        if (valid < kPage || (pi.resp && key0 + kPage - 1 > a.q_start + pi.tok_min))
-            mask_scores(s, valid, key0, pi.resp, vis_limit, lane >> 5);
-        softmax_page(s, m_ref, l, a.scale_log2, (LS_LDS char*)p_out, (LS_LDS float*)alpha_out, lane);
-    }
+    const int valid = pi.kt.valid(t);
+    const int64_t key0 = (pi.lp0 + t) * kPage;
+    if (valid < kPage || (pi.resp && key0 + kPage - 1 > a.q_start + pi.tok_min))
+        mask_scores(s, valid, key0, pi.resp, vis_limit, lane >> 5);
+    softmax_page(s, m_ref, l, a.scale_log2, (LS_LDS char*)p_out, (LS_LDS float*)alpha_out, lane);
 }
 
 // Output role, iteration t >= 1: fetch P(t-1) while the score waves multiply; then rescale O
@@ -313,18 +294,14 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
         n_tiles = (a.q_start + tok_max + 1 + kPage - 1) / kPage;
     }
 
-    PartInfo<D> pi{KeyTiles<D, kNW>(a, resp, lp0, kvh, w, lane)};
-    const KeyTiles<D, kNW>& kt = pi.kt;
+    // output wave g copies share g of every tile; the score waves use kt only for valid()
+    PartInfo<D> pi{OutTiles<D>(a, resp, lp0, kvh, g, lane)};
+    const OutTiles<D>& kt = pi.kt;
     pi.resp = resp;
     pi.lp0 = lp0;
     pi.n_tiles = n_tiles;
     pi.tok_min = r0 / a.g;
 
-    // prologue: K(0) in flight.  Page-table entries are read through the scalar cache one
-    // iteration before their copies and clamped where they are used.
-    int32_t phys_t = n_tiles > 0 ? kt.entry(0) : 0;
-    int32_t phys_t1 = n_tiles > 1 ? kt.entry(1) : 0;
-    if (n_tiles > 0) kt.copy(kt.tile(phys_t, 0, false), kt.valid(0), L.kb[0], w);
     char* p_grp = L.p[g];
     float* alpha_grp = L.alpha[g];
     LS_LDS float* fin_grp = (LS_LDS float*)L.fin_l[g];
@@ -349,16 +326,14 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
         }
         const int64_t vis_limit = a.q_start + my_tok;  // last response key this row sees
         float m_ref = -INFINITY, l = 0.f;
-        for (int64_t t = 0; t <= n_tiles; t++) {
-            const int32_t phys_t2 = t + 2 < n_tiles ? kt.entry(t + 2) : 0;
+        for (int64_t t = 0; t < n_tiles; t++) {
             uint32_t lk = la.k;
             asm volatile("" : "+v"(lk));
-            score_iter<D>(a, pi, t, phys_t, phys_t1,
-                          L.kb[(t + 1) & 1], L.vb[t & 1], L.kb[t & 1], p_grp, alpha_grp, qb, m_ref, l, vis_limit, lk,
-                          w, lane);
-            phys_t = phys_t1;
-            phys_t1 = phys_t2;
+            score_iter<D>(a, pi, t, L.kb[t & 1], p_grp, alpha_grp, qb, m_ref, l, vis_limit, lk, lane);
         }
+        // iteration n_tiles: the output waves' last page; nothing left to score
+        lds_barrier();
+        lds_barrier();
         // final statistics for the output waves, and this part's LSE
         const float l_tot = l + other_half(l);
         if (lane < 32) fin_grp[lane] = l_tot;
@@ -374,12 +349,17 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
             asm volatile("" : "+a"(o[dt]));
         }
         agpr_write_gap();
+        // prologue: K(0) in flight.  Page-table entries are read through the scalar cache one
+        // iteration before their copies and clamped where they are used.
+        int32_t phys_t = n_tiles > 0 ? kt.entry(0) : 0;
+        int32_t phys_t1 = n_tiles > 1 ? kt.entry(1) : 0;
+        if (n_tiles > 0) kt.copy(kt.tile(phys_t, 0, false), kt.valid(0), L.kb[0], g);
         // iteration 0: only the copies (no page has been scored yet)
         {
             const int32_t phys_t2 = 2 < n_tiles ? kt.entry(2) : 0;
             wait_vm_all();
             lds_barrier();
-            issue_copies<D>(kt, n_tiles, 0, phys_t, phys_t1, L.kb[1], L.vb[0], w);
+            issue_copies<D>(kt, n_tiles, 0, phys_t, phys_t1, L.kb[1], L.vb[0], g);
             lds_barrier();
             phys_t = phys_t1;
             phys_t1 = phys_t2;
@@ -389,7 +369,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
             uint32_t lv = la.v;
             asm volatile("" : "+v"(lv));
             output_iter<D>(a, pi, t, phys_t, phys_t1,
-                           L.kb[(t + 1) & 1], L.vb[t & 1], L.vb[(t - 1) & 1], p_grp, alpha_grp, o, lv, w, lane);
+                           L.kb[(t + 1) & 1], L.vb[t & 1], L.vb[(t - 1) & 1], p_grp, alpha_grp, o, lv, g, lane);
             phys_t = phys_t1;
             phys_t1 = phys_t2;
         }
