@@ -83,11 +83,11 @@ struct RowStage {
 // Copy group rows [r0, r0 + 32) of Q and dO (group-major, zero padded) and their
 // (lse2, delta) into an LDS stage.
 template <int D>
-__device__ __forceinline__ void issue_rows(const GroupRows& gr, int kvh, int64_t r0, char* stage, int w, int lane) {
+__device__ __forceinline__ void issue_rows(const GroupRows& gr, int kvh, int64_t r0, uint32_t stage, int w, int lane) {
     const int64_t base = ((int64_t)kvh * gr.rows_pad + r0) * D;
     dma_rows<D, 4, kRows>(gr.q + base, gr.dout + base, D, stage, stage + RowStage<D>::QBYTES, w, lane);
     if (w == 0 && lane < kRows * 8 / 16)
-        dma16(gr.lsed + kvh * gr.rows_pad + r0, kRows * 8, lane * 16, (LS_LDS void*)(stage + 2 * RowStage<D>::QBYTES));
+        dma16(gr.lsed + kvh * gr.rows_pad + r0, kRows * 8, lane * 16, stage + 2 * RowStage<D>::QBYTES);
 }
 
 // The same copy in pieces, so that a caller can spread it over its compute steps: piece p of
@@ -110,15 +110,15 @@ struct RowCopy {
             off[j] = (uint32_t)(j * JROWS + low) * (D * 2) + (uint32_t)((lane_x ^ swz<D>(j * JROWS)) << 4);
     }
 
-    __device__ __forceinline__ void piece(const GroupRows& gr, int kvh, int64_t r0, char* stage, int w, int lane,
+    __device__ __forceinline__ void piece(const GroupRows& gr, int kvh, int64_t r0, uint32_t stage, int w, int lane,
                                           int p) const {
         const int64_t base = ((int64_t)kvh * gr.rows_pad + r0) * D * 2;
         const int j = p % PER_WAVE;
         const char* src = (const char*)(p < PER_WAVE ? gr.q : gr.dout) + base;
-        char* dst = stage + (p < PER_WAVE ? 0 : RowStage<D>::QBYTES);
-        dma16(src, RowStage<D>::QBYTES, off[j], (LS_LDS void*)(dst + (j * 4 + w) * 1024));
+        const uint32_t dst = stage + (p < PER_WAVE ? 0 : RowStage<D>::QBYTES);
+        dma16(src, RowStage<D>::QBYTES, off[j], dst + (j * 4 + w) * 1024);
         if (p == 0 && w == 0 && lane < kRows * 8 / 16)
-            dma16(gr.lsed + kvh * gr.rows_pad + r0, kRows * 8, lane * 16, (LS_LDS void*)(stage + 2 * RowStage<D>::QBYTES));
+            dma16(gr.lsed + kvh * gr.rows_pad + r0, kRows * 8, lane * 16, stage + 2 * RowStage<D>::QBYTES);
     }
 };
 
@@ -171,8 +171,8 @@ struct Prob {
     uint32_t wp[2][4], wd[2][4];  // [u][word]
 };
 
-__device__ __forceinline__ void prob_unit(int unit, const f32x16& s, const f32x16& dp, f32x4 l, bool need_mask,
-                                          int rmh, float scale_log2, Prob& pr) {
+__device__ __forceinline__ void prob_unit(int unit, const f32x16& s, const f32x16& dp, f32x4 l, int rmh,
+                                          float scale_log2, Prob& pr) {
     const int u = unit >> 2, hb = (unit >> 1) & 1, j2 = unit & 1;
     float pv[2], dv[2];
 #pragma unroll
@@ -180,7 +180,7 @@ __device__ __forceinline__ void prob_unit(int unit, const f32x16& s, const f32x1
         const int j = 2 * j2 + e;
         const int i = 8 * u + 4 * hb + j;
         float p = fast_exp2(__builtin_fmaf(s[i], scale_log2, -l[2 * e]));
-        if (need_mask) p = (16 * u + 8 * hb + j) >= rmh ? p : 0.f;
+        p = (16 * u + 8 * hb + j) >= rmh ? p : 0.f;  // rmh <= 0 where no row precedes the key
         pv[e] = p;
         dv[e] = p * (dp[i] - l[2 * e + 1]);
     }
@@ -201,8 +201,8 @@ __device__ __forceinline__ f32x4 unit_lsd(int unit, const LS_LDS f32x2* lsd, int
 template <int D>
 __device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur, const LS_LDS char* stage,
                                                 uint32_t lv, const f32x16& s_n, const f32x16& dp_n,
-                                                const LS_LDS f32x2* lsd_n, bool mask_n, int rmh_n,
-                                                float scale_log2, int h, Prob& nxt) {
+                                                const LS_LDS f32x2* lsd_n, int rmh_n, float scale_log2, int h,
+                                                Prob& nxt) {
     using F = TileShape<D>;
     const LS_LDS char* lq = stage;
     const LS_LDS char* ldo = stage + RowStage<D>::QBYTES;
@@ -239,15 +239,14 @@ __device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur
         const bf16x8 dob = __builtin_bit_cast(bf16x8, __builtin_shufflevector(f[0], f[1], 0, 1, 2, 3, 4, 5, 6, 7));
         const bf16x8 qbt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(f[2], f[3], 0, 1, 2, 3, 4, 5, 6, 7));
         if (st_ + PT < NST) read_t(st_ + PT, f);
-        mfma32_agpr(st.dv[dt], pa[u], dob);
-        mfma32_agpr(st.dk[dt], sa[u], qbt);
+        mfma32_agpr2(st.dv[dt], pa[u], dob, st.dk[dt], sa[u], qbt);
         // units [st*NU/NST, (st+1)*NU/NST) of the next tile's phase 2 run beside this step;
         // constant loop bounds so that every unit index is a constant after unrolling
 #pragma unroll
         for (int un = 0; un < NU; un++)
             if (un >= st_ * NU / NST && un < (st_ + 1) * NU / NST) {
                 if (un + 1 < NU) lb[(un + 1) & 1] = unit_lsd(un + 1, lsd_n, h);
-                prob_unit(un, s_n, dp_n, lb[un & 1], mask_n, rmh_n, scale_log2, nxt);
+                prob_unit(un, s_n, dp_n, lb[un & 1], rmh_n, scale_log2, nxt);
             }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -259,15 +258,14 @@ __device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur
 // not wait for it.
 template <int D>
 __device__ __forceinline__ void dkdv_step(DkvState<D>& st, const char* __restrict__ stage_t,
-                                          const char* __restrict__ stage_n, char* __restrict__ dst, bool copy,
+                                          const char* __restrict__ stage_n, uint32_t dst,
                                           const GroupRows& gr, const RowCopy<D>& rc, int kvh, int64_t copy_r0,
                                           const Prob& cur, Prob& nxt,
-                                          LaneAddr<D> la, bool mask_n, int rmh_n, float scale_log2, int w,
-                                          int lane) {
+                                          LaneAddr<D> la, int rmh_n, float scale_log2, int w, int lane) {
     // the copies of the tile two ahead are spread over the S / dP steps, so that issuing them
-    // never stalls the wave for long and they overlap the matrix work
+    // never stalls the wave for long and they overlap the matrix work (near the end the caller
+    // passes the last tile again, into a stage nothing reads, so that there is no branch here)
     auto copy_step = [&](int ks) {
-        if (!copy) return;
 #pragma unroll
         for (int p = 0; p < RowCopy<D>::PIECES; p++)
             if (p * TileShape<D>::KS / RowCopy<D>::PIECES == ks) rc.piece(gr, kvh, copy_r0, dst, w, lane, p);
@@ -277,8 +275,8 @@ __device__ __forceinline__ void dkdv_step(DkvState<D>& st, const char* __restric
     f32x16 s_n, dp_n;
     tile_scores<D>(st, (const LS_LDS char*)stage_n, lk, s_n, dp_n, copy_step);
     tile_accumulate<D>(st, cur, (const LS_LDS char*)stage_t, lv, s_n, dp_n,
-                       (const LS_LDS f32x2*)((const LS_LDS char*)stage_n + 2 * RowStage<D>::QBYTES), mask_n, rmh_n,
-                       scale_log2, lane >> 5, nxt);
+                       (const LS_LDS f32x2*)((const LS_LDS char*)stage_n + 2 * RowStage<D>::QBYTES), rmh_n, scale_log2,
+                       lane >> 5, nxt);
 }
 
 // One workgroup: 4 waves over two consecutive 64-key pages (wave w: page w/2, keys
@@ -287,7 +285,8 @@ template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks) {
     using F = TileShape<D>;
-    __shared__ __attribute__((aligned(1024))) char stg[3][(RowStage<D>::BYTES + 1023) / 1024 * 1024];
+    constexpr int kStage = (RowStage<D>::BYTES + 1023) / 1024 * 1024;
+    __shared__ __attribute__((aligned(1024))) char stg[3][kStage];
 
     const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
     if (lb >= n_blocks) return;
@@ -357,13 +356,11 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks
     const int64_t my_key = page * kPage + 32 * kh + n;
     const int64_t row_min = resp ? (my_key - a.q_start) * a.g : 0;
 
-    // Row tile t needs the causal mask if some row in it precedes some key of the pair; rmh is
-    // the number of its rows (without the 4h of this lane's half) that precede this lane's key.
-    auto mask_of = [&](int64_t t, bool& need_mask, int& rmh) {
-        const int64_t r0 = r_begin + t * kRows;
-        need_mask = resp && r0 < (key0_pair + 2 * kPage - 1 - a.q_start) * a.g;
-        const int64_t rm = row_min - r0;
-        rmh = (rm < 0 ? 0 : (rm > kRows ? kRows : (int)rm)) - 4 * h;
+    // Causal mask of row tile t: rmh is the number of its rows (without the 4h of this lane's
+    // half) that precede this lane's key; it is <= 0 wherever no row does (all prompt keys).
+    auto rmh_of = [&](int64_t t) {
+        const int64_t rm = row_min - (r_begin + t * kRows);
+        return (rm < 0 ? 0 : (rm > kRows ? kRows : (int)rm)) - 4 * h;
     };
 
     // Pipeline over row tiles (three LDS stages): iteration t copies tile t+2, computes
@@ -371,35 +368,33 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks
     const LaneAddr<D> la(lane);
     const RowCopy<D> rc(w, lane);
     if (n_stages > 0) {
-        issue_rows<D>(gr, kvh, r_begin, stg[0], w, lane);
-        if (n_stages > 1) issue_rows<D>(gr, kvh, r_begin + kRows, stg[1], w, lane);
+        issue_rows<D>(gr, kvh, r_begin, lds_addr(stg[0]), w, lane);
+        if (n_stages > 1) issue_rows<D>(gr, kvh, r_begin + kRows, lds_addr(stg[1]), w, lane);
         wait_vm_all();
         __syncthreads();
         Prob cur;
         {
             f32x16 s0, dp0;
             tile_scores<D>(st, (const LS_LDS char*)stg[0], la.k, s0, dp0, [](int) {});
-            bool m0;
-            int rmh0;
-            mask_of(0, m0, rmh0);
+            const int rmh0 = rmh_of(0);
             const LS_LDS f32x2* lsd0 = (const LS_LDS f32x2*)((const LS_LDS char*)stg[0] + 2 * RowStage<D>::QBYTES);
 #pragma unroll
-            for (int un = 0; un < 8; un++) prob_unit(un, s0, dp0, unit_lsd(un, lsd0, h), m0, rmh0, a.scale_log2, cur);
+            for (int un = 0; un < 8; un++) prob_unit(un, s0, dp0, unit_lsd(un, lsd0, h), rmh0, a.scale_log2, cur);
         }
         for (int64_t t = 0; t < n_stages; t++) {
             // tile t+1 has landed; stage (t+2) % 3 was last read in iteration t-1
             wait_vm_all();
             __syncthreads();
             // the last iteration runs phases 1-2 on a stale stage; that result is never used
-            bool mn;
-            int rmhn;
-            mask_of(t + 1, mn, rmhn);
+            const int rmhn = rmh_of(t + 1);
             Prob nxt;
             const int it = (int)(t % 3);
-            dkdv_step<D>(st, stg[it], stg[it == 2 ? 0 : it + 1], stg[it == 0 ? 2 : it - 1], t + 2 < n_stages, gr,
-                         rc, kvh, r_begin + (t + 2) * kRows, cur, nxt, la, mn, rmhn, a.scale_log2, w, lane);
+            dkdv_step<D>(st, stg[it], stg[it == 2 ? 0 : it + 1], lds_addr(stg[0]) + (it == 0 ? 2 : it - 1) * kStage,
+                         gr, rc, kvh, r_begin + (t + 2 < n_stages ? t + 2 : n_stages - 1) * kRows, cur, nxt, la, rmhn,
+                         a.scale_log2, w, lane);
             cur = nxt;
         }
+        wait_vm_all();  // the last iterations' copies land before the workgroup's LDS is released
     }
 
     // ---- write this wave's keys: dK (scaled) and dV, element i is key 8(i/4) + 4h + i%4

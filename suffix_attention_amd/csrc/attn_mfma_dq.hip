@@ -124,13 +124,17 @@ __device__ __forceinline__ void page_accumulate(DqState<D>& st, const u32x4 (&ds
     };
 #pragma unroll
     for (int j = 0; j < PV; j++) read_kt(j, tlo[j], thi[j]);
+    // two steps (dt, dt + 1 of one key step) per matrix-instruction pair
 #pragma unroll
-    for (int st_ = 0; st_ < NST; st_++) {
+    for (int st_ = 0; st_ < NST; st_ += 2) {
         const int dt = st_ % F::DT, ku = st_ / F::DT;
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tlo[st_ % PV], thi[st_ % PV], 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 ka0 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tlo[st_ % PV], thi[st_ % PV], 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 ka1 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tlo[(st_ + 1) % PV], thi[(st_ + 1) % PV], 0, 1, 2, 3, 4, 5, 6, 7));
         if (st_ + PV < NST) read_kt(st_ + PV, tlo[st_ % PV], thi[st_ % PV]);
-        mfma32_agpr(st.dq[dt], ka, db[ku]);
+        if (st_ + 1 + PV < NST) read_kt(st_ + 1 + PV, tlo[(st_ + 1) % PV], thi[(st_ + 1) % PV]);
+        mfma32_agpr2(st.dq[dt], ka0, db[ku], st.dq[dt + 1], ka1, db[ku]);
         beside(st_);
+        beside(st_ + 1);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -154,24 +158,28 @@ __device__ __forceinline__ void units_at(int k, F&& f) {
 // return.  The LDS tiles are restrict pointers so that, once inlined, the compiler knows the
 // copies in flight cannot alias the tiles being read.
 template <bool MASK, int D, int NW>
-__device__ __forceinline__ void dq_iter(DqState<D>& st, const KeyTiles<D, NW>& kt, int64_t t, bool copy, int32_t e2,
-                                        char* __restrict__ k_dst, char* __restrict__ v_dst,
+__device__ __forceinline__ void dq_iter(DqState<D>& st, const KeyTiles<D, NW>& kt, int64_t t, int64_t last, bool copy,
+                                        int32_t e2,
+                                        uint32_t k_dst, uint32_t v_dst,
                                         const char* __restrict__ k_n, const char* __restrict__ v_n,
                                         const char* __restrict__ k_t, u32x4 (&ds)[4], f32x16& s1, f32x16& dp1,
                                         int lim_t, int lim_n, LaneAddr<D> la, float scale_log2, int w) {
     constexpr int PW = KeyTiles<D, NW>::PER_WAVE;
     constexpr int KS = TileShape<D>::KS;
     constexpr int NST = 4 * TileShape<D>::DT;
-    const int vn = kt.valid(t + 2);
-    const char* ksrc = kt.tile(e2, t + 2, false);
-    const char* vsrc = kt.tile(e2, t + 2, true);
+    // Near the end there is no page t+2: the last page is copied again instead, into buffers
+    // that nothing reads, so that the stretch has no branch (a branch would let the compiler
+    // move the vector work out of it)
+    const int64_t tc = copy ? t + 2 : last;
+    const int vn = kt.valid(tc);
+    const char* ksrc = kt.tile(e2, tc, false);
+    const char* vsrc = kt.tile(e2, tc, true);
     uint32_t lk = la.k, lv = la.v;
     asm volatile("" : "+v"(lk), "+v"(lv));
     f32x16 s0, dp0;
     tile_scores<D>(st, (const LS_LDS char*)k_n, (const LS_LDS char*)v_n, lk, s0, dp0, [&](int ks) {
         units_at<8, KS>(ks, [&](int un) { ds_unit<MASK>(un, 1, s1, dp1, lim_t, st, scale_log2, ds); });
-        if (copy)
-            units_at<2 * PW, KS>(ks, [&](int p) {
+        units_at<2 * PW, KS>(ks, [&](int p) {
                 if (p < PW) kt.copy_piece(ksrc, vn, k_dst, w, p);
                 else kt.copy_piece(vsrc, vn, v_dst, w, p - PW);
             });
@@ -257,15 +265,18 @@ void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
         return page_mask(need, valid, key0, resp, vis_limit, h);
     };
 
+    clear_lds(&kbuf[0][0], sizeof(kbuf), threadIdx.x, NW * 64);
+    clear_lds(&vbuf[0][0], sizeof(vbuf), threadIdx.x, NW * 64);
+    __syncthreads();
     if (n_tiles > 0) {
         // prologue: pages 0 and 1 in LDS; S, dP of page 0 and dS of its key tile 0
         const int32_t e0 = kt.entry(0);
-        kt.copy(kt.tile(e0, 0, false), kt.valid(0), kbuf[0], w);
-        kt.copy(kt.tile(e0, 0, true), kt.valid(0), vbuf[0], w);
+        kt.copy(kt.tile(e0, 0, false), kt.valid(0), lds_addr(kbuf[0]), w);
+        kt.copy(kt.tile(e0, 0, true), kt.valid(0), lds_addr(vbuf[0]), w);
         if (n_tiles > 1) {
             const int32_t e1 = kt.entry(1);
-            kt.copy(kt.tile(e1, 1, false), kt.valid(1), kbuf[1], w);
-            kt.copy(kt.tile(e1, 1, true), kt.valid(1), vbuf[1], w);
+            kt.copy(kt.tile(e1, 1, false), kt.valid(1), lds_addr(kbuf[1]), w);
+            kt.copy(kt.tile(e1, 1, true), kt.valid(1), lds_addr(vbuf[1]), w);
         }
         // page-table entries are read through the scalar cache one iteration before their
         // copies and clamped where they are used
@@ -295,11 +306,13 @@ void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
             const int k0 = (int)(t % 3), k1 = k0 == 2 ? 0 : k0 + 1, k2 = k0 == 0 ? 2 : k0 - 1;
             const int v0 = (int)(t & 1), v1 = v0 ^ 1;
             const PageMask m_n = mask_of(t + 1);
-            dq_iter<true, D, NW>(st, kt, t, t + 2 < n_tiles, e2, kbuf[k2], vbuf[v0], kbuf[k1], vbuf[v1], kbuf[k0], ds,
+            dq_iter<true, D, NW>(st, kt, t, n_tiles - 1, t + 2 < n_tiles, e2, lds_addr(kbuf[0]) + k2 * F::TILE,
+                                 lds_addr(vbuf[0]) + v0 * F::TILE, kbuf[k1], vbuf[v1], kbuf[k0], ds,
                                  s1, dp1, m_t.lim, m_n.lim, la, a.scale_log2, w);
             m_t = m_n;
             e2 = e3;
         }
+        wait_vm_all();  // the last iterations' copies land before the workgroup's LDS is released
     }
     mfma_drain();
     if (!row_ok) return;

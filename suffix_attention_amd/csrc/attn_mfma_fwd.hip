@@ -66,7 +66,7 @@ using OutTiles = KeyTiles<D, kGroups>;
 
 template <int D>
 __device__ __forceinline__ void issue_copies(const OutTiles<D>& kt, int64_t n_tiles, int64_t t, int32_t e_t,
-                                             int32_t e_t1, char* k_dst, char* v_dst, int w) {
+                                             int32_t e_t1, uint32_t k_dst, uint32_t v_dst, int w) {
     if (t + 1 < n_tiles) kt.copy(kt.tile(e_t1, t + 1, false), kt.valid(t + 1), k_dst, w);
     if (t < n_tiles) kt.copy(kt.tile(e_t, t, true), kt.valid(t), v_dst, w);
 }
@@ -233,7 +233,7 @@ __device__ __forceinline__ void score_iter(const AttnArgs& a, const PartInfo<D>&
 // if a row's reference moved and accumulate V(t-1) P(t-1).
 template <int D>
 __device__ __forceinline__ void output_iter(const AttnArgs& a, const PartInfo<D>& pi, int64_t t, int32_t phys_t,
-                                            int32_t phys_t1, char* __restrict__ k_dst, char* __restrict__ v_dst,
+                                            int32_t phys_t1, uint32_t k_dst, uint32_t v_dst,
                                             const char* __restrict__ v_prev, const char* __restrict__ p_in,
                                             const float* __restrict__ alpha_in, f32x16 (&o)[TileShape<D>::DT],
                                             uint32_t lv, int w, int lane) {
@@ -302,6 +302,9 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
     pi.n_tiles = n_tiles;
     pi.tok_min = r0 / a.g;
 
+    clear_lds(&L.kb[0][0], sizeof(L.kb), threadIdx.x, kNW * 64);
+    clear_lds(&L.vb[0][0], sizeof(L.vb), threadIdx.x, kNW * 64);
+    lds_barrier();
     char* p_grp = L.p[g];
     float* alpha_grp = L.alpha[g];
     LS_LDS float* fin_grp = (LS_LDS float*)L.fin_l[g];
@@ -353,13 +356,13 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
         // iteration before their copies and clamped where they are used.
         int32_t phys_t = n_tiles > 0 ? kt.entry(0) : 0;
         int32_t phys_t1 = n_tiles > 1 ? kt.entry(1) : 0;
-        if (n_tiles > 0) kt.copy(kt.tile(phys_t, 0, false), kt.valid(0), L.kb[0], g);
+        if (n_tiles > 0) kt.copy(kt.tile(phys_t, 0, false), kt.valid(0), lds_addr(L.kb[0]), g);
         // iteration 0: only the copies (no page has been scored yet)
         {
             const int32_t phys_t2 = 2 < n_tiles ? kt.entry(2) : 0;
             wait_vm_all();
             lds_barrier();
-            issue_copies<D>(kt, n_tiles, 0, phys_t, phys_t1, L.kb[1], L.vb[0], g);
+            issue_copies<D>(kt, n_tiles, 0, phys_t, phys_t1, lds_addr(L.kb[1]), lds_addr(L.vb[0]), g);
             lds_barrier();
             phys_t = phys_t1;
             phys_t1 = phys_t2;
@@ -369,7 +372,8 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
             uint32_t lv = la.v;
             asm volatile("" : "+v"(lv));
             output_iter<D>(a, pi, t, phys_t, phys_t1,
-                           L.kb[(t + 1) & 1], L.vb[t & 1], L.vb[(t - 1) & 1], p_grp, alpha_grp, o, lv, g, lane);
+                           lds_addr(L.kb[0]) + ((t + 1) & 1) * F::TILE, lds_addr(L.vb[0]) + (t & 1) * F::TILE,
+                           L.vb[(t - 1) & 1], p_grp, alpha_grp, o, lv, g, lane);
             phys_t = phys_t1;
             phys_t1 = phys_t2;
         }

@@ -73,17 +73,29 @@ inline int pad_grid(int n) { return (n + kXcds - 1) / kXcds * kXcds; }
 // ----------------------------------------------------------------------------------------
 // Direct global -> LDS copy of 16 bytes per lane, through a buffer resource over
 // [base, base + bytes): lane l reads base + off and its bytes land at lds_wave_base + 16 * l
-// (base, bytes and lds_wave_base uniform across the wave).  Offsets past `bytes` read as 0.
-// The buffer (MUBUF) form is used because it counts only in vmcnt: the global form also
-// counts as an LDS access, so while one is in flight the compiler can only wait for LDS reads
-// with lgkmcnt(0), which drains every operand prefetch of the matrix loops.
+// (base, bytes and lds_wave_base uniform across the wave; lds_wave_base is an LDS byte
+// address, see lds_addr).  Offsets past `bytes` read as 0.
+//
+// Issued as inline assembly, so the compiler's wait-count pass does not see it: the caller
+// waits for the copies itself (wait_vm_all() before the barrier that publishes a tile).  Seen
+// by the compiler, an LDS-writing load makes it guard LDS reads with waits it cannot always
+// prove unnecessary (lgkmcnt(0) for the global form; vmcnt(0) in straight-line code for the
+// buffer form), which drains the operand prefetch of the matrix loops.  The buffer form counts
+// only in vmcnt.  The leading s_nop covers the M0 write just before it.
 // ----------------------------------------------------------------------------------------
 constexpr int kRawBufferWord3 = 0x00020000;  // 32-bit data format, no swizzle, no index
-__device__ __forceinline__ void dma16(const void* base, uint32_t bytes, uint32_t off, LS_LDS void* lds_wave_base) {
-    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes,
-                                                                 kRawBufferWord3);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, off, 0, 0, 0);
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void dma16(const void* base, uint32_t bytes, uint32_t off, uint32_t lds_wave_base) {
+    const uint64_t b = (uint64_t)base;
+    const i32x4 rsrc = {__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)b),
+                        __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(b >> 32) & 0xffff),  // stride 0
+                        __builtin_amdgcn_readfirstlane((int32_t)bytes), kRawBufferWord3};
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base)));
 }
+
+// LDS byte address of a __shared__ object (folds to a constant for the kernel's own arrays).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const LS_LDS void*)p; }
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -105,6 +117,15 @@ __device__ __forceinline__ i16x4 lds_read_tr4(const LS_LDS void* p) {
 // vector-ALU code so that the compiler never moves it between these instructions.
 __device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Two independent ones back to back, behind one pair of wait states (one instruction fewer to
+// issue per pair; a single wave per SIMD issues roughly one instruction per four cycles).
+__device__ __forceinline__ void mfma32_agpr2(f32x16& acc0, const bf16x8& a0, const bf16x8& b0, f32x16& acc1,
+                                             const bf16x8& a1, const bf16x8& b1) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\tv_mfma_f32_32x32x16_bf16 %1, %4, %5, %1"
+                 : "+a"(acc0), "+a"(acc1)
+                 : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
 }
 
 // Enough wait states for any matrix instruction in flight to retire before its result is read

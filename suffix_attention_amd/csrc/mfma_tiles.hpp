@@ -34,7 +34,7 @@ __host__ __device__ constexpr int swz(int r) {
 // The key tiles of one part (a prompt shard: logical pages lp0.., walked through the page
 // table; or the response keys as 64-key "virtual pages"), with everything that does not change
 // from page to page computed once per workgroup, so that a page costs one page-table entry,
-// one scalar multiply-add and PER_WAVE direct-to-LDS copies per tile.
+// a few scalar operations and PER_WAVE direct-to-LDS copies per tile.
 //
 // Wave w's j-th copy fills 1 KiB block j*NW + w of an LDS tile, i.e. RPK = 512/D whole rows
 // starting at row j*JROWS + low; lane l writes 16-byte slot l of the block, so it fetches the
@@ -55,10 +55,7 @@ struct KeyTiles {
     int64_t keys;           // keys of the part counted from tile 0
     int32_t n_phys;
     uint32_t row_bytes;     // bytes between key rows inside a tile
-    uint32_t span;          // bytes from a tile's first row to the end of its last
     bool resp;
-    int low;                // first row of this lane's copies (plus j * JROWS)
-    int lane_x;             // this lane's chunk before the j part of the swizzle
     uint32_t off[PER_WAVE]; // this lane's byte offset in a full tile, copy j
 
     __device__ __forceinline__ KeyTiles(const AttnArgs& a, bool resp_, int64_t lp0, int kvh, int w, int lane) {
@@ -77,10 +74,9 @@ struct KeyTiles {
             row_bytes = (uint32_t)a.hkv * D * 2;
             keys = a.key_end;
         }
-        span = (kPage - 1) * row_bytes + D * 2;
         table = (const __attribute__((address_space(4))) int32_t*)a.table + (resp ? 0 : lp0);
-        low = w * RPK + lane / F::KCH;
-        lane_x = (lane % F::KCH) ^ swz<D>(low);
+        const int low = w * RPK + lane / F::KCH;      // first row of this lane's copies
+        const int lane_x = (lane % F::KCH) ^ swz<D>(low);
 #pragma unroll
         for (int j = 0; j < PER_WAVE; j++)
             off[j] = (uint32_t)(j * JROWS + low) * row_bytes + (uint32_t)((lane_x ^ swz<D>(j * JROWS)) << 4);
@@ -103,35 +99,32 @@ struct KeyTiles {
         return left < kPage ? (int)left : kPage;
     }
 
-    // Copy j (0 <= j < PER_WAVE) of this wave's share of one tile, so that a caller can spread
-    // a tile's copies over its compute steps; rows past `valid` repeat the last valid row.
-    __device__ __forceinline__ void copy_piece(const char* src, int valid_rows, char* lds, int w, int j) const {
-        uint32_t o = off[j];
-        if (valid_rows < kPage) {
-            const int r = j * JROWS + low;
-            const int rs = r < valid_rows ? r : valid_rows - 1;
-            o = (uint32_t)rs * row_bytes + (uint32_t)((lane_x ^ swz<D>(j * JROWS)) << 4);
-        }
-        dma16(src, span, o, (LS_LDS void*)(lds + (j * NW + w) * 1024));
+    // Bytes of a tile's source that hold its valid_rows (>= 1) keys.  Copies of rows past them
+    // fall outside the copy's buffer range and read as zero; the kernels also clear their key
+    // buffers once at the start (clear_lds), so those rows are finite either way (masked by the
+    // caller).
+    __device__ __forceinline__ uint32_t bytes_of(int valid_rows) const {
+        return (uint32_t)(valid_rows - 1) * row_bytes + D * 2;
     }
 
-    // Copy one tile into LDS (all NW waves together); rows past `valid` repeat the last valid
-    // row (finite, masked by the caller).
-    __device__ __forceinline__ void copy(const char* src, int valid_rows, char* lds, int w) const {
-        if (valid_rows == kPage) {
+    // Copy j (0 <= j < PER_WAVE) of this wave's share of one tile, so that a caller can spread
+    // a tile's copies over its compute steps.
+    __device__ __forceinline__ void copy_piece(const char* src, int valid_rows, uint32_t lds, int w, int j) const {
+        dma16(src, bytes_of(valid_rows), off[j], lds + (j * NW + w) * 1024);
+    }
+
+    // Copy one tile into LDS (all NW waves together).
+    __device__ __forceinline__ void copy(const char* src, int valid_rows, uint32_t lds, int w) const {
 #pragma unroll
-            for (int j = 0; j < PER_WAVE; j++) dma16(src, span, off[j], (LS_LDS void*)(lds + (j * NW + w) * 1024));
-        } else {
-#pragma unroll
-            for (int j = 0; j < PER_WAVE; j++) {
-                const int r = j * JROWS + low;
-                const int rs = r < valid_rows ? r : valid_rows - 1;
-                const uint32_t o = (uint32_t)rs * row_bytes + (uint32_t)((lane_x ^ swz<D>(j * JROWS)) << 4);
-                dma16(src, span, o, (LS_LDS void*)(lds + (j * NW + w) * 1024));
-            }
-        }
+        for (int j = 0; j < PER_WAVE; j++) copy_piece(src, valid_rows, lds, w, j);
     }
 };
+
+// Zero `bytes` (a multiple of 16) of LDS from p, by all `nthreads` threads of the workgroup;
+// the caller puts a barrier between this and any copy into the same memory.
+__device__ __forceinline__ void clear_lds(char* p, int bytes, int tid, int nthreads) {
+    for (int i = tid * 16; i < bytes; i += nthreads * 16) *(LS_LDS u32x4*)((LS_LDS char*)p + i) = u32x4{0, 0, 0, 0};
+}
 
 // Direct-to-LDS copy of ROWS full rows (D bf16 each, rows `stride` elements apart) from two
 // sources a, b into two LDS tiles, by all NW waves together.  Wave w's j-th copy fills 1 KiB
@@ -139,8 +132,8 @@ struct KeyTiles {
 // block, so it fetches the logical chunk that the swizzle puts there.  `w` must be
 // wave-uniform.
 template <int D, int NW, int ROWS>
-__device__ __forceinline__ void dma_rows(const bf16_t* a, const bf16_t* b, int64_t stride, char* lds_a,
-                                         char* lds_b, int w, int lane) {
+__device__ __forceinline__ void dma_rows(const bf16_t* a, const bf16_t* b, int64_t stride, uint32_t lds_a,
+                                         uint32_t lds_b, int w, int lane) {
     using F = TileShape<D>;
     constexpr int RPK = 512 / D;                 // rows per 1 KiB block
     constexpr int PER_WAVE = ROWS * D * 2 / 1024 / NW;
@@ -155,8 +148,8 @@ __device__ __forceinline__ void dma_rows(const bf16_t* a, const bf16_t* b, int64
         const uint32_t off = (uint32_t)((j * JROWS + low) * (int)stride + lc * 8) * 2u;
         const uint32_t bytes = (uint32_t)((ROWS - 1) * stride + D) * 2u;
         const int blk = j * NW + w;
-        dma16(a, bytes, off, (LS_LDS void*)(lds_a + blk * 1024));
-        dma16(b, bytes, off, (LS_LDS void*)(lds_b + blk * 1024));
+        dma16(a, bytes, off, lds_a + blk * 1024);
+        dma16(b, bytes, off, lds_b + blk * 1024);
     }
 }
 
