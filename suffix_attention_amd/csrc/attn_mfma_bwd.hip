@@ -131,30 +131,29 @@ struct DkvState {
 };
 
 // Phase 1 of a row tile: S = Q K^T and dP = dO V^T for 32 rows x 32 keys (element i is row
-// 8(i/4) + 4h + i%4 of the tile, key lane%32).  Q and dO fragments are read PD k-steps ahead.
+// 8(i/4) + 4h + i%4 of the tile, key lane%32).  Q and dO fragments are read PD k-steps ahead;
+// sk is the stage's LDS address plus the lane's natural-read offset.
 template <int D, typename Copy>
-__device__ __forceinline__ void tile_scores(const DkvState<D>& st, const LS_LDS char* stage, uint32_t lk, f32x16& s,
-                                            f32x16& dp, Copy&& copy_step) {
+__device__ __forceinline__ void tile_scores(const DkvState<D>& st, uint32_t sk, f32x16& s, f32x16& dp,
+                                            Copy&& copy_step) {
     using F = TileShape<D>;
-    const LS_LDS char* lq = stage;
-    const LS_LDS char* ldo = stage + RowStage<D>::QBYTES;
     s = f32x16{};
     dp = f32x16{};
     constexpr int PD = 3;
     bf16x8 qd[PD][2];
 #pragma unroll
     for (int j = 0; j < PD; j++) {
-        const uint32_t o = lk ^ (uint32_t)(j << 5);
-        qd[j][0] = *(const LS_LDS bf16x8*)(lq + o);
-        qd[j][1] = *(const LS_LDS bf16x8*)(ldo + o);
+        const uint32_t o = sk ^ (uint32_t)(j << 5);
+        qd[j][0] = lds_b128(o);
+        qd[j][1] = lds_b128(o + RowStage<D>::QBYTES);
     }
 #pragma unroll
     for (int ks = 0; ks < F::KS; ks++) {
         const bf16x8 qa = qd[ks % PD][0], da = qd[ks % PD][1];
         if (ks + PD < F::KS) {
-            const uint32_t o = lk ^ (uint32_t)((ks + PD) << 5);
-            qd[ks % PD][0] = *(const LS_LDS bf16x8*)(lq + o);
-            qd[ks % PD][1] = *(const LS_LDS bf16x8*)(ldo + o);
+            const uint32_t o = sk ^ (uint32_t)((ks + PD) << 5);
+            qd[ks % PD][0] = lds_b128(o);
+            qd[ks % PD][1] = lds_b128(o + RowStage<D>::QBYTES);
         }
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, st.kb[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, st.vb[ks], dp, 0, 0, 0);
@@ -188,24 +187,23 @@ __device__ __forceinline__ void prob_unit(int unit, const f32x16& s, const f32x1
     pr.wd[u][2 * hb + j2] = pack_bf16x2(dv[0], dv[1]);
 }
 
-// (LSE log2e, delta) of the two rows of unit `unit` (rows 16u + 8hb + 4h + 2j2, +1)
-__device__ __forceinline__ f32x4 unit_lsd(int unit, const LS_LDS f32x2* lsd, int h) {
+// (LSE log2e, delta) of the two rows of unit `unit` (rows 16u + 8hb + 4h + 2j2, +1); lsd_h is
+// the LDS address of the stage's pairs plus 8 bytes per row of the lane's 4h.
+__device__ __forceinline__ f32x4 unit_lsd(int unit, uint32_t lsd_h) {
     const int u = unit >> 2, hb = (unit >> 1) & 1, j2 = unit & 1;
-    return *(const LS_LDS f32x4*)(lsd + 16 * u + 8 * hb + 4 * h + 2 * j2);
+    return lds_f32x4(lsd_h + (16 * u + 8 * hb + 2 * j2) * 8);
 }
 
 // Phase 3 of row tile t: dV += P^T dO, dK += dS^T Q (dO, Q read transposed: rows are the
 // contraction), with phase 2 of row tile t+1 (its S, dP already computed) spread over the
 // steps so that its vector work runs while the matrix core is busy.  Step st = (u, dt), dt
-// fastest; fragments read PT steps ahead.
+// fastest; fragments read PT steps ahead.  sv is the stage's LDS address plus the lane's
+// transposed-read offset.
 template <int D>
-__device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur, const LS_LDS char* stage,
-                                                uint32_t lv, const f32x16& s_n, const f32x16& dp_n,
-                                                const LS_LDS f32x2* lsd_n, int rmh_n, float scale_log2, int h,
+__device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur, uint32_t sv, const f32x16& s_n,
+                                                const f32x16& dp_n, uint32_t lsd_n, int rmh_n, float scale_log2,
                                                 Prob& nxt) {
     using F = TileShape<D>;
-    const LS_LDS char* lq = stage;
-    const LS_LDS char* ldo = stage + RowStage<D>::QBYTES;
     bf16x8 pa[2], sa[2];
 #pragma unroll
     for (int u = 0; u < 2; u++) {
@@ -219,17 +217,17 @@ __device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur
     auto read_t = [&](int st_, i16x4* f) {
         const int dt = st_ % F::DT, u = st_ / F::DT;
         const int R = 16 * u;
-        const uint32_t a0 = (lv ^ tr_x<D>(dt, R)) + R * 2 * D;
-        const uint32_t a1 = (lv ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D;
-        f[0] = lds_read_tr4(ldo + a0);
-        f[1] = lds_read_tr4(ldo + a1);
-        f[2] = lds_read_tr4(lq + a0);
-        f[3] = lds_read_tr4(lq + a1);
+        const uint32_t a0 = (sv ^ tr_x<D>(dt, R)) + R * 2 * D;
+        const uint32_t a1 = (sv ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D;
+        f[0] = lds_tr4(a0 + RowStage<D>::QBYTES);
+        f[1] = lds_tr4(a1 + RowStage<D>::QBYTES);
+        f[2] = lds_tr4(a0);
+        f[3] = lds_tr4(a1);
     };
     // each unit's (LSE, delta) pair is read one unit ahead: a read issued just before its use
     // would make the wait for it (LDS returns in order) drain the prefetched operand reads too
     f32x4 lb[2];
-    lb[0] = unit_lsd(0, lsd_n, h);
+    lb[0] = unit_lsd(0, lsd_n);
 #pragma unroll
     for (int j = 0; j < PT; j++) read_t(j, fr[j]);
 #pragma unroll
@@ -245,7 +243,7 @@ __device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur
 #pragma unroll
         for (int un = 0; un < NU; un++)
             if (un >= st_ * NU / NST && un < (st_ + 1) * NU / NST) {
-                if (un + 1 < NU) lb[(un + 1) & 1] = unit_lsd(un + 1, lsd_n, h);
+                if (un + 1 < NU) lb[(un + 1) & 1] = unit_lsd(un + 1, lsd_n);
                 prob_unit(un, s_n, dp_n, lb[un & 1], rmh_n, scale_log2, nxt);
             }
         __builtin_amdgcn_sched_barrier(0);
@@ -257,8 +255,7 @@ __device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur
 // compiler knows the copy in flight (into `dst`) cannot alias the stages being read and does
 // not wait for it.
 template <int D>
-__device__ __forceinline__ void dkdv_step(DkvState<D>& st, const char* __restrict__ stage_t,
-                                          const char* __restrict__ stage_n, uint32_t dst,
+__device__ __forceinline__ void dkdv_step(DkvState<D>& st, uint32_t stage_t, uint32_t stage_n, uint32_t dst,
                                           const GroupRows& gr, const RowCopy<D>& rc, int kvh, int64_t copy_r0,
                                           const Prob& cur, Prob& nxt,
                                           LaneAddr<D> la, int rmh_n, float scale_log2, int w, int lane) {
@@ -273,10 +270,9 @@ __device__ __forceinline__ void dkdv_step(DkvState<D>& st, const char* __restric
     uint32_t lk = la.k, lv = la.v;
     asm volatile("" : "+v"(lk), "+v"(lv));
     f32x16 s_n, dp_n;
-    tile_scores<D>(st, (const LS_LDS char*)stage_n, lk, s_n, dp_n, copy_step);
-    tile_accumulate<D>(st, cur, (const LS_LDS char*)stage_t, lv, s_n, dp_n,
-                       (const LS_LDS f32x2*)((const LS_LDS char*)stage_n + 2 * RowStage<D>::QBYTES), rmh_n, scale_log2,
-                       lane >> 5, nxt);
+    tile_scores<D>(st, stage_n + lk, s_n, dp_n, copy_step);
+    tile_accumulate<D>(st, cur, stage_t + lv, s_n, dp_n, stage_n + 2 * RowStage<D>::QBYTES + (lane >> 5) * 32, rmh_n,
+                       scale_log2, nxt);
 }
 
 // One workgroup: 4 waves over two consecutive 64-key pages (wave w: page w/2, keys
@@ -367,19 +363,20 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks
     // S and dP of tile t+1, and accumulates tile t with tile t+1's P and dS formed beside it.
     const LaneAddr<D> la(lane);
     const RowCopy<D> rc(w, lane);
+    const uint32_t stg0 = lds_addr(stg[0]);
     if (n_stages > 0) {
-        issue_rows<D>(gr, kvh, r_begin, lds_addr(stg[0]), w, lane);
-        if (n_stages > 1) issue_rows<D>(gr, kvh, r_begin + kRows, lds_addr(stg[1]), w, lane);
+        issue_rows<D>(gr, kvh, r_begin, stg0, w, lane);
+        if (n_stages > 1) issue_rows<D>(gr, kvh, r_begin + kRows, stg0 + kStage, w, lane);
         wait_vm_all();
         __syncthreads();
         Prob cur;
         {
             f32x16 s0, dp0;
-            tile_scores<D>(st, (const LS_LDS char*)stg[0], la.k, s0, dp0, [](int) {});
+            tile_scores<D>(st, stg0 + la.k, s0, dp0, [](int) {});
             const int rmh0 = rmh_of(0);
-            const LS_LDS f32x2* lsd0 = (const LS_LDS f32x2*)((const LS_LDS char*)stg[0] + 2 * RowStage<D>::QBYTES);
+            const uint32_t lsd0 = stg0 + 2 * RowStage<D>::QBYTES + h * 32;
 #pragma unroll
-            for (int un = 0; un < 8; un++) prob_unit(un, s0, dp0, unit_lsd(un, lsd0, h), rmh0, a.scale_log2, cur);
+            for (int un = 0; un < 8; un++) prob_unit(un, s0, dp0, unit_lsd(un, lsd0), rmh0, a.scale_log2, cur);
         }
         for (int64_t t = 0; t < n_stages; t++) {
             // tile t+1 has landed; stage (t+2) % 3 was last read in iteration t-1
@@ -389,7 +386,8 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks
             const int rmhn = rmh_of(t + 1);
             Prob nxt;
             const int it = (int)(t % 3);
-            dkdv_step<D>(st, stg[it], stg[it == 2 ? 0 : it + 1], lds_addr(stg[0]) + (it == 0 ? 2 : it - 1) * kStage,
+            dkdv_step<D>(st, stg0 + it * kStage, stg0 + (it == 2 ? 0 : it + 1) * kStage,
+                         stg0 + (it == 0 ? 2 : it - 1) * kStage,
                          gr, rc, kvh, r_begin + (t + 2 < n_stages ? t + 2 : n_stages - 1) * kRows, cur, nxt, la, rmhn,
                          a.scale_log2, w, lane);
             cur = nxt;

@@ -28,21 +28,20 @@ struct DqState {
     float dlt;                      // delta of this lane's row
 };
 
-// Phase 1 of one 32-key tile of a page: S^T = K Q^T and dP^T = V dO^T (lds_k, lds_v point at
-// the tile's first key row), 16 k-steps of two matrix instructions; K and V fragments are read
-// PD steps ahead.  beside(ks) runs after step ks's matrix instructions: vector work or copies
-// that overlap them.
+// Phase 1 of one 32-key tile of a page: S^T = K Q^T and dP^T = V dO^T (ak, av: LDS address of
+// the tile's first key row in the K and V buffers plus the lane's natural-read offset), 16
+// k-steps of two matrix instructions; K and V fragments are read PD steps ahead.  beside(ks)
+// runs after step ks's matrix instructions: vector work or copies that overlap them.
 template <int D, typename Beside>
-__device__ __forceinline__ void tile_scores(const DqState<D>& st, const LS_LDS char* lds_k, const LS_LDS char* lds_v,
-                                            uint32_t lk, f32x16& s, f32x16& dp, Beside&& beside) {
+__device__ __forceinline__ void tile_scores(const DqState<D>& st, uint32_t ak, uint32_t av, f32x16& s, f32x16& dp,
+                                            Beside&& beside) {
     using F = TileShape<D>;
     s = dp = f32x16{};
     constexpr int PD = 3;
     bf16x8 kb[PD][2];
     auto read_kv = [&](int ks, bf16x8* b) {
-        const uint32_t o = lk ^ (uint32_t)(ks << 5);
-        b[0] = *(const LS_LDS bf16x8*)(lds_k + o);
-        b[1] = *(const LS_LDS bf16x8*)(lds_v + o);
+        b[0] = lds_b128(ak ^ (uint32_t)(ks << 5));
+        b[1] = lds_b128(av ^ (uint32_t)(ks << 5));
     };
 #pragma unroll
     for (int j = 0; j < PD; j++)
@@ -104,11 +103,11 @@ __device__ __forceinline__ void ds_unit(int unit, int kt, const f32x16& s, const
     out[2 * kt + u][t] = word;
 }
 
-// Phase 3 of page t: dQ^T += K^T dS^T (K read transposed).  Step st = (ku, dt), dt fastest;
-// K^T fragments read PV steps ahead; beside(st) runs after each step's matrix instruction.
+// Phase 3 of page t: dQ^T += K^T dS^T (K read transposed; sv: LDS address of page t's K tile
+// plus the lane's transposed-read offset).  Step st = (ku, dt), dt fastest; K^T fragments read
+// PV steps ahead; beside(st) runs after each step's matrix instruction.
 template <int D, typename Beside>
-__device__ __forceinline__ void page_accumulate(DqState<D>& st, const u32x4 (&ds)[4], const LS_LDS char* lds_k,
-                                                uint32_t lv, Beside&& beside) {
+__device__ __forceinline__ void page_accumulate(DqState<D>& st, const u32x4 (&ds)[4], uint32_t sv, Beside&& beside) {
     using F = TileShape<D>;
     bf16x8 db[4];
 #pragma unroll
@@ -119,8 +118,8 @@ __device__ __forceinline__ void page_accumulate(DqState<D>& st, const u32x4 (&ds
     auto read_kt = [&](int st_, i16x4& lo, i16x4& hi) {
         const int dt = st_ % F::DT, ku = st_ / F::DT;
         const int R = 32 * (ku >> 1) + 16 * (ku & 1);
-        lo = lds_read_tr4(lds_k + (lv ^ tr_x<D>(dt, R)) + R * 2 * D);
-        hi = lds_read_tr4(lds_k + (lv ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D);
+        lo = lds_tr4((sv ^ tr_x<D>(dt, R)) + R * 2 * D);
+        hi = lds_tr4((sv ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D);
     };
 #pragma unroll
     for (int j = 0; j < PV; j++) read_kt(j, tlo[j], thi[j]);
@@ -160,9 +159,8 @@ __device__ __forceinline__ void units_at(int k, F&& f) {
 template <bool MASK, int D, int NW>
 __device__ __forceinline__ void dq_iter(DqState<D>& st, const KeyTiles<D, NW>& kt, int64_t t, int64_t last, bool copy,
                                         int32_t e2,
-                                        uint32_t k_dst, uint32_t v_dst,
-                                        const char* __restrict__ k_n, const char* __restrict__ v_n,
-                                        const char* __restrict__ k_t, u32x4 (&ds)[4], f32x16& s1, f32x16& dp1,
+                                        uint32_t k_dst, uint32_t v_dst, uint32_t k_n, uint32_t v_n, uint32_t k_t,
+                                        u32x4 (&ds)[4], f32x16& s1, f32x16& dp1,
                                         int lim_t, int lim_n, LaneAddr<D> la, float scale_log2, int w) {
     constexpr int PW = KeyTiles<D, NW>::PER_WAVE;
     constexpr int KS = TileShape<D>::KS;
@@ -177,7 +175,7 @@ __device__ __forceinline__ void dq_iter(DqState<D>& st, const KeyTiles<D, NW>& k
     uint32_t lk = la.k, lv = la.v;
     asm volatile("" : "+v"(lk), "+v"(lv));
     f32x16 s0, dp0;
-    tile_scores<D>(st, (const LS_LDS char*)k_n, (const LS_LDS char*)v_n, lk, s0, dp0, [&](int ks) {
+    tile_scores<D>(st, k_n + lk, v_n + lk, s0, dp0, [&](int ks) {
         units_at<8, KS>(ks, [&](int un) { ds_unit<MASK>(un, 1, s1, dp1, lim_t, st, scale_log2, ds); });
         units_at<2 * PW, KS>(ks, [&](int p) {
                 if (p < PW) kt.copy_piece(ksrc, vn, k_dst, w, p);
@@ -185,11 +183,10 @@ __device__ __forceinline__ void dq_iter(DqState<D>& st, const KeyTiles<D, NW>& k
             });
     });
     u32x4 nxt[4];
-    page_accumulate<D>(st, ds, (const LS_LDS char*)k_t, lv, [&](int k) {
+    page_accumulate<D>(st, ds, k_t + lv, [&](int k) {
         units_at<8, NST>(k, [&](int un) { ds_unit<MASK>(un, 0, s0, dp0, lim_n, st, scale_log2, nxt); });
     });
-    tile_scores<D>(st, (const LS_LDS char*)k_n + 32 * 2 * D, (const LS_LDS char*)v_n + 32 * 2 * D, lk, s1, dp1,
-                   [](int) {});
+    tile_scores<D>(st, k_n + lk + 32 * 2 * D, v_n + lk + 32 * 2 * D, s1, dp1, [](int) {});
     ds[0] = nxt[0];
     ds[1] = nxt[1];
 }
@@ -265,18 +262,19 @@ void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
         return page_mask(need, valid, key0, resp, vis_limit, h);
     };
 
+    const uint32_t kb0 = lds_addr(kbuf[0]), vb0 = lds_addr(vbuf[0]);
     clear_lds(&kbuf[0][0], sizeof(kbuf), threadIdx.x, NW * 64);
     clear_lds(&vbuf[0][0], sizeof(vbuf), threadIdx.x, NW * 64);
     __syncthreads();
     if (n_tiles > 0) {
         // prologue: pages 0 and 1 in LDS; S, dP of page 0 and dS of its key tile 0
         const int32_t e0 = kt.entry(0);
-        kt.copy(kt.tile(e0, 0, false), kt.valid(0), lds_addr(kbuf[0]), w);
-        kt.copy(kt.tile(e0, 0, true), kt.valid(0), lds_addr(vbuf[0]), w);
+        kt.copy(kt.tile(e0, 0, false), kt.valid(0), kb0, w);
+        kt.copy(kt.tile(e0, 0, true), kt.valid(0), vb0, w);
         if (n_tiles > 1) {
             const int32_t e1 = kt.entry(1);
-            kt.copy(kt.tile(e1, 1, false), kt.valid(1), lds_addr(kbuf[1]), w);
-            kt.copy(kt.tile(e1, 1, true), kt.valid(1), lds_addr(vbuf[1]), w);
+            kt.copy(kt.tile(e1, 1, false), kt.valid(1), kb0 + F::TILE, w);
+            kt.copy(kt.tile(e1, 1, true), kt.valid(1), vb0 + F::TILE, w);
         }
         // page-table entries are read through the scalar cache one iteration before their
         // copies and clamped where they are used
@@ -288,9 +286,8 @@ void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
         PageMask m_t = mask_of(0);
         {
             f32x16 s0, dp0;
-            tile_scores<D>(st, (const LS_LDS char*)kbuf[0], (const LS_LDS char*)vbuf[0], la.k, s0, dp0, [](int) {});
-            tile_scores<D>(st, (const LS_LDS char*)kbuf[0] + 32 * 2 * D, (const LS_LDS char*)vbuf[0] + 32 * 2 * D, la.k,
-                           s1, dp1, [&](int ks) {
+            tile_scores<D>(st, kb0 + la.k, vb0 + la.k, s0, dp0, [](int) {});
+            tile_scores<D>(st, kb0 + la.k + 32 * 2 * D, vb0 + la.k + 32 * 2 * D, s1, dp1, [&](int ks) {
                                units_at<8, F::KS>(ks, [&](int un) {
                                    ds_unit<true>(un, 0, s0, dp0, m_t.lim, st, a.scale_log2, ds);
                                });
@@ -306,8 +303,8 @@ void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
             const int k0 = (int)(t % 3), k1 = k0 == 2 ? 0 : k0 + 1, k2 = k0 == 0 ? 2 : k0 - 1;
             const int v0 = (int)(t & 1), v1 = v0 ^ 1;
             const PageMask m_n = mask_of(t + 1);
-            dq_iter<true, D, NW>(st, kt, t, n_tiles - 1, t + 2 < n_tiles, e2, lds_addr(kbuf[0]) + k2 * F::TILE,
-                                 lds_addr(vbuf[0]) + v0 * F::TILE, kbuf[k1], vbuf[v1], kbuf[k0], ds,
+            dq_iter<true, D, NW>(st, kt, t, n_tiles - 1, t + 2 < n_tiles, e2, kb0 + k2 * F::TILE, vb0 + v0 * F::TILE,
+                                 kb0 + k1 * F::TILE, vb0 + v1 * F::TILE, kb0 + k0 * F::TILE, ds,
                                  s1, dp1, m_t.lim, m_n.lim, la, a.scale_log2, w);
             m_t = m_n;
             e2 = e3;

@@ -88,8 +88,7 @@ struct PartInfo {
 // S^T(t) = K(t) Q^T for the wave's 32 rows: two 32-key tiles, KS k-steps each, K fragments
 // read PD steps ahead.
 template <int D>
-__device__ __forceinline__ void scores(const bf16x8 (&qb)[TileShape<D>::KS], f32x16 (&s)[2], const LS_LDS char* lds_k,
-                                       uint32_t lk) {
+__device__ __forceinline__ void scores(const bf16x8 (&qb)[TileShape<D>::KS], f32x16 (&s)[2], uint32_t ak) {
     using F = TileShape<D>;
     constexpr int PD = 2;
     bf16x8 kbuf[PD][2];
@@ -97,17 +96,17 @@ __device__ __forceinline__ void scores(const bf16x8 (&qb)[TileShape<D>::KS], f32
     s[1] = f32x16{};
 #pragma unroll
     for (int j = 0; j < PD; j++) {
-        const LS_LDS char* pk = lds_k + (lk ^ (uint32_t)(j << 5));
-        kbuf[j][0] = *(const LS_LDS bf16x8*)(pk);
-        kbuf[j][1] = *(const LS_LDS bf16x8*)(pk + 32 * 2 * D);
+        const uint32_t pk = ak ^ (uint32_t)(j << 5);
+        kbuf[j][0] = lds_b128(pk);
+        kbuf[j][1] = lds_b128(pk + 32 * 2 * D);
     }
 #pragma unroll
     for (int ks = 0; ks < F::KS; ks++) {
         const bf16x8 k0 = kbuf[ks % PD][0], k1 = kbuf[ks % PD][1];
         if (ks + PD < F::KS) {
-            const LS_LDS char* pk = lds_k + (lk ^ (uint32_t)((ks + PD) << 5));
-            kbuf[ks % PD][0] = *(const LS_LDS bf16x8*)(pk);
-            kbuf[ks % PD][1] = *(const LS_LDS bf16x8*)(pk + 32 * 2 * D);
+            const uint32_t pk = ak ^ (uint32_t)((ks + PD) << 5);
+            kbuf[ks % PD][0] = lds_b128(pk);
+            kbuf[ks % PD][1] = lds_b128(pk + 32 * 2 * D);
         }
         s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qb[ks], s[0], 0, 0, 0);
         s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qb[ks], s[1], 0, 0, 0);
@@ -184,7 +183,7 @@ __device__ __forceinline__ void softmax_page(f32x16 (&s)[2], float& m_ref, float
 // ahead.
 template <int D>
 __device__ __forceinline__ void accumulate_pv(f32x16 (&o)[TileShape<D>::DT], const bf16x8 (&pb)[4],
-                                              const LS_LDS char* lds_v, uint32_t lv) {
+                                              uint32_t sv) {
     using F = TileShape<D>;
     constexpr int NST = 4 * F::DT;
     constexpr int PV = 4;
@@ -192,8 +191,8 @@ __device__ __forceinline__ void accumulate_pv(f32x16 (&o)[TileShape<D>::DT], con
     auto read_v = [&](int st, i16x4& lo, i16x4& hi) {
         const int dt = st % F::DT, ku = st / F::DT;
         const int R = 32 * (ku >> 1) + 16 * (ku & 1);
-        lo = lds_read_tr4(lds_v + (lv ^ tr_x<D>(dt, R)) + R * 2 * D);
-        hi = lds_read_tr4(lds_v + (lv ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D);
+        lo = lds_tr4((sv ^ tr_x<D>(dt, R)) + R * 2 * D);
+        hi = lds_tr4((sv ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D);
     };
 #pragma unroll
     for (int j = 0; j < PV; j++) read_v(j, vlo[j], vhi[j]);
@@ -214,13 +213,13 @@ __device__ __forceinline__ void accumulate_pv(f32x16 (&o)[TileShape<D>::DT], con
 // copies; then the softmax of page t while they multiply.
 template <int D>
 __device__ __forceinline__ void score_iter(const AttnArgs& a, const PartInfo<D>& pi, int64_t t,
-                                           const char* __restrict__ k_cur, char* __restrict__ p_out,
+                                           uint32_t k_cur, char* __restrict__ p_out,
                                            float* __restrict__ alpha_out, const bf16x8 (&qb)[TileShape<D>::KS],
                                            float& m_ref, float& l, int64_t vis_limit, uint32_t lk, int lane) {
     wait_vm_all();
     lds_barrier();
     f32x16 s[2];
-    scores<D>(qb, s, (const LS_LDS char*)k_cur, lk);
+    scores<D>(qb, s, k_cur + lk);
     lds_barrier();
     const int valid = pi.kt.valid(t);
     const int64_t key0 = (pi.lp0 + t) * kPage;
@@ -234,7 +233,7 @@ __device__ __forceinline__ void score_iter(const AttnArgs& a, const PartInfo<D>&
 template <int D>
 __device__ __forceinline__ void output_iter(const AttnArgs& a, const PartInfo<D>& pi, int64_t t, int32_t phys_t,
                                             int32_t phys_t1, uint32_t k_dst, uint32_t v_dst,
-                                            const char* __restrict__ v_prev, const char* __restrict__ p_in,
+                                            uint32_t v_prev, const char* __restrict__ p_in,
                                             const float* __restrict__ alpha_in, f32x16 (&o)[TileShape<D>::DT],
                                             uint32_t lv, int w, int lane) {
     using F = TileShape<D>;
@@ -254,7 +253,7 @@ __device__ __forceinline__ void output_iter(const AttnArgs& a, const PartInfo<D>
             for (int i = 0; i < 16; i++) o[dt][i] = agpr_scaled(o[dt][i], alpha);
         agpr_write_gap();
     }
-    accumulate_pv<D>(o, pb, (const LS_LDS char*)v_prev, lv);
+    accumulate_pv<D>(o, pb, v_prev + lv);
 }
 
 template <int D>
@@ -332,7 +331,8 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
         for (int64_t t = 0; t < n_tiles; t++) {
             uint32_t lk = la.k;
             asm volatile("" : "+v"(lk));
-            score_iter<D>(a, pi, t, L.kb[t & 1], p_grp, alpha_grp, qb, m_ref, l, vis_limit, lk, lane);
+            score_iter<D>(a, pi, t, lds_addr(L.kb[0]) + (t & 1) * F::TILE, p_grp, alpha_grp, qb, m_ref, l, vis_limit,
+                          lk, lane);
         }
         // iteration n_tiles: the output waves' last page; nothing left to score
         lds_barrier();
@@ -373,7 +373,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
             asm volatile("" : "+v"(lv));
             output_iter<D>(a, pi, t, phys_t, phys_t1,
                            lds_addr(L.kb[0]) + ((t + 1) & 1) * F::TILE, lds_addr(L.vb[0]) + (t & 1) * F::TILE,
-                           L.vb[(t - 1) & 1], p_grp, alpha_grp, o, lv, g, lane);
+                           lds_addr(L.vb[0]) + ((t - 1) & 1) * F::TILE, p_grp, alpha_grp, o, lv, g, lane);
             phys_t = phys_t1;
             phys_t1 = phys_t2;
         }

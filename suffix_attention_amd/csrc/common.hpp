@@ -97,6 +97,13 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t bytes, uint32_t
 // LDS byte address of a __shared__ object (folds to a constant for the kernel's own arrays).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const LS_LDS void*)p; }
 
+// Reads at an LDS byte address.  The matrix loops form operand addresses as (lane base +
+// buffer base) ^ step constant + row immediate: with buffers aligned to 1 KiB and the xor
+// confined to bits 4..8, adding the buffer base first commutes with the xor, so each read costs
+// one xor (the row offset goes into the instruction's immediate).
+__device__ __forceinline__ bf16x8 lds_b128(uint32_t a) { return *(const LS_LDS bf16x8*)(uintptr_t)a; }
+__device__ __forceinline__ f32x4 lds_f32x4(uint32_t a) { return *(const LS_LDS f32x4*)(uintptr_t)a; }
+
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // 4 bf16 from LDS through the gfx950 transpose read.  Within each 16-lane group, lane i
@@ -106,6 +113,7 @@ __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)
 __device__ __forceinline__ i16x4 lds_read_tr4(const LS_LDS void* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LS_LDS i16x4*)(p));
 }
+__device__ __forceinline__ i16x4 lds_tr4(uint32_t a) { return lds_read_tr4((const LS_LDS void*)(uintptr_t)a); }
 
 // Matrix-core multiply-add with the accumulator held in AGPRs, for kernels built with
 // VGPR-form matrix instructions (whose other accumulators feed vector-ALU work):
