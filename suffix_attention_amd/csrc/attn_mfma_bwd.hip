@@ -170,6 +170,7 @@ struct Prob {
     uint32_t wp[2][4], wd[2][4];  // [u][word]
 };
 
+template <bool MASK>
 __device__ __forceinline__ void prob_unit(int unit, const f32x16& s, const f32x16& dp, f32x4 l, int rmh,
                                           float scale_log2, Prob& pr) {
     const int u = unit >> 2, hb = (unit >> 1) & 1, j2 = unit & 1;
@@ -179,7 +180,7 @@ __device__ __forceinline__ void prob_unit(int unit, const f32x16& s, const f32x1
         const int j = 2 * j2 + e;
         const int i = 8 * u + 4 * hb + j;
         float p = fast_exp2(__builtin_fmaf(s[i], scale_log2, -l[2 * e]));
-        p = (16 * u + 8 * hb + j) >= rmh ? p : 0.f;  // rmh <= 0 where no row precedes the key
+        if (MASK) p = (16 * u + 8 * hb + j) >= rmh ? p : 0.f;  // rmh <= 0 where no row precedes the key
         pv[e] = p;
         dv[e] = p * (dp[i] - l[2 * e + 1]);
     }
@@ -199,7 +200,7 @@ __device__ __forceinline__ f32x4 unit_lsd(int unit, uint32_t lsd_h) {
 // steps so that its vector work runs while the matrix core is busy.  Step st = (u, dt), dt
 // fastest; fragments read PT steps ahead.  sv is the stage's LDS address plus the lane's
 // transposed-read offset.
-template <int D>
+template <bool MASK, int D>
 __device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur, uint32_t sv, const f32x16& s_n,
                                                 const f32x16& dp_n, uint32_t lsd_n, int rmh_n, float scale_log2,
                                                 Prob& nxt) {
@@ -244,7 +245,7 @@ __device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur
         for (int un = 0; un < NU; un++)
             if (un >= st_ * NU / NST && un < (st_ + 1) * NU / NST) {
                 if (un + 1 < NU) lb[(un + 1) & 1] = unit_lsd(un + 1, lsd_n);
-                prob_unit(un, s_n, dp_n, lb[un & 1], rmh_n, scale_log2, nxt);
+                prob_unit<MASK>(un, s_n, dp_n, lb[un & 1], rmh_n, scale_log2, nxt);
             }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -254,7 +255,7 @@ __device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur
 // tile t+1 beside it.  The LDS stages are restrict pointers so that, once inlined, the
 // compiler knows the copy in flight (into `dst`) cannot alias the stages being read and does
 // not wait for it.
-template <int D>
+template <bool MASK, int D>
 __device__ __forceinline__ void dkdv_step(DkvState<D>& st, uint32_t stage_t, uint32_t stage_n, uint32_t dst,
                                           const GroupRows& gr, const RowCopy<D>& rc, int kvh, int64_t copy_r0,
                                           const Prob& cur, Prob& nxt,
@@ -271,24 +272,25 @@ __device__ __forceinline__ void dkdv_step(DkvState<D>& st, uint32_t stage_t, uin
     asm volatile("" : "+v"(lk), "+v"(lv));
     f32x16 s_n, dp_n;
     tile_scores<D>(st, stage_n + lk, s_n, dp_n, copy_step);
-    tile_accumulate<D>(st, cur, stage_t + lv, s_n, dp_n, stage_n + 2 * RowStage<D>::QBYTES + (lane >> 5) * 32, rmh_n,
+    tile_accumulate<MASK, D>(st, cur, stage_t + lv, s_n, dp_n, stage_n + 2 * RowStage<D>::QBYTES + (lane >> 5) * 32, rmh_n,
                        scale_log2, nxt);
 }
 
 // One workgroup: 4 waves over two consecutive 64-key pages (wave w: page w/2, keys
-// 32 (w%2) .. +32).  Blocks [0, n_pp) are prompt page pairs, the rest response pairs.
-template <int D>
+// 32 (w%2) .. +32).  Pairs [0, n_pp) are prompt page pairs, the rest response pairs; a launch
+// covers pairs [pair0, pair0 + n_pairs_l) of every kv head.  MASK selects the causal mask, which
+// only response pairs need; the host launches the two kinds separately.
+template <int D, bool MASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks) {
+void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int pair0, int n_pairs_l, int n_blocks) {
     using F = TileShape<D>;
     constexpr int kStage = (RowStage<D>::BYTES + 1023) / 1024 * 1024;
     __shared__ __attribute__((aligned(1024))) char stg[3][kStage];
 
     const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
     if (lb >= n_blocks) return;
-    const int per_kvh = n_pp + n_rp;
-    const int kvh = lb / per_kvh;
-    const int pair = lb % per_kvh;
+    const int kvh = lb / n_pairs_l;
+    const int pair = pair0 + lb % n_pairs_l;
     const bool resp = pair >= n_pp;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -376,7 +378,7 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks
             const int rmh0 = rmh_of(0);
             const uint32_t lsd0 = stg0 + 2 * RowStage<D>::QBYTES + h * 32;
 #pragma unroll
-            for (int un = 0; un < 8; un++) prob_unit(un, s0, dp0, unit_lsd(un, lsd0), rmh0, a.scale_log2, cur);
+            for (int un = 0; un < 8; un++) prob_unit<MASK>(un, s0, dp0, unit_lsd(un, lsd0), rmh0, a.scale_log2, cur);
         }
         for (int64_t t = 0; t < n_stages; t++) {
             // tile t+1 has landed; stage (t+2) % 3 was last read in iteration t-1
@@ -386,7 +388,7 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int n_rp, int n_blocks
             const int rmhn = rmh_of(t + 1);
             Prob nxt;
             const int it = (int)(t % 3);
-            dkdv_step<D>(st, stg0 + it * kStage, stg0 + (it == 2 ? 0 : it + 1) * kStage,
+            dkdv_step<MASK, D>(st, stg0 + it * kStage, stg0 + (it == 2 ? 0 : it + 1) * kStage,
                          stg0 + (it == 0 ? 2 : it - 1) * kStage,
                          gr, rc, kvh, r_begin + (t + 2 < n_stages ? t + 2 : n_stages - 1) * kRows, cur, nxt, la, rmhn,
                          a.scale_log2, w, lane);
@@ -469,10 +471,11 @@ hipError_t launch_bwd_d(const AttnArgs& a, hipStream_t s) {
     // dK / dV
     const int n_pp = (int)((a.n_logical_pages + 1) / 2);
     const int n_rp = (int)((resp_tiles(a.key_end) + 1) / 2);
-    const int64_t nb_kv = (int64_t)(n_pp + n_rp) * a.hkv;
-    if (nb_kv > 0) {
+    if ((int64_t)(n_pp + n_rp) * a.hkv > 0) {
         KernelTimer kt("dkdv_mfma", s);
-        dkdv_mfma_kernel<D><<<pad_grid((int)nb_kv), 256, 0, s>>>(a, gr, n_pp, n_rp, (int)nb_kv);
+        const int nbp = n_pp * a.hkv, nbr = n_rp * a.hkv;
+        if (nbp > 0) dkdv_mfma_kernel<D, false><<<pad_grid(nbp), 256, 0, s>>>(a, gr, n_pp, 0, n_pp, nbp);
+        if (nbr > 0) dkdv_mfma_kernel<D, true><<<pad_grid(nbr), 256, 0, s>>>(a, gr, n_pp, n_pp, n_rp, nbr);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -60,17 +60,13 @@ __device__ __forceinline__ void tile_scores(const DqState<D>& st, uint32_t ak, u
 // Masking limit of one page for this lane's row: element i of key tile kt is key
 // 32kt + 8(i/4) + 4h + i%4 of the page, and gets P = 0 unless that key is below the page's
 // valid keys and, for response keys, at most the row's own position.  Both conditions fold into
-// one bound on 32kt + 8(i/4) + i%4 (the lane's 4h is taken out of it).  `on` is false when no
-// key of the page is masked for any row of the workgroup.
+// one bound on 32kt + 8(i/4) + i%4 (the lane's 4h is taken out of it).
 struct PageMask {
-    bool on;
     int lim;
 };
 
-__device__ __forceinline__ PageMask page_mask(bool need_mask, int valid, int64_t key0, bool resp, int64_t vis_limit,
-                                              int h) {
+__device__ __forceinline__ PageMask page_mask(int valid, int64_t key0, bool resp, int64_t vis_limit, int h) {
     PageMask m;
-    m.on = need_mask;
     m.lim = valid - 4 * h;
     if (resp) {
         const int64_t c = vis_limit - key0 - 4 * h + 1;
@@ -191,9 +187,63 @@ __device__ __forceinline__ void dq_iter(DqState<D>& st, const KeyTiles<D, NW>& k
     ds[1] = nxt[1];
 }
 
-template <int D, int NW>
+// Every page of the part through the pipeline, with or without the per-element mask.
+template <bool MASK, int D, int NW, typename MaskOf>
+__device__ __forceinline__ void dq_pages(DqState<D>& st, const KeyTiles<D, NW>& kt, int64_t n_tiles, MaskOf&& mask_of,
+                                         uint32_t kb0, uint32_t vb0, LaneAddr<D> la, float scale_log2, int w) {
+    using F = TileShape<D>;
+    // prologue: pages 0 and 1 in LDS; S, dP of page 0 and dS of its key tile 0
+    const int32_t e0 = kt.entry(0);
+    kt.copy(kt.tile(e0, 0, false), kt.valid(0), kb0, w);
+    kt.copy(kt.tile(e0, 0, true), kt.valid(0), vb0, w);
+    if (n_tiles > 1) {
+        const int32_t e1 = kt.entry(1);
+        kt.copy(kt.tile(e1, 1, false), kt.valid(1), kb0 + F::TILE, w);
+        kt.copy(kt.tile(e1, 1, true), kt.valid(1), vb0 + F::TILE, w);
+    }
+    // page-table entries are read through the scalar cache one iteration before their
+    // copies and clamped where they are used
+    int32_t e2 = n_tiles > 2 ? kt.entry(2) : 0;
+    wait_vm_all();
+    __syncthreads();
+    u32x4 ds[4];
+    f32x16 s1, dp1;
+    PageMask m_t = mask_of(0);
+    {
+        f32x16 s0, dp0;
+        tile_scores<D>(st, kb0 + la.k, vb0 + la.k, s0, dp0, [](int) {});
+        tile_scores<D>(st, kb0 + la.k + 32 * 2 * D, vb0 + la.k + 32 * 2 * D, s1, dp1, [&](int ks) {
+                           units_at<8, F::KS>(ks, [&](int un) {
+                               ds_unit<MASK>(un, 0, s0, dp0, m_t.lim, st, scale_log2, ds);
+                           });
+                       });
+    }
+    for (int64_t t = 0; t < n_tiles; t++) {
+        // K(t+1), V(t+1) have landed; K buffer (t+2) % 3 and V buffer t % 2 were last read
+        // in iteration t-1.  The last iteration runs phase 1 on stale tiles; that result is
+        // never used.
+        const int32_t e3 = t + 3 < n_tiles ? kt.entry(t + 3) : 0;
+        wait_vm_all();
+        __syncthreads();
+        const int k0 = (int)(t % 3), k1 = k0 == 2 ? 0 : k0 + 1, k2 = k0 == 0 ? 2 : k0 - 1;
+        const int v0 = (int)(t & 1), v1 = v0 ^ 1;
+        const PageMask m_n = mask_of(t + 1);
+        dq_iter<MASK, D, NW>(st, kt, t, n_tiles - 1, t + 2 < n_tiles, e2, kb0 + k2 * F::TILE, vb0 + v0 * F::TILE,
+                             kb0 + k1 * F::TILE, vb0 + v1 * F::TILE, kb0 + k0 * F::TILE, ds,
+                             s1, dp1, m_t.lim, m_n.lim, la, scale_log2, w);
+        m_t = m_n;
+        e2 = e3;
+    }
+    wait_vm_all();  // the last iterations' copies land before the workgroup's LDS is released
+    mfma_drain();
+}
+
+// Blocks (query tile, part, kv head) over parts [part0, part0 + n_parts_l).  MASK selects the
+// per-element mask, needed only in the response part and at a partial last prompt page; the
+// host launches the two kinds of parts separately, so that each kernel holds one pipeline.
+template <int D, int NW, bool MASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(1, 1)))
-void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
+void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int part0, int n_parts_l, int n_blocks) {
     using F = TileShape<D>;
     constexpr int BM = 32 * NW;
     __shared__ __attribute__((aligned(1024))) char kbuf[3][F::TILE];
@@ -202,8 +252,8 @@ void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
     const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
     if (lb >= n_blocks) return;
     const int qtile = lb % n_qtiles;
-    const int part = (lb / n_qtiles) % a.n_parts;
-    const int kvh = lb / (n_qtiles * a.n_parts);
+    const int part = part0 + (lb / n_qtiles) % n_parts_l;
+    const int kvh = lb / (n_qtiles * n_parts_l);
     const bool resp = part == a.n_shards;
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -255,62 +305,13 @@ void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
 
     const int64_t lp0 = resp ? 0 : a.shard_lo[part];
     const KeyTiles<D, NW> kt(a, resp, lp0, kvh, w, lane);
-    auto mask_of = [&](int64_t t) {
-        const int valid = kt.valid(t);
-        const int64_t key0 = (lp0 + t) * kPage;
-        const bool need = valid < kPage || (resp && key0 + kPage - 1 > a.q_start + tok_min);
-        return page_mask(need, valid, key0, resp, vis_limit, h);
-    };
+    auto mask_of = [&](int64_t t) { return page_mask(kt.valid(t), (lp0 + t) * kPage, resp, vis_limit, h); };
 
     const uint32_t kb0 = lds_addr(kbuf[0]), vb0 = lds_addr(vbuf[0]);
     clear_lds(&kbuf[0][0], sizeof(kbuf), threadIdx.x, NW * 64);
     clear_lds(&vbuf[0][0], sizeof(vbuf), threadIdx.x, NW * 64);
     __syncthreads();
-    if (n_tiles > 0) {
-        // prologue: pages 0 and 1 in LDS; S, dP of page 0 and dS of its key tile 0
-        const int32_t e0 = kt.entry(0);
-        kt.copy(kt.tile(e0, 0, false), kt.valid(0), kb0, w);
-        kt.copy(kt.tile(e0, 0, true), kt.valid(0), vb0, w);
-        if (n_tiles > 1) {
-            const int32_t e1 = kt.entry(1);
-            kt.copy(kt.tile(e1, 1, false), kt.valid(1), kb0 + F::TILE, w);
-            kt.copy(kt.tile(e1, 1, true), kt.valid(1), vb0 + F::TILE, w);
-        }
-        // page-table entries are read through the scalar cache one iteration before their
-        // copies and clamped where they are used
-        int32_t e2 = n_tiles > 2 ? kt.entry(2) : 0;
-        wait_vm_all();
-        __syncthreads();
-        u32x4 ds[4];
-        f32x16 s1, dp1;
-        PageMask m_t = mask_of(0);
-        {
-            f32x16 s0, dp0;
-            tile_scores<D>(st, kb0 + la.k, vb0 + la.k, s0, dp0, [](int) {});
-            tile_scores<D>(st, kb0 + la.k + 32 * 2 * D, vb0 + la.k + 32 * 2 * D, s1, dp1, [&](int ks) {
-                               units_at<8, F::KS>(ks, [&](int un) {
-                                   ds_unit<true>(un, 0, s0, dp0, m_t.lim, st, a.scale_log2, ds);
-                               });
-                           });
-        }
-        for (int64_t t = 0; t < n_tiles; t++) {
-            // K(t+1), V(t+1) have landed; K buffer (t+2) % 3 and V buffer t % 2 were last read
-            // in iteration t-1.  The last iteration runs phase 1 on stale tiles; that result is
-            // never used.
-            const int32_t e3 = t + 3 < n_tiles ? kt.entry(t + 3) : 0;
-            wait_vm_all();
-            __syncthreads();
-            const int k0 = (int)(t % 3), k1 = k0 == 2 ? 0 : k0 + 1, k2 = k0 == 0 ? 2 : k0 - 1;
-            const int v0 = (int)(t & 1), v1 = v0 ^ 1;
-            const PageMask m_n = mask_of(t + 1);
-            dq_iter<true, D, NW>(st, kt, t, n_tiles - 1, t + 2 < n_tiles, e2, kb0 + k2 * F::TILE, vb0 + v0 * F::TILE,
-                                 kb0 + k1 * F::TILE, vb0 + v1 * F::TILE, kb0 + k0 * F::TILE, ds,
-                                 s1, dp1, m_t.lim, m_n.lim, la, a.scale_log2, w);
-            m_t = m_n;
-            e2 = e3;
-        }
-        wait_vm_all();  // the last iterations' copies land before the workgroup's LDS is released
-    }
+    if (n_tiles > 0) dq_pages<MASK, D, NW>(st, kt, n_tiles, mask_of, kb0, vb0, la, a.scale_log2, w);
     mfma_drain();
     if (!row_ok) return;
     float* dst = a.dq_parts + (((int64_t)part * a.n_rows + my_tok) * a.hq + my_head) * (int64_t)D;
@@ -328,6 +329,21 @@ void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int n_blocks) {
     }
 }
 
+template <int D, int NW>
+hipError_t launch_dq_d(const AttnArgs& a, const GroupRows& gr, int64_t n_qtiles, hipStream_t s) {
+    // prompt shards (masked only when the last prompt page is partial), then the response part
+    if (a.n_shards > 0) {
+        const int nb = (int)(n_qtiles * a.n_shards * a.hkv);
+        if (a.prefix_len % kPage != 0)
+            dq_mfma_kernel<D, NW, true><<<pad_grid(nb), NW * 64, 0, s>>>(a, gr, (int)n_qtiles, 0, a.n_shards, nb);
+        else
+            dq_mfma_kernel<D, NW, false><<<pad_grid(nb), NW * 64, 0, s>>>(a, gr, (int)n_qtiles, 0, a.n_shards, nb);
+    }
+    const int nb = (int)(n_qtiles * a.hkv);
+    dq_mfma_kernel<D, NW, true><<<pad_grid(nb), NW * 64, 0, s>>>(a, gr, (int)n_qtiles, a.n_shards, 1, nb);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_dq_mfma(const AttnArgs& a, const GroupRows& gr, hipStream_t s) {
@@ -335,16 +351,14 @@ hipError_t launch_dq_mfma(const AttnArgs& a, const GroupRows& gr, hipStream_t s)
     constexpr int BM = 32 * NW;
     const int64_t rows_total = a.n_rows * a.g;
     const int64_t n_qtiles = (rows_total + BM - 1) / BM;
-    const int64_t nb_q = n_qtiles * a.n_parts * a.hkv;
-    if (nb_q == 0) return hipSuccess;
+    if (n_qtiles * a.n_parts * a.hkv == 0) return hipSuccess;
     KernelTimer kt("dq_mfma", s);
     switch (a.d) {
-        case 64: dq_mfma_kernel<64, NW><<<pad_grid((int)nb_q), NW * 64, 0, s>>>(a, gr, (int)n_qtiles, (int)nb_q); break;
-        case 128: dq_mfma_kernel<128, NW><<<pad_grid((int)nb_q), NW * 64, 0, s>>>(a, gr, (int)n_qtiles, (int)nb_q); break;
-        case 256: dq_mfma_kernel<256, NW><<<pad_grid((int)nb_q), NW * 64, 0, s>>>(a, gr, (int)n_qtiles, (int)nb_q); break;
+        case 64: return launch_dq_d<64, NW>(a, gr, n_qtiles, s);
+        case 128: return launch_dq_d<128, NW>(a, gr, n_qtiles, s);
+        case 256: return launch_dq_d<256, NW>(a, gr, n_qtiles, s);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace ls
