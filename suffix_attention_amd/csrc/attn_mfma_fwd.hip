@@ -14,14 +14,14 @@
 //                                                  already in the layout of an MFMA operand
 //   output wave g  O^T[D x 32] += V(t-1)^T P(t-1)^T V read transposed from LDS
 //                                                  (ds_read_b64_tr_b16), O in AGPRs
-// Every page has two barriers: after the first the score waves multiply while the output
-// waves fetch P and issue all of the page's copies; after the second the output waves
-// multiply while the score waves run the softmax.  The copies sit with the output waves
-// because a wave issues at most about one instruction per four cycles: the score wave's
-// stream (scores, softmax) is the long one, and its length sets the pace of the page.  The two waves of a SIMD thus take turns on its matrix core, and each one's
-// vector work hides under the other's matrix work.  Splitting the roles also halves the
-// registers a wave needs (the 32 x D output tile alone is 128 registers at D = 256), which
-// is what lets two waves share a SIMD.
+// Every page has two barriers: between them the output waves fetch P(t-1) from LDS into
+// registers; after the second the score waves compute S(t) and its softmax (writing P(t)) while
+// the output waves issue the page's copies and multiply V(t-1) P(t-1), so both waves of a SIMD
+// keep its matrix core busy at once.  The copies sit with the output waves because a wave
+// issues at most about one instruction per four cycles and the score wave's stream (scores,
+// softmax) is the longer one.  Each wave's vector work hides under the other's matrix work.
+// Splitting the roles also halves the registers a wave needs (the 32 x D output tile alone is
+// 128 registers at D = 256), which is what lets two waves share a SIMD.
 //
 // Keys are permuted inside each 16-key MFMA step so that P^T needs no data movement: the
 // order is the same on both operands, so the sum is unchanged.
@@ -209,8 +209,8 @@ __device__ __forceinline__ void accumulate_pv(f32x16 (&o)[TileShape<D>::DT], con
 // inlined, the compiler knows the copies just issued cannot alias the tiles being read and
 // does not wait for them before each read.
 
-// Score role, iteration t < n_tiles: S(t) while the output waves fetch P(t-1) and issue the
-// copies; then the softmax of page t while they multiply.
+// Score role, iteration t < n_tiles: once the output waves hold P(t-1) (second barrier), S(t)
+// and the softmax of page t, while they multiply V(t-1) P(t-1).
 template <int D>
 __device__ __forceinline__ void score_iter(const AttnArgs& a, const PartInfo<D>& pi, int64_t t,
                                            uint32_t k_cur, char* __restrict__ p_out,
@@ -218,9 +218,9 @@ __device__ __forceinline__ void score_iter(const AttnArgs& a, const PartInfo<D>&
                                            float& m_ref, float& l, int64_t vis_limit, uint32_t lk, int lane) {
     wait_vm_all();
     lds_barrier();
+    lds_barrier();  // the output waves have fetched P(t-1): P(t) may be written from here on
     f32x16 s[2];
     scores<D>(qb, s, k_cur + lk);
-    lds_barrier();
     const int valid = pi.kt.valid(t);
     const int64_t key0 = (pi.lp0 + t) * kPage;
     if (valid < kPage || (pi.resp && key0 + kPage - 1 > a.q_start + pi.tok_min))
@@ -228,8 +228,9 @@ __device__ __forceinline__ void score_iter(const AttnArgs& a, const PartInfo<D>&
     softmax_page(s, m_ref, l, a.scale_log2, (LS_LDS char*)p_out, (LS_LDS float*)alpha_out, lane);
 }
 
-// Output role, iteration t >= 1: fetch P(t-1) while the score waves multiply; then rescale O
-// if a row's reference moved and accumulate V(t-1) P(t-1).
+// Output role, iteration t >= 1: fetch P(t-1); after the second barrier issue the copies,
+// rescale O if a row's reference moved and accumulate V(t-1) P(t-1), while the score waves
+// compute S(t) and its softmax on the same SIMDs.
 template <int D>
 __device__ __forceinline__ void output_iter(const AttnArgs& a, const PartInfo<D>& pi, int64_t t, int32_t phys_t,
                                             int32_t phys_t1, uint32_t k_dst, uint32_t v_dst,
@@ -239,12 +240,12 @@ __device__ __forceinline__ void output_iter(const AttnArgs& a, const PartInfo<D>
     using F = TileShape<D>;
     wait_vm_all();
     lds_barrier();
-    issue_copies<D>(pi.kt, pi.n_tiles, t, phys_t, phys_t1, k_dst, v_dst, w);
     bf16x8 pb[4];
 #pragma unroll
     for (int ku = 0; ku < 4; ku++) pb[ku] = *(const LS_LDS bf16x8*)((const LS_LDS char*)p_in + (ku * 64 + lane) * 16);
     const float alpha = ((const LS_LDS float*)alpha_in)[lane & 31];
-    lds_barrier();
+    lds_barrier();  // P(t-1) is in registers: the score waves may overwrite it
+    issue_copies<D>(pi.kt, pi.n_tiles, t, phys_t, phys_t1, k_dst, v_dst, w);
     if (!__all(alpha == 1.f)) {
         mfma_drain();
 #pragma unroll
@@ -362,8 +363,8 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
             const int32_t phys_t2 = 2 < n_tiles ? kt.entry(2) : 0;
             wait_vm_all();
             lds_barrier();
-            issue_copies<D>(kt, n_tiles, 0, phys_t, phys_t1, lds_addr(L.kb[1]), lds_addr(L.vb[0]), g);
             lds_barrier();
+            issue_copies<D>(kt, n_tiles, 0, phys_t, phys_t1, lds_addr(L.kb[1]), lds_addr(L.vb[0]), g);
             phys_t = phys_t1;
             phys_t1 = phys_t2;
         }
