@@ -97,10 +97,12 @@ def ingest_counters(cfg_name: str, kernel: str, fetch_dir: str, write_dir: str, 
     """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE on the benchmark and on
     --calibrate-copy) into the traffic summary that the benchmark reports."""
     def per_launch(d, counter, match):
-        sums = _counter_sums(d, counter)
-        vals = [v for name, vs in sums.items() if match(name) for v in vs]
-        assert vals, (d, counter)
-        return sum(vals) / len(vals), len(vals)
+        # one library call of the kernel may dispatch several instantiations (the matrix
+        # passes launch masked and unmasked parts separately): sum them per call
+        sums = {name: vs for name, vs in _counter_sums(d, counter).items() if match(name)}
+        assert sums, (d, counter)
+        calls = max(len(vs) for vs in sums.values())
+        return sum(v for vs in sums.values() for v in vs) / calls, calls
 
     def biggest(d, counter):
         sums = _counter_sums(d, counter)
