@@ -181,9 +181,9 @@ __device__ __forceinline__ void softmax_page(f32x16 (&s)[2], float& m_ref, float
 // O^T += V^T P^T over one page.  Step st = (ku, dt) with dt fastest, so consecutive MFMAs
 // accumulate into different tiles; V^T fragments (rows 32kt + 16u + 8e) are read PV steps
 // ahead.
-template <int D>
-__device__ __forceinline__ void accumulate_pv(f32x16 (&o)[TileShape<D>::DT], const bf16x8 (&pb)[4],
-                                              uint32_t sv) {
+template <int D, typename Beside>
+__device__ __forceinline__ void accumulate_pv(f32x16 (&o)[TileShape<D>::DT], const bf16x8 (&pb)[4], uint32_t sv,
+                                              Beside&& beside) {
     using F = TileShape<D>;
     constexpr int NST = 4 * F::DT;
     constexpr int PV = 4;
@@ -202,6 +202,8 @@ __device__ __forceinline__ void accumulate_pv(f32x16 (&o)[TileShape<D>::DT], con
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[st % PV], vhi[st % PV], 0, 1, 2, 3, 4, 5, 6, 7));
         if (st + PV < NST) read_v(st + PV, vlo[st % PV], vhi[st % PV]);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ku], o[dt], 0, 0, 0);
+        beside(st);  // this step's share of the copies, beside the matrix work
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -220,7 +222,11 @@ __device__ __forceinline__ void score_iter(const AttnArgs& a, const PartInfo<D>&
     lds_barrier();
     lds_barrier();  // the output waves have fetched P(t-1): P(t) may be written from here on
     f32x16 s[2];
+    // the scores go first on the shared matrix core: the softmax waits for them, while the
+    // output wave's products can fill in behind
+    __builtin_amdgcn_s_setprio(2);
     scores<D>(qb, s, k_cur + lk);
+    __builtin_amdgcn_s_setprio(0);
     const int valid = pi.kt.valid(t);
     const int64_t key0 = (pi.lp0 + t) * kPage;
     if (valid < kPage || (pi.resp && key0 + kPage - 1 > a.q_start + pi.tok_min))
@@ -245,7 +251,6 @@ __device__ __forceinline__ void output_iter(const AttnArgs& a, const PartInfo<D>
     for (int ku = 0; ku < 4; ku++) pb[ku] = *(const LS_LDS bf16x8*)((const LS_LDS char*)p_in + (ku * 64 + lane) * 16);
     const float alpha = ((const LS_LDS float*)alpha_in)[lane & 31];
     lds_barrier();  // P(t-1) is in registers: the score waves may overwrite it
-    issue_copies<D>(pi.kt, pi.n_tiles, t, phys_t, phys_t1, k_dst, v_dst, w);
     if (!__all(alpha == 1.f)) {
         mfma_drain();
 #pragma unroll
@@ -254,7 +259,20 @@ __device__ __forceinline__ void output_iter(const AttnArgs& a, const PartInfo<D>
             for (int i = 0; i < 16; i++) o[dt][i] = agpr_scaled(o[dt][i], alpha);
         agpr_write_gap();
     }
-    accumulate_pv<D>(o, pb, v_prev + lv);
+    // K(t+1) and V(t) are copied one piece per step over the first steps, so that issuing them
+    // never holds up the matrix work.  Past the last tile the last one is copied again, into a
+    // buffer nothing reads, so that the steps carry no branch.
+    constexpr int PW = OutTiles<D>::PER_WAVE;
+    const int64_t last = pi.n_tiles - 1;
+    const bool ck = t + 1 < pi.n_tiles, cv = t < pi.n_tiles;
+    const int64_t tk = ck ? t + 1 : last, tv = cv ? t : last;
+    const char* ksrc = pi.kt.tile(ck ? phys_t1 : 0, tk, false);
+    const char* vsrc = pi.kt.tile(cv ? phys_t : 0, tv, true);
+    const int vk = pi.kt.valid(tk), vv = pi.kt.valid(tv);
+    accumulate_pv<D>(o, pb, v_prev + lv, [&](int st) {
+        if (st < PW) pi.kt.copy_piece(ksrc, vk, k_dst, w, st);
+        else if (st < 2 * PW) pi.kt.copy_piece(vsrc, vv, v_dst, w, st - PW);
+    });
 }
 
 template <int D>
@@ -378,6 +396,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
             phys_t = phys_t1;
             phys_t1 = phys_t2;
         }
+        wait_vm_all();  // the last iterations' copies land before the workgroup's LDS is released
         lds_barrier();
         const float l_tot = fin_grp[n];
         mfma_drain();
