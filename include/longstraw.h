@@ -166,6 +166,32 @@ int ls_replay_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
                   float* lse, void* workspace, size_t ws_bytes, ls_stream_t stream);
 
 /*
+ * ls_score_fwd -- forward-only scoring of several members' whole responses against the same
+ * captured prompt, in one launch (digest, "Method", step 2, pre-step scoring; explainer, "The
+ * move: change the graph boundary": the old- and reference-policy passes need no autograd
+ * graph, so nothing is kept for a backward and the members' rows can share every pass over
+ * the prompt pages).
+ *
+ * Member m's row i (response position i) sees every prompt key and the member's own response
+ * keys [0, i].  Each member's result equals ls_replay_fwd of its rows with q_start = 0 (the
+ * matrix-core path gives the same bits).
+ *
+ *   n_members       >= 0.
+ *   q               device [n_members, n_rows, hq, d] of pre->dtype.
+ *   k_resp, v_resp  device [n_members, n_rows, hkv, d] of pre->dtype.
+ *   o               device [n_members, n_rows, hq, d] of pre->dtype (written).
+ *   lse             device float32 [n_members, n_rows, hq] (written).
+ *   workspace       device, ws_bytes >= ls_score_workspace_bytes(pre, n_members, n_rows); its
+ *                   layout is the forward one for n_members * n_rows rows, member-major.
+ * The members' rows together obey the block-size limit of ls_fwd_workspace_bytes.
+ * Errors as for ls_replay_fwd.
+ */
+size_t ls_score_workspace_bytes(const ls_prefix_t* pre, int64_t n_members, int64_t n_rows);
+int ls_score_fwd(const ls_prefix_t* pre, int64_t n_members, const void* q, int64_t n_rows,
+                 const void* k_resp, const void* v_resp, void* o, float* lse, void* workspace,
+                 size_t ws_bytes, ls_stream_t stream);
+
+/*
  * ls_replay_bwd -- backward of one replayed response block for the loss sum(O * dO)
  * (digest, "Method", step 3: backpropagate and accumulate; explainer, "Two incompatible
  * architectures": response blocks replayed in reverse, K/V gradient pages allocated when

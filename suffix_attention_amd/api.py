@@ -189,6 +189,37 @@ def replay_fwd(prefix: Prefix, q: torch.Tensor, q_start: int, k_resp: torch.Tens
     return o, lse, ws
 
 
+def score_workspace_bytes(prefix: Prefix, n_members: int, n_rows: int) -> int:
+    st = prefix.struct()
+    n = lib().ls_score_workspace_bytes(C.byref(st), n_members, n_rows)
+    if n == 0 and n_members * n_rows > 0:
+        raise LongStrawError(_lib.LS_ERR_INVALID, lib().ls_last_error().decode())
+    return n
+
+
+def score_fwd(prefix: Prefix, q: torch.Tensor, k_resp: torch.Tensor, v_resp: torch.Tensor,
+              workspace: torch.Tensor | None = None, o: torch.Tensor | None = None,
+              lse: torch.Tensor | None = None):
+    """Forward-only scoring of several members' whole responses, batched: q is
+    [members, rows, hq, d], k_resp / v_resp [members, rows, hkv, d].  Returns (o, lse, workspace)
+    with o [members, rows, hq, d] and lse [members, rows, hq]."""
+    _dev(q, "q", dtype=prefix.dtype)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [members, rows, hq, d], got {tuple(q.shape)}")
+    n_members, n_rows = q.shape[0], q.shape[1]
+    _dev(k_resp, "k_resp", dtype=prefix.dtype, shape=(n_members, n_rows, prefix.hkv, prefix.d))
+    _dev(v_resp, "v_resp", dtype=prefix.dtype, shape=k_resp.shape)
+    o = torch.empty_like(q) if o is None else _dev(o, "o", dtype=prefix.dtype, shape=q.shape)
+    if lse is None:
+        lse = torch.empty((n_members, n_rows, prefix.hq), dtype=torch.float32, device=q.device)
+    _dev(lse, "lse", dtype=torch.float32, shape=(n_members, n_rows, prefix.hq))
+    ws = _workspace(score_workspace_bytes(prefix, n_members, n_rows), q.device, workspace)
+    st = prefix.struct()
+    check(lib().ls_score_fwd(C.byref(st), n_members, _ptr(q), n_rows, _ptr(k_resp), _ptr(v_resp), _ptr(o), _ptr(lse),
+                             _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return o, lse, ws
+
+
 def replay_bwd(prefix: Prefix, q, q_start: int, k_resp, v_resp, o, lse, dout, dk_resp, dv_resp,
                resp_first_touch: bool, dk_pages, dv_pages, shard_first_touch=None,
                workspace: torch.Tensor | None = None, dq: torch.Tensor | None = None):

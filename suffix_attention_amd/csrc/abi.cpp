@@ -118,6 +118,8 @@ ls::AttnArgs make_args(const ls_prefix_t* p, const void* q, int64_t n_rows, int6
     a.n_shards = p->n_shards;
     a.n_parts = p->n_shards + 1;
     for (int s = 0; s <= p->n_shards; s++) a.shard_lo[s] = p->shard_page_bounds[s];
+    a.n_members = 1;
+    a.part_rows = n_rows;
     return a;
 }
 
@@ -223,6 +225,58 @@ int ls_replay_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
                                                                      : ls::launch_fwd_generic(pre->dtype, a, s);
     if (e != hipSuccess) return hip_fail(e, "forward kernel");
     e = ls::launch_lse_merge(a.n_parts, rows, pre->d, a.o_parts, a.lse_parts, o, pre->dtype, lse, s);
+    return e == hipSuccess ? LS_OK : hip_fail(e, "LSE merge kernel");
+}
+
+size_t ls_score_workspace_bytes(const ls_prefix_t* pre, int64_t n_members, int64_t n_rows) {
+    g_err.clear();
+    if (check_prefix(pre) != LS_OK) return 0;
+    if (n_members < 0 || n_rows < 0) {
+        fail(LS_ERR_INVALID, "n_members=%lld, n_rows=%lld must be >= 0", (long long)n_members, (long long)n_rows);
+        return 0;
+    }
+    return fwd_ws(pre, n_members * n_rows);
+}
+
+int ls_score_fwd(const ls_prefix_t* pre, int64_t n_members, const void* q, int64_t n_rows, const void* k_resp,
+                 const void* v_resp, void* o, float* lse, void* workspace, size_t ws_bytes, ls_stream_t stream) {
+    g_err.clear();
+    int rc = check_prefix(pre);
+    if (rc != LS_OK) return rc;
+    if (n_members < 0) return fail(LS_ERR_INVALID, "n_members=%lld < 0", (long long)n_members);
+    // the members' rows together must fit one block's limits
+    rc = check_block(pre, q, n_members * n_rows, 0, k_resp, v_resp, n_members * n_rows);
+    if (rc != LS_OK) return rc;
+    if (n_members * n_rows == 0) return LS_OK;
+    if (!o || !lse) return fail(LS_ERR_INVALID, "o/lse is NULL");
+    const size_t need = fwd_ws(pre, n_members * n_rows);
+    if (!workspace || ws_bytes < need)
+        return fail(LS_ERR_WORKSPACE, "scoring workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+    ls::AttnArgs a = make_args(pre, q, n_rows, 0, k_resp, v_resp);
+    const int64_t all_rows = n_members * n_rows;
+    a.part_rows = all_rows;
+    a.resp_member_elems = n_rows * pre->hkv * pre->d;
+    a.o_parts = (float*)workspace;
+    a.lse_parts = a.o_parts + (size_t)a.n_parts * all_rows * pre->hq * pre->d;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (pre->dtype == LS_DTYPE_BF16 && !force_generic()) {
+        a.n_members = n_members;  // one launch over every member's rows
+        e = ls::launch_fwd_mfma(a, s);
+    } else {
+        // the exact f32 path runs the members one launch at a time into the same parts
+        const size_t esz = pre->dtype == LS_DTYPE_BF16 ? 2 : 4;
+        for (int64_t m = 0; m < n_members && e == hipSuccess; m++) {
+            ls::AttnArgs am = a;
+            am.q = (const char*)q + (size_t)(m * n_rows * pre->hq * pre->d) * esz;
+            am.k_resp = (const char*)k_resp + (size_t)(m * a.resp_member_elems) * esz;
+            am.v_resp = (const char*)v_resp + (size_t)(m * a.resp_member_elems) * esz;
+            am.row0 = m * n_rows;
+            e = ls::launch_fwd_generic(pre->dtype, am, s);
+        }
+    }
+    if (e != hipSuccess) return hip_fail(e, "scoring forward kernel");
+    e = ls::launch_lse_merge(a.n_parts, all_rows * pre->hq, pre->d, a.o_parts, a.lse_parts, o, pre->dtype, lse, s);
     return e == hipSuccess ? LS_OK : hip_fail(e, "LSE merge kernel");
 }
 

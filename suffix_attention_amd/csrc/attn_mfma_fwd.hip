@@ -275,15 +275,19 @@ __device__ __forceinline__ void output_iter(const AttnArgs& a, const PartInfo<D>
     });
 }
 
+// Blocks (query tile, part, kv head); the query tiles of each member (pre-step scoring runs
+// several members' blocks at once) are numbered member-major, n_qtiles_m per member.
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kNW * 64, kNW * 64), amdgpu_waves_per_eu(2, 2)))
-void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
+void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles, int n_blocks) {
     using F = TileShape<D>;
     __shared__ __attribute__((aligned(1024))) FwdLds<D> L;
 
     const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
     if (lb >= n_blocks) return;
-    const int qtile = lb % n_qtiles;
+    const int qtile_g = lb % n_qtiles;
+    const int member = qtile_g / n_qtiles_m;
+    const int qtile = qtile_g % n_qtiles_m;
     const int part = (lb / n_qtiles) % a.n_parts;
     const int kvh = lb / (n_qtiles * a.n_parts);
     const bool resp = part == a.n_shards;
@@ -300,6 +304,8 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
     const bool row_ok = my_row < rows_total;
     const int64_t my_tok = my_row / a.g;
     const int my_head = kvh * a.g + (int)(my_row % a.g);
+    const int64_t tok_base = (int64_t)member * a.n_rows;          // the member's first row in q
+    const int64_t out_row0 = a.row0 + tok_base;                     // ... and in the parts arrays
 
     // keys of this part
     const int64_t lp0 = resp ? 0 : a.shard_lo[part];
@@ -313,7 +319,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
     }
 
     // output wave g copies share g of every tile; the score waves use kt only for valid()
-    PartInfo<D> pi{OutTiles<D>(a, resp, lp0, kvh, g, lane)};
+    PartInfo<D> pi{OutTiles<D>(a, resp, lp0, kvh, g, lane, (int64_t)member * a.resp_member_elems * 2)};
     const OutTiles<D>& kt = pi.kt;
     pi.resp = resp;
     pi.lp0 = lp0;
@@ -338,7 +344,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
             const int64_t ld_row = row_ok ? my_row : rows_total - 1;
             const int64_t ld_tok = ld_row / a.g;
             const int ld_head = kvh * a.g + (int)(ld_row % a.g);
-            const bf16_t* qrow = (const bf16_t*)a.q + (ld_tok * a.hq + ld_head) * (int64_t)D + 8 * h;
+            const bf16_t* qrow = (const bf16_t*)a.q + ((tok_base + ld_tok) * a.hq + ld_head) * (int64_t)D + 8 * h;
 #pragma unroll
             for (int ks = 0; ks < F::KS; ks++) qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * ks));
             // read-only MFMA operand: keep it in AGPRs (after all loads are in flight)
@@ -361,7 +367,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
         if (lane < 32) fin_grp[lane] = l_tot;
         lds_barrier();
         if (row_ok && h == 0)
-            a.lse_parts[((int64_t)part * a.n_rows + my_tok) * a.hq + my_head] =
+            a.lse_parts[((int64_t)part * a.part_rows + out_row0 + my_tok) * a.hq + my_head] =
                 l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
     } else {
         f32x16 o[F::DT];
@@ -402,7 +408,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
         mfma_drain();
         if (row_ok) {
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-            float* dst = a.o_parts + (((int64_t)part * a.n_rows + my_tok) * a.hq + my_head) * (int64_t)D;
+            float* dst = a.o_parts + (((int64_t)part * a.part_rows + out_row0 + my_tok) * a.hq + my_head) * (int64_t)D;
 #pragma unroll
             for (int dt = 0; dt < F::DT; dt++) {
                 // normalise in place in the AGPRs; the stores read them from there
@@ -421,12 +427,13 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles, int n_blocks) {
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
-    const int64_t n_qtiles = (a.n_rows * a.g + kBM - 1) / kBM;
+    const int64_t n_qtiles_m = (a.n_rows * a.g + kBM - 1) / kBM;
+    const int64_t n_qtiles = n_qtiles_m * a.n_members;
     const int64_t n_blocks = n_qtiles * a.n_parts * a.hkv;
     if (n_blocks == 0) return hipSuccess;
     const int grid = pad_grid((int)n_blocks);
     KernelTimer kt("fwd_mfma", s);
-    fwd_mfma_kernel<D><<<grid, kNW * 64, 0, s>>>(a, (int)n_qtiles, (int)n_blocks);
+    fwd_mfma_kernel<D><<<grid, kNW * 64, 0, s>>>(a, (int)n_qtiles_m, (int)n_qtiles, (int)n_blocks);
     return hipGetLastError();
 }
 

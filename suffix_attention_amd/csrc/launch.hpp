@@ -31,9 +31,18 @@ struct AttnArgs {
     int n_shards;
     int n_parts;
     int64_t shard_lo[kMaxShards + 1];
-    // forward products
-    float* o_parts;    // [n_parts, n_rows, hq, d]
-    float* lse_parts;  // [n_parts, n_rows, hq]
+    // Pre-step scoring runs the blocks of n_members members in one forward (1 for a replay):
+    // member m's rows follow member m-1's in q; its response keys start resp_member_elems
+    // elements after member m-1's.
+    int64_t n_members;
+    int64_t resp_member_elems;
+    // forward products; part p holds rows [p * part_rows, (p + 1) * part_rows), of which this
+    // launch writes part_rows from row0 on (part_rows = n_members * n_rows, row0 = 0, unless a
+    // host loop runs the members one launch at a time)
+    int64_t part_rows;
+    int64_t row0;
+    float* o_parts;    // [n_parts, part_rows, hq, d]
+    float* lse_parts;  // [n_parts, part_rows, hq]
     // backward
     const void* o;
     const void* dout;

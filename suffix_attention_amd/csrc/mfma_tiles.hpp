@@ -58,7 +58,9 @@ struct KeyTiles {
     bool resp;
     uint32_t off[PER_WAVE]; // this lane's byte offset in a full tile, copy j
 
-    __device__ __forceinline__ KeyTiles(const AttnArgs& a, bool resp_, int64_t lp0, int kvh, int w, int lane) {
+    // resp_off: bytes from the response keys of the launch to those of this workgroup's member
+    __device__ __forceinline__ KeyTiles(const AttnArgs& a, bool resp_, int64_t lp0, int kvh, int w, int lane,
+                                        int64_t resp_off = 0) {
         resp = resp_;
         n_phys = (int32_t)a.n_phys;
         if (!resp) {
@@ -68,8 +70,8 @@ struct KeyTiles {
             row_bytes = D * 2;
             keys = a.prefix_len - lp0 * kPage;
         } else {
-            kbase = (const char*)a.k_resp + (int64_t)kvh * D * 2;
-            vbase = (const char*)a.v_resp + (int64_t)kvh * D * 2;
+            kbase = (const char*)a.k_resp + resp_off + (int64_t)kvh * D * 2;
+            vbase = (const char*)a.v_resp + resp_off + (int64_t)kvh * D * 2;
             tile_bytes = (int64_t)kPage * a.hkv * D * 2;
             row_bytes = (uint32_t)a.hkv * D * 2;
             keys = a.key_end;

@@ -104,6 +104,23 @@ def test_workspace_size_and_errors():
     assert "multiple" in _err()
 
 
+def test_score_workspace_and_validation():
+    """Batched scoring: the workspace is the forward one for members * rows rows; bad sizes,
+    missing outputs and short workspaces are rejected before any launch."""
+    p = _prefix()
+    lib = _lib.lib()
+    assert lib.ls_score_workspace_bytes(C.byref(p), 3, 16) == lib.ls_fwd_workspace_bytes(C.byref(p), 48)
+    assert lib.ls_score_workspace_bytes(C.byref(p), -1, 16) == 0 and "n_members" in _err()
+    need = lib.ls_score_workspace_bytes(C.byref(p), 2, 16)
+    score = lambda **kw: lib.ls_score_fwd(C.byref(p), kw.get("m", 2), kw.get("q", FAKE), 16, FAKE, FAKE,  # noqa: E731
+                                          kw.get("o", FAKE), FAKE, kw.get("ws", FAKE), kw.get("ws_bytes", need), None)
+    assert score(m=-1) == LS_ERR_INVALID
+    assert score(q=None) == LS_ERR_INVALID
+    assert score(o=None) == LS_ERR_INVALID
+    assert score(ws_bytes=need - 1) == LS_ERR_WORKSPACE
+    assert score(m=0, ws=None, ws_bytes=0) == 0  # nothing to score
+
+
 def test_empty_block_is_a_no_op():
     assert _fwd(_prefix(), n_rows=0, n_resp=0, ws=None, ws_bytes=0) == 0
 
