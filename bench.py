@@ -35,6 +35,8 @@ if ROOT not in sys.path:
 from suffix_attention_amd import api, configs, datagen, driver  # noqa: E402
 
 METRIC = "replay-attention fwd+bwd TFLOP/s and % bf16 MFMA peak at P=2M, G=8"
+# --workload score: the pre-step scoring pass (forward only, all G members batched)
+SCORE_METRIC = "pre-step scoring (forward-only, G members batched) TFLOP/s and % bf16 MFMA peak at P=2M, G=8"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 
@@ -190,6 +192,86 @@ def cpu_baseline(cfg, kp, vp, member, n_tok=64):
                       f"keys; counted with the same 14*Hq*d*pairs convention"}
 
 
+def cpu_baseline_score(cfg, kp, vp, member, n_tok=64):
+    """The oracle forward, untuned, on a bounded sample: the last n_tok response rows of member 0
+    (all heads) against prompt shard 0 and the response keys those rows see."""
+    from oracle import attention as orc  # test infrastructure; used only for this baseline leg
+
+    shard_tokens = min(cfg.P, (cfg.n_pages // cfg.S) * 64)
+    q_start = cfg.R - n_tok
+    to_np = lambda t: t.to("cpu", torch.float32).numpy()  # noqa: E731
+    kps, vps = to_np(kp[:shard_tokens]), to_np(vp[:shard_tokens])
+    kr, vr = to_np(member["kr"]), to_np(member["vr"])
+    q = to_np(member["q"][q_start:])
+    t0 = time.perf_counter()
+    orc.forward(q, kps, vps, kr, vr, q_start)
+    dt = time.perf_counter() - t0
+    flops = 4 * cfg.hq * cfg.d * configs.pairs(n_tok, q_start, shard_tokens)
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 3), "blas_threads": int(os.environ.get("OMP_NUM_THREADS", cores)),
+            "sample": f"float64 numpy oracle forward of the last {n_tok} response rows (all {cfg.hq} heads) of "
+                      f"member 0 over prompt shard 0 ({shard_tokens} keys) plus their {cfg.R} causal response "
+                      f"keys; counted as 4*Hq*d*pairs"}
+
+
+def bench_score(ns, cfg, dev, prefix, kp, vp, members):
+    """Pre-step scoring: every member's whole response, forward only, in one batched call per
+    step (ls_score_fwd)."""
+    q = torch.stack([m["q"] for m in members])
+    kr = torch.stack([m["kr"] for m in members])
+    vr = torch.stack([m["vr"] for m in members])
+    o, lse, ws = api.score_fwd(prefix, q, kr, vr)  # allocates outputs and workspace once
+    for _ in range(ns.warmup):
+        api.score_fwd(prefix, q, kr, vr, workspace=ws, o=o, lse=lse)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    api.profile_begin()
+    ev0.record()
+    for _ in range(ns.steps):
+        api.score_fwd(prefix, q, kr, vr, workspace=ws, o=o, lse=lse)
+    ev1.record()
+    torch.cuda.synchronize()
+    kstats = api.profile_end()
+    ms = ev0.elapsed_time(ev1)
+    pairs = configs.pairs(cfg.R, 0, cfg.P)
+    flops_step = cfg.G * 4 * cfg.hq * cfg.d * pairs
+    tflops = flops_step * ns.steps / (ms / 1e3) / 1e12
+    kern = {k: {"launches": v[0], "total_ms": round(v[1], 3), "mean_ms": round(v[1] / max(1, v[0]), 4)}
+            for k, v in kstats.items()}
+    achieved = ns.steps * flops_step / (kern["fwd_mfma"]["total_ms"] / 1e3) / 1e12
+    out = {
+        "metric": SCORE_METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": ns.steps,
+        "warmup": ns.warmup,
+        "ms_per_step": round(ms / ns.steps, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} scoring: one attention layer, P={cfg.P} prompt tokens in 64-token pages "
+                               f"with a seeded permuted page table, S={cfg.S} shards, G={cfg.G} members x R={cfg.R} "
+                               f"response rows scored forward-only in one batched call, Hq={cfg.hq}, "
+                               f"Hkv={cfg.hkv}, d={cfg.d}, N(0,1) inputs",
+                   "P": cfg.P, "R": cfg.R, "G": cfg.G, "S": cfg.S, "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "counted_tflop_per_step": round(flops_step / 1e12, 3),
+        "roofline": {"bound": "mfma", "kernel": "fwd_mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "flops_per_unit": "4*d per visible (row, key) pair and query head",
+                     "mean_launch_ms": kern["fwd_mfma"]["mean_ms"]},
+        "kernels": kern,
+        "peak_mem_gb": round(torch.cuda.max_memory_allocated(dev) / 1e9, 3),
+    }
+    if not ns.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_score(cfg, kp, vp, members[0])
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +279,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="c2m", choices=sorted(configs.CONFIGS))
     ap.add_argument("--G", type=int, default=None, help="override the group size")
+    ap.add_argument("--workload", default="replay", choices=["replay", "score"],
+                    help="replay: the fwd+bwd step (the headline); score: batched forward-only scoring")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a device copy of known size (for HBM counter calibration)")
@@ -228,6 +312,9 @@ def main():
     members = [datagen.member_inputs(cfg, i, dev) for i in range(cfg.G)]
     torch.cuda.synchronize()
     log(f"[bench] prefix captured ({cfg.n_pages} pages), {cfg.G} members resident")
+    if ns.workload == "score":
+        bench_score(ns, cfg, dev, prefix, kp, vp, members)
+        return
 
     if ns.warmup > 0:
         t = time.perf_counter()

@@ -75,3 +75,37 @@ def test_score_promptless_and_single_row():
     cs = _members(3, 130, 1, 6, 1, 256, torch.bfloat16, S=2, seed=71)
     o, lse = _score(cs, cs[0].prefix())
     _check_oracle(cs, o, lse)
+
+
+def test_score_at_2m_tokens_equals_replay_and_oracle_rows():
+    """The 2M-token prompt (c2m shape, permuted pages, 8 shards), two members batched: each
+    member's rows equal its own replay forward bit for bit, and sampled rows equal the oracle
+    computed one row at a time over all prompt and response keys."""
+    from suffix_attention_amd import configs, datagen
+
+    cfg = configs.CONFIGS["c2m"]
+    R = 256
+    log(f"case: score at P={cfg.P}, 2 members x {R} rows")
+    dev = "cuda"
+    table = datagen.page_table(cfg.n_pages, datagen.seed(cfg.cfg_id, datagen.TAG_PERM), dev)
+    kp, vp = datagen.prefix_kv(cfg, dev)
+    k_pages, v_pages = api.capture_pages(kp, vp, table, cfg.n_pages)
+    pre = api.Prefix(cfg.hq, cfg.hkv, cfg.d, cfg.dtype, cfg.P, table, k_pages, v_pages,
+                     api.even_shard_bounds(cfg.n_pages, cfg.S))
+    ms = [datagen.member_inputs(cfg, i, dev) for i in range(2)]
+    q = torch.stack([m["q"][:R] for m in ms])
+    kr = torch.stack([m["kr"][:R] for m in ms])
+    vr = torch.stack([m["vr"][:R] for m in ms])
+    o, lse, ws = api.score_fwd(pre, q, kr, vr)
+    del ws
+    torch.cuda.synchronize()
+    for i in range(2):
+        o1, l1, ws1 = api.replay_fwd(pre, q[i].contiguous(), 0, kr[i].contiguous(), vr[i].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(o[i], o1) and torch.equal(lse[i], l1), f"member {i}"
+        del ws1
+    kp_h, vp_h = np32(kp), np32(vp)
+    for i, row in ((0, 0), (0, R - 1), (1, 97)):
+        O, L = orc.forward(np32(q[i, row:row + 1]), kp_h, vp_h, np32(kr[i]), np32(vr[i]), row)
+        assert_close(f"O[{i},{row}]", np32(o[i, row:row + 1]), O)
+        assert_close(f"LSE[{i},{row}]", np32(lse[i, row:row + 1]), L)
