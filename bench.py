@@ -37,6 +37,10 @@ from suffix_attention_amd import api, configs, datagen, driver  # noqa: E402
 METRIC = "replay-attention fwd+bwd TFLOP/s and % bf16 MFMA peak at P=2M, G=8"
 # --workload score: the pre-step scoring pass (forward only, all G members batched)
 SCORE_METRIC = "pre-step scoring (forward-only, G members batched) TFLOP/s and % bf16 MFMA peak at P=2M, G=8"
+# --workload prefill: capture-side prefill (the prompt's causal attention, chunked, pages written)
+PREFILL_METRIC = "capture-side prefill (no-grad causal attention, chunked) TFLOP/s and % bf16 MFMA peak"
+# --workload reuse: consecutive optimizer cycles over one capture
+REUSE_METRIC = "prefix-reuse fwd+bwd TFLOP/s over consecutive G=8 cycles on one capture at P=4,456,448"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 
@@ -158,13 +162,24 @@ def block_pairs(cfg):
     return out
 
 
-def run_steps(prefix, members, cfg, n):
+def run_steps(prefix, members, cfg, n, cycle_log=None):
+    """n optimizer cycles: each a fresh group (gradient pages allocated at its first backward,
+    released at its end) replaying every member.  cycle_log, if given, receives (ms, peak bytes)
+    per cycle (events on the stream; each cycle ends with a synchronisation)."""
     last = None
     for _ in range(n):
         last = None  # release the previous group's gradient pages before allocating anew
+        if cycle_log is not None:
+            torch.cuda.reset_peak_memory_stats()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
         grp = driver.GroupReplay(prefix)
         results = [grp.replay_member(m["q"], m["kr"], m["vr"], m["do"], cfg.B, keep="none") for m in members]
         last = (grp, results)
+        if cycle_log is not None:
+            e1.record()
+            torch.cuda.synchronize()
+            cycle_log.append((e0.elapsed_time(e1), torch.cuda.max_memory_allocated()))
     return last
 
 
@@ -272,6 +287,49 @@ def bench_score(ns, cfg, dev, prefix, kp, vp, members):
     print(json.dumps(out), flush=True)
 
 
+def bench_prefill(ns, cfg, dev):
+    """Capture-side prefill of a P-token prompt in chunks (driver.prefill_capture): counted as
+    4*Hq*d per causal (row, key) pair."""
+    P, chunk = ns.prefill_tokens, ns.prefill_chunk
+    q = datagen.normal((P, cfg.hq, cfg.d), datagen.seed(cfg.cfg_id, 900), cfg.dtype, dev)
+    k = datagen.normal((P, cfg.hkv, cfg.d), datagen.seed(cfg.cfg_id, 901), cfg.dtype, dev)
+    v = datagen.normal((P, cfg.hkv, cfg.d), datagen.seed(cfg.cfg_id, 902), cfg.dtype, dev)
+    n_pages = api.n_logical_pages(P)
+    table = datagen.page_table(n_pages, datagen.seed(cfg.cfg_id, 903), dev)
+    for _ in range(ns.warmup):
+        driver.prefill_capture(q, k, v, table, n_pages, chunk, n_shards=cfg.S, keep_o=False)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    api.profile_begin()
+    ev0.record()
+    for _ in range(ns.steps):
+        pre, _, _ = driver.prefill_capture(q, k, v, table, n_pages, chunk, n_shards=cfg.S, keep_o=False)
+    ev1.record()
+    torch.cuda.synchronize()
+    kstats = api.profile_end()
+    ms = ev0.elapsed_time(ev1)
+    flops_step = 4 * cfg.hq * cfg.d * configs.pairs(P, 0, 0)
+    tflops = flops_step * ns.steps / (ms / 1e3) / 1e12
+    kern = {k_: {"launches": v_[0], "total_ms": round(v_[1], 3), "mean_ms": round(v_[1] / max(1, v_[0]), 4)}
+            for k_, v_ in kstats.items()}
+    achieved = ns.steps * flops_step / (kern["fwd_mfma"]["total_ms"] / 1e3) / 1e12
+    out = {"metric": PREFILL_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": ns.steps,
+           "warmup": ns.warmup, "ms_per_step": round(ms / ns.steps, 2), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16" if cfg.dtype == torch.bfloat16 else "f32", "data": "synthetic",
+           "config": {"workload": f"prefill: P={P} prompt tokens of one attention layer in chunks of {chunk}, each "
+                                  f"attending to the pages captured so far ({cfg.S} shards) plus itself causally, "
+                                  f"then captured; Hq={cfg.hq}, Hkv={cfg.hkv}, d={cfg.d}, N(0,1) inputs",
+                      "P": P, "chunk": chunk, "S": cfg.S, "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d},
+           "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+           "counted_tflop_per_step": round(flops_step / 1e12, 3),
+           "roofline": {"bound": "mfma", "kernel": "fwd_mfma", "achieved": round(achieved, 1),
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                        "traffic": None, "flops_per_unit": "4*d per visible (row, key) pair and query head",
+                        "mean_launch_ms": kern["fwd_mfma"]["mean_ms"]},
+           "kernels": kern}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -279,8 +337,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="c2m", choices=sorted(configs.CONFIGS))
     ap.add_argument("--G", type=int, default=None, help="override the group size")
-    ap.add_argument("--workload", default="replay", choices=["replay", "score"],
-                    help="replay: the fwd+bwd step (the headline); score: batched forward-only scoring")
+    ap.add_argument("--workload", default="replay", choices=["replay", "score", "prefill", "reuse"],
+                    help="replay: the fwd+bwd step (the headline); score: batched forward-only scoring; "
+                         "prefill: chunked capture-side prefill; reuse: consecutive G=8 cycles on one capture "
+                         "at P=4,456,448 (--steps cycles, per-cycle times and peaks)")
+    ap.add_argument("--prefill-tokens", type=int, default=524288)
+    ap.add_argument("--prefill-chunk", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a device copy of known size (for HBM counter calibration)")
@@ -301,6 +363,8 @@ def main():
     if ns.calibrate_copy:
         calibrate_copy()
         return
+    if ns.workload == "reuse" and ns.config == "c2m":
+        ns.config = "reuse4m"
     cfg = configs.CONFIGS[ns.config]
     if ns.G:
         cfg = cfg.with_(G=ns.G)
@@ -308,6 +372,9 @@ def main():
     torch.cuda.set_device(dev)
 
     log(f"[bench] config {cfg}")
+    if ns.workload == "prefill":
+        bench_prefill(ns, cfg, dev)
+        return
     prefix, kp, vp = build_prefix(cfg, dev)
     members = [datagen.member_inputs(cfg, i, dev) for i in range(cfg.G)]
     torch.cuda.synchronize()
@@ -328,7 +395,8 @@ def main():
     api.profile_begin()
     t0 = time.perf_counter()
     ev0.record()
-    grp, results = run_steps(prefix, members, cfg, ns.steps)
+    cycles = [] if ns.workload == "reuse" else None
+    grp, results = run_steps(prefix, members, cfg, ns.steps, cycle_log=cycles)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -385,6 +453,12 @@ def main():
         "peak_mem_gb_per_member": [round(p / 1e9, 3) for p in peaks],
         "peak_mem_gb": round(torch.cuda.max_memory_allocated(dev) / 1e9, 3),
     }
+    if cycles is not None:
+        out["metric"] = REUSE_METRIC
+        out["config"]["workload"] = (f"{cfg.name}: {ns.steps} consecutive optimizer cycles over one capture; "
+                                     + out["config"]["workload"].split(": ", 1)[1])
+        out["cycle_ms"] = [round(c[0], 1) for c in cycles]
+        out["cycle_peak_gb"] = [round(c[1] / 1e9, 3) for c in cycles]
     del grp, results
     if not ns.no_cpu_baseline:
         t = time.perf_counter()

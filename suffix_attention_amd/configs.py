@@ -50,6 +50,9 @@ CONFIGS = {
     "c2m": Config("c2m", 3, P=2097152, R=4096, B=1024, hq=24, hkv=4, d=256, dtype=torch.bfloat16, S=8, G=8),
     "stress": Config("stress", 4, P=4194304, R=262144, B=8192, hq=24, hkv=4, d=256, dtype=torch.bfloat16, S=16,
                      G=1),
+    # prefix reuse: consecutive G = 8 optimizer cycles over one capture of 4,456,448 positions
+    "reuse4m": Config("reuse4m", 5, P=4456448, R=4096, B=1024, hq=24, hkv=4, d=256, dtype=torch.bfloat16, S=8,
+                      G=8),
 }
 
 

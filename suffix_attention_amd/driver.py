@@ -104,3 +104,39 @@ def replay_group(prefix: api.Prefix, members: Iterable, block: int, keep: str = 
             on_member(i, r)
         results.append(r)
     return grp, results
+
+
+def prefill_capture(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, page_table: torch.Tensor, n_phys: int,
+                    chunk: int, n_shards: int = 1, keep_o: bool = True):
+    """Capture-side prefill without gradients: the prompt's own causal attention, chunk by chunk
+    (digest, "Method", step 1: the prompt is evaluated once without autograd and its KV pages are
+    retained).  Chunk [a, e) attends to the pages captured so far (tokens [0, a), split into
+    n_shards page ranges) plus itself under the causal mask -- exactly a replay forward with the
+    chunk as the "response" at q_start = 0 -- and its keys and values are then written into the
+    pools.  q [P, hq, d], k / v [P, hkv, d]; chunk is a multiple of the page size.
+
+    Returns (prefix over the whole prompt with n_shards shards, o [P, hq, d] or None, lse
+    [P, hq] or None)."""
+    if chunk <= 0 or chunk % api.PAGE:
+        raise ValueError(f"chunk={chunk} must be a positive multiple of {api.PAGE}")
+    P, hq, d = q.shape
+    hkv = k.shape[1]
+    dev = q.device
+    k_pages = torch.zeros((n_phys, hkv, api.PAGE, d), dtype=k.dtype, device=dev)
+    v_pages = torch.zeros_like(k_pages)
+    o = torch.empty_like(q) if keep_o else None
+    lse = torch.empty((P, hq), dtype=torch.float32, device=dev) if keep_o else None
+    ws = None
+    for a in range(0, P, chunk):
+        e = min(P, a + chunk)
+        pre = api.Prefix(hq, hkv, d, q.dtype, a, page_table, k_pages, v_pages,
+                         api.even_shard_bounds(api.n_logical_pages(a), n_shards))
+        need = api.fwd_workspace_bytes(pre, e - a)
+        if ws is None or ws.numel() * ws.element_size() < need:
+            ws = torch.empty(((need + 15) // 16) * 4, dtype=torch.float32, device=dev)
+        oc, lc, _ = api.replay_fwd(pre, q[a:e], 0, k[a:e], v[a:e], workspace=ws,
+                                   o=o[a:e] if keep_o else None, lse=lse[a:e] if keep_o else None)
+        api.capture_pages(k[a:e], v[a:e], page_table, n_phys, first_tok=a, k_pages=k_pages, v_pages=v_pages)
+    full = api.Prefix(hq, hkv, d, q.dtype, P, page_table, k_pages, v_pages,
+                      api.even_shard_bounds(api.n_logical_pages(P), n_shards))
+    return full, o, lse

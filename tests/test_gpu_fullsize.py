@@ -205,3 +205,28 @@ def test_block_size_does_not_change_the_result():
                        ("dV_resp", a.dv_resp, b.dv_resp), ("dK_pages", ga.dk_pages, gb.dk_pages),
                        ("dV_pages", ga.dv_pages, gb.dv_pages)):
         assert_close(name, np32(y), np32(x).astype(np.float64), atol=ATOL, rel_l2=REL_L2 / 5)
+
+
+def test_prefix_reuse_cycles_are_steady():
+    """Consecutive optimizer cycles over one capture (each a fresh group: gradient pages
+    allocated at its first backward and released at its end) give bit-identical gradient pages
+    and the same peak memory every cycle."""
+    cfg = configs.CONFIGS["c128k"].with_(P=65536, R=512, B=256, G=2)
+    log(f"case: prefix reuse, 3 cycles at P={cfg.P}, G={cfg.G}, R={cfg.R}, B={cfg.B}")
+    table = datagen.page_table(cfg.n_pages, datagen.seed(cfg.cfg_id, datagen.TAG_PERM), "cuda")
+    kp, vp = datagen.prefix_kv(cfg, "cuda")
+    pre = _prefix(cfg, kp, vp, table)
+    members = [datagen.member_inputs(cfg, i, "cuda") for i in range(cfg.G)]
+    pages, peaks = [], []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        grp, _ = driver.replay_group(pre, members, cfg.B, keep="none")
+        torch.cuda.synchronize()
+        peaks.append(torch.cuda.max_memory_allocated())
+        pages.append((grp.dk_pages.cpu(), grp.dv_pages.cpu()))  # host copies: device memory stays the same
+        del grp
+    for c in (1, 2):
+        assert torch.equal(pages[c][0], pages[0][0]) and torch.equal(pages[c][1], pages[0][1]), c
+    log(f"    peaks {peaks}")
+    assert peaks[1] == peaks[2]
