@@ -241,6 +241,17 @@ int ls_lse_merge(int n_parts, int64_t n_rows, int d, const float* o_parts,
                  ls_stream_t stream);
 
 /*
+ * ls_lse_merge_bf16num -- the same merge with the pages' BF16 numerator (explainer, "The fine
+ * print": the prototype's global attention merge keeps its numerator in BF16), to measure the
+ * error that choice adds.  Each term exp(L_p - m) O_p is rounded to bf16 and so is the running
+ * sum after every addition, in part order; L and the denominator sum_p exp(L_p - m) stay
+ * float32; O = numerator / denominator.  Arguments and errors as for ls_lse_merge.
+ */
+int ls_lse_merge_bf16num(int n_parts, int64_t n_rows, int d, const float* o_parts,
+                         const float* lse_parts, void* o_out, int out_dtype, float* lse_out,
+                         ls_stream_t stream);
+
+/*
  * Kernel timing, for diagnostics and benchmarks.  Between ls_profile_begin() and
  * ls_profile_end(), every kernel the library launches (from any thread, on any stream) is
  * bracketed by a pair of HIP events recorded on that kernel's stream, so each record is the

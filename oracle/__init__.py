@@ -12,6 +12,7 @@ from .attention import (  # noqa: F401
     forward_parts,
     gather_pages,
     lse_merge,
+    lse_merge_bf16_numerator,
     round_bf16,
     shard_token_bounds,
 )

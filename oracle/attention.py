@@ -253,6 +253,29 @@ def lse_merge(o_parts, lse_parts):
     return O, L
 
 
+def lse_merge_bf16_numerator(o_parts, lse_parts):
+    """The pages' own merge, whose numerator is BF16 (explainer, "The fine print").  Reading
+    (the pages give no more detail): each part's term exp(L_p - m) O_p is rounded to bf16 and
+    the running sum over the parts, in part order, is rounded to bf16 after every addition --
+    what a bf16 sum over the owners does; m, L and the denominator sum_p exp(L_p - m) are
+    exact; O = numerator / denominator.  Empty parts add nothing; empty rows give O = 0 and
+    L = -inf as in :func:`lse_merge`.
+    """
+    Lp = _f64(lse_parts)
+    Op = _f64(o_parts)
+    m = Lp.max(axis=0)
+    msafe = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(Lp - msafe[None])  # 0 for empty parts
+    den = w.sum(axis=0)
+    num = np.zeros(Op.shape[1:])
+    for p in range(Op.shape[0]):
+        num = round_bf16(num + round_bf16(w[p][..., None] * Op[p]))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        L = np.where(den > 0, msafe + np.log(den), -np.inf)
+        O = np.where((den > 0)[..., None], num / np.where(den > 0, den, 1.0)[..., None], 0.0)
+    return O, L
+
+
 # ---------------------------------------------------------------------------------------
 # Output rounding (the replayed block's output is a tensor of the model's dtype, bf16 on the
 # pages' runs: digest "Method", Qwen implementation; the backward's delta is formed from that

@@ -253,15 +253,18 @@ def replay_bwd(prefix: Prefix, q, q_start: int, k_resp, v_resp, o, lse, dout, dk
     return dq
 
 
-def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype: torch.dtype = torch.float32):
-    """Merge [n_parts, n_rows, d] partial outputs by their LSE [n_parts, n_rows] in float32."""
+def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype: torch.dtype = torch.float32,
+              bf16_numerator: bool = False):
+    """Merge [n_parts, n_rows, d] partial outputs by their LSE [n_parts, n_rows] in float32
+    (bf16_numerator: the pages' variant with a BF16 numerator, ls_lse_merge_bf16num)."""
     _dev(o_parts, "o_parts", dtype=torch.float32)
     n_parts, n_rows, d = o_parts.shape
     _dev(lse_parts, "lse_parts", dtype=torch.float32, shape=(n_parts, n_rows))
     o = torch.empty((n_rows, d), dtype=out_dtype, device=o_parts.device)
     lse = torch.empty((n_rows,), dtype=torch.float32, device=o_parts.device)
-    check(lib().ls_lse_merge(n_parts, n_rows, d, _ptr(o_parts), _ptr(lse_parts), _ptr(o), _dtype_code(out_dtype),
-                             _ptr(lse), _stream()))
+    fn = lib().ls_lse_merge_bf16num if bf16_numerator else lib().ls_lse_merge
+    check(fn(n_parts, n_rows, d, _ptr(o_parts), _ptr(lse_parts), _ptr(o), _dtype_code(out_dtype), _ptr(lse),
+             _stream()))
     return o, lse
 
 

@@ -332,8 +332,8 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
     return LS_OK;
 }
 
-int ls_lse_merge(int n_parts, int64_t n_rows, int d, const float* o_parts, const float* lse_parts, void* o_out,
-                 int out_dtype, float* lse_out, ls_stream_t stream) {
+static int lse_merge_impl(int n_parts, int64_t n_rows, int d, const float* o_parts, const float* lse_parts,
+                          void* o_out, int out_dtype, float* lse_out, ls_stream_t stream, bool bf16_numerator) {
     g_err.clear();
     if (n_parts < 1) return fail(LS_ERR_INVALID, "n_parts=%d < 1", n_parts);
     if (n_rows < 0) return fail(LS_ERR_INVALID, "n_rows < 0");
@@ -342,8 +342,18 @@ int ls_lse_merge(int n_parts, int64_t n_rows, int d, const float* o_parts, const
     if (n_rows == 0) return LS_OK;
     if (!o_parts || !lse_parts || !o_out || !lse_out) return fail(LS_ERR_INVALID, "NULL pointer argument");
     hipError_t e = ls::launch_lse_merge(n_parts, n_rows, d, o_parts, lse_parts, o_out, out_dtype, lse_out,
-                                        (hipStream_t)stream);
+                                        (hipStream_t)stream, bf16_numerator);
     return e == hipSuccess ? LS_OK : hip_fail(e, "LSE merge kernel");
+}
+
+int ls_lse_merge(int n_parts, int64_t n_rows, int d, const float* o_parts, const float* lse_parts, void* o_out,
+                 int out_dtype, float* lse_out, ls_stream_t stream) {
+    return lse_merge_impl(n_parts, n_rows, d, o_parts, lse_parts, o_out, out_dtype, lse_out, stream, false);
+}
+
+int ls_lse_merge_bf16num(int n_parts, int64_t n_rows, int d, const float* o_parts, const float* lse_parts,
+                         void* o_out, int out_dtype, float* lse_out, ls_stream_t stream) {
+    return lse_merge_impl(n_parts, n_rows, d, o_parts, lse_parts, o_out, out_dtype, lse_out, stream, true);
 }
 
 }  // extern "C"

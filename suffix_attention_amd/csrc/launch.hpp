@@ -87,7 +87,7 @@ hipError_t launch_gather(const void* pages, int dtype, const int32_t* table, int
 // reduce.hip
 hipError_t launch_lse_merge(int n_parts, int64_t n_rows, int d, const float* o_parts,
                             const float* lse_parts, void* o_out, int out_dtype, float* lse_out,
-                            hipStream_t s);
+                            hipStream_t s, bool bf16_numerator = false);
 hipError_t launch_delta(const void* o, const void* dout, int dtype, int64_t n_rows, int d,
                         float* delta, hipStream_t s);
 hipError_t launch_sum_parts(int n_parts, int64_t n, const float* parts, float* out,

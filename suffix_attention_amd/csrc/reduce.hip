@@ -11,8 +11,12 @@ namespace {
 // Composition of local softmax results into the global one (LongStraw digest, "Method",
 // Qwen implementation: global LSE/output merge; here numerator and weights are float32):
 //   L = m + log sum_p exp(L_p - m), m = max_p L_p;  O = sum_p exp(L_p - L) O_p.
+// BF16NUM is the pages' own variant, whose numerator is BF16 (explainer, "The fine print"):
+// each term exp(L_p - m) O_p is rounded to bf16 and so is the running sum after every
+// addition, in part order (a bf16 reduction over the owners); the denominator and L stay
+// float32, and O = numerator / sum_p exp(L_p - m).
 // Each thread owns 4 consecutive elements of one row.
-template <typename OutT>
+template <typename OutT, bool BF16NUM>
 __global__ __launch_bounds__(256) void lse_merge_kernel(int n_parts, int64_t n_rows, int d,
                                                         const float* __restrict__ o_parts,
                                                         const float* __restrict__ lse_parts,
@@ -34,12 +38,22 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(int n_parts, int64_t n_r
         for (int p = 0; p < n_parts; p++) {
             const float lp = lse_parts[(int64_t)p * n_rows + row];
             if (lp == -INFINITY) continue;
-            const float w = expf(lp - L);
             const float4 v = *reinterpret_cast<const float4*>(o_parts + ((int64_t)p * n_rows + row) * d + 4 * c);
-            acc[0] += w * v.x;
-            acc[1] += w * v.y;
-            acc[2] += w * v.z;
-            acc[3] += w * v.w;
+            const float ve[4] = {v.x, v.y, v.z, v.w};
+            if (BF16NUM) {
+                const float w = expf(lp - m);
+                auto rb = [](float x) { return bf16_to_f32(f32_to_bf16(x)); };
+#pragma unroll
+                for (int e = 0; e < 4; e++) acc[e] = rb(acc[e] + rb(w * ve[e]));
+            } else {
+                const float w = expf(lp - L);
+#pragma unroll
+                for (int e = 0; e < 4; e++) acc[e] += w * ve[e];
+            }
+        }
+        if (BF16NUM) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[e] /= ssum;
         }
     }
     OutT* dst = o_out + row * d + 4 * c;
@@ -86,15 +100,25 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int64_
 
 hipError_t launch_lse_merge(int n_parts, int64_t n_rows, int d, const float* o_parts,
                             const float* lse_parts, void* o_out, int out_dtype, float* lse_out,
-                            hipStream_t s) {
+                            hipStream_t s, bool bf16_numerator) {
     if (n_rows == 0) return hipSuccess;
     const int rows_per_block = 256 / (d / 4);
     const unsigned grid = (unsigned)((n_rows + rows_per_block - 1) / rows_per_block);
     KernelTimer kt("lse_merge", s);
-    if (out_dtype == 0)
-        lse_merge_kernel<float><<<grid, 256, 0, s>>>(n_parts, n_rows, d, o_parts, lse_parts, (float*)o_out, lse_out);
-    else
-        lse_merge_kernel<bf16_t><<<grid, 256, 0, s>>>(n_parts, n_rows, d, o_parts, lse_parts, (bf16_t*)o_out, lse_out);
+    if (bf16_numerator) {
+        if (out_dtype == 0)
+            lse_merge_kernel<float, true><<<grid, 256, 0, s>>>(n_parts, n_rows, d, o_parts, lse_parts, (float*)o_out,
+                                                               lse_out);
+        else
+            lse_merge_kernel<bf16_t, true><<<grid, 256, 0, s>>>(n_parts, n_rows, d, o_parts, lse_parts,
+                                                                (bf16_t*)o_out, lse_out);
+    } else if (out_dtype == 0) {
+        lse_merge_kernel<float, false><<<grid, 256, 0, s>>>(n_parts, n_rows, d, o_parts, lse_parts, (float*)o_out,
+                                                            lse_out);
+    } else {
+        lse_merge_kernel<bf16_t, false><<<grid, 256, 0, s>>>(n_parts, n_rows, d, o_parts, lse_parts, (bf16_t*)o_out,
+                                                             lse_out);
+    }
     return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ FAKE = 0x10000  # never dereferenced: every call below fails validation first
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ls_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ls_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_functions_exported():

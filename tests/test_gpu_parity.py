@@ -155,6 +155,40 @@ def test_lse_merge_matches_oracle():
     assert torch.equal(gob.cpu(), go.cpu().to(torch.bfloat16))
 
 
+def test_bf16_numerator_merge_variant():
+    """The pages' BF16-numerator merge (ls_lse_merge_bf16num) against its oracle on the same
+    float32 parts, and the error it adds against the exact result on a real block (9 parts:
+    8 prompt shards and the response)."""
+    log("case: bf16-numerator merge, synthetic parts and a P=1000 S=8 block")
+    g = torch.Generator().manual_seed(4)
+    n_parts, rows, d = 9, 257, 256
+    o = torch.randn(n_parts, rows, d, generator=g)
+    lse = torch.randn(n_parts, rows, generator=g) * 4
+    lse[2, :50] = float("-inf")
+    o[2, :50] = 0
+    Ov, Lv = orc.lse_merge_bf16_numerator(o.numpy(), lse.numpy())
+    go, gl = api.lse_merge(o.cuda(), lse.cuda(), torch.float32, bf16_numerator=True)
+    assert_close("bf16num O", np32(go), Ov, atol=2e-2, rel_l2=1e-3)
+    assert_close("bf16num L", np32(gl), Lv, atol=1e-5, rel_l2=1e-6)
+    # a single part: the part rounded to bf16, exactly
+    go1, _ = api.lse_merge(o[:1].cuda().contiguous(), lse[:1].cuda().contiguous(), torch.float32, bf16_numerator=True)
+    assert torch.equal(go1.cpu(), o[0].to(torch.bfloat16).to(torch.float32))
+    # on a real block: the variant against the exact output, next to the float32 merge's error
+    c = Case(1000, 128, 24, 4, 256, torch.bfloat16, seed=12, S=8)
+    pre = c.prefix()
+    q = c.q.cuda()
+    o32, _, ws = api.replay_fwd(pre, q, 0, c.kr.cuda(), c.vr.cuda())
+    op, lp = api.fwd_parts(pre, 128, ws)
+    hd = op.shape[-1]
+    ob, _ = api.lse_merge(op.reshape(op.shape[0], -1, hd).contiguous(), lp.reshape(lp.shape[0], -1).contiguous(),
+                          torch.float32, bf16_numerator=True)
+    torch.cuda.synchronize()
+    O, _ = orc.forward(np32(c.q), np32(c.kp), np32(c.vp), np32(c.kr), np32(c.vr), 0)
+    O = O.reshape(-1, hd)
+    assert_close("fp32 merge vs exact", np32(o32).reshape(-1, hd), O)
+    assert_close("bf16 numerator vs exact", np32(ob), O)
+
+
 def test_capture_gather_exact():
     """Capture then gather is a bit copy for a permuted table, a partial last page and chunked
     capture; f32 -> bf16 capture rounds to nearest-even."""

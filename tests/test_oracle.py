@@ -367,3 +367,56 @@ def test_round_bf16_matches_torch_rne_and_is_idempotent():
     ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(got, ref)
     assert np.array_equal(orc.round_bf16(got), got)
+
+
+# ---------------------------------------------------------------------------------------
+# The pages' BF16-numerator merge variant
+# ---------------------------------------------------------------------------------------
+
+def test_bf16_numerator_merge_single_part_rounds_once():
+    """One non-empty part: weight 1, denominator 1, so the result is that part rounded to bf16."""
+    rng = np.random.default_rng(5)
+    Op = rng.standard_normal((3, 4, 8))
+    Lp = np.full((3, 4), -np.inf)
+    Lp[1] = rng.standard_normal(4)
+    O, L = orc.lse_merge_bf16_numerator(Op, Lp)
+    assert np.array_equal(O, orc.round_bf16(Op[1]))
+    assert np.allclose(L, Lp[1], rtol=0, atol=1e-15)
+
+
+def test_bf16_numerator_merge_rounds_the_running_sum():
+    """Two parts of equal LSE (weights 1, denominator 2): a sum that bf16 holds exactly is
+    exact, and a term below half a bf16 step of the running sum is lost -- which a float64 or
+    float32 accumulation of the same bf16 terms would keep."""
+    Lp = np.zeros((2, 1))
+    O, _ = orc.lse_merge_bf16_numerator(np.array([[[1.5]], [[0.25]]]), Lp)
+    assert O[0, 0] == 0.875
+    O, _ = orc.lse_merge_bf16_numerator(np.array([[[1.0]], [[2.0 ** -9]]]), Lp)
+    assert O[0, 0] == 0.5  # exact merge: (1 + 2^-9) / 2
+    O, _ = orc.lse_merge(np.array([[[1.0]], [[2.0 ** -9]]]), Lp)
+    assert O[0, 0] == (1 + 2.0 ** -9) / 2
+
+
+def test_bf16_numerator_merge_error_is_bounded():
+    """Against the exact merge the error is at most one bf16 rounding per term and per
+    addition: |dO| <= sum_p (2 p + 1) 2^-9 max|partial sum| / denominator (a loose bound), and
+    empty rows stay O = 0, L = -inf."""
+    rng = np.random.default_rng(6)
+    n_parts, rows, d = 9, 50, 16
+    Op = rng.standard_normal((n_parts, rows, d))
+    Lp = rng.standard_normal((n_parts, rows)) * 3
+    Lp[2, :10] = -np.inf
+    Lp[:, -1] = -np.inf
+    O, L = orc.lse_merge_bf16_numerator(Op, Lp)
+    Oe, Le = orc.lse_merge(Op, Lp)
+    assert np.all(O[-1] == 0) and np.isneginf(L[-1])
+    m = np.max(Lp[:, :-1], axis=0)
+    w = np.exp(Lp[:, :-1] - m)
+    den = w.sum(axis=0)
+    scale = (np.abs(w[..., None] * Op[:, :-1]).sum(axis=0)) / den[:, None]
+    bound = sum(2 * p + 1 for p in range(n_parts)) * 2.0 ** -9 * scale
+    assert np.all(np.abs(O[:-1] - Oe[:-1]) <= bound)
+    assert np.max(np.abs(O[:-1] - Oe[:-1])) > 0  # the variant does lose precision
+    assert np.array_equal(np.isneginf(L), np.isneginf(Le))
+    fin = np.isfinite(L)
+    np.testing.assert_allclose(L[fin], Le[fin], rtol=0, atol=1e-12)
