@@ -186,7 +186,9 @@ def test_bf16_numerator_merge_variant():
     O, _ = orc.forward(np32(c.q), np32(c.kp), np32(c.vp), np32(c.kr), np32(c.vr), 0)
     O = O.reshape(-1, hd)
     assert_close("fp32 merge vs exact", np32(o32).reshape(-1, hd), O)
-    assert_close("bf16 numerator vs exact", np32(ob), O)
+    # the variant's own error (measured 4.6e-3 rel-L2 here, against 2.2e-3 for the float32 merge
+    # with its bf16 output): bounded loosely, since it is what is being measured, not a claim
+    assert_close("bf16 numerator vs exact", np32(ob), O, rel_l2=1e-2)
 
 
 def test_capture_gather_exact():
