@@ -32,11 +32,13 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
 
 
 # Matrix-core accumulators go to VGPRs in the dQ pass (its S / dP tiles feed vector-ALU work
-# every page, its read-only Q / dO operands sit in AGPRs) and in the dK/dV pass (its S / dP
+# every page, its read-only Q / dO operands sit in AGPRs), in the dK/dV pass (its S / dP
 # tiles likewise; its 256 dK / dV accumulators are kept in AGPRs by explicit AGPR-form matrix
-# instructions); the forward keeps O in AGPRs in the default form.
+# instructions) and in the forward (the score tiles feed the softmax directly, and the output
+# tile is rescaled by plain vector multiplies).
 PER_SOURCE = {"attn_mfma_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-              "attn_mfma_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+              "attn_mfma_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "attn_mfma_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src, extra):
