@@ -380,19 +380,22 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int pair0, int n_pairs
 #pragma unroll
             for (int un = 0; un < 8; un++) prob_unit<MASK>(un, s0, dp0, unit_lsd(un, lsd0), rmh0, a.scale_log2, cur);
         }
-        for (int64_t t = 0; t < n_stages; t++) {
+        // stage t % 3 is kept as a rotating counter (no 64-bit division in the loop)
+        const int n_st = (int)n_stages;
+        int it = 0;
+        for (int t = 0; t < n_st; t++) {
             // tile t+1 has landed; stage (t+2) % 3 was last read in iteration t-1
             wait_vm_all();
             __syncthreads();
             // the last iteration runs phases 1-2 on a stale stage; that result is never used
             const int rmhn = rmh_of(t + 1);
             Prob nxt;
-            const int it = (int)(t % 3);
-            dkdv_step<MASK, D>(st, stg0 + it * kStage, stg0 + (it == 2 ? 0 : it + 1) * kStage,
-                         stg0 + (it == 0 ? 2 : it - 1) * kStage,
-                         gr, rc, kvh, r_begin + (t + 2 < n_stages ? t + 2 : n_stages - 1) * kRows, cur, nxt, la, rmhn,
-                         a.scale_log2, w, lane);
+            const int it1 = it == 2 ? 0 : it + 1, it2 = it == 0 ? 2 : it - 1;
+            dkdv_step<MASK, D>(st, stg0 + it * kStage, stg0 + it1 * kStage, stg0 + it2 * kStage,
+                         gr, rc, kvh, r_begin + (int64_t)(t + 2 < n_st ? t + 2 : n_st - 1) * kRows, cur, nxt, la,
+                         rmhn, a.scale_log2, w, lane);
             cur = nxt;
+            it = it1;
         }
         wait_vm_all();  // the last iterations' copies land before the workgroup's LDS is released
     }
