@@ -127,11 +127,14 @@ __device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const 
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
-// Two independent ones back to back, behind one pair of wait states (one instruction fewer to
-// issue per pair; a single wave per SIMD issues roughly one instruction per four cycles).
+// Two independent ones back to back, with no wait states ahead of them: a single wave per SIMD
+// issues roughly one instruction per four cycles, so every instruction saved counts.  The
+// callers' A and B operands are LDS reads (covered by s_waitcnt) or vector-ALU results formed a
+// whole step earlier; tests/test_mfma_hazards.py scans the built assembly and fails if a
+// vector-ALU write of an operand ever lands within the two instructions ahead of one of them.
 __device__ __forceinline__ void mfma32_agpr2(f32x16& acc0, const bf16x8& a0, const bf16x8& b0, f32x16& acc1,
                                              const bf16x8& a1, const bf16x8& b1) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\tv_mfma_f32_32x32x16_bf16 %1, %4, %5, %1"
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\tv_mfma_f32_32x32x16_bf16 %1, %4, %5, %1"
                  : "+a"(acc0), "+a"(acc1)
                  : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
 }
