@@ -46,7 +46,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 
 # Algorithmic matrix work per visible (row, key) pair and query head, in units of 2*d flops
 # (one multiply-add GEMM over the head dimension), for each kernel that does it.
-KERNEL_UNITS = {"fwd_mfma": 2, "dkdv_mfma": 4, "dq_mfma": 3}
+KERNEL_UNITS = {"fwd_mfma": 2, "dkdv_mfma": 4, "dq_mfma": 3, "dqs_mfma": 1}
 
 # Measured HBM traffic of the dominant kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch,
 # scaled by the same counters on a copy of known size), written by --ingest-counters.  It is

@@ -143,6 +143,29 @@ size_t ls_fwd_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows);
 size_t ls_bwd_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows);
 
 /*
+ * ls_bwd_ds_workspace_bytes -- backward workspace that also holds the block's dS, for a block
+ * of n_rows rows whose response keys end at key_end = q_start + n_rows (0 on invalid
+ * arguments, with ls_last_error set).  Equal to ls_bwd_workspace_bytes for float32.
+ *
+ * The backward's dQ is scale * sum_j dS_ij K_j with dS = P (dP - delta) (the softmax gradient
+ * of exact attention, explainer "Serial replay makes G a schedule").  When ls_replay_bwd is
+ * given at least this many bytes (bf16 only), the key-stationary dK/dV pass also writes dS,
+ * rounded to bf16 as its matrix instructions take it, and the dQ pass reads it back, so the
+ * dQ pass multiplies once per (row, key) pair instead of recomputing S and dP.  With fewer
+ * bytes (but at least ls_bwd_workspace_bytes) the dQ pass recomputes them.  Both give dQ
+ * within the bf16 rounding of dS of each other; dK, dV, delta are the same either way.
+ *
+ * Layout: the recompute workspace, then from the next 256-byte boundary the stored dS, bf16
+ * [hkv][row tiles][key slots][32]: row tiles of 32 group rows (r = token * g + j for query
+ * head kv * g + j) padded to a multiple of 256 rows, key slots 128 per page pair, prompt pairs
+ * first.  The size is hkv * ceil(n_rows * g / 256) * 8 * 128 * (ceil(pages / 2) +
+ * ceil(ceil(key_end / 64) / 2)) * 64 bytes: 103 GB for 1,024 rows over a 2,097,152-token
+ * prompt with hq = 24, hkv = 4.  A workspace sized for the largest key_end serves every block
+ * of a member.
+ */
+size_t ls_bwd_ds_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows, int64_t key_end);
+
+/*
  * ls_replay_fwd -- forward of one replayed response block (digest, "Method", step 3:
  * serial response replay; explainer, "Serial replay makes G a schedule": exact attention;
  * "Two incompatible architectures": local softmax statistics composed into the exact
@@ -212,7 +235,9 @@ int ls_score_fwd(const ls_prefix_t* pre, int64_t n_members, const void* q, int64
  *                   shard_first_touch[s] != 0 (rows past prefix_len in a partial last
  *                   page are then written as zero).
  *   shard_first_touch  host uint8 [n_shards], or NULL for "accumulate everywhere".
- *   workspace       device, ws_bytes >= ls_bwd_workspace_bytes(pre, n_rows).
+ *   workspace       device, ws_bytes >= ls_bwd_workspace_bytes(pre, n_rows); with
+ *                   ws_bytes >= ls_bwd_ds_workspace_bytes(pre, n_rows, q_start + n_rows)
+ *                   (bf16) dQ is formed from the stored dS instead of a recompute.
  * Each gradient element has one writer per call (no atomics); results are
  * deterministic.  Errors as for ls_replay_fwd.
  */

@@ -51,6 +51,7 @@ _SIG = {
     "ls_gather_pages": (_I, [_P, _I, _P, _I64, _I64, _I64, _I64, _I, _I, _I, _P, _P]),
     "ls_fwd_workspace_bytes": (C.c_size_t, [C.POINTER(ls_prefix_t), _I64]),
     "ls_bwd_workspace_bytes": (C.c_size_t, [C.POINTER(ls_prefix_t), _I64]),
+    "ls_bwd_ds_workspace_bytes": (C.c_size_t, [C.POINTER(ls_prefix_t), _I64, _I64]),
     "ls_replay_fwd": (_I, [C.POINTER(ls_prefix_t), _P, _I64, _I64, _P, _P, _I64, _P, _P, _P, C.c_size_t, _P]),
     "ls_score_workspace_bytes": (C.c_size_t, [C.POINTER(ls_prefix_t), _I64, _I64]),
     "ls_score_fwd": (_I, [C.POINTER(ls_prefix_t), _I64, _P, _I64, _P, _P, _P, _P, _P, C.c_size_t, _P]),

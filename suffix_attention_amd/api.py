@@ -152,6 +152,25 @@ def bwd_workspace_bytes(prefix: Prefix, n_rows: int) -> int:
     return n
 
 
+def bwd_ds_workspace_bytes(prefix: Prefix, n_rows: int, key_end: int) -> int:
+    """Backward workspace that also holds the block's dS (bf16), so that dQ is formed from it
+    rather than recomputed; key_end = q_start + n_rows (the largest over a member's blocks
+    sizes one workspace for all of them)."""
+    st = prefix.struct()
+    n = lib().ls_bwd_ds_workspace_bytes(C.byref(st), n_rows, key_end)
+    if n == 0 and n_rows > 0:
+        raise LongStrawError(_lib.LS_ERR_INVALID, lib().ls_last_error().decode())
+    return n
+
+
+def ds_fits(nbytes: int, device, fraction: float = 0.9) -> bool:
+    """Whether a workspace of nbytes fits in what the device has free (counting the blocks
+    torch's allocator holds but does not use)."""
+    free, _ = torch.cuda.mem_get_info(device)
+    cached = torch.cuda.memory_reserved(device) - torch.cuda.memory_allocated(device)
+    return nbytes <= fraction * (free + cached)
+
+
 def _workspace(nbytes: int, device, given: torch.Tensor | None):
     if given is not None:
         if given.numel() * given.element_size() < nbytes:
@@ -222,9 +241,11 @@ def score_fwd(prefix: Prefix, q: torch.Tensor, k_resp: torch.Tensor, v_resp: tor
 
 def replay_bwd(prefix: Prefix, q, q_start: int, k_resp, v_resp, o, lse, dout, dk_resp, dv_resp,
                resp_first_touch: bool, dk_pages, dv_pages, shard_first_touch=None,
-               workspace: torch.Tensor | None = None, dq: torch.Tensor | None = None):
+               workspace: torch.Tensor | None = None, dq: torch.Tensor | None = None, store_ds: bool = False):
     """Backward of one block: returns dq (float32); accumulates or writes the response and
-    prompt key/value gradients in place."""
+    prompt key/value gradients in place.  store_ds (when no workspace is given) allocates the
+    larger workspace with which the library forms dQ from a stored dS; a given workspace
+    selects that path by its size alone."""
     _dev(q, "q", dtype=prefix.dtype)
     n_rows = q.shape[0]
     _dev(o, "o", dtype=prefix.dtype, shape=q.shape)
@@ -241,7 +262,10 @@ def replay_bwd(prefix: Prefix, q, q_start: int, k_resp, v_resp, o, lse, dout, dk
     flags = None
     if shard_first_touch is not None:
         flags = (C.c_uint8 * prefix.n_shards)(*[1 if f else 0 for f in shard_first_touch])
-    ws_bytes = bwd_workspace_bytes(prefix, n_rows)
+    if store_ds and workspace is None:
+        ws_bytes = bwd_ds_workspace_bytes(prefix, n_rows, q_start + n_rows)
+    else:
+        ws_bytes = bwd_workspace_bytes(prefix, n_rows)
     ws = _workspace(ws_bytes, q.device, workspace)
     st = prefix.struct()
     check(lib().ls_replay_bwd(C.byref(st), _ptr(q), n_rows, q_start, _ptr(k_resp), _ptr(v_resp), k_resp.shape[0],

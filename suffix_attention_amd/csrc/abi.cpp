@@ -132,6 +132,15 @@ size_t bwd_ws(const ls_prefix_t* p, int64_t n_rows) {
            ls::mfma_bwd_extra_bytes(n_rows, p->hq / p->hkv, p->hkv, p->d);
 }
 
+// Bytes of the stored dS (bf16, one per group row and key slot) of a block whose response keys
+// end at key_end, placed after the recompute workspace at a 256-byte boundary.
+size_t ds_offset(const ls_prefix_t* p, int64_t n_rows) { return (bwd_ws(p, n_rows) + 255) / 256 * 256; }
+size_t ds_bytes(const ls_prefix_t* p, int64_t n_rows, int64_t key_end) {
+    const int64_t rows_total = n_rows * (p->hq / p->hkv);
+    return (size_t)p->hkv * (size_t)ls::ds_row_tiles(rows_total) *
+           (size_t)ls::ds_key_slots(logical_pages(p->prefix_len, p->page_size), key_end, nullptr) * 64;
+}
+
 }  // namespace
 
 extern "C" {
@@ -201,6 +210,18 @@ size_t ls_bwd_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows) {
         return 0;
     }
     return bwd_ws(pre, n_rows);
+}
+
+size_t ls_bwd_ds_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows, int64_t key_end) {
+    g_err.clear();
+    if (check_prefix(pre) != LS_OK) return 0;
+    if (n_rows < 0 || key_end < n_rows) {
+        fail(LS_ERR_INVALID, "n_rows=%lld, key_end=%lld: need 0 <= n_rows <= key_end", (long long)n_rows,
+             (long long)key_end);
+        return 0;
+    }
+    if (pre->dtype != LS_DTYPE_BF16) return bwd_ws(pre, n_rows);  // the float32 path stores no dS
+    return ds_offset(pre, n_rows) + ds_bytes(pre, n_rows, key_end);
 }
 
 int ls_replay_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start, const void* k_resp,
@@ -314,6 +335,12 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (pre->dtype == LS_DTYPE_BF16 && !force_generic()) {
+        // a workspace that also holds the block's dS selects the stored-dS dQ pass
+        if (n_rows > 0 && ws_bytes >= ds_offset(pre, n_rows) + ds_bytes(pre, n_rows, a.key_end)) {
+            a.ds = (uint16_t*)((char*)workspace + ds_offset(pre, n_rows));
+            a.ds_rt = ls::ds_row_tiles(n_rows * a.g);
+            a.ds_kslots = ls::ds_key_slots(a.n_logical_pages, a.key_end, &a.ds_resp_slot0);
+        }
         e = ls::launch_bwd_mfma(a, s);  // its prep kernel also writes delta
     } else {
         e = ls::launch_delta(o, dout, pre->dtype, rows, pre->d, (float*)a.delta, s);

@@ -279,8 +279,10 @@ __device__ __forceinline__ void dkdv_step(DkvState<D>& st, uint32_t stage_t, uin
 // One workgroup: 4 waves over two consecutive 64-key pages (wave w: page w/2, keys
 // 32 (w%2) .. +32).  Pairs [0, n_pp) are prompt page pairs, the rest response pairs; a launch
 // covers pairs [pair0, pair0 + n_pairs_l) of every kv head.  MASK selects the causal mask, which
-// only response pairs need; the host launches the two kinds separately.
-template <int D, bool MASK>
+// only response pairs need; the host launches the two kinds separately.  DS also stores every
+// row tile's dS (a.ds), for the dQ pass to read; response pairs then walk every row tile, so
+// that the masked (row, key) pairs are stored as 0 too.
+template <int D, bool MASK, bool DS>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int pair0, int n_pairs_l, int n_blocks) {
     using F = TileShape<D>;
@@ -348,7 +350,7 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int pair0, int n_pairs
     // whose token is at least (first key of the pair) - q_start
     const int64_t key0_pair = 2 * (int64_t)(resp ? pair - n_pp : pair) * kPage;
     int64_t r_begin = 0;
-    if (resp && key0_pair > a.q_start) r_begin = (key0_pair - a.q_start) * a.g / kRows * kRows;
+    if (!DS && resp && key0_pair > a.q_start) r_begin = (key0_pair - a.q_start) * a.g / kRows * kRows;
     const int64_t n_stages = rows_total > r_begin ? (rows_total - r_begin + kRows - 1) / kRows : 0;
     // causal limit of this lane's key: visible to group rows >= (key - q_start) * g
     const int64_t my_key = page * kPage + 32 * kh + n;
@@ -383,10 +385,26 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int pair0, int n_pairs
         // stage t % 3 is kept as a rotating counter (no 64-bit division in the loop)
         const int n_st = (int)n_stages;
         int it = 0;
+        // stored dS of this lane: row tile t (r_begin = 0 here), key slot of its key, the 16
+        // positions of its lane half
+        u32x4* ds_p = nullptr;
+        int64_t ds_step = 0;
+        if (DS) {
+            const int64_t slot = 128 * (int64_t)pair + 64 * (w >> 1) + 32 * kh + n;
+            ds_p = (u32x4*)(a.ds + ((int64_t)kvh * a.ds_rt * a.ds_kslots + slot) * 32 + 16 * h);
+            ds_step = a.ds_kslots * 32 * 2 / 16;
+        }
         for (int t = 0; t < n_st; t++) {
             // tile t+1 has landed; stage (t+2) % 3 was last read in iteration t-1
             wait_vm_all();
             __syncthreads();
+            if (DS) {
+                // tile t's dS words, in register order: [key step u][word]; issued here so that
+                // they drain during the iteration, before the next wait for the copies
+                ds_p[0] = u32x4{cur.wd[0][0], cur.wd[0][1], cur.wd[0][2], cur.wd[0][3]};
+                ds_p[1] = u32x4{cur.wd[1][0], cur.wd[1][1], cur.wd[1][2], cur.wd[1][3]};
+                ds_p += ds_step;
+            }
             // the last iteration runs phases 1-2 on a stale stage; that result is never used
             const int rmhn = rmh_of(t + 1);
             Prob nxt;
@@ -477,13 +495,18 @@ hipError_t launch_bwd_d(const AttnArgs& a, hipStream_t s) {
     if ((int64_t)(n_pp + n_rp) * a.hkv > 0) {
         KernelTimer kt("dkdv_mfma", s);
         const int nbp = n_pp * a.hkv, nbr = n_rp * a.hkv;
-        if (nbp > 0) dkdv_mfma_kernel<D, false><<<pad_grid(nbp), 256, 0, s>>>(a, gr, n_pp, 0, n_pp, nbp);
-        if (nbr > 0) dkdv_mfma_kernel<D, true><<<pad_grid(nbr), 256, 0, s>>>(a, gr, n_pp, n_pp, n_rp, nbr);
+        if (a.ds) {
+            if (nbp > 0) dkdv_mfma_kernel<D, false, true><<<pad_grid(nbp), 256, 0, s>>>(a, gr, n_pp, 0, n_pp, nbp);
+            if (nbr > 0) dkdv_mfma_kernel<D, true, true><<<pad_grid(nbr), 256, 0, s>>>(a, gr, n_pp, n_pp, n_rp, nbr);
+        } else {
+            if (nbp > 0) dkdv_mfma_kernel<D, false, false><<<pad_grid(nbp), 256, 0, s>>>(a, gr, n_pp, 0, n_pp, nbp);
+            if (nbr > 0) dkdv_mfma_kernel<D, true, false><<<pad_grid(nbr), 256, 0, s>>>(a, gr, n_pp, n_pp, n_rp, nbr);
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // dQ parts (attn_mfma_dq.hip)
-    return launch_dq_mfma(a, gr, s);
+    // dQ parts: from the stored dS (attn_mfma_dqs.hip), else recomputed (attn_mfma_dq.hip)
+    return a.ds ? launch_dqs_mfma(a, s) : launch_dq_mfma(a, gr, s);
 }
 
 }  // namespace

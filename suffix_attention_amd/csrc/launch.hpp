@@ -55,7 +55,33 @@ struct AttnArgs {
     float* dk_resp;
     float* dv_resp;
     int resp_first_touch;
+    // stored dS (bf16), or null: the dK/dV pass then also writes dS = P (dP - delta) of every
+    // (group row, key) pair it forms, and the dQ pass reads it instead of recomputing S and dP.
+    // Layout [hkv][ds_rt][ds_kslots][32] bf16: for kv head h, 32-row tile rt of its group rows
+    // and key slot k, the 32 rows in the order of ds_row_of(); key slots are 128 per page pair,
+    // prompt pairs first (slot = logical key), the response pairs from ds_resp_slot0 on.
+    uint16_t* ds;
+    int64_t ds_rt;
+    int64_t ds_kslots;
+    int64_t ds_resp_slot0;
 };
+
+// Row (0..31) inside a 32-row tile of the stored-dS position p (0..31): the positions are in
+// the order the dK/dV pass holds dS in its registers (lane half h = p / 16, key step
+// u = (p / 8) % 2, word half hb = (p / 4) % 2).
+__host__ __device__ constexpr int ds_row_of(int p) {
+    return 16 * ((p >> 3) & 1) + 8 * ((p >> 2) & 1) + 4 * (p >> 4) + (p & 3);
+}
+
+// Stored-dS sizes for a block of rows_total group rows per kv head whose response keys end
+// at key_end: row tiles cover the rows padded to 256 (the dQ pass's row block), key slots
+// cover prompt and response pages rounded up to pairs (the dK/dV pass's unit).
+inline int64_t ds_row_tiles(int64_t rows_total) { return (rows_total + 255) / 256 * 8; }
+inline int64_t ds_key_slots(int64_t n_logical_pages, int64_t key_end, int64_t* resp_slot0) {
+    const int64_t pp = (n_logical_pages + 1) / 2, rp = ((key_end + 63) / 64 + 1) / 2;
+    if (resp_slot0) *resp_slot0 = 128 * pp;
+    return 128 * (pp + rp);
+}
 
 // Brackets one kernel launch with HIP events on its stream while profiling is on
 // (ls_profile_begin / ls_profile_end); does nothing otherwise.

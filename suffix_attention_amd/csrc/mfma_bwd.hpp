@@ -31,5 +31,7 @@ inline GroupRows group_rows(void* base, int64_t rows_pad, int hkv, int d) {
 }
 
 hipError_t launch_dq_mfma(const AttnArgs& a, const GroupRows& gr, hipStream_t s);
+// dQ parts from the dS that the dK/dV pass stored (a.ds)
+hipError_t launch_dqs_mfma(const AttnArgs& a, hipStream_t s);
 
 }  // namespace ls

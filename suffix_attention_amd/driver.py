@@ -52,11 +52,13 @@ class GroupReplay:
         return self.dk_pages, self.dv_pages
 
     def replay_member(self, q, kr, vr, do, block: int, keep: str = "all",
-                      on_block: Callable | None = None) -> MemberResult:
+                      on_block: Callable | None = None, store_ds: bool | None = None) -> MemberResult:
         """Forward + backward of one member's response, blocks in reverse order.
 
         keep: "all" returns o, lse, dq, dk_resp, dv_resp; "none" drops them at the end
-        (the prompt gradient pages still accumulate)."""
+        (the prompt gradient pages still accumulate).  store_ds: give the backward the
+        workspace in which it keeps dS for the dQ pass (True), or not (False); None does so
+        when it fits in device memory."""
         p = self.prefix
         R = q.shape[0]
         dev = q.device
@@ -71,8 +73,13 @@ class GroupReplay:
         nb = (R + block - 1) // block
         rows0 = min(block, R)
         ws_f = torch.empty((api.fwd_workspace_bytes(p, rows0) + 3) // 4, dtype=torch.float32, device=dev)
-        ws_b = torch.empty((max(4, api.bwd_workspace_bytes(p, rows0)) + 3) // 4, dtype=torch.float32,
-                           device=dev)
+        nb_ws = api.bwd_workspace_bytes(p, rows0)
+        if store_ds is not False and p.dtype == torch.bfloat16:
+            # the first block replayed (the last) sees the most response keys: its size serves all
+            nb_ds = api.bwd_ds_workspace_bytes(p, rows0, R)
+            if store_ds or api.ds_fits(nb_ds, dev):
+                nb_ws = nb_ds
+        ws_b = torch.empty((max(4, nb_ws) + 3) // 4, dtype=torch.float32, device=dev)
         for b in reversed(range(nb)):
             a, e = b * block, min(R, (b + 1) * block)
             api.replay_fwd(p, q[a:e], a, kr, vr, workspace=ws_f, o=o[a:e], lse=lse[a:e])
@@ -91,14 +98,15 @@ class GroupReplay:
 
 
 def replay_group(prefix: api.Prefix, members: Iterable, block: int, keep: str = "all",
-                 on_member: Callable | None = None) -> tuple[GroupReplay, list[MemberResult]]:
+                 on_member: Callable | None = None,
+                 store_ds: bool | None = None) -> tuple[GroupReplay, list[MemberResult]]:
     """Replay every member serially.  `members` yields dicts with q, kr, vr, do (device
     tensors), or callables returning one, so inputs can be produced one member at a time."""
     grp = GroupReplay(prefix)
     results = []
     for i, m in enumerate(members):
         inp = m() if callable(m) else m
-        r = grp.replay_member(inp["q"], inp["kr"], inp["vr"], inp["do"], block, keep=keep)
+        r = grp.replay_member(inp["q"], inp["kr"], inp["vr"], inp["do"], block, keep=keep, store_ds=store_ds)
         del inp
         if on_member is not None:
             on_member(i, r)

@@ -84,8 +84,10 @@ class Case:
         return api.Prefix(self.hq, self.hkv, self.d, self.dtype, self.P, table, k_pages, v_pages,
                           list(self.bounds))
 
-    def gpu(self, q_start, n_rows, prefix=None, kr=None, vr=None, first_touch=True):
-        """Forward + backward of rows [q_start, q_start + n_rows) through the C ABI."""
+    def gpu(self, q_start, n_rows, prefix=None, kr=None, vr=None, first_touch=True, store_ds=False):
+        """Forward + backward of rows [q_start, q_start + n_rows) through the C ABI.  store_ds
+        gives the backward a workspace large enough for its stored-dS dQ pass, filled with NaN
+        so that any slot the dK/dV pass did not write and the dQ pass still used would show."""
         pre = prefix or self.prefix()
         dev = "cuda"
         q = self.q[q_start:q_start + n_rows].to(dev).contiguous()
@@ -99,8 +101,13 @@ class Case:
         dv_r = torch.full(kr.shape, float("nan"), dtype=torch.float32, device=dev)
         dk_p = torch.full(pre.k_pages.shape, float("nan"), dtype=torch.float32, device=dev)
         dv_p = torch.full(pre.k_pages.shape, float("nan"), dtype=torch.float32, device=dev)
+        ws = None
+        if store_ds:
+            nbytes = api.bwd_ds_workspace_bytes(pre, n_rows, q_start + n_rows)
+            assert nbytes > api.bwd_workspace_bytes(pre, n_rows)
+            ws = torch.full(((nbytes + 3) // 4,), float("nan"), dtype=torch.float32, device=dev)
         dq = api.replay_bwd(pre, q, q_start, kr, vr, o, lse, do, dk_r, dv_r, True, dk_p, dv_p,
-                            shard_first_touch=[first_touch] * pre.n_shards)
+                            shard_first_touch=[first_touch] * pre.n_shards, workspace=ws)
         torch.cuda.synchronize()
         return dict(o=o, lse=lse, dq=dq, dkr=dk_r, dvr=dv_r, dk_pages=dk_p, dv_pages=dv_p,
                     o_parts=o_parts, lse_parts=lse_parts, prefix=pre)
@@ -130,10 +137,10 @@ class Case:
                                  self.token_bounds(), q_start)
 
 
-def check_against_oracle(case: Case, q_start: int, n_rows: int, res=None, parts=True, atol=None):
+def check_against_oracle(case: Case, q_start: int, n_rows: int, res=None, parts=True, atol=None, store_ds=False):
     """atol: optional per-tensor max-abs bounds (for inputs scaled away from N(0, 1))."""
     atol = atol or {}
-    res = res or case.gpu(q_start, n_rows)
+    res = res or case.gpu(q_start, n_rows, store_ds=store_ds)
     # The backward's delta is formed from the stored output, which has the input dtype; the
     # oracle's reference backward takes its own output rounded the same way.
     ref_exact = case.oracle(q_start, n_rows)

@@ -31,7 +31,8 @@ def _prefix(cfg, kp, vp, table):
 
 
 def _block(pre, m, q_start, n):
-    """One replayed block (forward + first-touch backward) through the C ABI."""
+    """One replayed block (forward + first-touch backward) through the C ABI, with the
+    stored-dS backward that the benchmark runs at this size."""
     q, do = m["q"][q_start:q_start + n].contiguous(), m["do"][q_start:q_start + n].contiguous()
     o, lse, _ = api.replay_fwd(pre, q, q_start, m["kr"], m["vr"])
     dkr = torch.empty(m["kr"].shape, dtype=torch.float32, device="cuda")
@@ -39,7 +40,7 @@ def _block(pre, m, q_start, n):
     dkp = torch.empty(pre.k_pages.shape, dtype=torch.float32, device="cuda")
     dvp = torch.empty_like(dkp)
     dq = api.replay_bwd(pre, q, q_start, m["kr"], m["vr"], o, lse, do, dkr, dvr, True, dkp, dvp,
-                        shard_first_touch=[True] * pre.n_shards)
+                        shard_first_touch=[True] * pre.n_shards, store_ds=True)
     torch.cuda.synchronize()
     return dict(o=o, lse=lse, dq=dq, dkr=dkr, dvr=dvr, dkp=dkp, dvp=dvp)
 

@@ -215,3 +215,69 @@ def test_capture_gather_exact():
     table = torch.arange(8, dtype=torch.int32)
     kpg, vpg = api.capture_pages(x.cuda(), x.cuda(), table.cuda(), 8, page_dtype=torch.bfloat16)
     assert torch.equal(api.gather_pages(kpg, table.cuda(), P).cpu(), x.to(torch.bfloat16))
+
+
+# ---- the stored-dS backward: the dK/dV pass writes dS, the dQ pass reads it back
+
+STORED_DS_CASES = [
+    # (P, R, hq, hkv, d, S, q_start, n_rows, seed): every head dim, GQA 6 with a ragged prompt
+    # tail and a mid-response block, a row count that is not a multiple of the dQ pass's
+    # 256-row block, a promptless block, a single row
+    (700, 160, 6, 2, 64, 3, 32, 96, 21),
+    (700, 160, 6, 2, 128, 3, 32, 96, 22),
+    (700, 160, 6, 2, 256, 3, 32, 96, 23),
+    (1000, 300, 24, 4, 256, 8, 100, 200, 24),
+    (1500, 700, 12, 2, 256, 5, 0, 700, 25),
+    (0, 200, 6, 2, 256, 1, 72, 128, 26),
+    (130, 5, 6, 1, 256, 2, 4, 1, 27),
+]
+
+
+@pytest.mark.parametrize("case", STORED_DS_CASES, ids=lambda c: f"P{c[0]}_R{c[1]}_h{c[2]}x{c[3]}_d{c[4]}_S{c[5]}_rows{c[6]}+{c[7]}")
+def test_stored_ds_matches_oracle(case):
+    P, R, hq, hkv, d, S, q0, n, seed = case
+    log(f"case: stored dS bf16 P={P} R={R} hq={hq} hkv={hkv} d={d} S={S} rows [{q0}, {q0 + n})")
+    c = Case(P, R, hq, hkv, d, torch.bfloat16, seed=seed, S=S)
+    check_against_oracle(c, q0, n, parts=False, store_ds=True)
+
+
+def test_stored_ds_uneven_and_empty_shards():
+    log("case: stored dS, bounds [0,0,3,3,11,20]")
+    c = Case(1280, 64, 12, 4, 256, torch.bfloat16, seed=28, bounds=[0, 0, 3, 3, 11, 20])
+    check_against_oracle(c, 0, 64, parts=False, store_ds=True)
+
+
+def test_stored_ds_equals_recompute():
+    """Both dQ passes see the same dS: the forward and dK/dV are bit-identical (the dK/dV pass
+    only adds the exact zeros of the rows it now also walks), and dQ agrees to the rounding of
+    the two contraction orders."""
+    log("case: stored dS vs recompute P=2000 R=384 hq=24 hkv=4 d=256 S=4 rows [128, 384)")
+    c = Case(2000, 384, 24, 4, 256, torch.bfloat16, seed=29, S=4)
+    pre = c.prefix()
+    a = c.gpu(128, 256, prefix=pre)
+    b = c.gpu(128, 256, prefix=pre, store_ds=True)
+    for k in ("o", "lse", "dkr", "dvr", "dk_pages", "dv_pages"):
+        assert torch.equal(a[k][torch.isfinite(a[k])], b[k][torch.isfinite(a[k])]), k
+    assert_close("dQ", np32(b["dq"]), np32(a["dq"]).astype(np.float64), atol=2e-3, rel_l2=1e-4)
+
+
+def test_stored_ds_keys_never_read_and_deterministic():
+    """NaN in unseen response keys and in the unused rows of the partial last page changes
+    nothing on the stored-dS path either, and two runs agree bit for bit."""
+    log("case: stored dS, NaN poisoning P=650 R=256 rows [64, 128)")
+    c = Case(650, 256, 6, 2, 256, torch.bfloat16, seed=30, S=2)
+    clean = c.gpu(64, 64, store_ds=True)
+    again = c.gpu(64, 64, store_ds=True)
+    for k in ("o", "lse", "dq", "dkr", "dvr", "dk_pages", "dv_pages"):
+        fin = torch.isfinite(clean[k])
+        assert torch.equal(clean[k][fin], again[k][fin]), k
+    kr = c.kr.clone()
+    vr = c.vr.clone()
+    kr[128:] = float("nan")
+    vr[128:] = float("nan")
+    pre = c.prefix(pool_fill=float("nan"))
+    dirty = c.gpu(64, 64, prefix=pre, kr=kr, vr=vr, store_ds=True)
+    for k in ("o", "lse", "dq"):
+        assert torch.equal(clean[k], dirty[k]), k
+    assert torch.equal(clean["dkr"][:128], dirty["dkr"][:128])
+    assert np.array_equal(c.logical(clean["dk_pages"]), c.logical(dirty["dk_pages"]))

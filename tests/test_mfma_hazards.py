@@ -23,7 +23,7 @@ import pytest
 
 from suffix_attention_amd import build
 
-SOURCES = ["attn_mfma_bwd.hip", "attn_mfma_dq.hip"]
+SOURCES = ["attn_mfma_bwd.hip", "attn_mfma_dq.hip", "attn_mfma_dqs.hip"]
 
 
 def _regs(tok: str) -> set:
