@@ -162,6 +162,11 @@ def block_pairs(cfg):
     return out
 
 
+# Backward workspace: None lets the driver keep dS for the dQ pass when it fits in device
+# memory; True / False force either dQ pass.
+STORE_DS = None
+
+
 def run_steps(prefix, members, cfg, n, cycle_log=None):
     """n optimizer cycles: each a fresh group (gradient pages allocated at its first backward,
     released at its end) replaying every member.  cycle_log, if given, receives (ms, peak bytes)
@@ -174,7 +179,8 @@ def run_steps(prefix, members, cfg, n, cycle_log=None):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
         grp = driver.GroupReplay(prefix)
-        results = [grp.replay_member(m["q"], m["kr"], m["vr"], m["do"], cfg.B, keep="none") for m in members]
+        results = [grp.replay_member(m["q"], m["kr"], m["vr"], m["do"], cfg.B, keep="none", store_ds=STORE_DS)
+                   for m in members]
         last = (grp, results)
         if cycle_log is not None:
             e1.record()
@@ -344,6 +350,8 @@ def main():
     ap.add_argument("--prefill-tokens", type=int, default=524288)
     ap.add_argument("--prefill-chunk", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--store-ds", default="auto", choices=["auto", "on", "off"],
+                    help="dQ from the dS stored by the dK/dV pass (auto: when it fits in device memory)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a device copy of known size (for HBM counter calibration)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
@@ -368,6 +376,8 @@ def main():
     cfg = configs.CONFIGS[ns.config]
     if ns.G:
         cfg = cfg.with_(G=ns.G)
+    global STORE_DS
+    STORE_DS = {"auto": None, "on": True, "off": False}[ns.store_ds]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 

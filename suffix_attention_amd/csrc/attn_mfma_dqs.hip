@@ -85,9 +85,11 @@ __device__ __forceinline__ void units_at(int k, Fn&& f) {
         if (un >= k * N / STEPS && un < (k + 1) * N / STEPS) f(un);
 }
 
+// Blocks (256-row block, part, kv head), dealt to the XCDs by deal_block(): every XCD gets an
+// equal run of the long prompt-shard blocks, then of the short response-part blocks.
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void dqs_mfma_kernel(AttnArgs a, int n_rblocks, int part0, int n_parts_l, int n_blocks) {
+void dqs_mfma_kernel(AttnArgs a, int n_rblocks) {
     using F = TileShape<D>;
     constexpr int NW = 4;
     constexpr int PW = KeyTiles<D, NW>::PER_WAVE;  // K copies per wave per page
@@ -96,11 +98,11 @@ void dqs_mfma_kernel(AttnArgs a, int n_rblocks, int part0, int n_parts_l, int n_
     __shared__ __attribute__((aligned(1024))) char kbuf[2][F::TILE];
     __shared__ __attribute__((aligned(1024))) char dbuf[3][NW][kDsWave];
 
-    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
-    if (lb >= n_blocks) return;
-    const int rblock = lb % n_rblocks;
-    const int part = part0 + (lb / n_rblocks) % n_parts_l;
-    const int kvh = lb / (n_rblocks * n_parts_l);
+    const XcdBlock blk = deal_block(blockIdx.x, n_rblocks, a.n_shards, a.n_parts, a.hkv);
+    if (blk.qtile_g < 0) return;
+    const int rblock = blk.qtile_g;
+    const int part = blk.part;
+    const int kvh = blk.kvh;
     const bool resp = part == a.n_shards;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -219,9 +221,8 @@ template <int D>
 hipError_t launch_dqs_d(const AttnArgs& a, hipStream_t s) {
     const int64_t rows_total = a.n_rows * a.g;
     const int n_rblocks = (int)((rows_total + 255) / 256);
-    const int nb = n_rblocks * a.n_parts * a.hkv;
-    if (nb == 0) return hipSuccess;
-    dqs_mfma_kernel<D><<<pad_grid(nb), 256, 0, s>>>(a, n_rblocks, 0, a.n_parts, nb);
+    if (n_rblocks == 0) return hipSuccess;
+    dqs_mfma_kernel<D><<<deal_grid(n_rblocks, a.n_shards, a.n_parts, a.hkv), 256, 0, s>>>(a, n_rblocks);
     return hipGetLastError();
 }
 

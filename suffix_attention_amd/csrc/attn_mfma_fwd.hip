@@ -328,51 +328,15 @@ __device__ __forceinline__ void output_copy_slot(const PartInfo<D>& pi, int64_t 
 }
 
 // Blocks (query tile, part, kv head); the query tiles of each member (pre-step scoring runs
-// several members' blocks at once) are numbered member-major, n_qtiles_m per member.
-//
-// Only one block fits on a compute unit, and a prompt-shard block runs for thousands of pages
-// while a response-part block runs for a few, so the order in which blocks reach the XCDs
-// decides the balance.  The hardware deals block ids round-robin to the eight XCDs; each XCD
-// takes an equal, contiguous run of the prompt-shard blocks (kv head, shard, query tile
-// order: the query tiles that read the same pages share that XCD's L2) and then an equal run
-// of the response-part blocks, which fill in behind the long ones.  Padding ids return.
-struct FwdBlock {
-    int qtile_g, part, kvh;  // qtile_g < 0: padding
-};
-
-__device__ __forceinline__ FwdBlock fwd_block(int b, int n_qtiles, int n_shards, int n_parts, int hkv) {
-    const int x = b % kXcds, slot = b / kXcds;
-    const int n_long = n_qtiles * n_shards * hkv;
-    const int lq = n_long / kXcds, lr = n_long % kXcds;
-    const int cnt_l = lq + (x < lr ? 1 : 0);
-    if (slot < cnt_l) {
-        const int item = x * lq + (x < lr ? x : lr) + slot;
-        return {item % n_qtiles, (item / n_qtiles) % n_shards, item / (n_qtiles * n_shards)};
-    }
-    // short runs are dealt from the other end, so that the XCDs holding an extra long block
-    // are the last to hold an extra short one
-    const int n_rp = n_parts - n_shards;
-    const int n_short = n_qtiles * n_rp * hkv;
-    const int xr = kXcds - 1 - x;
-    const int sq = n_short / kXcds, sr = n_short % kXcds;
-    const int s2 = slot - cnt_l;
-    if (s2 >= sq + (xr < sr ? 1 : 0)) return {-1, 0, 0};
-    const int item = xr * sq + (xr < sr ? xr : sr) + s2;
-    return {item % n_qtiles, n_shards + (item / n_qtiles) % n_rp, item / (n_qtiles * n_rp)};
-}
-
-inline int fwd_grid(int64_t n_qtiles, int n_shards, int n_parts, int hkv) {
-    const int64_t n_long = n_qtiles * n_shards * hkv, n_short = n_qtiles * (n_parts - n_shards) * hkv;
-    return (int)(kXcds * ((n_long + kXcds - 1) / kXcds + (n_short + kXcds - 1) / kXcds));
-}
-
+// several members' blocks at once) are numbered member-major, n_qtiles_m per member.  They
+// reach the XCDs as deal_block() orders them (long prompt-shard blocks first, evenly).
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kNW * 64, kNW * 64), amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles) {
     using F = TileShape<D>;
     __shared__ __attribute__((aligned(1024))) FwdLds<D> L;
 
-    const FwdBlock blk = fwd_block(blockIdx.x, n_qtiles, a.n_shards, a.n_parts, a.hkv);
+    const XcdBlock blk = deal_block(blockIdx.x, n_qtiles, a.n_shards, a.n_parts, a.hkv);
     if (blk.qtile_g < 0) return;
     const int qtile_g = blk.qtile_g;
     const int member = qtile_g / n_qtiles_m;
@@ -530,7 +494,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
     const int64_t n_qtiles = n_qtiles_m * a.n_members;
     const int64_t n_blocks = n_qtiles * a.n_parts * a.hkv;
     if (n_blocks == 0) return hipSuccess;
-    const int grid = fwd_grid(n_qtiles, a.n_shards, a.n_parts, a.hkv);
+    const int grid = deal_grid(n_qtiles, a.n_shards, a.n_parts, a.hkv);
     KernelTimer kt("fwd_mfma", s);
     fwd_mfma_kernel<D><<<grid, kNW * 64, 0, s>>>(a, (int)n_qtiles_m, (int)n_qtiles);
     return hipGetLastError();

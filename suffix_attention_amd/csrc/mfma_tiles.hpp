@@ -183,4 +183,43 @@ __host__ __device__ constexpr uint32_t tr_x(int dt, int R) {
     return (uint32_t)(((4 * dt) ^ swz<D>(R)) << 4);
 }
 
+// Blocks (query tile, part, kv head) of the matrix-core kernels that walk a part's keys for a
+// tile of query rows (the forward, the dQ passes).
+//
+// Only one block fits on a compute unit, and a prompt-shard block runs for thousands of pages
+// while a response-part block runs for a few, so the order in which blocks reach the XCDs
+// decides the balance.  The hardware deals block ids round-robin to the eight XCDs; each XCD
+// takes an equal, contiguous run of the prompt-shard blocks (kv head, shard, query tile
+// order: the query tiles that read the same pages share that XCD's L2) and then an equal run
+// of the response-part blocks, which fill in behind the long ones.  Padding ids return.
+struct XcdBlock {
+    int qtile_g, part, kvh;  // qtile_g < 0: padding
+};
+
+__device__ __forceinline__ XcdBlock deal_block(int b, int n_qtiles, int n_shards, int n_parts, int hkv) {
+    const int x = b % kXcds, slot = b / kXcds;
+    const int n_long = n_qtiles * n_shards * hkv;
+    const int lq = n_long / kXcds, lr = n_long % kXcds;
+    const int cnt_l = lq + (x < lr ? 1 : 0);
+    if (slot < cnt_l) {
+        const int item = x * lq + (x < lr ? x : lr) + slot;
+        return {item % n_qtiles, (item / n_qtiles) % n_shards, item / (n_qtiles * n_shards)};
+    }
+    // short runs are dealt from the other end, so that the XCDs holding an extra long block
+    // are the last to hold an extra short one
+    const int n_rp = n_parts - n_shards;
+    const int n_short = n_qtiles * n_rp * hkv;
+    const int xr = kXcds - 1 - x;
+    const int sq = n_short / kXcds, sr = n_short % kXcds;
+    const int s2 = slot - cnt_l;
+    if (s2 >= sq + (xr < sr ? 1 : 0)) return {-1, 0, 0};
+    const int item = xr * sq + (xr < sr ? xr : sr) + s2;
+    return {item % n_qtiles, n_shards + (item / n_qtiles) % n_rp, item / (n_qtiles * n_rp)};
+}
+
+inline int deal_grid(int64_t n_qtiles, int n_shards, int n_parts, int hkv) {
+    const int64_t n_long = n_qtiles * n_shards * hkv, n_short = n_qtiles * (n_parts - n_shards) * hkv;
+    return (int)(kXcds * ((n_long + kXcds - 1) / kXcds + (n_short + kXcds - 1) / kXcds));
+}
+
 }  // namespace ls
