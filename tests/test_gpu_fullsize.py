@@ -30,9 +30,9 @@ def _prefix(cfg, kp, vp, table):
                       api.even_shard_bounds(cfg.n_pages, cfg.S))
 
 
-def _block(pre, m, q_start, n):
-    """One replayed block (forward + first-touch backward) through the C ABI, with the
-    stored-dS backward that the benchmark runs at this size."""
+def _block(pre, m, q_start, n, store_ds=True):
+    """One replayed block (forward + first-touch backward) through the C ABI; by default with
+    the stored-dS backward that the benchmark runs at the 2M-token size."""
     q, do = m["q"][q_start:q_start + n].contiguous(), m["do"][q_start:q_start + n].contiguous()
     o, lse, _ = api.replay_fwd(pre, q, q_start, m["kr"], m["vr"])
     dkr = torch.empty(m["kr"].shape, dtype=torch.float32, device="cuda")
@@ -40,20 +40,20 @@ def _block(pre, m, q_start, n):
     dkp = torch.empty(pre.k_pages.shape, dtype=torch.float32, device="cuda")
     dvp = torch.empty_like(dkp)
     dq = api.replay_bwd(pre, q, q_start, m["kr"], m["vr"], o, lse, do, dkr, dvr, True, dkp, dvp,
-                        shard_first_touch=[True] * pre.n_shards, store_ds=True)
+                        shard_first_touch=[True] * pre.n_shards, store_ds=store_ds)
     torch.cuda.synchronize()
     return dict(o=o, lse=lse, dq=dq, dkr=dkr, dvr=dvr, dkp=dkp, dvp=dvp)
 
 
-def test_c2m_block_sampled_rows_and_gradient_sums():
-    cfg = C2M
-    q_start, n = cfg.R - cfg.B, cfg.B
-    log(f"case: c2m P={cfg.P} block rows [{q_start}, {q_start + n}) sampled rows + gradient sums")
+def _sampled_rows_and_gradient_sums(cfg, q_start, n, rows, store_ds):
+    """The block [q_start, q_start + n) of member 0 at the config's full size: sampled rows of
+    one kv head against the oracle over every key they see, and the gradient identities over
+    all keys."""
     table = datagen.page_table(cfg.n_pages, datagen.seed(cfg.cfg_id, datagen.TAG_PERM), "cuda")
     kp, vp = datagen.prefix_kv(cfg, "cuda")
     pre = _prefix(cfg, kp, vp, table)
     m = datagen.member_inputs(cfg, 0, "cuda")
-    res = _block(pre, m, q_start, n)
+    res = _block(pre, m, q_start, n, store_ds=store_ds)
     g = cfg.g
     kend = q_start + n
 
@@ -61,8 +61,8 @@ def test_c2m_block_sampled_rows_and_gradient_sums():
     kvh = 1
     heads = slice(kvh * g, (kvh + 1) * g)
     kp1, vp1 = np32(kp[:, kvh:kvh + 1]), np32(vp[:, kvh:kvh + 1])
-    kr1, vr1 = np32(m["kr"][:, kvh:kvh + 1]), np32(m["vr"][:, kvh:kvh + 1])
-    for r in (0, 511, n - 1):
+    kr1, vr1 = np32(m["kr"][:kend, kvh:kvh + 1]), np32(m["vr"][:kend, kvh:kvh + 1])
+    for r in rows:
         pos = q_start + r
         qr = np32(m["q"][pos:pos + 1, heads])
         dor = np32(m["do"][pos:pos + 1, heads])
@@ -73,20 +73,45 @@ def test_c2m_block_sampled_rows_and_gradient_sums():
         assert_close("O", np32(res["o"][r:r + 1, heads]), O)
         assert_close("LSE", np32(res["lse"][r:r + 1, heads]), L)
         assert_close("dQ", np32(res["dq"][r:r + 1, heads]), gr["dq"])
-    del kp1, vp1
+    del kp1, vp1, kp, vp
 
     # sum over every key the block sees of dV = sum over its rows and group heads of dO;
     # sum of dK = scale * sum_rows sum_keys dS q = 0, because sum_keys dS = delta - delta
     f64 = torch.float64
-    dv_sum = res["dvp"].to(f64).sum(dim=(0, 2)) + res["dvr"][:kend].to(f64).sum(dim=0)      # [hkv, d]
-    dk_sum = res["dkp"].to(f64).sum(dim=(0, 2)) + res["dkr"][:kend].to(f64).sum(dim=0)
-    do_sum = m["do"][q_start:kend].to(f64).view(n, cfg.hkv, g, cfg.d).sum(dim=(0, 2))
+    dv_sum = res["dvp"].sum(dim=(0, 2), dtype=f64) + res["dvr"][:kend].sum(dim=0, dtype=f64)      # [hkv, d]
+    dk_sum = res["dkp"].sum(dim=(0, 2), dtype=f64) + res["dkr"][:kend].sum(dim=0, dtype=f64)
+    do_sum = m["do"][q_start:kend].view(n, cfg.hkv, g, cfg.d).sum(dim=(0, 2), dtype=f64)
     rel_dv = float((dv_sum - do_sum).norm() / do_sum.norm())
-    dk_rss = float(torch.sqrt((res["dkp"].to(f64) ** 2).sum() + (res["dkr"][:kend].to(f64) ** 2).sum()))
-    rel_dk = float(dk_sum.norm()) / dk_rss
+    dk_sq = sum(float(torch.linalg.vector_norm(x, dtype=f64) ** 2) for x in (res["dkp"], res["dkr"][:kend]))
+    rel_dk = float(dk_sum.norm()) / math.sqrt(dk_sq)
     log(f"    sum dV vs sum dO rel={rel_dv:.3e}; |sum dK| / ||dK||_F = {rel_dk:.3e}")
     assert rel_dv <= 5e-3
     assert rel_dk <= 2e-2
+
+
+def test_c2m_block_sampled_rows_and_gradient_sums():
+    cfg = C2M
+    q_start, n = cfg.R - cfg.B, cfg.B
+    log(f"case: c2m P={cfg.P} block rows [{q_start}, {q_start + n}) sampled rows + gradient sums")
+    _sampled_rows_and_gradient_sums(cfg, q_start, n, (0, 511, n - 1), store_ds=True)
+
+
+def test_c1m_block_sampled_rows_and_gradient_sums():
+    """The 1M-token workload's last reverse block of 512 rows (of a 2,048-token response)."""
+    cfg = configs.CONFIGS["c1m"]
+    q_start, n = cfg.R - cfg.B, cfg.B
+    log(f"case: c1m P={cfg.P} block rows [{q_start}, {q_start + n}) sampled rows + gradient sums")
+    _sampled_rows_and_gradient_sums(cfg, q_start, n, (0, 300, n - 1), store_ds=True)
+
+
+def test_stress_block_sampled_rows_and_gradient_sums():
+    """The stress workload's last reverse block: 8,192 rows at the end of a 262,144-token
+    response over a 4,194,304-token prompt in 16 shards, so its rows see 4,456,448 keys.  One
+    block's dS would take 1.75 TB, so the backward recomputes (as the driver chooses there)."""
+    cfg = configs.CONFIGS["stress"]
+    q_start, n = cfg.R - cfg.B, cfg.B
+    log(f"case: stress P={cfg.P} S={cfg.S} block rows [{q_start}, {q_start + n}) sampled rows + gradient sums")
+    _sampled_rows_and_gradient_sums(cfg, q_start, n, (0, 4097, n - 1), store_ds=False)
 
 
 def test_c2m_zero_keys_closed_form():
