@@ -155,6 +155,11 @@ size_t ls_bwd_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows);
  * bytes (but at least ls_bwd_workspace_bytes) the dQ pass recomputes them.  Both give dQ
  * within the bf16 rounding of dS of each other; dK, dV, delta are the same either way.
  *
+ * A workspace between the two sizes that holds the dS of at least one kv head, i.e. at least
+ * round_up(ls_bwd_workspace_bytes, 256) + (ls_bwd_ds_workspace_bytes - that) / hkv bytes,
+ * selects the stored-dS pass in chunks of as many kv heads as it holds (dK/dV then dQ per
+ * chunk; kv heads are independent, so the results are the same bit for bit).
+ *
  * Layout: the recompute workspace, then from the next 256-byte boundary the stored dS, bf16
  * [hkv][row tiles][key slots][32]: row tiles of 32 group rows (r = token * g + j for query
  * head kv * g + j) padded to a multiple of 256 rows, key slots 128 per page pair, prompt pairs

@@ -152,15 +152,19 @@ def bwd_workspace_bytes(prefix: Prefix, n_rows: int) -> int:
     return n
 
 
-def bwd_ds_workspace_bytes(prefix: Prefix, n_rows: int, key_end: int) -> int:
+def bwd_ds_workspace_bytes(prefix: Prefix, n_rows: int, key_end: int, heads: int | None = None) -> int:
     """Backward workspace that also holds the block's dS (bf16), so that dQ is formed from it
     rather than recomputed; key_end = q_start + n_rows (the largest over a member's blocks
-    sizes one workspace for all of them)."""
+    sizes one workspace for all of them).  heads < hkv sizes it for that many kv heads' dS,
+    which the library then processes a chunk of kv heads at a time."""
     st = prefix.struct()
     n = lib().ls_bwd_ds_workspace_bytes(C.byref(st), n_rows, key_end)
     if n == 0 and n_rows > 0:
         raise LongStrawError(_lib.LS_ERR_INVALID, lib().ls_last_error().decode())
-    return n
+    if heads is None or heads >= prefix.hkv or prefix.dtype != torch.bfloat16:
+        return n
+    base = (bwd_workspace_bytes(prefix, n_rows) + 255) // 256 * 256
+    return base + heads * ((n - base) // prefix.hkv)
 
 
 def ds_fits(nbytes: int, device, fraction: float = 0.9) -> bool:

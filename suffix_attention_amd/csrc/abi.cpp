@@ -335,11 +335,16 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (pre->dtype == LS_DTYPE_BF16 && !force_generic()) {
-        // a workspace that also holds the block's dS selects the stored-dS dQ pass
-        if (n_rows > 0 && ws_bytes >= ds_offset(pre, n_rows) + ds_bytes(pre, n_rows, a.key_end)) {
-            a.ds = (uint16_t*)((char*)workspace + ds_offset(pre, n_rows));
+        // a workspace that also holds the dS of one or more kv heads selects the stored-dS dQ
+        // pass, run over as many kv heads at a time as the workspace holds
+        const size_t per_head = ds_bytes(pre, n_rows, a.key_end) / (size_t)pre->hkv;
+        const size_t off = ds_offset(pre, n_rows);
+        if (n_rows > 0 && per_head > 0 && ws_bytes >= off + per_head) {
+            a.ds = (uint16_t*)((char*)workspace + off);
             a.ds_rt = ls::ds_row_tiles(n_rows * a.g);
             a.ds_kslots = ls::ds_key_slots(a.n_logical_pages, a.key_end, &a.ds_resp_slot0);
+            const size_t fit = (ws_bytes - off) / per_head;
+            a.ds_heads = fit < (size_t)pre->hkv ? (int)fit : pre->hkv;
         }
         e = ls::launch_bwd_mfma(a, s);  // its prep kernel also writes delta
     } else {

@@ -291,7 +291,7 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int pair0, int n_pairs
 
     const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
     if (lb >= n_blocks) return;
-    const int kvh = lb / n_pairs_l;
+    const int kvh = (DS ? a.ds_kvh0 : 0) + lb / n_pairs_l;
     const int pair = pair0 + lb % n_pairs_l;
     const bool resp = pair >= n_pp;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -391,7 +391,7 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int pair0, int n_pairs
         int64_t ds_step = 0;
         if (DS) {
             const int64_t slot = 128 * (int64_t)pair + 64 * (w >> 1) + 32 * kh + n;
-            ds_p = (u32x4*)(a.ds + ((int64_t)kvh * a.ds_rt * a.ds_kslots + slot) * 32 + 16 * h);
+            ds_p = (u32x4*)(a.ds + ((int64_t)(kvh - a.ds_kvh0) * a.ds_rt * a.ds_kslots + slot) * 32 + 16 * h);
             ds_step = a.ds_kslots * 32 * 2 / 16;
         }
         for (int t = 0; t < n_st; t++) {
@@ -492,21 +492,34 @@ hipError_t launch_bwd_d(const AttnArgs& a, hipStream_t s) {
     // dK / dV
     const int n_pp = (int)((a.n_logical_pages + 1) / 2);
     const int n_rp = (int)((resp_tiles(a.key_end) + 1) / 2);
+    if (a.ds) {
+        // stored dS, a chunk of kv heads at a time: dK/dV writes the chunk's dS, dQ reads it
+        for (int k0 = 0; k0 < a.hkv; k0 += a.ds_heads) {
+            AttnArgs c = a;
+            c.ds_kvh0 = k0;
+            const int nh = a.hkv - k0 < a.ds_heads ? a.hkv - k0 : a.ds_heads;
+            if ((int64_t)(n_pp + n_rp) * nh > 0) {
+                KernelTimer kt("dkdv_mfma", s);
+                const int nbp = n_pp * nh, nbr = n_rp * nh;
+                if (nbp > 0) dkdv_mfma_kernel<D, false, true><<<pad_grid(nbp), 256, 0, s>>>(c, gr, n_pp, 0, n_pp, nbp);
+                if (nbr > 0) dkdv_mfma_kernel<D, true, true><<<pad_grid(nbr), 256, 0, s>>>(c, gr, n_pp, n_pp, n_rp, nbr);
+            }
+            hipError_t e = hipGetLastError();
+            if (e == hipSuccess) e = launch_dqs_mfma(c, nh, s);  // attn_mfma_dqs.hip
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     if ((int64_t)(n_pp + n_rp) * a.hkv > 0) {
         KernelTimer kt("dkdv_mfma", s);
         const int nbp = n_pp * a.hkv, nbr = n_rp * a.hkv;
-        if (a.ds) {
-            if (nbp > 0) dkdv_mfma_kernel<D, false, true><<<pad_grid(nbp), 256, 0, s>>>(a, gr, n_pp, 0, n_pp, nbp);
-            if (nbr > 0) dkdv_mfma_kernel<D, true, true><<<pad_grid(nbr), 256, 0, s>>>(a, gr, n_pp, n_pp, n_rp, nbr);
-        } else {
-            if (nbp > 0) dkdv_mfma_kernel<D, false, false><<<pad_grid(nbp), 256, 0, s>>>(a, gr, n_pp, 0, n_pp, nbp);
-            if (nbr > 0) dkdv_mfma_kernel<D, true, false><<<pad_grid(nbr), 256, 0, s>>>(a, gr, n_pp, n_pp, n_rp, nbr);
-        }
+        if (nbp > 0) dkdv_mfma_kernel<D, false, false><<<pad_grid(nbp), 256, 0, s>>>(a, gr, n_pp, 0, n_pp, nbp);
+        if (nbr > 0) dkdv_mfma_kernel<D, true, false><<<pad_grid(nbr), 256, 0, s>>>(a, gr, n_pp, n_pp, n_rp, nbr);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // dQ parts: from the stored dS (attn_mfma_dqs.hip), else recomputed (attn_mfma_dq.hip)
-    return a.ds ? launch_dqs_mfma(a, s) : launch_dq_mfma(a, gr, s);
+    // dQ parts recomputed (attn_mfma_dq.hip)
+    return launch_dq_mfma(a, gr, s);
 }
 
 }  // namespace

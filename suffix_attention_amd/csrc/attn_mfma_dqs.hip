@@ -89,7 +89,7 @@ __device__ __forceinline__ void units_at(int k, Fn&& f) {
 // equal run of the long prompt-shard blocks, then of the short response-part blocks.
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void dqs_mfma_kernel(AttnArgs a, int n_rblocks) {
+void dqs_mfma_kernel(AttnArgs a, int n_rblocks, int n_kvh) {
     using F = TileShape<D>;
     constexpr int NW = 4;
     constexpr int PW = KeyTiles<D, NW>::PER_WAVE;  // K copies per wave per page
@@ -98,11 +98,11 @@ void dqs_mfma_kernel(AttnArgs a, int n_rblocks) {
     __shared__ __attribute__((aligned(1024))) char kbuf[2][F::TILE];
     __shared__ __attribute__((aligned(1024))) char dbuf[3][NW][kDsWave];
 
-    const XcdBlock blk = deal_block(blockIdx.x, n_rblocks, a.n_shards, a.n_parts, a.hkv);
+    const XcdBlock blk = deal_block(blockIdx.x, n_rblocks, a.n_shards, a.n_parts, n_kvh);
     if (blk.qtile_g < 0) return;
     const int rblock = blk.qtile_g;
     const int part = blk.part;
-    const int kvh = blk.kvh;
+    const int kvh = a.ds_kvh0 + blk.kvh;  // the stored dS holds kv heads from ds_kvh0 on
     const bool resp = part == a.n_shards;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -128,7 +128,7 @@ void dqs_mfma_kernel(AttnArgs a, int n_rblocks) {
     }
     const KeyTiles<D, NW> kt(a, resp, lp0, kvh, w, lane);
     // the wave's dS source: row tile rt0 (rt0 + 1 is ds_rt_bytes further), from key slot0 on
-    const char* ds0 = (const char*)(a.ds + (((int64_t)kvh * a.ds_rt + rt0) * a.ds_kslots + slot0) * 32);
+    const char* ds0 = (const char*)(a.ds + (((int64_t)blk.kvh * a.ds_rt + rt0) * a.ds_kslots + slot0) * 32);
     const int64_t ds_rt_bytes = a.ds_kslots * 64;
     // copy j of the wave's dS for page t: row tile j / 4, keys 16 (j % 4) .. +16 (1 KiB)
     auto ds_piece = [&](int64_t t, uint32_t dst, int j) {
@@ -218,22 +218,22 @@ void dqs_mfma_kernel(AttnArgs a, int n_rblocks) {
 }
 
 template <int D>
-hipError_t launch_dqs_d(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_dqs_d(const AttnArgs& a, int n_kvh, hipStream_t s) {
     const int64_t rows_total = a.n_rows * a.g;
     const int n_rblocks = (int)((rows_total + 255) / 256);
-    if (n_rblocks == 0) return hipSuccess;
-    dqs_mfma_kernel<D><<<deal_grid(n_rblocks, a.n_shards, a.n_parts, a.hkv), 256, 0, s>>>(a, n_rblocks);
+    if (n_rblocks == 0 || n_kvh == 0) return hipSuccess;
+    dqs_mfma_kernel<D><<<deal_grid(n_rblocks, a.n_shards, a.n_parts, n_kvh), 256, 0, s>>>(a, n_rblocks, n_kvh);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_dqs_mfma(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_dqs_mfma(const AttnArgs& a, int n_kvh, hipStream_t s) {
     KernelTimer kt("dqs_mfma", s);
     switch (a.d) {
-        case 64: return launch_dqs_d<64>(a, s);
-        case 128: return launch_dqs_d<128>(a, s);
-        case 256: return launch_dqs_d<256>(a, s);
+        case 64: return launch_dqs_d<64>(a, n_kvh, s);
+        case 128: return launch_dqs_d<128>(a, n_kvh, s);
+        case 256: return launch_dqs_d<256>(a, n_kvh, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -60,10 +60,15 @@ struct AttnArgs {
     // Layout [hkv][ds_rt][ds_kslots][32] bf16: for kv head h, 32-row tile rt of its group rows
     // and key slot k, the 32 rows in the order of ds_row_of(); key slots are 128 per page pair,
     // prompt pairs first (slot = logical key), the response pairs from ds_resp_slot0 on.
+    // When the workspace holds dS for only some kv heads, the backward runs in chunks of
+    // ds_heads kv heads (dK/dV, then dQ, per chunk); ds_kvh0 is the first kv head of the chunk
+    // being launched, and the stored dS is indexed by kv head - ds_kvh0.
     uint16_t* ds;
     int64_t ds_rt;
     int64_t ds_kslots;
     int64_t ds_resp_slot0;
+    int ds_heads;
+    int ds_kvh0;
 };
 
 // Row (0..31) inside a 32-row tile of the stored-dS position p (0..31): the positions are in

@@ -31,7 +31,8 @@ inline GroupRows group_rows(void* base, int64_t rows_pad, int hkv, int d) {
 }
 
 hipError_t launch_dq_mfma(const AttnArgs& a, const GroupRows& gr, hipStream_t s);
-// dQ parts from the dS that the dK/dV pass stored (a.ds)
-hipError_t launch_dqs_mfma(const AttnArgs& a, hipStream_t s);
+// dQ parts of kv heads [a.ds_kvh0, a.ds_kvh0 + n_kvh) from the dS that the dK/dV pass stored
+// for them (a.ds)
+hipError_t launch_dqs_mfma(const AttnArgs& a, int n_kvh, hipStream_t s);
 
 }  // namespace ls

@@ -58,7 +58,8 @@ class GroupReplay:
         keep: "all" returns o, lse, dq, dk_resp, dv_resp; "none" drops them at the end
         (the prompt gradient pages still accumulate).  store_ds: give the backward the
         workspace in which it keeps dS for the dQ pass (True), or not (False); None does so
-        when it fits in device memory."""
+        when it fits in device memory, for all kv heads at once or for an equal chunk of
+        them at a time."""
         p = self.prefix
         R = q.shape[0]
         dev = q.device
@@ -75,10 +76,18 @@ class GroupReplay:
         ws_f = torch.empty((api.fwd_workspace_bytes(p, rows0) + 3) // 4, dtype=torch.float32, device=dev)
         nb_ws = api.bwd_workspace_bytes(p, rows0)
         if store_ds is not False and p.dtype == torch.bfloat16:
-            # the first block replayed (the last) sees the most response keys: its size serves all
+            # the first block replayed (the last) sees the most response keys: its size serves
+            # all; without room for every kv head's dS, the largest number of kv heads dividing
+            # hkv (equal chunks) whose dS fits
             nb_ds = api.bwd_ds_workspace_bytes(p, rows0, R)
             if store_ds or api.ds_fits(nb_ds, dev):
                 nb_ws = nb_ds
+            else:
+                for k in range(p.hkv - 1, 0, -1):
+                    nb_k = api.bwd_ds_workspace_bytes(p, rows0, R, heads=k)
+                    if p.hkv % k == 0 and api.ds_fits(nb_k, dev):
+                        nb_ws = nb_k
+                        break
         ws_b = torch.empty((max(4, nb_ws) + 3) // 4, dtype=torch.float32, device=dev)
         for b in reversed(range(nb)):
             a, e = b * block, min(R, (b + 1) * block)

@@ -281,3 +281,38 @@ def test_stored_ds_keys_never_read_and_deterministic():
         assert torch.equal(clean[k], dirty[k]), k
     assert torch.equal(clean["dkr"][:128], dirty["dkr"][:128])
     assert np.array_equal(c.logical(clean["dk_pages"]), c.logical(dirty["dk_pages"]))
+
+
+def test_stored_ds_in_kv_head_chunks_is_bitwise_the_same():
+    """A workspace with room for the dS of 1, 2 or 3 of the 4 kv heads runs the stored-dS
+    backward a chunk of kv heads at a time; kv heads are independent, so every output is the
+    same bit for bit as with room for all of them."""
+    log("case: stored dS in kv-head chunks P=1500 R=256 hq=24 hkv=4 d=256 S=3 rows [64, 256)")
+    c = Case(1500, 256, 24, 4, 256, torch.bfloat16, seed=31, S=3)
+    pre = c.prefix()
+    dev = "cuda"
+    q0, n = 64, 192
+    q, do = c.q[q0:q0 + n].to(dev).contiguous(), c.do[q0:q0 + n].to(dev).contiguous()
+    kr, vr = c.kr.to(dev), c.vr.to(dev)
+    o, lse, _ = api.replay_fwd(pre, q, q0, kr, vr)
+
+    def run(heads):
+        nbytes = api.bwd_ds_workspace_bytes(pre, n, q0 + n, heads=heads)
+        ws = torch.full(((nbytes + 3) // 4,), float("nan"), dtype=torch.float32, device=dev)
+        dk_r = torch.empty(kr.shape, dtype=torch.float32, device=dev)
+        dv_r = torch.empty_like(dk_r)
+        dk_p = torch.empty(pre.k_pages.shape, dtype=torch.float32, device=dev)
+        dv_p = torch.empty_like(dk_p)
+        dq = api.replay_bwd(pre, q, q0, kr, vr, o, lse, do, dk_r, dv_r, True, dk_p, dv_p,
+                            shard_first_touch=[True] * pre.n_shards, workspace=ws)
+        torch.cuda.synchronize()
+        return dq, dk_r[:q0 + n], dv_r[:q0 + n], dk_p, dv_p
+
+    full = run(None)
+    ref = c.oracle(q0, n, o_used=c.stored(c.oracle(q0, n)["o"]))
+    assert_close("dQ", np32(full[0]), ref["dq"])
+    assert api.bwd_ds_workspace_bytes(pre, n, q0 + n, heads=1) < api.bwd_ds_workspace_bytes(pre, n, q0 + n)
+    for heads in (1, 2, 3):
+        got = run(heads)
+        for name, a, b in zip(("dq", "dk_r", "dv_r", "dk_p", "dv_p"), full, got):
+            assert torch.equal(a, b), (heads, name)
