@@ -161,9 +161,9 @@ size_t ls_bwd_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows);
  * chunk; kv heads are independent, so the results are the same bit for bit).
  *
  * Layout: the recompute workspace, then from the next 256-byte boundary the stored dS, bf16
- * [hkv][row tiles][key slots][32]: row tiles of 32 group rows (r = token * g + j for query
- * head kv * g + j) padded to a multiple of 256 rows, key slots 128 per page pair, prompt pairs
- * first.  The size is hkv * ceil(n_rows * g / 256) * 8 * 128 * (ceil(pages / 2) +
+ * [kv heads of the chunk][row tiles][key slots][32] (the same space serves each chunk in
+ * turn): row tiles of 32 group rows (r = token * g + j for query head kv * g + j) padded to a
+ * multiple of 256 rows, key slots 128 per page pair, prompt pairs first.  The size is hkv * ceil(n_rows * g / 256) * 8 * 128 * (ceil(pages / 2) +
  * ceil(ceil(key_end / 64) / 2)) * 64 bytes: 103 GB for 1,024 rows over a 2,097,152-token
  * prompt with hq = 24, hkv = 4.  A workspace sized for the largest key_end serves every block
  * of a member.
