@@ -104,6 +104,21 @@ def test_workspace_size_and_errors():
     assert "multiple" in _err()
 
 
+def test_stored_ds_workspace_size():
+    """The backward workspace with room for dS: the recompute workspace rounded up to 256
+    bytes, then kv heads x row tiles (group rows padded to 256, 32 per tile) x key slots (128
+    per page pair, prompt and response pairs) x 64 bytes; float32 stores none."""
+    p = _prefix()
+    lib = _lib.lib()
+    base = (lib.ls_bwd_workspace_bytes(C.byref(p), 16) + 255) // 256 * 256
+    # 16 rows x g 4 = 64 group rows -> 8 row tiles; 2 prompt pages -> 1 pair
+    assert lib.ls_bwd_ds_workspace_bytes(C.byref(p), 16, 16) == base + 2 * 8 * 128 * (1 + 1) * 64
+    assert lib.ls_bwd_ds_workspace_bytes(C.byref(p), 16, 200) == base + 2 * 8 * 128 * (1 + 2) * 64
+    assert lib.ls_bwd_ds_workspace_bytes(C.byref(p), 16, 15) == 0 and "key_end" in _err()
+    f = _prefix(dtype=LS_DTYPE_F32)
+    assert lib.ls_bwd_ds_workspace_bytes(C.byref(f), 16, 16) == lib.ls_bwd_workspace_bytes(C.byref(f), 16)
+
+
 def test_score_workspace_and_validation():
     """Batched scoring: the workspace is the forward one for members * rows rows; bad sizes,
     missing outputs and short workspaces are rejected before any launch."""
