@@ -167,9 +167,11 @@ def bwd_ds_workspace_bytes(prefix: Prefix, n_rows: int, key_end: int, heads: int
     return base + heads * ((n - base) // prefix.hkv)
 
 
-def ds_fits(nbytes: int, device, fraction: float = 0.9) -> bool:
+def ds_fits(nbytes: int, device, fraction: float = 0.9, budget: int | None = None) -> bool:
     """Whether a workspace of nbytes fits in what the device has free (counting the blocks
-    torch's allocator holds but does not use)."""
+    torch's allocator holds but does not use), or in `budget` bytes when one is given."""
+    if budget is not None:
+        return nbytes <= budget
     free, _ = torch.cuda.mem_get_info(device)
     cached = torch.cuda.memory_reserved(device) - torch.cuda.memory_allocated(device)
     return nbytes <= fraction * (free + cached)

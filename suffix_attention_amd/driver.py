@@ -52,14 +52,15 @@ class GroupReplay:
         return self.dk_pages, self.dv_pages
 
     def replay_member(self, q, kr, vr, do, block: int, keep: str = "all",
-                      on_block: Callable | None = None, store_ds: bool | None = None) -> MemberResult:
+                      on_block: Callable | None = None, store_ds: bool | None = None,
+                      ds_budget: int | None = None) -> MemberResult:
         """Forward + backward of one member's response, blocks in reverse order.
 
         keep: "all" returns o, lse, dq, dk_resp, dv_resp; "none" drops them at the end
         (the prompt gradient pages still accumulate).  store_ds: give the backward the
         workspace in which it keeps dS for the dQ pass (True), or not (False); None does so
-        when it fits in device memory, for all kv heads at once or for an equal chunk of
-        them at a time."""
+        when it fits in device memory (or in ds_budget bytes, if given), for all kv heads at
+        once or for an equal chunk of them at a time."""
         p = self.prefix
         R = q.shape[0]
         dev = q.device
@@ -80,12 +81,12 @@ class GroupReplay:
             # all; without room for every kv head's dS, the largest number of kv heads dividing
             # hkv (equal chunks) whose dS fits
             nb_ds = api.bwd_ds_workspace_bytes(p, rows0, R)
-            if store_ds or api.ds_fits(nb_ds, dev):
+            if store_ds or api.ds_fits(nb_ds, dev, budget=ds_budget):
                 nb_ws = nb_ds
             else:
                 for k in range(p.hkv - 1, 0, -1):
                     nb_k = api.bwd_ds_workspace_bytes(p, rows0, R, heads=k)
-                    if p.hkv % k == 0 and api.ds_fits(nb_k, dev):
+                    if p.hkv % k == 0 and api.ds_fits(nb_k, dev, budget=ds_budget):
                         nb_ws = nb_k
                         break
         ws_b = torch.empty((max(4, nb_ws) + 3) // 4, dtype=torch.float32, device=dev)
@@ -107,15 +108,16 @@ class GroupReplay:
 
 
 def replay_group(prefix: api.Prefix, members: Iterable, block: int, keep: str = "all",
-                 on_member: Callable | None = None,
-                 store_ds: bool | None = None) -> tuple[GroupReplay, list[MemberResult]]:
+                 on_member: Callable | None = None, store_ds: bool | None = None,
+                 ds_budget: int | None = None) -> tuple[GroupReplay, list[MemberResult]]:
     """Replay every member serially.  `members` yields dicts with q, kr, vr, do (device
     tensors), or callables returning one, so inputs can be produced one member at a time."""
     grp = GroupReplay(prefix)
     results = []
     for i, m in enumerate(members):
         inp = m() if callable(m) else m
-        r = grp.replay_member(inp["q"], inp["kr"], inp["vr"], inp["do"], block, keep=keep, store_ds=store_ds)
+        r = grp.replay_member(inp["q"], inp["kr"], inp["vr"], inp["do"], block, keep=keep, store_ds=store_ds,
+                              ds_budget=ds_budget)
         del inp
         if on_member is not None:
             on_member(i, r)

@@ -215,6 +215,31 @@ def test_group_accumulation_is_linear_and_peak_memory_flat():
         assert rel <= 1e-5
 
 
+def test_group_with_kv_head_chunks_of_stored_ds():
+    """With a memory budget that holds the dS of only two of the four kv heads, the driver runs
+    the stored-dS backward a chunk of two kv heads at a time: every member's outputs and the
+    group's gradient pages equal those of the unchunked replay bit for bit, and each member's
+    peak memory is below the unchunked one (by the same amount for every member; the members'
+    kept outputs raise later members' peaks equally in both runs)."""
+    cfg = SMALL.with_(G=2)
+    log(f"case: group of {cfg.G} members, P={cfg.P}, R={cfg.R}, B=512, stored dS in chunks of 2 kv heads")
+    pre = _small_prefix(cfg)
+    members = [lambda i=i: datagen.member_inputs(cfg, i, "cuda") for i in range(cfg.G)]
+    full_ws = api.bwd_ds_workspace_bytes(pre, 512, cfg.R)
+    two = api.bwd_ds_workspace_bytes(pre, 512, cfg.R, heads=2)
+    assert two < full_ws
+    g_full, r_full = driver.replay_group(pre, members, 512, ds_budget=full_ws)
+    g_two, r_two = driver.replay_group(pre, members, 512, ds_budget=two)
+    for a, b in zip(r_full, r_two):
+        for name in ("o", "lse", "dq", "dk_resp", "dv_resp"):
+            assert torch.equal(getattr(a, name), getattr(b, name)), name
+    assert torch.equal(g_full.dk_pages, g_two.dk_pages) and torch.equal(g_full.dv_pages, g_two.dv_pages)
+    peaks_full, peaks_two = [r.peak_bytes for r in r_full], [r.peak_bytes for r in r_two]
+    log(f"    peak bytes per member: all heads {peaks_full}, two-head chunks {peaks_two}")
+    saved = [f - t for f, t in zip(peaks_full, peaks_two)]
+    assert saved[0] > 0 and len(set(saved)) == 1, saved
+
+
 def test_block_size_does_not_change_the_result():
     cfg = SMALL
     log(f"case: member replayed with B=1024 and B=384 (ragged), P={cfg.P}, R={cfg.R}")
