@@ -35,6 +35,13 @@ if ROOT not in sys.path:
 from suffix_attention_amd import api, configs, datagen, driver  # noqa: E402
 
 METRIC = "replay-attention fwd+bwd TFLOP/s and % bf16 MFMA peak at P=2M, G=8"
+
+
+def replay_metric(cfg) -> str:
+    """The headline metric names the 2M-token, G = 8 workload; other configs name their own P, G."""
+    if cfg.name == "c2m":
+        return METRIC
+    return f"replay-attention fwd+bwd TFLOP/s and % bf16 MFMA peak at P={cfg.P}, G={cfg.G}"
 # --workload score: the pre-step scoring pass (forward only, all G members batched)
 SCORE_METRIC = "pre-step scoring (forward-only, G members batched) TFLOP/s and % bf16 MFMA peak at P=2M, G=8"
 # --workload prefill: capture-side prefill (the prompt's causal attention, chunked, pages written)
@@ -143,6 +150,36 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+MICROBENCH = os.path.join(ROOT, "bench", "libmicrobench.so")
+
+
+def measured_ceilings() -> dict:
+    """The chip's matrix-core and HBM ceilings as the committed microbenchmarks reach them
+    (bench/hip/mfma_peak.hip, bench/hip/hbm_bw.hip): best of a few timed launches each."""
+    import ctypes as C
+    lib = C.CDLL(MICROBENCH)
+    lib.mb_mfma_peak.argtypes = [C.c_int, C.c_int, C.c_int, C.POINTER(C.c_double)]
+    lib.mb_hbm.argtypes = [C.c_int, C.c_size_t, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_double)]
+    out = {}
+    v = C.c_double(0)
+    best = 0.0
+    for blocks in (256, 512):  # one and two waves on every SIMD
+        rc = lib.mb_mfma_peak(blocks, 200000, 3, C.byref(v))
+        assert rc == 0, rc
+        best = max(best, v.value)
+    out["mfma_bf16_tflops"] = round(best, 1)
+    for name, mode, fill in (("hbm_read_gbs", 0, 1), ("hbm_read_zeros_gbs", 0, 0), ("hbm_write_gbs", 1, 1),
+                             ("hbm_copy_gbs", 2, 1)):
+        best = 0.0
+        for blocks in (2048, 8192):
+            rc = lib.mb_hbm(mode, 4 << 30, fill, blocks, 5, C.byref(v))
+            assert rc == 0, rc
+            best = max(best, v.value)
+        out[name] = round(best, 1)
+    out["source"] = "bench/hip/mfma_peak.hip (32x32x16 bf16 chains, every SIMD), bench/hip/hbm_bw.hip (4 GiB)"
+    return out
+
+
 def build_prefix(cfg, dev):
     table = datagen.page_table(cfg.n_pages, datagen.seed(cfg.cfg_id, datagen.TAG_PERM), dev)
     kp, vp = datagen.prefix_kv(cfg, dev)
@@ -162,36 +199,66 @@ def block_pairs(cfg):
     return out
 
 
-# Backward workspace: None lets the driver keep dS for the dQ pass when it fits in device
-# memory; True / False force either dQ pass.
+# Backward: None lets the driver keep dS for the dQ pass when it fits in device memory (or in
+# DS_BUDGET bytes), all kv heads at once or in chunks; True / False force either dQ pass.
 STORE_DS = None
+DS_BUDGET = None
 
 
-def run_steps(prefix, members, cfg, n, cycle_log=None):
+def run_steps(prefix, members, cfg, n, cycle_log=None, store_ds="default"):
     """n optimizer cycles: each a fresh group (gradient pages allocated at its first backward,
-    released at its end) replaying every member.  cycle_log, if given, receives (ms, peak bytes)
-    per cycle (events on the stream; each cycle ends with a synchronisation)."""
+    released at its end) replaying every member, every member's peak device memory recorded.
+    cycle_log, if given, receives (ms, peak bytes) per cycle (events on the stream; each cycle
+    ends with a synchronisation)."""
     last = None
+    store_ds = STORE_DS if store_ds == "default" else store_ds
     for _ in range(n):
         last = None  # release the previous group's gradient pages before allocating anew
         if cycle_log is not None:
-            torch.cuda.reset_peak_memory_stats()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-        grp = driver.GroupReplay(prefix)
-        results = [grp.replay_member(m["q"], m["kr"], m["vr"], m["do"], cfg.B, keep="none", store_ds=STORE_DS)
-                   for m in members]
+        grp = driver.GroupReplay(prefix, store_ds=store_ds, ds_budget=DS_BUDGET, track_peak=True)
+        results = [grp.replay_member(m["q"], m["kr"], m["vr"], m["do"], cfg.B, keep="none") for m in members]
         last = (grp, results)
         if cycle_log is not None:
             e1.record()
             torch.cuda.synchronize()
-            cycle_log.append((e0.elapsed_time(e1), torch.cuda.max_memory_allocated()))
+            cycle_log.append((e0.elapsed_time(e1), grp.peak_bytes))
     return last
+
+
+def memory_vs_g(prefix, members, cfg, timed_grp) -> dict:
+    """Peak device memory of a group at G = 2 and at the config's G, with the backward of the
+    timed run and with the recomputing one (untimed runs; the timed run itself is the timed
+    form's figure at the config's G)."""
+    out = {}
+    for label, store in (("timed_form", STORE_DS), ("recompute", False)):
+        row = {}
+        for g_ in sorted({2, cfg.G}):
+            if label == "timed_form" and g_ == cfg.G:
+                peak = timed_grp.peak_bytes
+            else:
+                grp, _ = run_steps(prefix, members[:g_], cfg, 1, store_ds=store)
+                peak = grp.peak_bytes
+                del grp
+            row[f"G={g_}"] = round(peak / 1e9, 3)
+        out[label] = row
+    out["timed_form"]["form"] = timed_grp.plan.describe(prefix)
+    return out
+
+
+def blas_library() -> str:
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:  # noqa: BLE001
+        return "unknown"
 
 
 def cpu_baseline(cfg, kp, vp, member, n_tok=64):
     """The oracle, untuned, on a bounded sample: the last n_tok response rows of member 0
-    (all heads) against prompt shard 0 and the response keys those rows see."""
+    (all heads) against prompt shard 0 and the response keys those rows see; with the time the
+    whole step would take at the sample's rate (extrapolated by counted work)."""
     from oracle import attention as orc  # test infrastructure; used only for this baseline leg
 
     shard_tokens = min(cfg.P, (cfg.n_pages // cfg.S) * 64)
@@ -206,8 +273,13 @@ def cpu_baseline(cfg, kp, vp, member, n_tok=64):
     dt = time.perf_counter() - t0
     flops = configs.counted_flops(n_tok, q_start, shard_tokens, cfg.hq, cfg.d)
     cores = len(os.sched_getaffinity(0))
+    step_flops = cfg.G * configs.member_flops(cfg)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": round(dt, 3), "blas_threads": int(os.environ.get("OMP_NUM_THREADS", cores)),
+            "blas": blas_library(),
+            "extrapolated_step_s": round(dt * step_flops / flops, 1),
+            "extrapolated": "time of one whole step (every member, every block, all keys) at the sample's rate: "
+                            "sample seconds x counted step work / counted sample work",
             "sample": f"float64 numpy oracle fwd+bwd of the last {n_tok} response rows (all {cfg.hq} heads) of "
                       f"member 0 over prompt shard 0 ({shard_tokens} keys) plus their {cfg.R} causal response "
                       f"keys; counted with the same 14*Hq*d*pairs convention"}
@@ -351,7 +423,14 @@ def main():
     ap.add_argument("--prefill-chunk", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--store-ds", default="auto", choices=["auto", "on", "off"],
-                    help="dQ from the dS stored by the dK/dV pass (auto: when it fits in device memory)")
+                    help="dQ from the dS stored by the dK/dV pass (auto: when it fits in device memory or in "
+                         "--ds-budget-gb, all kv heads at once or in chunks)")
+    ap.add_argument("--ds-budget-gb", type=float, default=None,
+                    help="device-memory budget for the backward workspace (auto picks the largest dS chunking "
+                         "that fits)")
+    ap.add_argument("--no-memory-sweep", action="store_true",
+                    help="skip the untimed G=2 / recompute runs that report peak memory versus G")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the matrix-core and HBM microbenchmarks")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a device copy of known size (for HBM counter calibration)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
@@ -376,8 +455,9 @@ def main():
     cfg = configs.CONFIGS[ns.config]
     if ns.G:
         cfg = cfg.with_(G=ns.G)
-    global STORE_DS
+    global STORE_DS, DS_BUDGET
     STORE_DS = {"auto": None, "on": True, "off": False}[ns.store_ds]
+    DS_BUDGET = None if ns.ds_budget_gb is None else int(ns.ds_budget_gb * 1e9)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
@@ -393,6 +473,11 @@ def main():
         bench_score(ns, cfg, dev, prefix, kp, vp, members)
         return
 
+    ceilings = None
+    if not ns.no_ceilings:
+        ceilings = measured_ceilings()
+        log(f"[bench] measured ceilings {ceilings}")
+
     if ns.warmup > 0:
         t = time.perf_counter()
         run_steps(prefix, members, cfg, ns.warmup)
@@ -400,7 +485,6 @@ def main():
         log(f"[bench] warmup {ns.warmup} step(s) {time.perf_counter() - t:.1f} s")
 
     torch.cuda.synchronize()
-    torch.cuda.reset_peak_memory_stats(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     api.profile_begin()
     t0 = time.perf_counter()
@@ -425,8 +509,7 @@ def main():
     dom = max((k for k in kern if k in KERNEL_UNITS), key=lambda k: kern[k]["total_ms"])
     alg_flops_total = ns.steps * cfg.G * sum(2 * KERNEL_UNITS[dom] * cfg.hq * cfg.d * p for p in pairs)
     n_launch = kern[dom]["launches"]
-    # one launch per block, or one per chunk of kv heads when a block's dS is stored a chunk at a time
-    assert n_launch % blocks_timed == 0, (dom, n_launch, blocks_timed)
+    # one launch per block, or one per chunk when a block's dS is stored a chunk at a time
     achieved = alg_flops_total / (kern[dom]["total_ms"] / 1e3) / 1e12
     for k in kern:
         if k in KERNEL_UNITS:
@@ -434,8 +517,9 @@ def main():
             kern[k]["tflops"] = round(f / (kern[k]["total_ms"] / 1e3) / 1e12, 1)
 
     peaks = [r.peak_bytes for r in results]
+    plan = grp.plan
     out = {
-        "metric": METRIC,
+        "metric": replay_metric(cfg),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -459,17 +543,29 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(cfg.name, dom),
                      "flops_per_unit": f"{2 * KERNEL_UNITS[dom]}*d per visible (row, key) pair and query head",
-                     "mean_launch_ms": kern[dom]["mean_ms"], "launches_per_block": n_launch // blocks_timed},
+                     "mean_launch_ms": kern[dom]["mean_ms"], "launches_per_block": round(n_launch / blocks_timed, 3)},
         "kernels": kern,
+        "backward": {"form": plan.describe(prefix), "ds_heads": plan.heads, "ds_parts": plan.parts,
+                     "workspace_gb": round(results[0].ws_bytes / 1e9, 3),
+                     "ds_budget_gb": ns.ds_budget_gb},
         "peak_mem_gb_per_member": [round(p / 1e9, 3) for p in peaks],
-        "peak_mem_gb": round(torch.cuda.max_memory_allocated(dev) / 1e9, 3),
+        "peak_mem_gb": round(max(peaks) / 1e9, 3),
     }
+    if ceilings is not None:
+        out["measured_ceilings"] = ceilings
+        out["pct_measured_mfma_peak"] = round(100 * tflops / ceilings["mfma_bf16_tflops"], 2)
+        out["roofline"]["measured_peak"] = ceilings["mfma_bf16_tflops"]
+        out["roofline"]["frac_measured_peak"] = round(achieved / ceilings["mfma_bf16_tflops"], 4)
     if cycles is not None:
         out["metric"] = REUSE_METRIC
         out["config"]["workload"] = (f"{cfg.name}: {ns.steps} consecutive optimizer cycles over one capture; "
                                      + out["config"]["workload"].split(": ", 1)[1])
         out["cycle_ms"] = [round(c[0], 1) for c in cycles]
         out["cycle_peak_gb"] = [round(c[1] / 1e9, 3) for c in cycles]
+    if not ns.no_memory_sweep and cycles is None:
+        t = time.perf_counter()
+        out["peak_mem_gb_vs_G"] = memory_vs_g(prefix, members, cfg, grp)
+        log(f"[bench] memory sweep {time.perf_counter() - t:.1f} s: {out['peak_mem_gb_vs_G']}")
     del grp, results
     if not ns.no_cpu_baseline:
         t = time.perf_counter()

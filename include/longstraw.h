@@ -28,7 +28,8 @@
  *    sum exp(s).  Query head h reads kv head h / (hq / hkv).
  *
  * Supported shapes: hq % hkv == 0; d in {64, 128, 256}; page_size == 64;
- * 1 <= n_shards <= 64.  The bf16 path runs on matrix cores; the f32 path is exact f32.
+ * 1 <= n_shards <= 64.  The bf16 path runs on matrix cores; the f32 path is exact f32 on the
+ * vector ALUs.
  */
 #ifndef LONGSTRAW_H
 #define LONGSTRAW_H
@@ -115,6 +116,19 @@ int ls_capture_pages(const void* k_src, const void* v_src, int src_dtype, int64_
                      int hkv, int d, int page_size, ls_stream_t stream);
 
 /*
+ * ls_check_page_table -- host-side check of the caller contract on a page table: every entry
+ * of page_table_host (host int32 [n_logical_pages]) lies in [0, n_phys_pages) and no two
+ * logical pages share a physical page.  The kernels do not check the table (a bad entry is
+ * clamped into the pool so that it cannot fault, and two logical pages on one physical page
+ * would give that page two writers of its gradient), so a caller that builds its own table can
+ * run this once per capture, before the table is uploaded.  Runs on the host only; it reads the
+ * table and nothing else.
+ * Errors: LS_ERR_INVALID (NULL table, an entry out of range, a repeated entry; the message
+ * names the first offending logical page).
+ */
+int ls_check_page_table(const int32_t* page_table_host, int64_t n_logical_pages, int64_t n_phys_pages);
+
+/*
  * ls_gather_pages -- read tokens [first_tok, first_tok + n_tok) of a pool back into logical
  * order: dst device [n_tok, hkv, d] of `dtype`, a bit copy.  The inverse of capture, for
  * checking the page-table walk.  Errors as for ls_capture_pages.
@@ -155,20 +169,40 @@ size_t ls_bwd_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows);
  * bytes (but at least ls_bwd_workspace_bytes) the dQ pass recomputes them.  Both give dQ
  * within the bf16 rounding of dS of each other; dK, dV, delta are the same either way.
  *
- * A workspace between the two sizes that holds the dS of at least one kv head, i.e. at least
- * round_up(ls_bwd_workspace_bytes, 256) + (ls_bwd_ds_workspace_bytes - that) / hkv bytes,
- * selects the stored-dS pass in chunks of as many kv heads as it holds (dK/dV then dQ per
- * chunk; kv heads are independent, so the results are the same bit for bit).
+ * Chunks.  A smaller workspace still selects the stored-dS pass if it holds the dS of part of
+ * the block; the block is then run a chunk at a time (dK/dV of the chunk, which writes its dS,
+ * then dQ of the chunk, which reads it; the same space serves each chunk in turn).  Kv heads
+ * are independent and key parts (the n_shards prompt shards in order, then the response keys)
+ * give separate dQ parts, so every chunking gives the same results bit for bit.  The chunking
+ * a workspace of ws_bytes selects:
+ *   - if it holds every key's dS of at least one kv head: chunks of as many kv heads as it
+ *     holds (at most hkv), each over all keys;
+ *   - otherwise one kv head at a time, by the largest number k of consecutive key parts such
+ *     that it holds the dS of the largest chunk of k parts;
+ *   - otherwise none: the dQ pass recomputes.
+ * ls_bwd_ds_chunk_workspace_bytes gives the exact size for a chosen chunking, so that a caller
+ * can pin the chunking for every block of a response.
  *
  * Layout: the recompute workspace, then from the next 256-byte boundary the stored dS, bf16
- * [kv heads of the chunk][row tiles][key slots][32] (the same space serves each chunk in
- * turn): row tiles of 32 group rows (r = token * g + j for query head kv * g + j) padded to a
- * multiple of 256 rows, key slots 128 per page pair, prompt pairs first.  The size is hkv * ceil(n_rows * g / 256) * 8 * 128 * (ceil(pages / 2) +
- * ceil(ceil(key_end / 64) / 2)) * 64 bytes: 103 GB for 1,024 rows over a 2,097,152-token
- * prompt with hq = 24, hkv = 4.  A workspace sized for the largest key_end serves every block
- * of a member.
+ * [kv heads of the chunk][row tiles][key slots][32]: row tiles of 32 group rows (r = token * g +
+ * j for query head kv * g + j) padded to a multiple of 256 rows, key slots 128 per page pair of
+ * the chunk (its prompt pairs first, then its response pairs).  Over all keys the size is
+ * hkv * ceil(n_rows * g / 256) * 8 * 128 * (ceil(pages / 2) + ceil(ceil(key_end / 64) / 2)) * 64
+ * bytes: 103 GB for 1,024 rows over a 2,097,152-token prompt with hq = 24, hkv = 4.  A workspace
+ * sized for the largest key_end serves every block of a member.
  */
 size_t ls_bwd_ds_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows, int64_t key_end);
+
+/*
+ * ls_bwd_ds_chunk_workspace_bytes -- the backward workspace with which ls_replay_bwd runs the
+ * stored-dS pass in chunks of `heads` kv heads by `parts` consecutive key parts (see
+ * ls_bwd_ds_workspace_bytes): heads in [1, hkv] with parts == n_shards + 1 (all keys), or
+ * heads == 1 with parts in [1, n_shards + 1].  (heads = hkv, parts = n_shards + 1) equals
+ * ls_bwd_ds_workspace_bytes.  Returns 0 on invalid arguments, with ls_last_error set; for
+ * float32 it equals ls_bwd_workspace_bytes.
+ */
+size_t ls_bwd_ds_chunk_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows, int64_t key_end, int heads,
+                                       int parts);
 
 /*
  * ls_replay_fwd -- forward of one replayed response block (digest, "Method", step 3:
@@ -241,8 +275,9 @@ int ls_score_fwd(const ls_prefix_t* pre, int64_t n_members, const void* q, int64
  *                   page are then written as zero).
  *   shard_first_touch  host uint8 [n_shards], or NULL for "accumulate everywhere".
  *   workspace       device, ws_bytes >= ls_bwd_workspace_bytes(pre, n_rows); with
- *                   ws_bytes >= ls_bwd_ds_workspace_bytes(pre, n_rows, q_start + n_rows)
- *                   (bf16) dQ is formed from the stored dS instead of a recompute.
+ *                   room for the block's dS, or for a chunk of it (bf16; see
+ *                   ls_bwd_ds_workspace_bytes), dQ is formed from the stored dS instead of
+ *                   a recompute.
  * Each gradient element has one writer per call (no atomics); results are
  * deterministic.  Errors as for ls_replay_fwd.
  */

@@ -106,14 +106,19 @@ def version() -> int:
 
 def capture_pages(k: torch.Tensor, v: torch.Tensor, page_table: torch.Tensor, n_phys: int,
                   page_dtype: torch.dtype | None = None, first_tok: int = 0,
-                  k_pages: torch.Tensor | None = None, v_pages: torch.Tensor | None = None):
+                  k_pages: torch.Tensor | None = None, v_pages: torch.Tensor | None = None,
+                  check_table: bool = True):
     """Write prompt keys/values [n_tok, hkv, d] (tokens first_tok ..) into page pools
-    [n_phys, hkv, 64, d]; allocates the pools (zeroed) when not given."""
+    [n_phys, hkv, 64, d]; allocates the pools (zeroed) when not given.  check_table first checks
+    on the host that the table is one to one into [0, n_phys) (a copy of the table to the host,
+    so the stream is synchronised once)."""
     _dev(k, "k")
     _dev(v, "v", dtype=k.dtype, shape=k.shape)
     _dev(page_table, "page_table", dtype=torch.int32)
     n_tok, hkv, d = k.shape
     page_dtype = page_dtype or k.dtype
+    if check_table:
+        check_page_table(page_table, n_phys)
     if k_pages is None:
         k_pages = torch.zeros((n_phys, hkv, PAGE, d), dtype=page_dtype, device=k.device)
         v_pages = torch.zeros_like(k_pages)
@@ -152,19 +157,30 @@ def bwd_workspace_bytes(prefix: Prefix, n_rows: int) -> int:
     return n
 
 
-def bwd_ds_workspace_bytes(prefix: Prefix, n_rows: int, key_end: int, heads: int | None = None) -> int:
+def bwd_ds_workspace_bytes(prefix: Prefix, n_rows: int, key_end: int, heads: int | None = None,
+                           parts: int | None = None) -> int:
     """Backward workspace that also holds the block's dS (bf16), so that dQ is formed from it
     rather than recomputed; key_end = q_start + n_rows (the largest over a member's blocks
-    sizes one workspace for all of them).  heads < hkv sizes it for that many kv heads' dS,
-    which the library then processes a chunk of kv heads at a time."""
+    sizes one workspace for all of them).  With heads (< hkv) or parts (< n_shards + 1) it is
+    sized for chunks of that many kv heads by that many consecutive key parts, which the
+    library then runs one after another (ls_bwd_ds_chunk_workspace_bytes)."""
     st = prefix.struct()
-    n = lib().ls_bwd_ds_workspace_bytes(C.byref(st), n_rows, key_end)
+    if heads is None and parts is None:
+        n = lib().ls_bwd_ds_workspace_bytes(C.byref(st), n_rows, key_end)
+    else:
+        heads = prefix.hkv if heads is None else heads
+        parts = prefix.n_shards + 1 if parts is None else parts
+        n = lib().ls_bwd_ds_chunk_workspace_bytes(C.byref(st), n_rows, key_end, heads, parts)
     if n == 0 and n_rows > 0:
         raise LongStrawError(_lib.LS_ERR_INVALID, lib().ls_last_error().decode())
-    if heads is None or heads >= prefix.hkv or prefix.dtype != torch.bfloat16:
-        return n
-    base = (bwd_workspace_bytes(prefix, n_rows) + 255) // 256 * 256
-    return base + heads * ((n - base) // prefix.hkv)
+    return n
+
+
+def check_page_table(page_table: torch.Tensor, n_phys: int) -> None:
+    """Raise LongStrawError unless the table maps logical pages one to one into [0, n_phys)
+    (ls_check_page_table, on a host copy of the table)."""
+    host = page_table.detach().to("cpu", torch.int32).contiguous()
+    check(lib().ls_check_page_table(C.c_void_p(host.data_ptr()) if host.numel() else None, host.numel(), n_phys))
 
 
 def ds_fits(nbytes: int, device, fraction: float = 0.9, budget: int | None = None) -> bool:

@@ -3,7 +3,9 @@
     python -m suffix_attention_amd.build [--jobs N] [--save-temps DIR]
 
 Every source under csrc/ is compiled to an object in csrc/_build/, then linked into
-suffix_attention_amd/liblongstraw.so next to this file.
+suffix_attention_amd/liblongstraw.so next to this file.  The measurement microbenchmarks under
+bench/hip/ (matrix-core and HBM ceilings, which bench.py reports against) are built the same way
+into bench/libmicrobench.so.
 """
 from __future__ import annotations
 
@@ -20,6 +22,11 @@ BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "liblongstraw.so")
 SOURCES = ["abi.cpp", "profile.cpp", "capture.hip", "reduce.hip", "attn_generic.hip", "attn_mfma_fwd.hip",
            "attn_mfma_bwd.hip", "attn_mfma_dq.hip", "attn_mfma_dqs.hip"]
+
+ROOT = os.path.dirname(HERE)
+BENCH_HIP = os.path.join(ROOT, "bench", "hip")
+BENCH_SOURCES = ["mfma_peak.hip", "hbm_bw.hip"]
+BENCH_LIB = os.path.join(ROOT, "bench", "libmicrobench.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -42,9 +49,9 @@ PER_SOURCE = {"attn_mfma_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "attn_mfma_dqs.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def _compile(src, extra):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *PER_SOURCE.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, extra, src_dir=CSRC, obj_dir=BUILD):
+    obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *PER_SOURCE.get(src, []), *extra, "-c", os.path.join(src_dir, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so; that is harmless
     noise = [ln for ln in (r.stderr or "").splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
@@ -66,13 +73,31 @@ def build(jobs: int | None = None, save_temps: str | None = None, verbose: bool 
             if err and verbose:
                 print(f"[{src}] {err}", file=sys.stderr)
             objs.append(obj)
-    tmp = LIB + ".tmp"
+    _link(objs, LIB)
+    build_microbench()
+    return LIB
+
+
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+
+
+def build_microbench() -> str:
+    obj_dir = os.path.join(BENCH_HIP, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    objs = []
+    with cf.ThreadPoolExecutor(max_workers=len(BENCH_SOURCES)) as ex:
+        for src, obj, rc, err, cmd in ex.map(lambda s_: _compile(s_, [], BENCH_HIP, obj_dir), BENCH_SOURCES):
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{err}")
+            objs.append(obj)
+    _link(objs, BENCH_LIB)
+    return BENCH_LIB
 
 
 def clean():

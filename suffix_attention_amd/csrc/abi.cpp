@@ -9,9 +9,9 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/longstraw.h"
-#include "common.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -33,16 +33,6 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 bool d_supported(int d) { return d == 64 || d == 128 || d == 256; }
-
-// The generic (vector-ALU) kernels run the f32 path; bf16 runs on the matrix cores unless
-// LS_KERNELS=generic asks for the generic kernels (a debugging aid).
-bool force_generic() {
-    static const bool v = [] {
-        const char* e = std::getenv("LS_KERNELS");
-        return e && std::strcmp(e, "generic") == 0;
-    }();
-    return v;
-}
 
 int64_t logical_pages(int64_t n_tok, int page_size) { return (n_tok + page_size - 1) / page_size; }
 
@@ -120,6 +110,9 @@ ls::AttnArgs make_args(const ls_prefix_t* p, const void* q, int64_t n_rows, int6
     for (int s = 0; s <= p->n_shards; s++) a.shard_lo[s] = p->shard_page_bounds[s];
     a.n_members = 1;
     a.part_rows = n_rows;
+    a.pg_lo = 0;
+    a.pg_hi = a.n_logical_pages;
+    a.ds_parts = a.n_parts;
     return a;
 }
 
@@ -133,12 +126,16 @@ size_t bwd_ws(const ls_prefix_t* p, int64_t n_rows) {
 }
 
 // Bytes of the stored dS (bf16, one per group row and key slot) of a block whose response keys
-// end at key_end, placed after the recompute workspace at a 256-byte boundary.
+// end at key_end, placed after the recompute workspace at a 256-byte boundary: per kv head, for
+// chunks of `parts` consecutive key parts (n_shards + 1: all keys at once).
 size_t ds_offset(const ls_prefix_t* p, int64_t n_rows) { return (bwd_ws(p, n_rows) + 255) / 256 * 256; }
-size_t ds_bytes(const ls_prefix_t* p, int64_t n_rows, int64_t key_end) {
+size_t ds_head_bytes(const ls_prefix_t* p, int64_t n_rows, int64_t key_end, int parts) {
     const int64_t rows_total = n_rows * (p->hq / p->hkv);
-    return (size_t)p->hkv * (size_t)ls::ds_row_tiles(rows_total) *
-           (size_t)ls::ds_key_slots(logical_pages(p->prefix_len, p->page_size), key_end, nullptr) * 64;
+    return (size_t)ls::ds_row_tiles(rows_total) *
+           (size_t)ls::ds_chunk_slots(p->shard_page_bounds, p->n_shards, key_end, parts) * 64;
+}
+size_t ds_bytes(const ls_prefix_t* p, int64_t n_rows, int64_t key_end) {
+    return (size_t)p->hkv * ds_head_bytes(p, n_rows, key_end, p->n_shards + 1);
 }
 
 }  // namespace
@@ -170,6 +167,28 @@ int ls_capture_pages(const void* k_src, const void* v_src, int src_dtype, int64_
     hipError_t e = ls::launch_capture(k_src, v_src, src_dtype, n_tok, first_tok, page_table, k_pages, v_pages, page_dtype,
                                       n_phys_pages, hkv, d, (hipStream_t)stream);
     return e == hipSuccess ? LS_OK : hip_fail(e, "capture kernel");
+}
+
+int ls_check_page_table(const int32_t* page_table_host, int64_t n_logical_pages, int64_t n_phys_pages) {
+    g_err.clear();
+    if (n_logical_pages < 0) return fail(LS_ERR_INVALID, "n_logical_pages=%lld < 0", (long long)n_logical_pages);
+    if (n_logical_pages == 0) return LS_OK;
+    if (!page_table_host) return fail(LS_ERR_INVALID, "page_table_host is NULL");
+    if (n_phys_pages < n_logical_pages)
+        return fail(LS_ERR_INVALID, "%lld logical pages cannot map one to one into %lld physical pages",
+                    (long long)n_logical_pages, (long long)n_phys_pages);
+    std::vector<uint8_t> seen((size_t)n_phys_pages, 0);
+    for (int64_t i = 0; i < n_logical_pages; i++) {
+        const int32_t e = page_table_host[i];
+        if (e < 0 || e >= n_phys_pages)
+            return fail(LS_ERR_INVALID, "page_table[%lld] = %d is outside [0, %lld)", (long long)i, e,
+                        (long long)n_phys_pages);
+        if (seen[(size_t)e])
+            return fail(LS_ERR_INVALID, "page_table[%lld] = %d: physical page already mapped by an earlier logical page",
+                        (long long)i, e);
+        seen[(size_t)e] = 1;
+    }
+    return LS_OK;
 }
 
 int ls_gather_pages(const void* pages, int dtype, const int32_t* page_table, int64_t n_logical_pages,
@@ -224,26 +243,63 @@ size_t ls_bwd_ds_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows, int64_t
     return ds_offset(pre, n_rows) + ds_bytes(pre, n_rows, key_end);
 }
 
-int ls_replay_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start, const void* k_resp,
-                  const void* v_resp, int64_t n_resp_keys, void* o, float* lse, void* workspace, size_t ws_bytes,
-                  ls_stream_t stream) {
+size_t ls_bwd_ds_chunk_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows, int64_t key_end, int heads,
+                                       int parts) {
     g_err.clear();
+    if (check_prefix(pre) != LS_OK) return 0;
+    if (n_rows < 0 || key_end < n_rows) {
+        fail(LS_ERR_INVALID, "n_rows=%lld, key_end=%lld: need 0 <= n_rows <= key_end", (long long)n_rows,
+             (long long)key_end);
+        return 0;
+    }
+    const int n_all = pre->n_shards + 1;
+    if (heads < 1 || heads > pre->hkv || parts < 1 || parts > n_all || (heads > 1 && parts < n_all)) {
+        fail(LS_ERR_INVALID, "chunks of %d kv heads by %d key parts: need 1 <= heads <= hkv (%d), 1 <= parts <= %d, "
+             "and all parts when heads > 1", heads, parts, pre->hkv, n_all);
+        return 0;
+    }
+    if (pre->dtype != LS_DTYPE_BF16) return bwd_ws(pre, n_rows);
+    return ds_offset(pre, n_rows) + (size_t)heads * ds_head_bytes(pre, n_rows, key_end, parts);
+}
+
+// Checks of a forward call, before any launch: LS_OK with nothing to do for an empty block is
+// reported through *empty.
+static int check_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start, const void* k_resp,
+                     const void* v_resp, int64_t n_resp_keys, void* o, float* lse, bool* empty) {
     int rc = check_prefix(pre);
     if (rc != LS_OK) return rc;
     rc = check_block(pre, q, n_rows, q_start, k_resp, v_resp, n_resp_keys);
     if (rc != LS_OK) return rc;
-    if (n_rows == 0) return LS_OK;
+    *empty = n_rows == 0;
+    if (*empty) return LS_OK;
     if (!o || !lse) return fail(LS_ERR_INVALID, "o/lse is NULL");
+    return LS_OK;
+}
+
+static int run_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start, const void* k_resp,
+                   const void* v_resp, void* o, float* lse, void* workspace, ls_stream_t stream);
+
+int ls_replay_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start, const void* k_resp,
+                  const void* v_resp, int64_t n_resp_keys, void* o, float* lse, void* workspace, size_t ws_bytes,
+                  ls_stream_t stream) {
+    g_err.clear();
+    bool empty = false;
+    const int rc = check_fwd(pre, q, n_rows, q_start, k_resp, v_resp, n_resp_keys, o, lse, &empty);
+    if (rc != LS_OK || empty) return rc;
     const size_t need = fwd_ws(pre, n_rows);
     if (!workspace || ws_bytes < need)
         return fail(LS_ERR_WORKSPACE, "forward workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+    return run_fwd(pre, q, n_rows, q_start, k_resp, v_resp, o, lse, workspace, stream);
+}
+
+static int run_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start, const void* k_resp,
+                   const void* v_resp, void* o, float* lse, void* workspace, ls_stream_t stream) {
     ls::AttnArgs a = make_args(pre, q, n_rows, q_start, k_resp, v_resp);
     const int64_t rows = n_rows * pre->hq;
     a.o_parts = (float*)workspace;
     a.lse_parts = a.o_parts + (size_t)a.n_parts * rows * pre->d;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = (pre->dtype == LS_DTYPE_BF16 && !force_generic()) ? ls::launch_fwd_mfma(a, s)
-                                                                     : ls::launch_fwd_generic(pre->dtype, a, s);
+    hipError_t e = pre->dtype == LS_DTYPE_BF16 ? ls::launch_fwd_mfma(a, s) : ls::launch_fwd_generic(a, s);
     if (e != hipSuccess) return hip_fail(e, "forward kernel");
     e = ls::launch_lse_merge(a.n_parts, rows, pre->d, a.o_parts, a.lse_parts, o, pre->dtype, lse, s);
     return e == hipSuccess ? LS_OK : hip_fail(e, "LSE merge kernel");
@@ -281,19 +337,19 @@ int ls_score_fwd(const ls_prefix_t* pre, int64_t n_members, const void* q, int64
     a.lse_parts = a.o_parts + (size_t)a.n_parts * all_rows * pre->hq * pre->d;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
-    if (pre->dtype == LS_DTYPE_BF16 && !force_generic()) {
+    if (pre->dtype == LS_DTYPE_BF16) {
         a.n_members = n_members;  // one launch over every member's rows
         e = ls::launch_fwd_mfma(a, s);
     } else {
         // the exact f32 path runs the members one launch at a time into the same parts
-        const size_t esz = pre->dtype == LS_DTYPE_BF16 ? 2 : 4;
+        const size_t esz = 4;
         for (int64_t m = 0; m < n_members && e == hipSuccess; m++) {
             ls::AttnArgs am = a;
             am.q = (const char*)q + (size_t)(m * n_rows * pre->hq * pre->d) * esz;
             am.k_resp = (const char*)k_resp + (size_t)(m * a.resp_member_elems) * esz;
             am.v_resp = (const char*)v_resp + (size_t)(m * a.resp_member_elems) * esz;
             am.row0 = m * n_rows;
-            e = ls::launch_fwd_generic(pre->dtype, am, s);
+            e = ls::launch_fwd_generic(am, s);
         }
     }
     if (e != hipSuccess) return hip_fail(e, "scoring forward kernel");
@@ -334,22 +390,37 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
             if (shard_first_touch[s]) a.first_touch_mask |= 1ull << s;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    if (pre->dtype == LS_DTYPE_BF16 && !force_generic()) {
-        // a workspace that also holds the dS of one or more kv heads selects the stored-dS dQ
-        // pass, run over as many kv heads at a time as the workspace holds
-        const size_t per_head = ds_bytes(pre, n_rows, a.key_end) / (size_t)pre->hkv;
+    if (pre->dtype == LS_DTYPE_BF16) {
+        // A workspace that also holds some stored dS selects the stored-dS dQ pass: with room
+        // for every key's dS of at least one kv head, in chunks of as many kv heads as it holds;
+        // otherwise one kv head at a time by the largest number of consecutive key parts whose
+        // dS it holds.  With room for none, the dQ pass recomputes.
+        const int n_all = pre->n_shards + 1;
         const size_t off = ds_offset(pre, n_rows);
-        if (n_rows > 0 && per_head > 0 && ws_bytes >= off + per_head) {
+        const size_t room = ws_bytes > off ? ws_bytes - off : 0;
+        const size_t per_head = ds_head_bytes(pre, n_rows, a.key_end, n_all);
+        int heads = 0, parts = n_all;
+        if (n_rows > 0 && per_head > 0 && room >= per_head) {
+            const size_t fit = room / per_head;
+            heads = fit < (size_t)pre->hkv ? (int)fit : pre->hkv;
+        } else if (n_rows > 0) {
+            for (int k = n_all - 1; k >= 1 && heads == 0; k--)
+                if (room >= ds_head_bytes(pre, n_rows, a.key_end, k)) {
+                    heads = 1;
+                    parts = k;
+                }
+        }
+        if (heads > 0) {
             a.ds = (uint16_t*)((char*)workspace + off);
             a.ds_rt = ls::ds_row_tiles(n_rows * a.g);
-            a.ds_kslots = ls::ds_key_slots(a.n_logical_pages, a.key_end, &a.ds_resp_slot0);
-            const size_t fit = (ws_bytes - off) / per_head;
-            a.ds_heads = fit < (size_t)pre->hkv ? (int)fit : pre->hkv;
+            a.ds_kslots = ls::ds_chunk_slots(pre->shard_page_bounds, pre->n_shards, a.key_end, parts);
+            a.ds_heads = heads;
+            a.ds_parts = parts;
         }
         e = ls::launch_bwd_mfma(a, s);  // its prep kernel also writes delta
     } else {
         e = ls::launch_delta(o, dout, pre->dtype, rows, pre->d, (float*)a.delta, s);
-        if (e == hipSuccess) e = ls::launch_bwd_generic(pre->dtype, a, s);
+        if (e == hipSuccess) e = ls::launch_bwd_generic(a, s);
     }
     if (e != hipSuccess) return hip_fail(e, "backward kernels");
     e = ls::launch_sum_parts(a.n_parts, rows * pre->d, a.dq_parts, dq, s);

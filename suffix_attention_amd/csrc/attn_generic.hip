@@ -399,12 +399,8 @@ hipError_t bwd_dispatch(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_fwd_generic(int dtype, const AttnArgs& a, hipStream_t s) {
-    return dtype == 0 ? fwd_dispatch<float>(a, s) : fwd_dispatch<bf16_t>(a, s);
-}
+hipError_t launch_fwd_generic(const AttnArgs& a, hipStream_t s) { return fwd_dispatch<float>(a, s); }
 
-hipError_t launch_bwd_generic(int dtype, const AttnArgs& a, hipStream_t s) {
-    return dtype == 0 ? bwd_dispatch<float>(a, s) : bwd_dispatch<bf16_t>(a, s);
-}
+hipError_t launch_bwd_generic(const AttnArgs& a, hipStream_t s) { return bwd_dispatch<float>(a, s); }
 
 }  // namespace ls

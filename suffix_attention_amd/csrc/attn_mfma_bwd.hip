@@ -303,8 +303,11 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int pair0, int n_pairs
     // ---- this wave's 32 keys
     const int64_t page = 2 * (int64_t)(resp ? pair - n_pp : pair) + (w >> 1);  // logical or response page
     const int64_t n_pages_here = resp ? (a.key_end + kPage - 1) / kPage : a.n_logical_pages;
-    const bool page_ok = page < n_pages_here;
-    const int64_t src_page = page_ok ? page : page - 1;  // an existing page to read (never written)
+    const bool page_exists = page < n_pages_here;
+    // the wave writes its page's gradients only if the launch owns the page (a chunk of key
+    // parts owns its shards' pages; a pair cut by the chunk's edge has one page of each chunk)
+    const bool page_ok = page_exists && (resp || (page >= a.pg_lo && page < a.pg_hi));
+    const int64_t src_page = page_exists ? page : page - 1;  // an existing page to read
     const int kh = w & 1;
     int32_t phys = 0;
     int valid;
@@ -390,7 +393,8 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int pair0, int n_pairs
         u32x4* ds_p = nullptr;
         int64_t ds_step = 0;
         if (DS) {
-            const int64_t slot = 128 * (int64_t)pair + 64 * (w >> 1) + 32 * kh + n;
+            const int64_t slot = (resp ? a.ds_resp_slot0 + 128 * (int64_t)(pair - n_pp) : 128 * ((int64_t)pair - a.ds_pair0)) +
+                                 64 * (w >> 1) + 32 * kh + n;
             ds_p = (u32x4*)(a.ds + ((int64_t)(kvh - a.ds_kvh0) * a.ds_rt * a.ds_kslots + slot) * 32 + 16 * h);
             ds_step = a.ds_kslots * 32 * 2 / 16;
         }
@@ -493,20 +497,33 @@ hipError_t launch_bwd_d(const AttnArgs& a, hipStream_t s) {
     const int n_pp = (int)((a.n_logical_pages + 1) / 2);
     const int n_rp = (int)((resp_tiles(a.key_end) + 1) / 2);
     if (a.ds) {
-        // stored dS, a chunk of kv heads at a time: dK/dV writes the chunk's dS, dQ reads it
+        // stored dS, a chunk at a time (ds_heads kv heads by ds_parts consecutive key parts):
+        // dK/dV writes the chunk's dS, then dQ reads it for the chunk's parts
+        const int n_all = a.n_shards + 1;
         for (int k0 = 0; k0 < a.hkv; k0 += a.ds_heads) {
-            AttnArgs c = a;
-            c.ds_kvh0 = k0;
             const int nh = a.hkv - k0 < a.ds_heads ? a.hkv - k0 : a.ds_heads;
-            if ((int64_t)(n_pp + n_rp) * nh > 0) {
-                KernelTimer kt("dkdv_mfma", s);
-                const int nbp = n_pp * nh, nbr = n_rp * nh;
-                if (nbp > 0) dkdv_mfma_kernel<D, false, true><<<pad_grid(nbp), 256, 0, s>>>(c, gr, n_pp, 0, n_pp, nbp);
-                if (nbr > 0) dkdv_mfma_kernel<D, true, true><<<pad_grid(nbr), 256, 0, s>>>(c, gr, n_pp, n_pp, n_rp, nbr);
+            for (int p0 = 0; p0 < n_all; p0 += a.ds_parts) {
+                const int p1 = p0 + a.ds_parts < n_all ? p0 + a.ds_parts : n_all;
+                const PartChunk pc = part_chunk(a.shard_lo, a.n_shards, a.key_end, p0, p1);
+                AttnArgs c = a;
+                c.ds_kvh0 = k0;
+                c.pg_lo = pc.pg_lo;
+                c.pg_hi = pc.pg_hi;
+                c.ds_pair0 = pc.pair_lo;
+                c.ds_resp_slot0 = 128 * pc.n_pairs;
+                const int nbp = (int)pc.n_pairs * nh, nbr = pc.resp ? n_rp * nh : 0;
+                if (nbp + nbr > 0) {
+                    KernelTimer kt("dkdv_mfma", s);
+                    if (nbp > 0)
+                        dkdv_mfma_kernel<D, false, true><<<pad_grid(nbp), 256, 0, s>>>(c, gr, n_pp, (int)pc.pair_lo,
+                                                                                        (int)pc.n_pairs, nbp);
+                    if (nbr > 0) dkdv_mfma_kernel<D, true, true><<<pad_grid(nbr), 256, 0, s>>>(c, gr, n_pp, n_pp, n_rp, nbr);
+                }
+                hipError_t e = hipGetLastError();
+                const int s1 = p1 < a.n_shards ? p1 : a.n_shards;
+                if (e == hipSuccess) e = launch_dqs_mfma(c, nh, p0 < s1 ? p0 : 0, p0 < s1 ? s1 - p0 : 0, pc.resp, s);
+                if (e != hipSuccess) return e;
             }
-            hipError_t e = hipGetLastError();
-            if (e == hipSuccess) e = launch_dqs_mfma(c, nh, s);  // attn_mfma_dqs.hip
-            if (e != hipSuccess) return e;
         }
         return hipSuccess;
     }
@@ -523,11 +540,6 @@ hipError_t launch_bwd_d(const AttnArgs& a, hipStream_t s) {
 }
 
 }  // namespace
-
-size_t mfma_bwd_extra_bytes(int64_t n_rows, int g, int hkv, int d) {
-    const size_t rp = (size_t)rows_padded(n_rows * g);
-    return (sizeof(f32x2) + 2 * sizeof(bf16_t) * (size_t)d) * rp * (size_t)hkv;
-}
 
 hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t s) {
     switch (a.d) {

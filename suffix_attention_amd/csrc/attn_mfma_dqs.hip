@@ -89,7 +89,7 @@ __device__ __forceinline__ void units_at(int k, Fn&& f) {
 // equal run of the long prompt-shard blocks, then of the short response-part blocks.
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void dqs_mfma_kernel(AttnArgs a, int n_rblocks, int n_kvh) {
+void dqs_mfma_kernel(AttnArgs a, int n_rblocks, int n_kvh, int part0, int n_sp, int n_rp) {
     using F = TileShape<D>;
     constexpr int NW = 4;
     constexpr int PW = KeyTiles<D, NW>::PER_WAVE;  // K copies per wave per page
@@ -98,10 +98,10 @@ void dqs_mfma_kernel(AttnArgs a, int n_rblocks, int n_kvh) {
     __shared__ __attribute__((aligned(1024))) char kbuf[2][F::TILE];
     __shared__ __attribute__((aligned(1024))) char dbuf[3][NW][kDsWave];
 
-    const XcdBlock blk = deal_block(blockIdx.x, n_rblocks, a.n_shards, a.n_parts, n_kvh);
+    const XcdBlock blk = deal_block(blockIdx.x, n_rblocks, n_sp, n_sp + n_rp, n_kvh);
     if (blk.qtile_g < 0) return;
     const int rblock = blk.qtile_g;
-    const int part = blk.part;
+    const int part = blk.part < n_sp ? part0 + blk.part : a.n_shards;
     const int kvh = a.ds_kvh0 + blk.kvh;  // the stored dS holds kv heads from ds_kvh0 on
     const bool resp = part == a.n_shards;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -119,7 +119,7 @@ void dqs_mfma_kernel(AttnArgs a, int n_rblocks, int n_kvh) {
     if (!resp) {
         lp0 = a.shard_lo[part];
         n_tiles = a.shard_lo[part + 1] - lp0;
-        slot0 = lp0 * kPage;
+        slot0 = lp0 * kPage - 128 * a.ds_pair0;  // the chunk's key slots start at its first page pair
     } else {
         int64_t tok_max = (r0 + 255) / a.g;
         if (tok_max > a.n_rows - 1) tok_max = a.n_rows - 1;
@@ -218,22 +218,24 @@ void dqs_mfma_kernel(AttnArgs a, int n_rblocks, int n_kvh) {
 }
 
 template <int D>
-hipError_t launch_dqs_d(const AttnArgs& a, int n_kvh, hipStream_t s) {
+hipError_t launch_dqs_d(const AttnArgs& a, int n_kvh, int part0, int n_sp, int n_rp, hipStream_t s) {
     const int64_t rows_total = a.n_rows * a.g;
     const int n_rblocks = (int)((rows_total + 255) / 256);
-    if (n_rblocks == 0 || n_kvh == 0) return hipSuccess;
-    dqs_mfma_kernel<D><<<deal_grid(n_rblocks, a.n_shards, a.n_parts, n_kvh), 256, 0, s>>>(a, n_rblocks, n_kvh);
+    if (n_rblocks == 0 || n_kvh == 0 || n_sp + n_rp == 0) return hipSuccess;
+    dqs_mfma_kernel<D><<<deal_grid(n_rblocks, n_sp, n_sp + n_rp, n_kvh), 256, 0, s>>>(a, n_rblocks, n_kvh, part0,
+                                                                                      n_sp, n_rp);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_dqs_mfma(const AttnArgs& a, int n_kvh, hipStream_t s) {
+hipError_t launch_dqs_mfma(const AttnArgs& a, int n_kvh, int part0, int n_sp, bool resp, hipStream_t s) {
     KernelTimer kt("dqs_mfma", s);
+    const int n_rp = resp ? 1 : 0;
     switch (a.d) {
-        case 64: return launch_dqs_d<64>(a, n_kvh, s);
-        case 128: return launch_dqs_d<128>(a, n_kvh, s);
-        case 256: return launch_dqs_d<256>(a, n_kvh, s);
+        case 64: return launch_dqs_d<64>(a, n_kvh, part0, n_sp, n_rp, s);
+        case 128: return launch_dqs_d<128>(a, n_kvh, part0, n_sp, n_rp, s);
+        case 256: return launch_dqs_d<256>(a, n_kvh, part0, n_sp, n_rp, s);
         default: return hipErrorInvalidValue;
     }
 }

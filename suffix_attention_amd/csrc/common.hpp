@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.hpp"
+
 namespace ls {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -16,9 +18,6 @@ typedef uint16_t bf16_t;  // storage type of a bfloat16 in memory
 
 #define LS_LDS __attribute__((address_space(3)))
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kPage = 64;  // tokens per KV page
 
 // ----------------------------------------------------------------------------------------
 // Scalar conversions.  bf16 -> f32 is exact; f32 -> bf16 rounds to nearest-even in hardware.

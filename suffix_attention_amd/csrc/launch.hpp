@@ -7,6 +7,9 @@
 namespace ls {
 
 constexpr int kMaxShards = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kPage = 64;  // tokens per KV page
 
 // Everything one replay-attention launch needs, passed by value to the kernels.
 struct AttnArgs {
@@ -62,13 +65,22 @@ struct AttnArgs {
     // prompt pairs first (slot = logical key), the response pairs from ds_resp_slot0 on.
     // When the workspace holds dS for only some kv heads, the backward runs in chunks of
     // ds_heads kv heads (dK/dV, then dQ, per chunk); ds_kvh0 is the first kv head of the chunk
-    // being launched, and the stored dS is indexed by kv head - ds_kvh0.
+    // being launched, and the stored dS is indexed by kv head - ds_kvh0.  When it holds less
+    // than one kv head's dS over all keys, the chunks are one kv head by ds_parts consecutive
+    // key parts (shards in order, then the response): a chunk's prompt page pairs start at
+    // ds_pair0 (its key slot 0) and its response pairs, if it has the response part, at
+    // ds_resp_slot0.
     uint16_t* ds;
     int64_t ds_rt;
     int64_t ds_kslots;
     int64_t ds_resp_slot0;
+    int64_t ds_pair0;
     int ds_heads;
+    int ds_parts;
     int ds_kvh0;
+    // prompt pages [pg_lo, pg_hi) are the ones whose K/V gradients a dK/dV launch writes (all
+    // logical pages, except in a chunk of key parts: the chunk's shards)
+    int64_t pg_lo, pg_hi;
 };
 
 // Row (0..31) inside a 32-row tile of the stored-dS position p (0..31): the positions are in
@@ -86,6 +98,45 @@ inline int64_t ds_key_slots(int64_t n_logical_pages, int64_t key_end, int64_t* r
     const int64_t pp = (n_logical_pages + 1) / 2, rp = ((key_end + 63) / 64 + 1) / 2;
     if (resp_slot0) *resp_slot0 = 128 * pp;
     return 128 * (pp + rp);
+}
+
+// A chunk of consecutive key parts [p0, p1) (parts 0 .. n_shards - 1 are the prompt shards,
+// part n_shards the response): its prompt pages [pg_lo, pg_hi), the page pairs that cover them
+// (pairs are the dK/dV pass's unit; a pair cut by the chunk's edge is walked by both chunks, each
+// writing only its own page), and its key slots (prompt pairs first, then the response pairs).
+struct PartChunk {
+    int p0, p1;
+    int64_t pg_lo, pg_hi;      // prompt pages (pg_lo == pg_hi: none)
+    int64_t pair_lo, n_pairs;  // prompt page pairs [pair_lo, pair_lo + n_pairs)
+    bool resp;                 // the chunk holds the response part
+    int64_t n_resp_pairs;
+    int64_t slots() const { return 128 * (n_pairs + (resp ? n_resp_pairs : 0)); }
+};
+
+inline PartChunk part_chunk(const int64_t* shard_lo, int n_shards, int64_t key_end, int p0, int p1) {
+    PartChunk c;
+    c.p0 = p0;
+    c.p1 = p1;
+    const int s1 = p1 < n_shards ? p1 : n_shards;
+    c.pg_lo = p0 < n_shards ? shard_lo[p0] : shard_lo[n_shards];
+    c.pg_hi = p0 < n_shards ? shard_lo[s1] : c.pg_lo;
+    c.pair_lo = c.pg_lo / 2;
+    c.n_pairs = c.pg_hi > c.pg_lo ? (c.pg_hi + 1) / 2 - c.pair_lo : 0;
+    c.resp = p1 > n_shards;
+    c.n_resp_pairs = ((key_end + 63) / 64 + 1) / 2;
+    return c;
+}
+
+// Key slots per kv head that the stored dS needs for chunks of `parts` consecutive key parts:
+// the largest chunk's.
+inline int64_t ds_chunk_slots(const int64_t* shard_lo, int n_shards, int64_t key_end, int parts) {
+    int64_t m = 0;
+    for (int p0 = 0; p0 < n_shards + 1; p0 += parts) {
+        const int p1 = p0 + parts < n_shards + 1 ? p0 + parts : n_shards + 1;
+        const int64_t sl = part_chunk(shard_lo, n_shards, key_end, p0, p1).slots();
+        m = sl > m ? sl : m;
+    }
+    return m;
 }
 
 // Brackets one kernel launch with HIP events on its stream while profiling is on
@@ -125,16 +176,21 @@ hipError_t launch_sum_parts(int n_parts, int64_t n, const float* parts, float* o
                             hipStream_t s);
 hipError_t launch_zero(float* p, int64_t n, hipStream_t s);
 
-// attn_generic.hip: LDS-tiled kernels on the vector ALUs (exact f32 path)
-hipError_t launch_fwd_generic(int dtype, const AttnArgs& a, hipStream_t s);
-hipError_t launch_bwd_generic(int dtype, const AttnArgs& a, hipStream_t s);
+// attn_generic.hip: LDS-tiled kernels on the vector ALUs (the exact float32 path)
+hipError_t launch_fwd_generic(const AttnArgs& a, hipStream_t s);
+hipError_t launch_bwd_generic(const AttnArgs& a, hipStream_t s);
 
 // attn_mfma_fwd.hip / attn_mfma_bwd.hip: bf16 matrix-core kernels
 hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t s);
-// bytes the matrix-core backward keeps after the dQ parts: (LSE * log2 e, delta) and the Q
-// and dO rows of every kv head's group, group-major and padded to a multiple of 64 rows
-size_t mfma_bwd_extra_bytes(int64_t n_rows, int g, int hkv, int d);
+// bytes the matrix-core backward keeps after the dQ parts: (LSE * log2 e, delta) float32 pairs
+// and the bf16 Q and dO rows of every kv head's group, group-major and padded to a multiple of
+// 64 rows
+constexpr int kRowPad = 64;
+inline int64_t rows_padded(int64_t rows) { return (rows + kRowPad - 1) / kRowPad * kRowPad; }
+inline size_t mfma_bwd_extra_bytes(int64_t n_rows, int g, int hkv, int d) {
+    return (2 * sizeof(float) + 2 * sizeof(uint16_t) * (size_t)d) * (size_t)rows_padded(n_rows * g) * (size_t)hkv;
+}
 
 // Backward workspace layout (float32 elements from the start): delta [n_rows * hq] padded to a
 // multiple of 64, then dq_parts [n_parts, n_rows, hq, d], then the matrix-core extra.

@@ -9,9 +9,6 @@ namespace ls {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kRowPad = 64;
-inline int64_t rows_padded(int64_t rows) { return (rows + kRowPad - 1) / kRowPad * kRowPad; }
-
 // Per-kv-head, group-major views of the block: row r of kv head h is (token r / g, query head
 // h * g + r % g); rows_pad rows per head.
 struct GroupRows {
@@ -32,7 +29,7 @@ inline GroupRows group_rows(void* base, int64_t rows_pad, int hkv, int d) {
 
 hipError_t launch_dq_mfma(const AttnArgs& a, const GroupRows& gr, hipStream_t s);
 // dQ parts of kv heads [a.ds_kvh0, a.ds_kvh0 + n_kvh) from the dS that the dK/dV pass stored
-// for them (a.ds)
-hipError_t launch_dqs_mfma(const AttnArgs& a, int n_kvh, hipStream_t s);
+// for them (a.ds): shard parts [part0, part0 + n_sp), and the response part if `resp`
+hipError_t launch_dqs_mfma(const AttnArgs& a, int n_kvh, int part0, int n_sp, bool resp, hipStream_t s);
 
 }  // namespace ls

@@ -1,0 +1,196 @@
+// Host-only checks of the C ABI front end (abi.cpp), built with the host compiler's address and
+// undefined-behaviour sanitizers against stand-in kernel launchers (abi_stubs.cpp): argument
+// validation, workspace sizing, the stored-dS chunk plan, the page-table check and the per-thread
+// error message.  Device pointers are fake and never dereferenced (no launch happens).  Prints
+// one line per check and exits non-zero on the first failure.
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/longstraw.h"
+#include "abi_stubs.hpp"
+
+namespace {
+
+int g_failed = 0;
+
+void expect(bool ok, const char* what) {
+    std::printf("%s %s\n", ok ? "ok" : "FAIL", what);
+    if (!ok) g_failed++;
+}
+
+void* fake(uintptr_t i) { return (void*)(0x100000 + 0x1000 * i); }
+
+struct Prefix {
+    std::vector<int64_t> bounds;
+    ls_prefix_t p{};
+    Prefix(int hq, int hkv, int d, int dtype, int64_t prefix_len, std::vector<int64_t> b) : bounds(std::move(b)) {
+        p.hq = hq;
+        p.hkv = hkv;
+        p.d = d;
+        p.page_size = 64;
+        p.dtype = dtype;
+        p.n_shards = (int)bounds.size() - 1;
+        p.prefix_len = prefix_len;
+        p.n_phys_pages = (prefix_len + 63) / 64 + 3;
+        p.page_table = (const int32_t*)fake(1);
+        p.k_pages = fake(2);
+        p.v_pages = fake(3);
+        p.shard_page_bounds = bounds.data();
+        p.softmax_scale = 0.0625f;
+    }
+};
+
+std::vector<int64_t> even(int64_t pages, int s) {
+    std::vector<int64_t> b;
+    for (int i = 0; i <= s; i++) b.push_back(i * pages / s);
+    return b;
+}
+
+int bwd(const ls_prefix_t* p, int64_t n, int64_t q0, size_t ws_bytes, int first = 1) {
+    return ls_replay_bwd(p, fake(4), n, q0, fake(5), fake(6), q0 + n + 5, fake(7), (const float*)fake(8), fake(9),
+                         (float*)fake(10), (float*)fake(11), (float*)fake(12), first, (float*)fake(13),
+                         (float*)fake(14), nullptr, fake(15), ws_bytes, nullptr);
+}
+
+void page_table_checks() {
+    const int32_t good[5] = {4, 0, 2, 1, 3};
+    expect(ls_check_page_table(good, 5, 5) == LS_OK, "page table: a permutation");
+    expect(ls_check_page_table(good, 3, 7) == LS_OK, "page table: injective into a larger pool");
+    const int32_t dup[4] = {0, 2, 2, 1};
+    expect(ls_check_page_table(dup, 4, 4) == LS_ERR_INVALID &&
+               std::strstr(ls_last_error(), "page_table[2]") != nullptr,
+           "page table: a repeated entry names its logical page");
+    const int32_t out[3] = {0, -1, 1};
+    expect(ls_check_page_table(out, 3, 3) == LS_ERR_INVALID && std::strstr(ls_last_error(), "outside") != nullptr,
+           "page table: a negative entry");
+    const int32_t big[3] = {0, 1, 3};
+    expect(ls_check_page_table(big, 3, 3) == LS_ERR_INVALID, "page table: an entry past the pool");
+    expect(ls_check_page_table(good, 5, 4) == LS_ERR_INVALID, "page table: more logical than physical pages");
+    expect(ls_check_page_table(nullptr, 0, 0) == LS_OK, "page table: empty");
+    expect(ls_check_page_table(nullptr, 2, 2) == LS_ERR_INVALID, "page table: NULL");
+    std::vector<int32_t> large(1 << 16);
+    for (uint32_t i = 0; i < (1u << 16); i++) large[i] = (int32_t)((i * 40503u) & 0xffffu);  // odd multiplier: a permutation
+    expect(ls_check_page_table(large.data(), 1 << 16, 1 << 16) == LS_OK, "page table: 65,536 pages");
+}
+
+void prefix_checks() {
+    Prefix ok(24, 4, 256, LS_DTYPE_BF16, 2000, {0, 5, 19, 32});
+    expect(ls_fwd_workspace_bytes(&ok.p, 100) == 4ull * 4 * 100 * 24 * 257, "forward workspace size");
+    Prefix bad = ok;
+    bad.p.shard_page_bounds = bad.bounds.data();
+    bad.bounds[3] = 31;
+    expect(ls_fwd_workspace_bytes(&bad.p, 10) == 0 && std::strstr(ls_last_error(), "shard bounds"),
+           "bounds must end at the number of logical pages");
+    Prefix many(8, 2, 64, LS_DTYPE_BF16, 64 * 640, even(640, 64));
+    expect(ls_fwd_workspace_bytes(&many.p, 16) > 0, "64 shards accepted");
+    Prefix too_many(8, 2, 64, LS_DTYPE_BF16, 64 * 650, even(650, 65));
+    expect(ls_fwd_workspace_bytes(&too_many.p, 16) == 0, "65 shards rejected");
+    Prefix empty(8, 2, 64, LS_DTYPE_BF16, 0, {0, 0});
+    empty.p.page_table = nullptr;
+    empty.p.k_pages = empty.p.v_pages = nullptr;
+    expect(ls_fwd_workspace_bytes(&empty.p, 16) > 0, "an empty prompt needs no pages");
+    expect(ls_replay_fwd(&ok.p, fake(4), int64_t(1) << 40, 0, fake(5), fake(6), int64_t(1) << 41, fake(7),
+                         (float*)fake(8), fake(9), ~size_t(0), nullptr) == LS_ERR_INVALID,
+           "a block too large for the kernels' 32-bit offsets is rejected");
+}
+
+void dispatch_checks() {
+    Prefix pb(24, 4, 256, LS_DTYPE_BF16, 2000, {0, 5, 19, 32});
+    const size_t fw = ls_fwd_workspace_bytes(&pb.p, 100);
+    stub::last = stub::Record();
+    int rc = ls_replay_fwd(&pb.p, fake(4), 100, 44, fake(5), fake(6), 144, fake(7), (float*)fake(8), fake(9), fw,
+                           nullptr);
+    expect(rc == LS_OK && std::string(stub::last.name) == "lse_merge" && stub::last.calls == 2,
+           "bf16 forward: matrix-core forward, then the merge");
+    expect(stub::last.args.key_end == 144 && stub::last.args.n_parts == 4 && stub::last.args.shard_lo[2] == 19 &&
+               stub::last.args.o_parts == (float*)fake(9),
+           "forward arguments: key range, parts, shard bounds, workspace");
+    expect(ls_replay_fwd(&pb.p, fake(4), 100, 44, fake(5), fake(6), 144, fake(7), (float*)fake(8), fake(9), fw - 1,
+                         nullptr) == LS_ERR_WORKSPACE,
+           "a short forward workspace is rejected");
+    Prefix pf(4, 1, 64, LS_DTYPE_F32, 4096, {0, 32, 64});
+    stub::last = stub::Record();
+    rc = ls_replay_fwd(&pf.p, fake(4), 256, 0, fake(5), fake(6), 256, fake(7), (float*)fake(8), fake(9),
+                       ls_fwd_workspace_bytes(&pf.p, 256), nullptr);
+    expect(rc == LS_OK && stub::last.calls == 2, "f32 forward: the vector-ALU forward, then the merge");
+}
+
+void chunk_plan_checks() {
+    // 2,000-token prompt in 3 uneven shards, 24/4 heads, a 128-row block at rows [128, 256)
+    Prefix pb(24, 4, 256, LS_DTYPE_BF16, 2000, {0, 5, 19, 32});
+    const int64_t n = 128, q0 = 128, kend = q0 + n;
+    const size_t rec = ls_bwd_workspace_bytes(&pb.p, n);
+    stub::last = stub::Record();
+    expect(bwd(&pb.p, n, q0, rec) == LS_OK && stub::last.bwd.ds == nullptr, "recompute workspace: no stored dS");
+    const size_t all = ls_bwd_ds_workspace_bytes(&pb.p, n, kend);
+    expect(all == ls_bwd_ds_chunk_workspace_bytes(&pb.p, n, kend, 4, 4), "chunk size of (all heads, all parts)");
+    stub::last = stub::Record();
+    expect(bwd(&pb.p, n, q0, all) == LS_OK && stub::last.bwd.ds != nullptr && stub::last.bwd.ds_heads == 4 &&
+               stub::last.bwd.ds_parts == 4,
+           "full workspace: every kv head over all keys");
+    for (int h = 1; h <= 3; h++) {
+        const size_t ws = ls_bwd_ds_chunk_workspace_bytes(&pb.p, n, kend, h, 4);
+        stub::last = stub::Record();
+        const bool ok = bwd(&pb.p, n, q0, ws) == LS_OK && stub::last.bwd.ds_heads == h && stub::last.bwd.ds_parts == 4;
+        expect(ok, ("exact workspace of " + std::to_string(h) + " kv head(s) selects that chunk").c_str());
+    }
+    for (int k = 1; k <= 3; k++) {
+        const size_t ws = ls_bwd_ds_chunk_workspace_bytes(&pb.p, n, kend, 1, k);
+        stub::last = stub::Record();
+        const bool ok = bwd(&pb.p, n, q0, ws) == LS_OK && stub::last.bwd.ds_heads == 1 &&
+                        stub::last.bwd.ds_parts >= k && stub::last.bwd.ds_parts < 4 &&
+                        stub::last.bwd.ds_kslots ==
+                            ls::ds_chunk_slots(pb.bounds.data(), 3, kend, stub::last.bwd.ds_parts);
+        expect(ok, ("exact workspace of 1 kv head x " + std::to_string(k) + " part(s) selects a part chunk").c_str());
+    }
+    const size_t one = ls_bwd_ds_chunk_workspace_bytes(&pb.p, n, kend, 1, 1);
+    stub::last = stub::Record();
+    expect(bwd(&pb.p, n, q0, one - 1) == LS_OK && stub::last.bwd.ds == nullptr,
+           "one byte short of the smallest chunk: recompute");
+    expect(ls_bwd_ds_chunk_workspace_bytes(&pb.p, n, kend, 2, 3) == 0, "several kv heads need all key parts");
+    expect(ls_bwd_ds_chunk_workspace_bytes(&pb.p, n, kend, 0, 4) == 0, "zero heads rejected");
+    expect(ls_bwd_ds_chunk_workspace_bytes(&pb.p, n, kend, 1, 5) == 0, "more parts than there are rejected");
+    // the chunks: odd page bounds put a page pair in two chunks; the response is the last part
+    const ls::PartChunk c0 = ls::part_chunk(pb.bounds.data(), 3, kend, 0, 1);
+    const ls::PartChunk c1 = ls::part_chunk(pb.bounds.data(), 3, kend, 1, 2);
+    const ls::PartChunk c3 = ls::part_chunk(pb.bounds.data(), 3, kend, 3, 4);
+    expect(c0.pg_lo == 0 && c0.pg_hi == 5 && c0.pair_lo == 0 && c0.n_pairs == 3 && !c0.resp, "chunk of shard 0");
+    expect(c1.pg_lo == 5 && c1.pg_hi == 19 && c1.pair_lo == 2 && c1.n_pairs == 8 && !c1.resp, "chunk of shard 1");
+    expect(c3.n_pairs == 0 && c3.resp && c3.n_resp_pairs == 2, "chunk of the response keys");
+    // first touch past the block: the response gradients past key_end are zeroed
+    stub::last = stub::Record();
+    expect(bwd(&pb.p, n, q0, rec, 1) == LS_OK && std::string(stub::last.name) == "zero",
+           "first touch zeroes response gradients past the block");
+    Prefix pf(4, 1, 64, LS_DTYPE_F32, 4096, {0, 32, 64});
+    expect(ls_bwd_ds_workspace_bytes(&pf.p, 64, 64) == ls_bwd_workspace_bytes(&pf.p, 64),
+           "f32 stores no dS");
+}
+
+void thread_checks() {
+    // the error message belongs to the calling thread
+    const int32_t dup[2] = {1, 1};
+    ls_check_page_table(dup, 2, 2);
+    std::string other;
+    std::thread t([&] {
+        const int32_t good[2] = {1, 0};
+        ls_check_page_table(good, 2, 2);
+        other = ls_last_error();
+    });
+    t.join();
+    expect(other.empty() && std::strstr(ls_last_error(), "already mapped") != nullptr, "per-thread error message");
+}
+
+}  // namespace
+
+int main() {
+    page_table_checks();
+    prefix_checks();
+    dispatch_checks();
+    chunk_plan_checks();
+    thread_checks();
+    std::printf("%s: %d failure(s)\n", g_failed ? "FAILED" : "PASSED", g_failed);
+    return g_failed ? 1 : 0;
+}

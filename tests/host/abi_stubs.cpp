@@ -1,0 +1,42 @@
+// Host-only stand-ins for the kernel launchers that the C ABI front end (abi.cpp) calls, so that
+// the front end can be built with the host compiler and its sanitizers, without a GPU.  Each
+// records the arguments of its last call and returns hipSuccess; nothing is launched.
+#include "abi_stubs.hpp"
+
+namespace stub {
+Record last;
+}
+
+namespace ls {
+
+static hipError_t note(const char* name, const AttnArgs* a = nullptr) {
+    stub::last.calls++;
+    stub::last.name = name;
+    if (a) stub::last.args = *a;
+    return hipSuccess;
+}
+
+hipError_t launch_capture(const void*, const void*, int, int64_t, int64_t, const int32_t*, void*, void*, int, int64_t,
+                          int, int, hipStream_t) {
+    return note("capture");
+}
+hipError_t launch_gather(const void*, int, const int32_t*, int64_t, int64_t, int64_t, int, int, void*, hipStream_t) {
+    return note("gather");
+}
+hipError_t launch_lse_merge(int, int64_t, int, const float*, const float*, void*, int, float*, hipStream_t, bool) {
+    return note("lse_merge");
+}
+hipError_t launch_delta(const void*, const void*, int, int64_t, int, float*, hipStream_t) { return note("delta"); }
+hipError_t launch_sum_parts(int, int64_t, const float*, float*, hipStream_t) { return note("sum_parts"); }
+hipError_t launch_zero(float*, int64_t, hipStream_t) { return note("zero"); }
+hipError_t launch_fwd_generic(const AttnArgs& a, hipStream_t) { return note("fwd_generic", &a); }
+hipError_t launch_bwd_generic(const AttnArgs& a, hipStream_t) { return note("bwd_generic", &a); }
+hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t) { return note("fwd_mfma", &a); }
+hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t) {
+    // the stored-dS chunk plan the front end chose is what a test checks, so keep it apart from
+    // the merge / sum launches that follow
+    stub::last.bwd = a;
+    return note("bwd_mfma", &a);
+}
+
+}  // namespace ls

@@ -180,3 +180,47 @@ def test_profile_begin_end_without_launches():
     n = C.c_int(0)
     # end without begin is an error
     assert _lib.lib().ls_profile_end(None, 0, C.byref(n)) == LS_ERR_INVALID
+
+
+def test_stored_ds_chunk_workspace_sizes():
+    """Chunks of h kv heads over all key parts take h heads' share of the dS; one kv head by k key
+    parts takes the largest chunk's key slots; invalid chunkings are rejected."""
+    p = _prefix()
+    lib = _lib.lib()
+    base = (lib.ls_bwd_workspace_bytes(C.byref(p), 16) + 255) // 256 * 256
+    full = lib.ls_bwd_ds_workspace_bytes(C.byref(p), 16, 16)
+    assert lib.ls_bwd_ds_chunk_workspace_bytes(C.byref(p), 16, 16, 2, 3) == full
+    assert lib.ls_bwd_ds_chunk_workspace_bytes(C.byref(p), 16, 16, 1, 3) == base + 8 * 128 * 2 * 64
+    # shards of one page each and the response (one pair): every single part is one page pair
+    assert lib.ls_bwd_ds_chunk_workspace_bytes(C.byref(p), 16, 16, 1, 1) == base + 8 * 128 * 1 * 64
+    assert lib.ls_bwd_ds_chunk_workspace_bytes(C.byref(p), 16, 16, 2, 1) == 0 and "all parts" in _err()
+    assert lib.ls_bwd_ds_chunk_workspace_bytes(C.byref(p), 16, 16, 3, 3) == 0
+    assert lib.ls_bwd_ds_chunk_workspace_bytes(C.byref(p), 16, 16, 1, 0) == 0
+
+
+def test_check_page_table():
+    lib = _lib.lib()
+
+    def chk(entries, n_phys):
+        arr = (C.c_int32 * max(1, len(entries)))(*entries)
+        return lib.ls_check_page_table(C.cast(arr, C.c_void_p), len(entries), n_phys)
+
+    assert chk([3, 0, 2, 1], 4) == 0
+    assert chk([3, 0, 2], 6) == 0
+    assert chk([0, 1, 1, 2], 4) == LS_ERR_INVALID and "page_table[2]" in _err()
+    assert chk([0, 4], 4) == LS_ERR_INVALID and "outside" in _err()
+    assert chk([0, -2], 4) == LS_ERR_INVALID
+    assert chk([0, 1, 2], 2) == LS_ERR_INVALID
+    assert lib.ls_check_page_table(None, 0, 0) == 0
+    assert lib.ls_check_page_table(None, 3, 3) == LS_ERR_INVALID
+
+
+def test_binding_checks_tables_before_capture():
+    """api.capture_pages checks the table on the host before anything is launched."""
+    import torch
+
+    from suffix_attention_amd import api
+    with pytest.raises(_lib.LongStrawError, match="already mapped"):
+        api.check_page_table(torch.tensor([0, 2, 2], dtype=torch.int32), 3)
+    api.check_page_table(torch.tensor([2, 0, 1], dtype=torch.int32), 3)
+

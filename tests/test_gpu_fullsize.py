@@ -30,22 +30,28 @@ def _prefix(cfg, kp, vp, table):
                       api.even_shard_bounds(cfg.n_pages, cfg.S))
 
 
-def _block(pre, m, q_start, n, store_ds=True):
+def _block(pre, m, q_start, n, store_ds=True, parts=None):
     """One replayed block (forward + first-touch backward) through the C ABI; by default with
-    the stored-dS backward that the benchmark runs at the 2M-token size."""
+    the stored-dS backward that the benchmark runs at the 2M-token size.  parts: run the
+    stored-dS backward one kv head by `parts` consecutive key parts at a time."""
     q, do = m["q"][q_start:q_start + n].contiguous(), m["do"][q_start:q_start + n].contiguous()
     o, lse, _ = api.replay_fwd(pre, q, q_start, m["kr"], m["vr"])
     dkr = torch.empty(m["kr"].shape, dtype=torch.float32, device="cuda")
     dvr = torch.empty_like(dkr)
     dkp = torch.empty(pre.k_pages.shape, dtype=torch.float32, device="cuda")
     dvp = torch.empty_like(dkp)
+    ws = None
+    if parts is not None:
+        nbytes = api.bwd_ds_workspace_bytes(pre, n, q_start + n, heads=1, parts=parts)
+        ws = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device="cuda")
     dq = api.replay_bwd(pre, q, q_start, m["kr"], m["vr"], o, lse, do, dkr, dvr, True, dkp, dvp,
-                        shard_first_touch=[True] * pre.n_shards, store_ds=store_ds)
+                        shard_first_touch=[True] * pre.n_shards, store_ds=store_ds, workspace=ws)
+    del ws
     torch.cuda.synchronize()
-    return dict(o=o, lse=lse, dq=dq, dkr=dkr, dvr=dvr, dkp=dkp, dvp=dvp)
+    return dict(o=o, lse=lse, dq=dq, dkr=dkr, dvr=dvr, dkp=dkp, dvp=dvp, q=q, do=do)
 
 
-def _sampled_rows_and_gradient_sums(cfg, q_start, n, rows, store_ds):
+def _sampled_rows_and_gradient_sums(cfg, q_start, n, rows, store_ds, parts=None):
     """The block [q_start, q_start + n) of member 0 at the config's full size: sampled rows of
     one kv head against the oracle over every key they see, and the gradient identities over
     all keys."""
@@ -53,7 +59,7 @@ def _sampled_rows_and_gradient_sums(cfg, q_start, n, rows, store_ds):
     kp, vp = datagen.prefix_kv(cfg, "cuda")
     pre = _prefix(cfg, kp, vp, table)
     m = datagen.member_inputs(cfg, 0, "cuda")
-    res = _block(pre, m, q_start, n, store_ds=store_ds)
+    res = _block(pre, m, q_start, n, store_ds=store_ds, parts=parts)
     g = cfg.g
     kend = q_start + n
 
@@ -85,8 +91,11 @@ def _sampled_rows_and_gradient_sums(cfg, q_start, n, rows, store_ds):
     dk_sq = sum(float(torch.linalg.vector_norm(x, dtype=f64) ** 2) for x in (res["dkp"], res["dkr"][:kend]))
     rel_dk = float(dk_sum.norm()) / math.sqrt(dk_sq)
     log(f"    sum dV vs sum dO rel={rel_dv:.3e}; |sum dK| / ||dK||_F = {rel_dk:.3e}")
-    assert rel_dv <= 5e-3
-    assert rel_dk <= 2e-2
+    assert rel_dv <= REL_L2
+    # sum_j dK_j is exactly 0, so what remains is the sum of the per-key errors; errors that are
+    # independent across keys add up to their Frobenius norm, so |sum dK| / ||dK||_F is about the
+    # relative L2 error of dK itself, which the per-element parity bounds by REL_L2
+    assert rel_dk <= REL_L2
 
 
 def test_c2m_block_sampled_rows_and_gradient_sums():
@@ -104,14 +113,19 @@ def test_c1m_block_sampled_rows_and_gradient_sums():
     _sampled_rows_and_gradient_sums(cfg, q_start, n, (0, 300, n - 1), store_ds=True)
 
 
-def test_stress_block_sampled_rows_and_gradient_sums():
+@pytest.mark.parametrize("form", ["recompute", "stored dS, 1 kv head x 2 key parts"])
+def test_stress_block_sampled_rows_and_gradient_sums(form):
     """The stress workload's last reverse block: 8,192 rows at the end of a 262,144-token
     response over a 4,194,304-token prompt in 16 shards, so its rows see 4,456,448 keys.  One
-    block's dS would take 1.75 TB, so the backward recomputes (as the driver chooses there)."""
+    block's dS over all keys would take 1.75 TB, so the backward either recomputes or stores dS
+    one kv head by two key parts (two shards, or the response keys) at a time: 52 GB."""
     cfg = configs.CONFIGS["stress"]
     q_start, n = cfg.R - cfg.B, cfg.B
-    log(f"case: stress P={cfg.P} S={cfg.S} block rows [{q_start}, {q_start + n}) sampled rows + gradient sums")
-    _sampled_rows_and_gradient_sums(cfg, q_start, n, (0, 4097, n - 1), store_ds=False)
+    log(f"case: stress P={cfg.P} S={cfg.S} block rows [{q_start}, {q_start + n}) {form}: sampled rows + gradient sums")
+    if form == "recompute":
+        _sampled_rows_and_gradient_sums(cfg, q_start, n, (0, 4097, n - 1), store_ds=False)
+    else:
+        _sampled_rows_and_gradient_sums(cfg, q_start, n, (0, 4097, n - 1), store_ds=False, parts=2)
 
 
 def test_c2m_zero_keys_closed_form():
@@ -198,7 +212,7 @@ def test_group_accumulation_is_linear_and_peak_memory_flat():
     log(f"case: group of {cfg.G} members, P={cfg.P}, R={cfg.R}, B=512")
     pre = _small_prefix(cfg)
     members = [lambda i=i: datagen.member_inputs(cfg, i, "cuda") for i in range(cfg.G)]
-    grp, results = driver.replay_group(pre, members, 512, keep="none")
+    grp, results = driver.replay_group(pre, members, 512, keep="none", track_peak=True)
     peaks = [r.peak_bytes for r in results]
     log(f"    per-member peak device memory: {peaks}")
     assert len(set(peaks)) == 1, peaks
@@ -228,8 +242,9 @@ def test_group_with_kv_head_chunks_of_stored_ds():
     full_ws = api.bwd_ds_workspace_bytes(pre, 512, cfg.R)
     two = api.bwd_ds_workspace_bytes(pre, 512, cfg.R, heads=2)
     assert two < full_ws
-    g_full, r_full = driver.replay_group(pre, members, 512, ds_budget=full_ws)
-    g_two, r_two = driver.replay_group(pre, members, 512, ds_budget=two)
+    g_full, r_full = driver.replay_group(pre, members, 512, ds_budget=full_ws, track_peak=True)
+    g_two, r_two = driver.replay_group(pre, members, 512, ds_budget=two, track_peak=True)
+    assert g_full.plan == driver.BwdPlan(cfg.hkv, cfg.S + 1) and g_two.plan == driver.BwdPlan(2, cfg.S + 1)
     for a, b in zip(r_full, r_two):
         for name in ("o", "lse", "dq", "dk_resp", "dv_resp"):
             assert torch.equal(getattr(a, name), getattr(b, name)), name

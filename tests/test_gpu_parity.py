@@ -283,12 +283,16 @@ def test_stored_ds_keys_never_read_and_deterministic():
     assert np.array_equal(c.logical(clean["dk_pages"]), c.logical(dirty["dk_pages"]))
 
 
-def test_stored_ds_in_kv_head_chunks_is_bitwise_the_same():
+@pytest.mark.parametrize("bounds", [[0, 8, 16, 24], [0, 5, 5, 13, 24]])
+def test_stored_ds_in_chunks_is_bitwise_the_same(bounds):
     """A workspace with room for the dS of 1, 2 or 3 of the 4 kv heads runs the stored-dS
-    backward a chunk of kv heads at a time; kv heads are independent, so every output is the
-    same bit for bit as with room for all of them."""
-    log("case: stored dS in kv-head chunks P=1500 R=256 hq=24 hkv=4 d=256 S=3 rows [64, 256)")
-    c = Case(1500, 256, 24, 4, 256, torch.bfloat16, seed=31, S=3)
+    backward a chunk of kv heads at a time, and one with room for less than one kv head's dS
+    over all keys runs one kv head by k consecutive key parts at a time (a page pair cut by a
+    chunk's odd page bound is walked by both chunks, each writing its own page); kv heads and key
+    parts are independent, so every output is the same bit for bit as with room for all of them.
+    The workspace starts as NaN, so a slot read but never written would show."""
+    log(f"case: stored dS in chunks P=1500 R=256 hq=24 hkv=4 d=256 shards {bounds} rows [64, 256)")
+    c = Case(1500, 256, 24, 4, 256, torch.bfloat16, seed=31, bounds=bounds)
     pre = c.prefix()
     dev = "cuda"
     q0, n = 64, 192
@@ -296,8 +300,8 @@ def test_stored_ds_in_kv_head_chunks_is_bitwise_the_same():
     kr, vr = c.kr.to(dev), c.vr.to(dev)
     o, lse, _ = api.replay_fwd(pre, q, q0, kr, vr)
 
-    def run(heads):
-        nbytes = api.bwd_ds_workspace_bytes(pre, n, q0 + n, heads=heads)
+    def run(heads, parts):
+        nbytes = api.bwd_ds_workspace_bytes(pre, n, q0 + n, heads=heads, parts=parts)
         ws = torch.full(((nbytes + 3) // 4,), float("nan"), dtype=torch.float32, device=dev)
         dk_r = torch.empty(kr.shape, dtype=torch.float32, device=dev)
         dv_r = torch.empty_like(dk_r)
@@ -308,11 +312,15 @@ def test_stored_ds_in_kv_head_chunks_is_bitwise_the_same():
         torch.cuda.synchronize()
         return dq, dk_r[:q0 + n], dv_r[:q0 + n], dk_p, dv_p
 
-    full = run(None)
+    full = run(None, None)
     ref = c.oracle(q0, n, o_used=c.stored(c.oracle(q0, n)["o"]))
     assert_close("dQ", np32(full[0]), ref["dq"])
-    assert api.bwd_ds_workspace_bytes(pre, n, q0 + n, heads=1) < api.bwd_ds_workspace_bytes(pre, n, q0 + n)
-    for heads in (1, 2, 3):
-        got = run(heads)
+    assert_close("dK_prompt", c.logical(full[3]), ref["dkp"])
+    n_all = pre.n_shards + 1
+    sizes = [api.bwd_ds_workspace_bytes(pre, n, q0 + n, heads=1, parts=k) for k in range(1, n_all + 1)]
+    assert sizes == sorted(sizes) and sizes[-1] < api.bwd_ds_workspace_bytes(pre, n, q0 + n)
+    plans = [(h, n_all) for h in (1, 2, 3)] + [(1, k) for k in range(1, n_all)]
+    for heads, parts in plans:
+        got = run(heads, parts)
         for name, a, b in zip(("dq", "dk_r", "dv_r", "dk_p", "dv_p"), full, got):
-            assert torch.equal(a, b), (heads, name)
+            assert torch.equal(a, b), (heads, parts, name)
