@@ -227,23 +227,24 @@ def run_steps(prefix, members, cfg, n, cycle_log=None, store_ds="default"):
     return last
 
 
-def memory_vs_g(prefix, members, cfg, timed_grp) -> dict:
+def memory_vs_g(prefix, members, cfg, timed_peak: int, timed_form: str) -> dict:
     """Peak device memory of a group at G = 2 and at the config's G, with the backward of the
-    timed run and with the recomputing one (untimed runs; the timed run itself is the timed
-    form's figure at the config's G)."""
+    timed run and with the recomputing one (untimed runs, each a fresh group after the previous
+    one's gradient pages are released; the timed run itself is the timed form's figure at the
+    config's G)."""
     out = {}
     for label, store in (("timed_form", STORE_DS), ("recompute", False)):
         row = {}
         for g_ in sorted({2, cfg.G}):
             if label == "timed_form" and g_ == cfg.G:
-                peak = timed_grp.peak_bytes
+                peak = timed_peak
             else:
                 grp, _ = run_steps(prefix, members[:g_], cfg, 1, store_ds=store)
                 peak = grp.peak_bytes
                 del grp
             row[f"G={g_}"] = round(peak / 1e9, 3)
         out[label] = row
-    out["timed_form"]["form"] = timed_grp.plan.describe(prefix)
+    out["timed_form"]["form"] = timed_form
     return out
 
 
@@ -562,11 +563,13 @@ def main():
                                      + out["config"]["workload"].split(": ", 1)[1])
         out["cycle_ms"] = [round(c[0], 1) for c in cycles]
         out["cycle_peak_gb"] = [round(c[1] / 1e9, 3) for c in cycles]
+    timed_peak, timed_form = grp.peak_bytes, plan.describe(prefix)
+    del grp, results  # release the timed group's gradient pages before anything else runs
     if not ns.no_memory_sweep and cycles is None:
         t = time.perf_counter()
-        out["peak_mem_gb_vs_G"] = memory_vs_g(prefix, members, cfg, grp)
+        out["peak_mem_gb_vs_G"] = memory_vs_g(prefix, members, cfg, timed_peak, timed_form)
+        torch.cuda.synchronize()
         log(f"[bench] memory sweep {time.perf_counter() - t:.1f} s: {out['peak_mem_gb_vs_G']}")
-    del grp, results
     if not ns.no_cpu_baseline:
         t = time.perf_counter()
         out["cpu_baseline"] = cpu_baseline(cfg, kp, vp, members[0])

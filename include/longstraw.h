@@ -272,7 +272,8 @@ int ls_score_fwd(const ls_prefix_t* pre, int64_t n_members, const void* q, int64
  *                   device float32 [n_phys_pages, hkv, page_size, d], indexed like the
  *                   pools: prompt-key gradients are added in, or written for shards whose
  *                   shard_first_touch[s] != 0 (rows past prefix_len in a partial last
- *                   page are then written as zero).
+ *                   page are then written as zero).  Physical pages that no logical page
+ *                   maps to are left untouched.
  *   shard_first_touch  host uint8 [n_shards], or NULL for "accumulate everywhere".
  *   workspace       device, ws_bytes >= ls_bwd_workspace_bytes(pre, n_rows); with
  *                   room for the block's dS, or for a chunk of it (bf16; see
