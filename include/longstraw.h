@@ -228,6 +228,24 @@ int ls_replay_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
                   float* lse, void* workspace, size_t ws_bytes, ls_stream_t stream);
 
 /*
+ * ls_replay_fwd_noalloc -- ls_replay_fwd for callers that cannot allocate device memory (code
+ * under stream capture, tight serving loops, harnesses that forbid allocation).  The per-part
+ * results live in a fixed scratch array of LS_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on, until the process ends, instead of in a caller's workspace.  Arguments,
+ * results and errors are those of ls_replay_fwd without the workspace; a block whose forward
+ * workspace (ls_fwd_workspace_bytes) exceeds LS_NOALLOC_SCRATCH_BYTES fails with
+ * LS_ERR_WORKSPACE before any launch (split it into smaller blocks).  Nothing is allocated: the
+ * first call on a device looks up that device's array (hipGetSymbolAddress); a failure there is
+ * LS_ERR_HIP.  Every call on one GPU uses that GPU's one array, which keeps the last call's
+ * contents, so calls that overlap on one GPU (on other streams or from other threads) race;
+ * calls ordered on the device give exactly ls_replay_fwd's results.
+ */
+#define LS_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int ls_replay_fwd_noalloc(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start,
+                          const void* k_resp, const void* v_resp, int64_t n_resp_keys, void* o,
+                          float* lse, ls_stream_t stream);
+
+/*
  * ls_score_fwd -- forward-only scoring of several members' whole responses against the same
  * captured prompt, in one launch (digest, "Method", step 2, pre-step scoring; explainer, "The
  * move: change the graph boundary": the old- and reference-policy passes need no autograd

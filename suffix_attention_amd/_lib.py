@@ -55,6 +55,7 @@ _SIG = {
     "ls_bwd_ds_chunk_workspace_bytes": (C.c_size_t, [C.POINTER(ls_prefix_t), _I64, _I64, _I, _I]),
     "ls_check_page_table": (_I, [_P, _I64, _I64]),
     "ls_replay_fwd": (_I, [C.POINTER(ls_prefix_t), _P, _I64, _I64, _P, _P, _I64, _P, _P, _P, C.c_size_t, _P]),
+    "ls_replay_fwd_noalloc": (_I, [C.POINTER(ls_prefix_t), _P, _I64, _I64, _P, _P, _I64, _P, _P, _P]),
     "ls_score_workspace_bytes": (C.c_size_t, [C.POINTER(ls_prefix_t), _I64, _I64]),
     "ls_score_fwd": (_I, [C.POINTER(ls_prefix_t), _I64, _P, _I64, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "ls_replay_bwd": (_I, [C.POINTER(ls_prefix_t), _P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _I,

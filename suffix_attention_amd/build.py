@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "liblongstraw.so")
 SOURCES = ["abi.cpp", "profile.cpp", "capture.hip", "reduce.hip", "attn_generic.hip", "attn_mfma_fwd.hip",
-           "attn_mfma_bwd.hip", "attn_mfma_dq.hip", "attn_mfma_dqs.hip"]
+           "attn_mfma_bwd.hip", "attn_mfma_dq.hip", "attn_mfma_dqs.hip", "noalloc.hip"]
 
 ROOT = os.path.dirname(HERE)
 BENCH_HIP = os.path.join(ROOT, "bench", "hip")

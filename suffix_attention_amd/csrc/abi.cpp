@@ -262,8 +262,8 @@ size_t ls_bwd_ds_chunk_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows, i
     return ds_offset(pre, n_rows) + (size_t)heads * ds_head_bytes(pre, n_rows, key_end, parts);
 }
 
-// Checks of a forward call, before any launch: LS_OK with nothing to do for an empty block is
-// reported through *empty.
+// Checks of a forward call, before any launch (shared by ls_replay_fwd and the no-allocation
+// variant): LS_OK with nothing to do for an empty block is reported through *empty.
 static int check_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start, const void* k_resp,
                      const void* v_resp, int64_t n_resp_keys, void* o, float* lse, bool* empty) {
     int rc = check_prefix(pre);
@@ -290,6 +290,29 @@ int ls_replay_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
     if (!workspace || ws_bytes < need)
         return fail(LS_ERR_WORKSPACE, "forward workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
     return run_fwd(pre, q, n_rows, q_start, k_resp, v_resp, o, lse, workspace, stream);
+}
+
+int ls_replay_fwd_noalloc(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start, const void* k_resp,
+                          const void* v_resp, int64_t n_resp_keys, void* o, float* lse, ls_stream_t stream) {
+    g_err.clear();
+    bool empty = false;
+    const int rc = check_fwd(pre, q, n_rows, q_start, k_resp, v_resp, n_resp_keys, o, lse, &empty);
+    if (rc != LS_OK || empty) return rc;
+    const size_t need = fwd_ws(pre, n_rows);
+    if (need > (size_t)LS_NOALLOC_SCRATCH_BYTES) {
+        const size_t per_row = fwd_ws(pre, 1);
+        return fail(LS_ERR_WORKSPACE,
+                    "a block of %lld rows needs %zu bytes of forward scratch; the no-allocation forward holds %zu "
+                    "(at most %zu rows at this shape): split the block",
+                    (long long)n_rows, need, (size_t)LS_NOALLOC_SCRATCH_BYTES,
+                    per_row ? (size_t)LS_NOALLOC_SCRATCH_BYTES / per_row : 0);
+    }
+    void* scratch = nullptr;
+    size_t scratch_bytes = 0;
+    const hipError_t e = ls::noalloc_scratch(&scratch, &scratch_bytes);
+    if (e != hipSuccess) return hip_fail(e, "scratch set-up (hipGetSymbolAddress)");
+    if (scratch_bytes < need) return fail(LS_ERR_WORKSPACE, "scratch of %zu bytes, %zu needed", scratch_bytes, need);
+    return run_fwd(pre, q, n_rows, q_start, k_resp, v_resp, o, lse, scratch, stream);
 }
 
 static int run_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start, const void* k_resp,

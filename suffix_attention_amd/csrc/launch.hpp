@@ -158,6 +158,10 @@ class KernelTimer {
 // Key-range helpers shared by host launch code.
 inline int64_t resp_tiles(int64_t key_end) { return (key_end + 63) / 64; }
 
+// noalloc.hip: this device's fixed scratch array for ls_replay_fwd_noalloc (its device address,
+// set up on the first call with this device current) and its size
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 // capture.hip
 hipError_t launch_capture(const void* k_src, const void* v_src, int src_dtype, int64_t n_tok,
                           int64_t first_tok, const int32_t* table, void* k_pages, void* v_pages,

@@ -118,6 +118,25 @@ void dispatch_checks() {
     expect(rc == LS_OK && stub::last.calls == 2, "f32 forward: the vector-ALU forward, then the merge");
 }
 
+void noalloc_checks() {
+    Prefix pb(24, 4, 256, LS_DTYPE_BF16, 64 * 80, even(80, 8));
+    const int64_t per_row = (int64_t)ls_fwd_workspace_bytes(&pb.p, 1);
+    const int64_t max_rows = (int64_t)(LS_NOALLOC_SCRATCH_BYTES / per_row);
+    stub::last = stub::Record();
+    int rc = ls_replay_fwd_noalloc(&pb.p, fake(4), max_rows + 1, 0, fake(5), fake(6), max_rows + 1, fake(7),
+                                   (float*)fake(8), nullptr);
+    expect(rc == LS_ERR_WORKSPACE && stub::last.calls == 0 && std::strstr(ls_last_error(), "split the block"),
+           "no-allocation forward: one row past the scratch is refused before any launch");
+    stub::last = stub::Record();
+    rc = ls_replay_fwd_noalloc(&pb.p, fake(4), max_rows, 0, fake(5), fake(6), max_rows, fake(7), (float*)fake(8),
+                               nullptr);
+    expect(rc == LS_OK && stub::last.args.o_parts == (float*)0x7000000 && std::string(stub::last.name) == "lse_merge",
+           "no-allocation forward: the largest block runs in the scratch array");
+    stub::last = stub::Record();
+    rc = ls_replay_fwd_noalloc(&pb.p, fake(4), 0, 0, fake(5), fake(6), 0, fake(7), (float*)fake(8), nullptr);
+    expect(rc == LS_OK && stub::last.calls == 0, "no-allocation forward: an empty block does nothing");
+}
+
 void chunk_plan_checks() {
     // 2,000-token prompt in 3 uneven shards, 24/4 heads, a 128-row block at rows [128, 256)
     Prefix pb(24, 4, 256, LS_DTYPE_BF16, 2000, {0, 5, 19, 32});
@@ -189,6 +208,7 @@ int main() {
     page_table_checks();
     prefix_checks();
     dispatch_checks();
+    noalloc_checks();
     chunk_plan_checks();
     thread_checks();
     std::printf("%s: %d failure(s)\n", g_failed ? "FAILED" : "PASSED", g_failed);

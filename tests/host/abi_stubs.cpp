@@ -3,6 +3,8 @@
 // records the arguments of its last call and returns hipSuccess; nothing is launched.
 #include "abi_stubs.hpp"
 
+#include "../../include/longstraw.h"
+
 namespace stub {
 Record last;
 }
@@ -32,6 +34,13 @@ hipError_t launch_zero(float*, int64_t, hipStream_t) { return note("zero"); }
 hipError_t launch_fwd_generic(const AttnArgs& a, hipStream_t) { return note("fwd_generic", &a); }
 hipError_t launch_bwd_generic(const AttnArgs& a, hipStream_t) { return note("bwd_generic", &a); }
 hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t) { return note("fwd_mfma", &a); }
+hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
+    stub::last.calls++;
+    stub::last.name = "noalloc_scratch";
+    *ptr = (void*)0x7000000;
+    *bytes = LS_NOALLOC_SCRATCH_BYTES;
+    return hipSuccess;
+}
 hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t) {
     // the stored-dS chunk plan the front end chose is what a test checks, so keep it apart from
     // the merge / sum launches that follow
