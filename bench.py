@@ -176,7 +176,15 @@ def measured_ceilings() -> dict:
             assert rc == 0, rc
             best = max(best, v.value)
         out[name] = round(best, 1)
-    out["source"] = "bench/hip/mfma_peak.hip (32x32x16 bf16 chains, every SIMD), bench/hip/hbm_bw.hip (4 GiB)"
+    lib.mb_lds.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_double)]
+    for name, mode in (("lds_read_b128_tbs", 0), ("lds_read_tr_b64_tbs", 1),
+                       ("mfma_lds_fed_1kib_per_mfma_tflops", 2), ("mfma_lds_fed_1kib_per_2mfma_tflops", 3)):
+        for waves in (4, 8):
+            rc = lib.mb_lds(mode, 256, waves, 100000, 3, C.byref(v))
+            assert rc == 0, rc
+            out[f"{name}_{waves}w"] = round(v.value, 1)
+    out["source"] = ("bench/hip/mfma_peak.hip (32x32x16 bf16 chains, every SIMD), bench/hip/hbm_bw.hip (4 GiB), "
+                     "bench/hip/lds_bw.hip (one workgroup of 4 or 8 waves per CU)")
     return out
 
 

@@ -25,7 +25,7 @@ SOURCES = ["abi.cpp", "profile.cpp", "capture.hip", "reduce.hip", "attn_generic.
 
 ROOT = os.path.dirname(HERE)
 BENCH_HIP = os.path.join(ROOT, "bench", "hip")
-BENCH_SOURCES = ["mfma_peak.hip", "hbm_bw.hip"]
+BENCH_SOURCES = ["mfma_peak.hip", "hbm_bw.hip", "lds_bw.hip"]
 BENCH_LIB = os.path.join(ROOT, "bench", "libmicrobench.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
