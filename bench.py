@@ -178,7 +178,8 @@ def measured_ceilings() -> dict:
         out[name] = round(best, 1)
     lib.mb_lds.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_double)]
     for name, mode in (("lds_read_b128_tbs", 0), ("lds_read_tr_b64_tbs", 1),
-                       ("mfma_lds_fed_1kib_per_mfma_tflops", 2), ("mfma_lds_fed_1kib_per_2mfma_tflops", 3)):
+                       ("mfma_lds_fed_1kib_per_mfma_tflops", 2), ("mfma_lds_fed_1kib_per_2mfma_tflops", 3),
+                       ("mfma_lds_fed_2tr_per_mfma_tflops", 4)):
         for waves in (4, 8):
             rc = lib.mb_lds(mode, 256, waves, 100000, 3, C.byref(v))
             assert rc == 0, rc
