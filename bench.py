@@ -158,16 +158,19 @@ def measured_ceilings() -> dict:
     (bench/hip/mfma_peak.hip, bench/hip/hbm_bw.hip): best of a few timed launches each."""
     import ctypes as C
     lib = C.CDLL(MICROBENCH)
-    lib.mb_mfma_peak.argtypes = [C.c_int, C.c_int, C.c_int, C.POINTER(C.c_double)]
+    lib.mb_mfma_peak.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_double)]
     lib.mb_hbm.argtypes = [C.c_int, C.c_size_t, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_double)]
     out = {}
     v = C.c_double(0)
-    best = 0.0
-    for blocks in (256, 512):  # one and two waves on every SIMD
-        rc = lib.mb_mfma_peak(blocks, 200000, 3, C.byref(v))
-        assert rc == 0, rc
-        best = max(best, v.value)
-    out["mfma_bf16_tflops"] = round(best, 1)
+    # random operands: launches of about 130 ms, as long as the library's own, since the
+    # clock keeps falling for tens of milliseconds under that load
+    for key, rand, iters in (("mfma_bf16_tflops", 0, 100000), ("mfma_bf16_random_operands_tflops", 1, 400000)):
+        best = 0.0
+        for blocks in (256, 512):  # one and two waves on every SIMD
+            rc = lib.mb_mfma_peak(blocks, iters if blocks == 256 else iters // 2, 3, rand, C.byref(v))
+            assert rc == 0, rc
+            best = max(best, v.value)
+        out[key] = round(best, 1)
     for name, mode, fill in (("hbm_read_gbs", 0, 1), ("hbm_read_zeros_gbs", 0, 0), ("hbm_write_gbs", 1, 1),
                              ("hbm_copy_gbs", 2, 1)):
         best = 0.0
@@ -566,6 +569,11 @@ def main():
         out["pct_measured_mfma_peak"] = round(100 * tflops / ceilings["mfma_bf16_tflops"], 2)
         out["roofline"]["measured_peak"] = ceilings["mfma_bf16_tflops"]
         out["roofline"]["frac_measured_peak"] = round(achieved / ceilings["mfma_bf16_tflops"], 4)
+        # the same chains on random operands: the ceiling the chip holds on N(0, 1)-like data
+        rnd = ceilings["mfma_bf16_random_operands_tflops"]
+        out["pct_random_operand_mfma_ceiling"] = round(100 * tflops / rnd, 2)
+        out["roofline"]["random_operand_peak"] = rnd
+        out["roofline"]["frac_random_operand_peak"] = round(achieved / rnd, 4)
     if cycles is not None:
         out["metric"] = REUSE_METRIC
         out["config"]["workload"] = (f"{cfg.name}: {ns.steps} consecutive optimizer cycles over one capture; "
