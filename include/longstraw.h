@@ -221,6 +221,8 @@ size_t ls_bwd_ds_chunk_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows, i
  *   o               device [n_rows, hq, d] of pre->dtype (written).
  *   lse             device float32 [n_rows, hq] (written).
  *   workspace       device, ws_bytes >= ls_fwd_workspace_bytes(pre, n_rows).
+ * Inputs are not checked for NaN: a NaN in a row's query (or in a key or value it sees) makes
+ * that row's O and LSE NaN, and leaves every other row exactly as without it.
  * Errors: LS_ERR_INVALID, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP.
  */
 int ls_replay_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start,
@@ -313,7 +315,7 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
  * explainer "The fine print", here every step is float32):
  *   L = m + log sum_p exp(L_p - m), m = max_p L_p;  O = sum_p exp(L_p - L) O_p.
  * A part with L_p = -inf adds nothing; a row where every part is -inf gets L = -inf and
- * O = 0.  With n_parts == 1 the result equals the input exactly.
+ * O = 0; a row with a NaN L_p gets NaN.  With n_parts == 1 the result equals the input exactly.
  *
  *   o_parts   device float32 [n_parts, n_rows, d]
  *   lse_parts device float32 [n_parts, n_rows]
@@ -334,6 +336,36 @@ int ls_lse_merge(int n_parts, int64_t n_rows, int d, const float* o_parts,
 int ls_lse_merge_bf16num(int n_parts, int64_t n_rows, int d, const float* o_parts,
                          const float* lse_parts, void* o_out, int out_dtype, float* lse_out,
                          ls_stream_t stream);
+
+/*
+ * One-writer counters, a debug check of the backward's ownership rule (each gradient element
+ * has exactly one writer per call, which is why the kernels need no atomics: digest,
+ * "Method", step 3 accumulates every member's K/V gradients into the same pages, and the
+ * explainer, "Two incompatible architectures, same transaction", writes them per page).
+ * While counters are registered on the calling thread (ls_debug_set_owner_counts with a
+ * non-NULL buffer), every ls_replay_bwd call on that thread first zeroes them on its stream
+ * and then every writer adds 1 to the slot of what it writes:
+ *   slot (phys * hkv + kv) * 2 + half                    prompt gradient half-page (keys
+ *                                                        32 half .. +32 of physical page phys);
+ *   R + (page * hkv + kv) * 2 + half                     response gradient half-page, with
+ *                                                        R = n_phys_pages * hkv * 2;
+ *   Q + (part * n_rows + token) * hq + head              dQ part row (part n_shards is the
+ *                                                        response), with
+ *                                                        Q = R + ceil(key_end / 64) * hkv * 2.
+ * After a correct call every slot holds 1 if the call writes it and 0 otherwise; a slot above
+ * 1 is a second writer.  The caller reads the counters back (the library never synchronises).
+ * Counting uses device atomics and costs time; it is for tests and debugging.
+ *
+ * ls_debug_owner_slots -- slots needed for a block of n_rows rows whose response keys end at
+ *   key_end (= q_start + n_rows); 0 (with an error message) for an invalid descriptor.
+ * ls_debug_set_owner_counts -- register `counts` (device uint32 [n_slots], owned by the
+ *   caller, which keeps it alive while registered) for this thread's backward calls; NULL
+ *   turns the counting off.  A registered ls_replay_bwd call fails with LS_ERR_INVALID if
+ *   n_slots is below ls_debug_owner_slots for its block, and with LS_ERR_UNSUPPORTED for
+ *   float32 descriptors (the counters cover the bf16 matrix-core kernels).
+ */
+size_t ls_debug_owner_slots(const ls_prefix_t* pre, int64_t n_rows, int64_t key_end);
+int ls_debug_set_owner_counts(uint32_t* counts, size_t n_slots);
 
 /*
  * Kernel timing, for diagnostics and benchmarks.  Between ls_profile_begin() and

@@ -62,6 +62,8 @@ _SIG = {
                            _P, _P, _P, _P, C.c_size_t, _P]),
     "ls_lse_merge": (_I, [_I, _I64, _I, _P, _P, _P, _I, _P, _P]),
     "ls_lse_merge_bf16num": (_I, [_I, _I64, _I, _P, _P, _P, _I, _P, _P]),
+    "ls_debug_owner_slots": (C.c_size_t, [C.POINTER(ls_prefix_t), _I64, _I64]),
+    "ls_debug_set_owner_counts": (_I, [_P, C.c_size_t]),
     "ls_profile_begin": (_I, []),
     "ls_profile_end": (_I, [C.POINTER(ls_kernel_stat_t), _I, C.POINTER(_I)]),
 }

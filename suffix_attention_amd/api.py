@@ -183,6 +183,42 @@ def check_page_table(page_table: torch.Tensor, n_phys: int) -> None:
     check(lib().ls_check_page_table(C.c_void_p(host.data_ptr()) if host.numel() else None, host.numel(), n_phys))
 
 
+def owner_slots(prefix: Prefix, n_rows: int, key_end: int) -> int:
+    """Slots of the one-writer counters for a block (ls_debug_owner_slots)."""
+    st = prefix.struct()
+    n = lib().ls_debug_owner_slots(C.byref(st), n_rows, key_end)
+    if n == 0:
+        raise LongStrawError(_lib.LS_ERR_INVALID, lib().ls_last_error().decode())
+    return n
+
+
+class OwnerCounts:
+    """One-writer counters registered for this thread's backward calls while the context is
+    open (ls_debug_set_owner_counts): each call zeroes them, then every writer of a gradient
+    half-page or dQ part row adds 1 to its slot.  check() raises if any slot was written
+    twice."""
+
+    def __init__(self, n_slots: int, device="cuda"):
+        self.counts = torch.zeros((n_slots,), dtype=torch.int32, device=device)
+
+    def __enter__(self):
+        check(lib().ls_debug_set_owner_counts(_ptr(self.counts), self.counts.numel()))
+        return self
+
+    def __exit__(self, *exc):
+        lib().ls_debug_set_owner_counts(None, 0)
+        return False
+
+    def check(self, what: str = "backward") -> torch.Tensor:
+        """The counters on the host (a synchronisation); raises unless every slot is 0 or 1."""
+        c = self.counts.cpu()
+        bad = torch.nonzero(c > 1).flatten()
+        if bad.numel():
+            raise RuntimeError(f"{what}: {bad.numel()} counter slots have more than one writer "
+                               f"(first slot {int(bad[0])}, count {int(c[bad[0]])})")
+        return c
+
+
 def ds_fits(nbytes: int, device, fraction: float = 0.9, budget: int | None = None) -> bool:
     """Whether a workspace of nbytes fits in what the device has free (counting the blocks
     torch's allocator holds but does not use), or in `budget` bytes when one is given."""

@@ -17,6 +17,8 @@
 namespace {
 
 thread_local std::string g_err;
+thread_local uint32_t* g_owner = nullptr;  // one-writer counters of this thread's debug runs
+thread_local size_t g_owner_slots = 0;
 
 int fail(int code, const char* fmt, ...) {
     char buf[512];
@@ -396,6 +398,18 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
     if (need > 0 && (!workspace || ws_bytes < need))
         return fail(LS_ERR_WORKSPACE, "backward workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
     ls::AttnArgs a = make_args(pre, q, n_rows, q_start, k_resp, v_resp);
+    int64_t owner_slots = 0;
+    if (g_owner) {
+        if (pre->dtype != LS_DTYPE_BF16)
+            return fail(LS_ERR_UNSUPPORTED, "one-writer counters cover the bf16 matrix-core kernels only");
+        owner_slots = ls::owner_slots(pre->n_phys_pages, pre->hkv, pre->hq, pre->n_shards + 1, n_rows, a.key_end);
+        if (g_owner_slots < (size_t)owner_slots)
+            return fail(LS_ERR_INVALID, "one-writer counters: %lld slots needed, %zu registered", (long long)owner_slots,
+                        g_owner_slots);
+        a.owner = g_owner;
+        a.owner_resp0 = ls::owner_resp0(pre->n_phys_pages, pre->hkv);
+        a.owner_dq0 = ls::owner_dq0(pre->n_phys_pages, pre->hkv, a.key_end);
+    }
     const int64_t rows = n_rows * pre->hq;
     a.o = o;
     a.dout = dout;
@@ -413,6 +427,10 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
             if (shard_first_touch[s]) a.first_touch_mask |= 1ull << s;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    if (owner_slots > 0) {  // zero bits are the same for uint32 and float32
+        e = ls::launch_zero((float*)a.owner, owner_slots, s);
+        if (e != hipSuccess) return hip_fail(e, "zero kernel");
+    }
     if (pre->dtype == LS_DTYPE_BF16) {
         // A workspace that also holds some stored dS selects the stored-dS dQ pass: with room
         // for every key's dS of at least one kv head, in chunks of as many kv heads as it holds;
@@ -455,6 +473,24 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
         if (e == hipSuccess) e = ls::launch_zero(dv_resp + off, cnt, s);
         if (e != hipSuccess) return hip_fail(e, "zero kernel");
     }
+    return LS_OK;
+}
+
+size_t ls_debug_owner_slots(const ls_prefix_t* pre, int64_t n_rows, int64_t key_end) {
+    g_err.clear();
+    if (check_prefix(pre) != LS_OK) return 0;
+    if (n_rows < 0 || key_end < n_rows) {
+        fail(LS_ERR_INVALID, "n_rows=%lld, key_end=%lld", (long long)n_rows, (long long)key_end);
+        return 0;
+    }
+    return (size_t)ls::owner_slots(pre->n_phys_pages, pre->hkv, pre->hq, pre->n_shards + 1, n_rows, key_end);
+}
+
+int ls_debug_set_owner_counts(uint32_t* counts, size_t n_slots) {
+    g_err.clear();
+    if (counts && n_slots == 0) return fail(LS_ERR_INVALID, "n_slots is 0");
+    g_owner = counts;
+    g_owner_slots = counts ? n_slots : 0;
     return LS_OK;
 }
 

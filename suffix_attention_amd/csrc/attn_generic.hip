@@ -134,12 +134,12 @@ __global__ __launch_bounds__(NT) void fwd_generic_kernel(AttnArgs a) {
         const int64_t tok = r / a.g;
         const int h = kvh * a.g + (int)(r % a.g);
         const float l = l_s[orow];
-        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const float inv = l != 0.f ? 1.f / l : 0.f;  // 0: no key seen; NaN inputs stay NaN
         const int64_t prow = (int64_t)part * a.part_rows + a.row0 + tok;
         float* dst = a.o_parts + (prow * a.hq + h) * D;
 #pragma unroll
         for (int j = 0; j < OC; j++) dst[oc0 + 16 * j] = o[j] * inv;
-        if (oc0 == 0) a.lse_parts[prow * a.hq + h] = l > 0.f ? m_s[orow] + logf(l) : -INFINITY;
+        if (oc0 == 0) a.lse_parts[prow * a.hq + h] = l != 0.f ? m_s[orow] + logf(l) : -INFINITY;
     }
 }
 

@@ -425,6 +425,9 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int pair0, int n_pairs
     // ---- write this wave's keys: dK (scaled) and dV, element i is key 8(i/4) + 4h + i%4
     mfma_drain();
     if (!page_ok) return;
+    if (a.owner && lane == 0)  // debug run: this wave writes its half of the page
+        atomicAdd(a.owner + (resp ? a.owner_resp0 + (page * a.hkv + kvh) * 2 + kh
+                                  : ((int64_t)phys * a.hkv + kvh) * 2 + kh), 1u);
     bool first;
     float *gk, *gv;
     int64_t key_stride;

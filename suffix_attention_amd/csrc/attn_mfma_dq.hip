@@ -315,6 +315,8 @@ void dq_mfma_kernel(AttnArgs a, GroupRows gr, int n_qtiles, int part0, int n_par
     mfma_drain();
     if (!row_ok) return;
     float* dst = a.dq_parts + (((int64_t)part * a.n_rows + my_tok) * a.hq + my_head) * (int64_t)D;
+    if (a.owner && h == 0)  // debug run: this lane pair writes the row
+        atomicAdd(a.owner + a.owner_dq0 + ((int64_t)part * a.n_rows + my_tok) * a.hq + my_head, 1u);
 #pragma unroll
     for (int dt = 0; dt < F::DT; dt++) {
         // scale in place in the AGPRs; the stores read them from there

@@ -203,6 +203,8 @@ void dqs_mfma_kernel(AttnArgs a, int n_rblocks, int n_kvh, int part0, int n_sp, 
         const int64_t tok = row / a.g;
         const int head = kvh * a.g + (int)(row % a.g);
         float* dst = a.dq_parts + (((int64_t)part * a.n_rows + tok) * a.hq + head) * (int64_t)D;
+        if (a.owner && h == 0)  // debug run: this lane pair writes the row
+            atomicAdd(a.owner + a.owner_dq0 + ((int64_t)part * a.n_rows + tok) * a.hq + head, 1u);
 #pragma unroll
         for (int dt = 0; dt < F::DT; dt++) {
 #pragma unroll

@@ -434,9 +434,11 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles) {
         const float l_tot = l + other_half(l);
         if (lane < 32) fin_grp[lane] = l_tot;
         lds_barrier();
+        // l_tot is 0 exactly when the row sees no key of the part (LSE -inf, O 0); a NaN in the
+        // row's inputs leaves it NaN, and NaN is what the row's LSE and O then hold
         if (row_ok && h == 0)
             a.lse_parts[((int64_t)part * a.part_rows + out_row0 + my_tok) * a.hq + my_head] =
-                l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
+                l_tot != 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
     } else {
         f32x16 o[F::DT];
 #pragma unroll
@@ -471,7 +473,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles) {
         lds_barrier();
         const float l_tot = fin_grp[n];
         if (row_ok) {
-            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            const float inv = l_tot != 0.f ? 1.f / l_tot : 0.f;
             float* dst = a.o_parts + (((int64_t)part * a.part_rows + out_row0 + my_tok) * a.hq + my_head) * (int64_t)D;
 #pragma unroll
             for (int dt = 0; dt < F::DT; dt++) {

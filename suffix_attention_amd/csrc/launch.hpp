@@ -81,7 +81,22 @@ struct AttnArgs {
     // prompt pages [pg_lo, pg_hi) are the ones whose K/V gradients a dK/dV launch writes (all
     // logical pages, except in a chunk of key parts: the chunk's shards)
     int64_t pg_lo, pg_hi;
+    // One-writer counters of a debug run (null: off).  Every writer of a gradient half-page or
+    // of a dQ part row adds 1 to its slot: prompt half-pages at ((phys * hkv + kv) * 2 + half),
+    // response half-pages from owner_resp0 on at ((page * hkv + kv) * 2 + half), dQ part rows
+    // from owner_dq0 on at ((part * n_rows + token) * hq + head).
+    uint32_t* owner;
+    int64_t owner_resp0, owner_dq0;
 };
+
+// Slots of the one-writer counters for a block of n_rows rows whose response keys end at key_end.
+inline int64_t owner_resp0(int64_t n_phys, int hkv) { return n_phys * hkv * 2; }
+inline int64_t owner_dq0(int64_t n_phys, int hkv, int64_t key_end) {
+    return owner_resp0(n_phys, hkv) + (key_end + 63) / 64 * hkv * 2;
+}
+inline int64_t owner_slots(int64_t n_phys, int hkv, int hq, int n_parts, int64_t n_rows, int64_t key_end) {
+    return owner_dq0(n_phys, hkv, key_end) + (int64_t)n_parts * n_rows * hq;
+}
 
 // Row (0..31) inside a 32-row tile of the stored-dS position p (0..31): the positions are in
 // the order the dK/dV pass holds dS in its registers (lane half h = p / 16, key step

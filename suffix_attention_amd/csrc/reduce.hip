@@ -27,8 +27,13 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(int n_parts, int64_t n_r
     const int64_t row = (int64_t)blockIdx.x * rows_per_block + threadIdx.x / vecs;
     const int c = threadIdx.x % vecs;
     if (threadIdx.x >= rows_per_block * vecs || row >= n_rows) return;
+    // the largest part LSE, NaN if any part is NaN (a NaN input then gives a NaN row rather
+    // than one that looks empty)
     float m = -INFINITY;
-    for (int p = 0; p < n_parts; p++) m = fmaxf(m, lse_parts[(int64_t)p * n_rows + row]);
+    for (int p = 0; p < n_parts; p++) {
+        const float lp = lse_parts[(int64_t)p * n_rows + row];
+        m = (lp > m || lp != lp) ? lp : m;
+    }
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     float L = -INFINITY;
     if (m != -INFINITY) {

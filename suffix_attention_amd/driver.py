@@ -18,6 +18,7 @@ from typing import Callable, Iterable
 import torch
 
 from . import api
+from .trace import trace_range
 
 
 @dataclass(frozen=True)
@@ -69,7 +70,10 @@ class GroupReplay:
     first; one kv head by the largest number of key parts) whose workspace fits in ds_budget
     bytes, or in 90% of what the device has free at the first member, else recomputes.
     track_peak: record each member's peak device memory (this resets torch's peak counter at
-    each member's start); peak_bytes is then the largest over the group's members."""
+    each member's start); peak_bytes is then the largest over the group's members.
+    check_owners: a debug run: every backward counts its writers (api.OwnerCounts) and the
+    driver raises if a gradient half-page or a dQ part row had two (one host sync per block).
+    Members, blocks and each block's forward and backward are roctx ranges (trace.py)."""
     prefix: api.Prefix
     store_ds: bool | None = None
     ds_budget: int | None = None
@@ -79,6 +83,8 @@ class GroupReplay:
     touched: list = field(default_factory=list)  # per shard: gradient pages already written
     plan: BwdPlan | None = None
     peak_bytes: int = 0
+    check_owners: bool = False
+    members_done: int = 0
 
     def __post_init__(self):
         if not self.touched:
@@ -120,6 +126,20 @@ class GroupReplay:
 
         keep: "all" returns o, lse, dq, dk_resp, dv_resp; "none" drops them at the end
         (the prompt gradient pages still accumulate)."""
+        with trace_range(f"member {self.members_done}"):
+            r = self._replay_member(q, kr, vr, do, block, keep, on_block)
+        self.members_done += 1
+        return r
+
+    def _backward(self, args, kwargs, n: int, key_end: int, dev, where: str):
+        if not self.check_owners:
+            api.replay_bwd(*args, **kwargs)
+            return
+        with api.OwnerCounts(api.owner_slots(self.prefix, n, key_end), dev) as oc:
+            api.replay_bwd(*args, **kwargs)
+        oc.check(where)
+
+    def _replay_member(self, q, kr, vr, do, block: int, keep: str, on_block: Callable | None) -> MemberResult:
         p = self.prefix
         R = q.shape[0]
         dev = q.device
@@ -136,7 +156,8 @@ class GroupReplay:
         ws_f = torch.empty((api.fwd_workspace_bytes(p, rows0) + 3) // 4, dtype=torch.float32, device=dev)
         ws_b = None
         for i, (a, e) in enumerate(blocks):
-            api.replay_fwd(p, q[a:e], a, kr, vr, workspace=ws_f, o=o[a:e], lse=lse[a:e])
+            with trace_range(f"block [{a}, {e}) forward"):
+                api.replay_fwd(p, q[a:e], a, kr, vr, workspace=ws_f, o=o[a:e], lse=lse[a:e])
             if ws_b is None:
                 # the first backward: gradient pages (once per group), the plan (once per group),
                 # and this member's workspace, sized for the largest of its blocks
@@ -148,8 +169,10 @@ class GroupReplay:
             # the workspace view is sized for this block exactly, so every block runs the plan
             nbytes = self._ws_bytes(self.plan, e - a, e)
             first = [not t for t in self.touched]
-            api.replay_bwd(p, q[a:e], a, kr, vr, o[a:e], lse[a:e], do[a:e], dk_r, dv_r, i == 0, dk_p, dv_p,
-                           shard_first_touch=first, workspace=ws_b[:(max(4, nbytes) + 3) // 4], dq=dq[a:e])
+            with trace_range(f"block [{a}, {e}) backward"):
+                self._backward((p, q[a:e], a, kr, vr, o[a:e], lse[a:e], do[a:e], dk_r, dv_r, i == 0, dk_p, dv_p),
+                               dict(shard_first_touch=first, workspace=ws_b[:(max(4, nbytes) + 3) // 4], dq=dq[a:e]),
+                               e - a, e, dev, f"member {self.members_done} block [{a}, {e})")
             self.touched = [True] * p.n_shards
             if on_block is not None:
                 on_block((a, e))
@@ -167,11 +190,13 @@ class GroupReplay:
 
 def replay_group(prefix: api.Prefix, members: Iterable, block: int, keep: str = "all",
                  on_member: Callable | None = None, store_ds: bool | None = None,
-                 ds_budget: int | None = None, track_peak: bool = False) -> tuple[GroupReplay, list[MemberResult]]:
+                 ds_budget: int | None = None, track_peak: bool = False,
+                 check_owners: bool = False) -> tuple[GroupReplay, list[MemberResult]]:
     """Replay every member serially.  `members` yields dicts with q, kr, vr, do (device
     tensors), or callables returning one, so inputs can be produced one member at a time.
-    store_ds, ds_budget and track_peak as for GroupReplay."""
-    grp = GroupReplay(prefix, store_ds=store_ds, ds_budget=ds_budget, track_peak=track_peak)
+    store_ds, ds_budget, track_peak and check_owners as for GroupReplay."""
+    grp = GroupReplay(prefix, store_ds=store_ds, ds_budget=ds_budget, track_peak=track_peak,
+                      check_owners=check_owners)
     results = []
     for i, m in enumerate(members):
         inp = m() if callable(m) else m

@@ -224,3 +224,59 @@ def test_binding_checks_tables_before_capture():
         api.check_page_table(torch.tensor([0, 2, 2], dtype=torch.int32), 3)
     api.check_page_table(torch.tensor([2, 0, 1], dtype=torch.int32), 3)
 
+
+
+def test_owner_counter_slots_and_registration():
+    """The one-writer counter layout documented in the header: prompt half-pages, response
+    half-pages, dQ part rows; registration rejects a buffer of zero slots; a registered
+    backward checks the size (and the dtype) before anything is launched."""
+    lib = _lib.lib()
+    p = _prefix()  # hq 8, hkv 2, 2 shards, 2 physical pages
+    n_rows, key_end = 16, 80
+    want = 2 * 2 * 2 + ((key_end + 63) // 64) * 2 * 2 + 3 * n_rows * 8
+    assert lib.ls_debug_owner_slots(C.byref(p), n_rows, key_end) == want
+    assert lib.ls_debug_owner_slots(C.byref(_prefix(hkv=3)), n_rows, key_end) == 0 and "hq" in _err()
+    assert lib.ls_debug_owner_slots(C.byref(p), 20, 10) == 0
+    assert lib.ls_debug_set_owner_counts(FAKE, 0) == LS_ERR_INVALID
+    try:
+        assert lib.ls_debug_set_owner_counts(FAKE, 10) == 0
+        rc = lib.ls_replay_bwd(C.byref(p), FAKE, 16, 0, FAKE, FAKE, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
+                               FAKE, FAKE, None, FAKE, 1 << 30, None)
+        assert rc == LS_ERR_INVALID and "slots needed" in _err()
+        rc = lib.ls_replay_bwd(C.byref(_prefix(dtype=LS_DTYPE_F32)), FAKE, 16, 0, FAKE, FAKE, 16, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, FAKE, 1, FAKE, FAKE, None, FAKE, 1 << 30, None)
+        assert rc == LS_ERR_UNSUPPORTED and "bf16" in _err()
+    finally:
+        assert lib.ls_debug_set_owner_counts(None, 0) == 0
+
+
+def test_owner_counts_check_flags_a_second_writer():
+    """OwnerCounts.check passes counters of 0 and 1 and names the first slot written twice."""
+    import torch
+
+    from suffix_attention_amd import api
+    oc = api.OwnerCounts(12, device="cpu")
+    oc.counts[[0, 3, 4]] = 1
+    assert int(oc.check().sum()) == 3
+    oc.counts[7] = 2
+    with pytest.raises(RuntimeError, match="first slot 7, count 2"):
+        oc.check()
+    assert torch.equal(oc.counts[:7], torch.tensor([1, 0, 0, 1, 1, 0, 0], dtype=torch.int32))
+
+
+def test_trace_ranges_nest_and_pop_on_errors():
+    """roctx ranges (a no-op where the roctx library cannot be loaded) nest, and a range is
+    popped when its body raises."""
+    from suffix_attention_amd import trace
+    with trace.trace_range("outer"):
+        with trace.trace_range("inner"):
+            pass
+    with pytest.raises(ValueError):
+        with trace.trace_range("raises"):
+            raise ValueError("x")
+    if trace.available():
+        # the library's own depth counter: pushing returns the depth before the push
+        lib = trace._roctx()
+        depth = lib.roctxRangePushA(b"probe")
+        lib.roctxRangePop()
+        assert depth == 0, depth

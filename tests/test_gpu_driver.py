@@ -105,8 +105,12 @@ def _budget(pre, heads, parts):
 
 
 @pytest.mark.parametrize("form", ["stored dS, 1 kv head", "stored dS, 1 kv head x 2 key parts",
-                                  "stored dS, all", "recompute"])
+                                  "stored dS, all", "recompute",
+                                  "stored dS, 1 kv head x 2 key parts, writers counted"])
 def test_group_replay_matches_oracle(group_case, form):
+    """The writers-counted form runs every backward with the one-writer counters registered
+    (the driver raises if any gradient half-page or dQ part row gets two writers) and must
+    still match the oracle."""
     c = group_case
     pre = c["pre"]
     kw, plan = {
@@ -114,6 +118,8 @@ def test_group_replay_matches_oracle(group_case, form):
         "stored dS, 1 kv head x 2 key parts": (dict(ds_budget=_budget(pre, 1, 2)), driver.BwdPlan(1, 2)),
         "stored dS, all": (dict(store_ds=True), driver.BwdPlan(HKV, 4)),
         "recompute": (dict(store_ds=False), driver.BwdPlan(0, 0)),
+        "stored dS, 1 kv head x 2 key parts, writers counted": (
+            dict(ds_budget=_budget(pre, 1, 2), check_owners=True), driver.BwdPlan(1, 2)),
     }[form]
     log(f"case: group of {G} members P={P} S=3 {BOUNDS} R={R} B={B} ({form})")
     _poison_allocator()
