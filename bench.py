@@ -38,14 +38,18 @@ METRIC = "replay-attention fwd+bwd TFLOP/s and % bf16 MFMA peak at P=2M, G=8"
 
 
 def replay_metric(cfg) -> str:
-    """The headline metric names the 2M-token, G = 8 workload; other configs name their own P, G."""
-    if cfg.name == "c2m":
+    """The headline metric names the 2M-token, G = 8 workload as configured; any other
+    configuration (another config, or c2m with G, B or S overridden) names its own sizes."""
+    if cfg == configs.CONFIGS["c2m"]:
         return METRIC
-    return f"replay-attention fwd+bwd TFLOP/s and % bf16 MFMA peak at P={cfg.P}, G={cfg.G}"
+    return f"replay-attention fwd+bwd TFLOP/s and % bf16 MFMA peak at P={cfg.P}, G={cfg.G}, B={cfg.B}, S={cfg.S}"
 # --workload score: the pre-step scoring pass (forward only, all G members batched)
 SCORE_METRIC = "pre-step scoring (forward-only, G members batched) TFLOP/s and % bf16 MFMA peak at P=2M, G=8"
 # --workload prefill: capture-side prefill (the prompt's causal attention, chunked, pages written)
 PREFILL_METRIC = "capture-side prefill (no-grad causal attention, chunked) TFLOP/s and % bf16 MFMA peak"
+# --workload blocksweep: small response blocks, where the replay turns HBM-bound
+SWEEP_METRIC = ("replay block-size sweep at P=2M: algorithmic HBM GB/s per replayed block (K/V pools read by the "
+                "forward and the backward, fp32 K/V gradient pages read and written)")
 # --workload reuse: consecutive optimizer cycles over one capture
 REUSE_METRIC = "prefix-reuse fwd+bwd TFLOP/s over consecutive G=8 cycles on one capture at P=4,456,448"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix-core peak (published)
@@ -321,6 +325,54 @@ def cpu_baseline_score(cfg, kp, vp, member, n_tok=64):
                       f"keys; counted as 4*Hq*d*pairs"}
 
 
+def bench_blocksweep(ns, cfg, dev, prefix, members):
+    """Small response blocks.  Per block the replay reads the K/V pools twice (forward and
+    backward, 2 x 4 bytes per key, kv head and element) and reads and writes the fp32 K/V
+    gradient pages (16 bytes), 24 bytes in all, while its matrix work shrinks with the block:
+    below about 90 rows a block is bound by HBM.  Member 0 is replayed in full at each block
+    size of --sweep-B (one untimed replay first, then --steps timed ones, each a fresh group);
+    the rate is those algorithmic bytes over the measured time (the first block of a group
+    only writes the gradient pages, so the figure slightly overstates the bytes)."""
+    sizes = [int(x) for x in ns.sweep_B.split(",")]
+    m = members[0]
+    alg_block = 24 * cfg.P * cfg.hkv * cfg.d
+    rows = []
+    for b in sizes:
+        c = cfg.with_(B=b, G=1)
+        run_steps(prefix, [m], c, 1)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        api.profile_begin()
+        ev0.record()
+        run_steps(prefix, [m], c, ns.steps)
+        ev1.record()
+        torch.cuda.synchronize()
+        kstats = api.profile_end()
+        ms = ev0.elapsed_time(ev1)
+        n_blocks = ns.steps * c.n_blocks
+        gbs = alg_block * n_blocks / (ms / 1e3) / 1e9
+        tflops = configs.member_flops(c) * ns.steps / (ms / 1e3) / 1e12
+        row = {"B": b, "blocks": c.n_blocks, "ms_per_block": round(ms / n_blocks, 3),
+               "alg_gb_per_block": round(alg_block / 1e9, 2), "alg_gbs": round(gbs, 1),
+               "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2), "counted_tflops": round(tflops, 1),
+               "kernels_ms_per_block": {k: round(v[1] / n_blocks, 3) for k, v in sorted(kstats.items())}}
+        log(f"[bench] B={b}: {row}")
+        rows.append(row)
+    first = rows[0]
+    out = {"metric": SWEEP_METRIC, "value": first["alg_gbs"], "unit": "GB/s", "n_gpus": 1, "steps": ns.steps,
+           "warmup": 1, "ms_per_step": first["ms_per_block"] * first["blocks"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"{cfg.name}: member 0 replayed in blocks of {ns.sweep_B} rows, P={cfg.P} prompt "
+                                  f"tokens in 64-token pages, S={cfg.S} shards, R={cfg.R}, Hq={cfg.hq}, Hkv={cfg.hkv}, "
+                                  f"d={cfg.d}, N(0,1) inputs; value is the smallest block size",
+                      "P": cfg.P, "R": cfg.R, "S": cfg.S, "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d},
+           "roofline": {"bound": "hbm", "kernel": "whole block", "achieved": first["alg_gbs"], "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(first["alg_gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+                        "bytes_per_unit": "24 B per (prompt key, kv head, element) per block"},
+           "sweep": rows}
+    print(json.dumps(out), flush=True)
+
+
 def bench_score(ns, cfg, dev, prefix, kp, vp, members):
     """Pre-step scoring: every member's whole response, forward only, in one batched call per
     step (ls_score_fwd)."""
@@ -428,10 +480,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="c2m", choices=sorted(configs.CONFIGS))
     ap.add_argument("--G", type=int, default=None, help="override the group size")
-    ap.add_argument("--workload", default="replay", choices=["replay", "score", "prefill", "reuse"],
+    ap.add_argument("--B", type=int, default=None, help="override the response block size")
+    ap.add_argument("--S", type=int, default=None, help="override the number of prompt shards")
+    ap.add_argument("--sweep-B", default="16,64,256", help="block sizes of --workload blocksweep")
+    ap.add_argument("--workload", default="replay", choices=["replay", "score", "prefill", "reuse", "blocksweep"],
                     help="replay: the fwd+bwd step (the headline); score: batched forward-only scoring; "
                          "prefill: chunked capture-side prefill; reuse: consecutive G=8 cycles on one capture "
-                         "at P=4,456,448 (--steps cycles, per-cycle times and peaks)")
+                         "at P=4,456,448 (--steps cycles, per-cycle times and peaks); blocksweep: member 0 at "
+                         "the block sizes of --sweep-B, algorithmic HBM GB/s")
     ap.add_argument("--prefill-tokens", type=int, default=524288)
     ap.add_argument("--prefill-chunk", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -468,6 +524,10 @@ def main():
     cfg = configs.CONFIGS[ns.config]
     if ns.G:
         cfg = cfg.with_(G=ns.G)
+    if ns.B:
+        cfg = cfg.with_(B=ns.B)
+    if ns.S:
+        cfg = cfg.with_(S=ns.S)
     global STORE_DS, DS_BUDGET
     STORE_DS = {"auto": None, "on": True, "off": False}[ns.store_ds]
     DS_BUDGET = None if ns.ds_budget_gb is None else int(ns.ds_budget_gb * 1e9)
@@ -484,6 +544,9 @@ def main():
     log(f"[bench] prefix captured ({cfg.n_pages} pages), {cfg.G} members resident")
     if ns.workload == "score":
         bench_score(ns, cfg, dev, prefix, kp, vp, members)
+        return
+    if ns.workload == "blocksweep":
+        bench_blocksweep(ns, cfg, dev, prefix, members)
         return
 
     ceilings = None

@@ -145,12 +145,16 @@ int ls_gather_pages(const void* pages, int dtype, const int32_t* page_table,
  * Forward workspace layout (float32, from offset 0; n_parts = n_shards + 1):
  *   o_parts   [n_parts, n_rows, hq, d]   part p < n_shards: shard p; last: response keys
  *   lse_parts [n_parts, n_rows, hq]      -inf where a part has no key (O part = 0 there)
- * so that callers may inspect each owner's local result.
+ * so that callers may inspect each owner's local result; for a bf16 block whose shards are
+ * split into k page ranges (see ls_replay_fwd), the same two arrays for the n_shards * k + 1
+ * ranges follow.
  * Backward workspace layout (from offset 0):
  *   delta     float32 [n_rows, hq], padded to a multiple of 64 elements: rowsum(dO * O)
  *   dq_parts  float32 [n_parts, n_rows, hq, d]
  *   then, for bf16, per kv head and query row of its group (padded to a multiple of 64
- *   rows): (LSE * log2 e, delta) float32 pairs, then the Q rows and the dO rows (bf16).
+ *   rows): (LSE * log2 e, delta) float32 pairs, then the Q rows and the dO rows (bf16);
+ *   then, for a bf16 block whose stored-dS dQ pass splits its shards into k page ranges, at a
+ *   256-byte boundary, float32 dQ partials [n_shards * k + 1, n_rows, hq, d].
  * A block may have at most about 2^32 / (16 * hq * d) rows (174,000 at hq = 24, d = 256).
  */
 size_t ls_fwd_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows);
@@ -223,6 +227,12 @@ size_t ls_bwd_ds_chunk_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows, i
  *   workspace       device, ws_bytes >= ls_fwd_workspace_bytes(pre, n_rows).
  * Inputs are not checked for NaN: a NaN in a row's query (or in a key or value it sees) makes
  * that row's O and LSE NaN, and leaves every other row exactly as without it.
+ * A small block has too few query tiles to fill the GPU with one workgroup per (query tile,
+ * part, kv head); its shards are then split into k contiguous page ranges (up to 256 ranges,
+ * at least 64 pages each on average), and the ranges' results merged into their shard's part
+ * before the final merge, so the parts in the workspace keep the layout above and the
+ * workspace size (ls_fwd_workspace_bytes) includes the ranges' results.  The stored-dS dQ pass
+ * does the same (ls_bwd_workspace_bytes).
  * Errors: LS_ERR_INVALID, LS_ERR_UNSUPPORTED, LS_ERR_WORKSPACE, LS_ERR_HIP.
  */
 int ls_replay_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start,
@@ -349,9 +359,14 @@ int ls_lse_merge_bf16num(int n_parts, int64_t n_rows, int d, const float* o_part
  *                                                        32 half .. +32 of physical page phys);
  *   R + (page * hkv + kv) * 2 + half                     response gradient half-page, with
  *                                                        R = n_phys_pages * hkv * 2;
- *   Q + (part * n_rows + token) * hq + head              dQ part row (part n_shards is the
- *                                                        response), with
- *                                                        Q = R + ceil(key_end / 64) * hkv * 2.
+ *   Q + (part * n_rows + token) * hq + head              dQ partial row, with
+ *                                                        Q = R + ceil(key_end / 64) * hkv * 2:
+ *                                                        part < n_shards a shard, n_shards the
+ *                                                        response; when the stored-dS dQ pass of
+ *                                                        a small block splits every shard into k
+ *                                                        page ranges (see ls_replay_fwd), part
+ *                                                        < n_shards * k a range, n_shards * k
+ *                                                        the response.
  * After a correct call every slot holds 1 if the call writes it and 0 otherwise; a slot above
  * 1 is a second writer.  The caller reads the counters back (the library never synchronises).
  * Counting uses device atomics and costs time; it is for tests and debugging.

@@ -118,13 +118,45 @@ ls::AttnArgs make_args(const ls_prefix_t* p, const void* q, int64_t n_rows, int6
     return a;
 }
 
-size_t fwd_ws(const ls_prefix_t* p, int64_t n_rows) {
-    return sizeof(float) * (size_t)(p->n_shards + 1) * (size_t)n_rows * (size_t)p->hq * (size_t)(p->d + 1);
+// Sub-range splits of a small block's shards (bf16 matrix-core passes only; launch.hpp).
+int fwd_k(const ls_prefix_t* p, int64_t n_rows) {
+    if (p->dtype != LS_DTYPE_BF16) return 1;
+    return ls::fwd_split(n_rows, p->hq / p->hkv, p->n_shards, p->hkv, logical_pages(p->prefix_len, p->page_size));
+}
+int dqs_k(const ls_prefix_t* p, int64_t n_rows) {
+    if (p->dtype != LS_DTYPE_BF16) return 1;
+    return ls::dqs_split(n_rows, p->hq / p->hkv, p->n_shards, p->hkv, logical_pages(p->prefix_len, p->page_size));
 }
 
-size_t bwd_ws(const ls_prefix_t* p, int64_t n_rows) {
+// Forward workspace: the parts [n_parts, rows, d] float32 and their LSE [n_parts, rows], then,
+// when the block's shards are split, the same for the n_shards * k + 1 sub-ranges.
+size_t fwd_parts_bytes(const ls_prefix_t* p, int64_t n_rows, int64_t n_parts) {
+    return sizeof(float) * (size_t)n_parts * (size_t)n_rows * (size_t)p->hq * (size_t)(p->d + 1);
+}
+size_t fwd_ws(const ls_prefix_t* p, int64_t n_rows) {
+    const int k = fwd_k(p, n_rows);
+    size_t b = fwd_parts_bytes(p, n_rows, p->n_shards + 1);
+    if (k > 1) b += fwd_parts_bytes(p, n_rows, (int64_t)p->n_shards * k + 1);
+    return b;
+}
+
+// Backward workspace: delta, the dQ parts, the matrix-core passes' row copies, then, when the
+// dQ pass of a small block splits its shards, the sub-ranges' dQ partials at a 256-byte boundary.
+size_t bwd_base(const ls_prefix_t* p, int64_t n_rows) {
     return sizeof(float) * ((size_t)ls::bwd_delta_elems(n_rows, p->hq) + (size_t)(p->n_shards + 1) * n_rows * p->hq * p->d) +
            ls::mfma_bwd_extra_bytes(n_rows, p->hq / p->hkv, p->hkv, p->d);
+}
+size_t dq_sub_offset(const ls_prefix_t* p, int64_t n_rows) { return (bwd_base(p, n_rows) + 255) / 256 * 256; }
+size_t bwd_ws(const ls_prefix_t* p, int64_t n_rows) {
+    const int k = dqs_k(p, n_rows);
+    if (k <= 1) return bwd_base(p, n_rows);
+    return dq_sub_offset(p, n_rows) +
+           sizeof(float) * ((size_t)p->n_shards * k + 1) * (size_t)n_rows * (size_t)p->hq * (size_t)p->d;
+}
+// dQ partials the stored-dS backward forms (shards and response, or their sub-ranges)
+int dq_parts_formed(const ls_prefix_t* p, int64_t n_rows) {
+    const int k = dqs_k(p, n_rows);
+    return k > 1 ? p->n_shards * k + 1 : p->n_shards + 1;
 }
 
 // Bytes of the stored dS (bf16, one per group row and key slot) of a block whose response keys
@@ -324,8 +356,30 @@ static int run_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_
     a.o_parts = (float*)workspace;
     a.lse_parts = a.o_parts + (size_t)a.n_parts * rows * pre->d;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = pre->dtype == LS_DTYPE_BF16 ? ls::launch_fwd_mfma(a, s) : ls::launch_fwd_generic(a, s);
-    if (e != hipSuccess) return hip_fail(e, "forward kernel");
+    hipError_t e;
+    const int k = fwd_k(pre, n_rows);
+    if (k > 1) {
+        // a small block: the forward over k sub-ranges of every shard, each shard's ranges then
+        // merged into its part (the response part copied by a one-part merge, which is exact)
+        ls::AttnArgs b = a;
+        b.n_shards = pre->n_shards * k;
+        b.n_parts = b.n_shards + 1;
+        ls::split_bounds(a.shard_lo, pre->n_shards, k, b.shard_lo);
+        b.o_parts = a.lse_parts + (size_t)a.n_parts * rows;
+        b.lse_parts = b.o_parts + (size_t)b.n_parts * rows * pre->d;
+        e = ls::launch_fwd_mfma(b, s);
+        if (e != hipSuccess) return hip_fail(e, "forward kernel");
+        for (int sh = 0; sh <= pre->n_shards && e == hipSuccess; sh++) {
+            const int n = sh < pre->n_shards ? k : 1;
+            e = ls::launch_lse_merge(n, rows, pre->d, b.o_parts + (size_t)sh * k * rows * pre->d,
+                                     b.lse_parts + (size_t)sh * k * rows, a.o_parts + (size_t)sh * rows * pre->d,
+                                     LS_DTYPE_F32, a.lse_parts + (size_t)sh * rows, s);
+        }
+        if (e != hipSuccess) return hip_fail(e, "LSE merge kernel");
+    } else {
+        e = pre->dtype == LS_DTYPE_BF16 ? ls::launch_fwd_mfma(a, s) : ls::launch_fwd_generic(a, s);
+        if (e != hipSuccess) return hip_fail(e, "forward kernel");
+    }
     e = ls::launch_lse_merge(a.n_parts, rows, pre->d, a.o_parts, a.lse_parts, o, pre->dtype, lse, s);
     return e == hipSuccess ? LS_OK : hip_fail(e, "LSE merge kernel");
 }
@@ -402,7 +456,8 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
     if (g_owner) {
         if (pre->dtype != LS_DTYPE_BF16)
             return fail(LS_ERR_UNSUPPORTED, "one-writer counters cover the bf16 matrix-core kernels only");
-        owner_slots = ls::owner_slots(pre->n_phys_pages, pre->hkv, pre->hq, pre->n_shards + 1, n_rows, a.key_end);
+        owner_slots = ls::owner_slots(pre->n_phys_pages, pre->hkv, pre->hq, dq_parts_formed(pre, n_rows), n_rows,
+                                      a.key_end);
         if (g_owner_slots < (size_t)owner_slots)
             return fail(LS_ERR_INVALID, "one-writer counters: %lld slots needed, %zu registered", (long long)owner_slots,
                         g_owner_slots);
@@ -457,6 +512,11 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
             a.ds_kslots = ls::ds_chunk_slots(pre->shard_page_bounds, pre->n_shards, a.key_end, parts);
             a.ds_heads = heads;
             a.ds_parts = parts;
+            const int k = dqs_k(pre, n_rows);
+            if (k > 1 && parts == n_all) {  // a small block: the dQ pass over shard sub-ranges
+                a.dq_sub = (float*)((char*)workspace + dq_sub_offset(pre, n_rows));
+                a.dq_sub_k = k;
+            }
         }
         e = ls::launch_bwd_mfma(a, s);  // its prep kernel also writes delta
     } else {
@@ -464,7 +524,10 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
         if (e == hipSuccess) e = ls::launch_bwd_generic(a, s);
     }
     if (e != hipSuccess) return hip_fail(e, "backward kernels");
-    e = ls::launch_sum_parts(a.n_parts, rows * pre->d, a.dq_parts, dq, s);
+    if (a.dq_sub_k > 1)
+        e = ls::launch_sum_parts(pre->n_shards * a.dq_sub_k + 1, rows * pre->d, a.dq_sub, dq, s);
+    else
+        e = ls::launch_sum_parts(a.n_parts, rows * pre->d, a.dq_parts, dq, s);
     if (e != hipSuccess) return hip_fail(e, "dQ part sum kernel");
     if (resp_first_touch && n_resp_keys > a.key_end) {
         const int64_t off = a.key_end * pre->hkv * pre->d;
@@ -483,7 +546,8 @@ size_t ls_debug_owner_slots(const ls_prefix_t* pre, int64_t n_rows, int64_t key_
         fail(LS_ERR_INVALID, "n_rows=%lld, key_end=%lld", (long long)n_rows, (long long)key_end);
         return 0;
     }
-    return (size_t)ls::owner_slots(pre->n_phys_pages, pre->hkv, pre->hq, pre->n_shards + 1, n_rows, key_end);
+    return (size_t)ls::owner_slots(pre->n_phys_pages, pre->hkv, pre->hq, dq_parts_formed(pre, n_rows), n_rows,
+                                   key_end);
 }
 
 int ls_debug_set_owner_counts(uint32_t* counts, size_t n_slots) {

@@ -524,7 +524,17 @@ hipError_t launch_bwd_d(const AttnArgs& a, hipStream_t s) {
                 }
                 hipError_t e = hipGetLastError();
                 const int s1 = p1 < a.n_shards ? p1 : a.n_shards;
-                if (e == hipSuccess) e = launch_dqs_mfma(c, nh, p0 < s1 ? p0 : 0, p0 < s1 ? s1 - p0 : 0, pc.resp, s);
+                if (e == hipSuccess && a.dq_sub_k > 1 && p0 == 0 && p1 == n_all) {
+                    // a small block: the dQ pass over k sub-ranges of every shard, into dq_sub
+                    AttnArgs r = c;
+                    r.n_shards = a.n_shards * a.dq_sub_k;
+                    r.n_parts = r.n_shards + 1;
+                    split_bounds(a.shard_lo, a.n_shards, a.dq_sub_k, r.shard_lo);
+                    r.dq_parts = a.dq_sub;
+                    e = launch_dqs_mfma(r, nh, 0, r.n_shards, true, s);
+                } else if (e == hipSuccess) {
+                    e = launch_dqs_mfma(c, nh, p0 < s1 ? p0 : 0, p0 < s1 ? s1 - p0 : 0, pc.resp, s);
+                }
                 if (e != hipSuccess) return e;
             }
         }

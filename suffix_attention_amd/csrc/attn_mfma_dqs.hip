@@ -109,7 +109,7 @@ void dqs_mfma_kernel(AttnArgs a, int n_rblocks, int n_kvh, int part0, int n_sp, 
     const int h = lane >> 5;
     const int n = lane & 31;
     const int64_t rows_total = a.n_rows * a.g;
-    const int64_t r0 = (int64_t)rblock * 256;
+    const int64_t r0 = (int64_t)rblock * kDqsTileRows;
     const int64_t rt0 = r0 / 32 + 2 * w;  // the wave's first row tile
 
     // pages of the part: a prompt shard's pages, or the response pages up to the last key the
@@ -222,7 +222,7 @@ void dqs_mfma_kernel(AttnArgs a, int n_rblocks, int n_kvh, int part0, int n_sp, 
 template <int D>
 hipError_t launch_dqs_d(const AttnArgs& a, int n_kvh, int part0, int n_sp, int n_rp, hipStream_t s) {
     const int64_t rows_total = a.n_rows * a.g;
-    const int n_rblocks = (int)((rows_total + 255) / 256);
+    const int n_rblocks = (int)((rows_total + kDqsTileRows - 1) / kDqsTileRows);
     if (n_rblocks == 0 || n_kvh == 0 || n_sp + n_rp == 0) return hipSuccess;
     dqs_mfma_kernel<D><<<deal_grid(n_rblocks, n_sp, n_sp + n_rp, n_kvh), 256, 0, s>>>(a, n_rblocks, n_kvh, part0,
                                                                                       n_sp, n_rp);

@@ -45,6 +45,7 @@ constexpr float kLazyLog2 = 8.f;
 constexpr int kNW = 8;           // waves per workgroup
 constexpr int kGroups = 4;       // 32-row groups per workgroup
 constexpr int kBM = 32 * kGroups;
+static_assert(kBM == kFwdTileRows, "the host's sub-part split assumes this tile");
 
 template <int D>
 struct FwdLds {

@@ -6,7 +6,10 @@
 
 namespace ls {
 
-constexpr int kMaxShards = 64;
+constexpr int kMaxShards = 64;     // prompt shards a caller may use
+constexpr int kMaxSubParts = 256;  // key ranges a launch may split the prompt into (below)
+constexpr int kFwdTileRows = 128;  // group rows per forward workgroup
+constexpr int kDqsTileRows = 256;  // group rows per workgroup of the stored-dS dQ pass
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kPage = 64;  // tokens per KV page
@@ -33,7 +36,7 @@ struct AttnArgs {
     // parts: shard s = logical pages [shard_lo[s], shard_lo[s+1]); part n_shards = response
     int n_shards;
     int n_parts;
-    int64_t shard_lo[kMaxShards + 1];
+    int64_t shard_lo[kMaxSubParts + 1];
     // Pre-step scoring runs the blocks of n_members members in one forward (1 for a replay):
     // member m's rows follow member m-1's in q; its response keys start resp_member_elems
     // elements after member m-1's.
@@ -87,15 +90,50 @@ struct AttnArgs {
     // from owner_dq0 on at ((part * n_rows + token) * hq + head).
     uint32_t* owner;
     int64_t owner_resp0, owner_dq0;
+    // The stored-dS dQ pass over shard sub-ranges (dq_sub_k > 1, a chunk over all key parts
+    // only): its per-range dQ partials [n_shards * dq_sub_k + 1, n_rows, hq, d], summed instead
+    // of dq_parts.
+    float* dq_sub;
+    int dq_sub_k;
 };
+
+// Sub-parts.  The forward and the stored-dS dQ pass run one workgroup per (query tile, part,
+// kv head); a small block has few query tiles, so with the shards as parts most compute units
+// would idle (a 16-row block at 8 shards and 4 kv heads: 36 workgroups for 256 compute units).
+// Such a pass splits each shard into k contiguous page ranges, enough for about three
+// workgroups per compute unit but at least 64 pages a range on average, and merges (forward)
+// or sums (dQ) what the ranges give.
+inline int sub_split(int64_t n_qtiles, int n_shards, int hkv, int64_t n_logical_pages) {
+    constexpr int64_t kTarget = 3 * 256;
+    const int64_t base = n_qtiles * n_shards * hkv;
+    if (base <= 0 || base >= kTarget) return 1;
+    int64_t k = (kTarget + base - 1) / base;
+    const int64_t by_pages = n_logical_pages / ((int64_t)n_shards * 64);
+    if (k > by_pages) k = by_pages;
+    if (k > kMaxSubParts / n_shards) k = kMaxSubParts / n_shards;
+    return k < 1 ? 1 : (int)k;
+}
+inline int fwd_split(int64_t n_rows, int g, int n_shards, int hkv, int64_t n_logical_pages) {
+    return sub_split((n_rows * g + kFwdTileRows - 1) / kFwdTileRows, n_shards, hkv, n_logical_pages);
+}
+inline int dqs_split(int64_t n_rows, int g, int n_shards, int hkv, int64_t n_logical_pages) {
+    return sub_split((n_rows * g + kDqsTileRows - 1) / kDqsTileRows, n_shards, hkv, n_logical_pages);
+}
+// Page bounds of the k ranges of every shard: out[s * k + j] = lo[s] + (lo[s+1] - lo[s]) j / k,
+// out[n_shards * k] = lo[n_shards] (ranges of a short shard may be empty).
+inline void split_bounds(const int64_t* lo, int n_shards, int k, int64_t* out) {
+    for (int s = 0; s < n_shards; s++)
+        for (int j = 0; j < k; j++) out[s * k + j] = lo[s] + (lo[s + 1] - lo[s]) * j / k;
+    out[n_shards * k] = lo[n_shards];
+}
 
 // Slots of the one-writer counters for a block of n_rows rows whose response keys end at key_end.
 inline int64_t owner_resp0(int64_t n_phys, int hkv) { return n_phys * hkv * 2; }
 inline int64_t owner_dq0(int64_t n_phys, int hkv, int64_t key_end) {
     return owner_resp0(n_phys, hkv) + (key_end + 63) / 64 * hkv * 2;
 }
-inline int64_t owner_slots(int64_t n_phys, int hkv, int hq, int n_parts, int64_t n_rows, int64_t key_end) {
-    return owner_dq0(n_phys, hkv, key_end) + (int64_t)n_parts * n_rows * hq;
+inline int64_t owner_slots(int64_t n_phys, int hkv, int hq, int n_dq_parts, int64_t n_rows, int64_t key_end) {
+    return owner_dq0(n_phys, hkv, key_end) + (int64_t)n_dq_parts * n_rows * hq;
 }
 
 // Row (0..31) inside a 32-row tile of the stored-dS position p (0..31): the positions are in

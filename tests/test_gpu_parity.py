@@ -325,3 +325,14 @@ def test_stored_ds_in_chunks_is_bitwise_the_same(bounds):
         got = run(heads, parts)
         for name, a, b in zip(("dq", "dk_r", "dv_r", "dk_p", "dv_p"), full, got):
             assert torch.equal(a, b), (heads, parts, name)
+
+
+@pytest.mark.parametrize("store_ds", [False, True])
+def test_small_block_over_a_long_prompt_splits_its_shards(store_ds):
+    """A 16-row block over a 65,536-token prompt in two uneven shards (3 and 1,021 pages): the
+    forward's and the stored-dS dQ pass's grids would hold only a few workgroups, so both split
+    every shard into 8 page ranges (the 3-page shard into mostly empty ones) and combine them.
+    Every output and each shard's partial (O, LSE) match the oracle."""
+    c = Case(65536, 64, 6, 2, 256, seed=31, bounds=[0, 3, 1024])
+    log(f"case: 16-row block over P=65536 in shards {c.bounds}, {'stored dS' if store_ds else 'recompute'}")
+    check_against_oracle(c, 24, 16, store_ds=store_ds)

@@ -83,6 +83,45 @@ def test_backward_has_one_writer_per_gradient_element(plan):
 
 
 @pytest.mark.parametrize("store_ds", [False, True])
+def test_one_writer_per_element_with_split_shards(store_ds):
+    """A 16-row block over 65,536 prompt tokens in 2 shards: the stored-dS dQ pass splits each
+    shard into page ranges, each forming its own dQ partial, so the counters hold one dQ region
+    per range (the header's "dQ partial" slots, sized by ls_debug_owner_slots); each must be
+    written once, and the recomputing backward writes only the first n_shards + 1 of them."""
+    Pl, hq, hkv, d, bounds = 65536, 6, 2, 256, [0, 300, 1024]
+    c = Case(Pl, 64, hq, hkv, d, seed=33, bounds=list(bounds))
+    pre = c.prefix()
+    dev = "cuda"
+    q_start, n = 24, 16
+    key_end = q_start + n
+    log(f"case: one-writer counters, 16-row block over P={Pl} ({'stored dS' if store_ds else 'recompute'})")
+    q = c.q[q_start:key_end].to(dev).contiguous()
+    do = c.do[q_start:key_end].to(dev).contiguous()
+    kr, vr = c.kr.to(dev), c.vr.to(dev)
+    o, lse, _ = api.replay_fwd(pre, q, q_start, kr, vr)
+    g = [torch.zeros(kr.shape, dtype=torch.float32, device=dev) for _ in range(2)]
+    g += [torch.zeros(pre.k_pages.shape, dtype=torch.float32, device=dev) for _ in range(2)]
+    slots = api.owner_slots(pre, n, key_end)
+    r0 = c.n_phys * hkv * 2
+    q0 = r0 + (key_end + 63) // 64 * hkv * 2
+    n_dq = (slots - q0) // (n * hq)
+    assert n_dq > len(bounds), "expected the dQ pass to split the shards"
+    with api.OwnerCounts(slots, dev) as oc:
+        api.replay_bwd(pre, q, q_start, kr, vr, o, lse, do, g[0], g[1], True, g[2], g[3],
+                       shard_first_touch=[True] * pre.n_shards, store_ds=store_ds)
+        torch.cuda.synchronize()
+    got = oc.check()
+    exp = torch.zeros(slots, dtype=torch.int32)
+    for phys in c.table.tolist():
+        exp[phys * hkv * 2:(phys + 1) * hkv * 2] = 1
+    exp[r0:q0] = 1
+    exp[q0:q0 + (n_dq if store_ds else len(bounds)) * n * hq] = 1
+    diff = torch.nonzero(got != exp).flatten()
+    assert diff.numel() == 0, f"slot {int(diff[0])}: counted {int(got[diff[0]])}, expected {int(exp[diff[0]])}"
+    log(f"    {n_dq} dQ partial regions, {int(got.sum())} slots written once")
+
+
+@pytest.mark.parametrize("store_ds", [False, True])
 def test_nan_in_one_query_row_stays_in_its_row(store_ds):
     c = Case(700, 160, 6, 2, 128, seed=5, S=3)  # g = 3: heads 0-2 on kv head 0
     pre = c.prefix()
