@@ -391,7 +391,8 @@ size_t ls_score_workspace_bytes(const ls_prefix_t* pre, int64_t n_members, int64
         fail(LS_ERR_INVALID, "n_members=%lld, n_rows=%lld must be >= 0", (long long)n_members, (long long)n_rows);
         return 0;
     }
-    return fwd_ws(pre, n_members * n_rows);
+    // the parts only: scoring batches every member's rows into one launch and never splits shards
+    return fwd_parts_bytes(pre, n_members * n_rows, pre->n_shards + 1);
 }
 
 int ls_score_fwd(const ls_prefix_t* pre, int64_t n_members, const void* q, int64_t n_rows, const void* k_resp,
@@ -405,7 +406,7 @@ int ls_score_fwd(const ls_prefix_t* pre, int64_t n_members, const void* q, int64
     if (rc != LS_OK) return rc;
     if (n_members * n_rows == 0) return LS_OK;
     if (!o || !lse) return fail(LS_ERR_INVALID, "o/lse is NULL");
-    const size_t need = fwd_ws(pre, n_members * n_rows);
+    const size_t need = fwd_parts_bytes(pre, n_members * n_rows, pre->n_shards + 1);
     if (!workspace || ws_bytes < need)
         return fail(LS_ERR_WORKSPACE, "scoring workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
     ls::AttnArgs a = make_args(pre, q, n_rows, 0, k_resp, v_resp);
