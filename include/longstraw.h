@@ -274,7 +274,10 @@ int ls_replay_fwd_noalloc(const ls_prefix_t* pre, const void* q, int64_t n_rows,
  *   o               device [n_members, n_rows, hq, d] of pre->dtype (written).
  *   lse             device float32 [n_members, n_rows, hq] (written).
  *   workspace       device, ws_bytes >= ls_score_workspace_bytes(pre, n_members, n_rows); its
- *                   layout is the forward one for n_members * n_rows rows, member-major.
+ *                   layout is the forward one for n_members * n_rows rows, member-major, with
+ *                   the shards split into page ranges as a replay block of n_rows rows would
+ *                   be (see ls_replay_fwd), so that each member's O and LSE equal those of its
+ *                   own ls_replay_fwd bit for bit.
  * The members' rows together obey the block-size limit of ls_fwd_workspace_bytes.
  * Errors as for ls_replay_fwd.
  */

@@ -133,11 +133,31 @@ int dqs_k(const ls_prefix_t* p, int64_t n_rows) {
 size_t fwd_parts_bytes(const ls_prefix_t* p, int64_t n_rows, int64_t n_parts) {
     return sizeof(float) * (size_t)n_parts * (size_t)n_rows * (size_t)p->hq * (size_t)(p->d + 1);
 }
-size_t fwd_ws(const ls_prefix_t* p, int64_t n_rows) {
-    const int k = fwd_k(p, n_rows);
-    size_t b = fwd_parts_bytes(p, n_rows, p->n_shards + 1);
-    if (k > 1) b += fwd_parts_bytes(p, n_rows, (int64_t)p->n_shards * k + 1);
+size_t fwd_ws_k(const ls_prefix_t* p, int64_t rows, int k) {
+    size_t b = fwd_parts_bytes(p, rows, p->n_shards + 1);
+    if (k > 1) b += fwd_parts_bytes(p, rows, (int64_t)p->n_shards * k + 1);
     return b;
+}
+size_t fwd_ws(const ls_prefix_t* p, int64_t n_rows) { return fwd_ws_k(p, n_rows, fwd_k(p, n_rows)); }
+
+// The matrix-core forward over the parts of `a` (its o_parts / lse_parts hold part_rows_hq rows
+// of (row, head) per part).  With k > 1 it runs over k page ranges of every shard, writing their
+// results after the parts, and then merges each shard's ranges into the shard's part (the
+// response part is copied by a one-part merge, which is exact).
+hipError_t fwd_mfma_parts(const ls::AttnArgs& a, int n_shards, int k, int64_t part_rows_hq, int d, hipStream_t s) {
+    if (k <= 1) return ls::launch_fwd_mfma(a, s);
+    ls::AttnArgs b = a;
+    b.n_shards = n_shards * k;
+    b.n_parts = b.n_shards + 1;
+    ls::split_bounds(a.shard_lo, n_shards, k, b.shard_lo);
+    b.o_parts = a.lse_parts + (size_t)a.n_parts * part_rows_hq;
+    b.lse_parts = b.o_parts + (size_t)b.n_parts * part_rows_hq * d;
+    hipError_t e = ls::launch_fwd_mfma(b, s);
+    for (int sh = 0; sh <= n_shards && e == hipSuccess; sh++)
+        e = ls::launch_lse_merge(sh < n_shards ? k : 1, part_rows_hq, d, b.o_parts + (size_t)sh * k * part_rows_hq * d,
+                                 b.lse_parts + (size_t)sh * k * part_rows_hq, a.o_parts + (size_t)sh * part_rows_hq * d,
+                                 LS_DTYPE_F32, a.lse_parts + (size_t)sh * part_rows_hq, s);
+    return e;
 }
 
 // Backward workspace: delta, the dQ parts, the matrix-core passes' row copies, then, when the
@@ -356,30 +376,9 @@ static int run_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_
     a.o_parts = (float*)workspace;
     a.lse_parts = a.o_parts + (size_t)a.n_parts * rows * pre->d;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e;
-    const int k = fwd_k(pre, n_rows);
-    if (k > 1) {
-        // a small block: the forward over k sub-ranges of every shard, each shard's ranges then
-        // merged into its part (the response part copied by a one-part merge, which is exact)
-        ls::AttnArgs b = a;
-        b.n_shards = pre->n_shards * k;
-        b.n_parts = b.n_shards + 1;
-        ls::split_bounds(a.shard_lo, pre->n_shards, k, b.shard_lo);
-        b.o_parts = a.lse_parts + (size_t)a.n_parts * rows;
-        b.lse_parts = b.o_parts + (size_t)b.n_parts * rows * pre->d;
-        e = ls::launch_fwd_mfma(b, s);
-        if (e != hipSuccess) return hip_fail(e, "forward kernel");
-        for (int sh = 0; sh <= pre->n_shards && e == hipSuccess; sh++) {
-            const int n = sh < pre->n_shards ? k : 1;
-            e = ls::launch_lse_merge(n, rows, pre->d, b.o_parts + (size_t)sh * k * rows * pre->d,
-                                     b.lse_parts + (size_t)sh * k * rows, a.o_parts + (size_t)sh * rows * pre->d,
-                                     LS_DTYPE_F32, a.lse_parts + (size_t)sh * rows, s);
-        }
-        if (e != hipSuccess) return hip_fail(e, "LSE merge kernel");
-    } else {
-        e = pre->dtype == LS_DTYPE_BF16 ? ls::launch_fwd_mfma(a, s) : ls::launch_fwd_generic(a, s);
-        if (e != hipSuccess) return hip_fail(e, "forward kernel");
-    }
+    hipError_t e = pre->dtype == LS_DTYPE_BF16 ? fwd_mfma_parts(a, pre->n_shards, fwd_k(pre, n_rows), rows, pre->d, s)
+                                               : ls::launch_fwd_generic(a, s);
+    if (e != hipSuccess) return hip_fail(e, "forward kernel");
     e = ls::launch_lse_merge(a.n_parts, rows, pre->d, a.o_parts, a.lse_parts, o, pre->dtype, lse, s);
     return e == hipSuccess ? LS_OK : hip_fail(e, "LSE merge kernel");
 }
@@ -391,8 +390,8 @@ size_t ls_score_workspace_bytes(const ls_prefix_t* pre, int64_t n_members, int64
         fail(LS_ERR_INVALID, "n_members=%lld, n_rows=%lld must be >= 0", (long long)n_members, (long long)n_rows);
         return 0;
     }
-    // the parts only: scoring batches every member's rows into one launch and never splits shards
-    return fwd_parts_bytes(pre, n_members * n_rows, pre->n_shards + 1);
+    // the page-range split follows each member's block size, as ls_replay_fwd would choose it
+    return fwd_ws_k(pre, n_members * n_rows, fwd_k(pre, n_rows));
 }
 
 int ls_score_fwd(const ls_prefix_t* pre, int64_t n_members, const void* q, int64_t n_rows, const void* k_resp,
@@ -406,7 +405,7 @@ int ls_score_fwd(const ls_prefix_t* pre, int64_t n_members, const void* q, int64
     if (rc != LS_OK) return rc;
     if (n_members * n_rows == 0) return LS_OK;
     if (!o || !lse) return fail(LS_ERR_INVALID, "o/lse is NULL");
-    const size_t need = fwd_parts_bytes(pre, n_members * n_rows, pre->n_shards + 1);
+    const size_t need = fwd_ws_k(pre, n_members * n_rows, fwd_k(pre, n_rows));
     if (!workspace || ws_bytes < need)
         return fail(LS_ERR_WORKSPACE, "scoring workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
     ls::AttnArgs a = make_args(pre, q, n_rows, 0, k_resp, v_resp);
@@ -418,8 +417,10 @@ int ls_score_fwd(const ls_prefix_t* pre, int64_t n_members, const void* q, int64
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
     if (pre->dtype == LS_DTYPE_BF16) {
-        a.n_members = n_members;  // one launch over every member's rows
-        e = ls::launch_fwd_mfma(a, s);
+        // one launch over every member's rows, split into the page ranges that each member's
+        // own replay would use, so that a member scores bit for bit as it replays
+        a.n_members = n_members;
+        e = fwd_mfma_parts(a, pre->n_shards, fwd_k(pre, n_rows), all_rows * pre->hq, pre->d, s);
     } else {
         // the exact f32 path runs the members one launch at a time into the same parts
         const size_t esz = 4;

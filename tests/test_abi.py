@@ -120,17 +120,19 @@ def test_stored_ds_workspace_size():
 
 
 def test_score_workspace_and_validation():
-    """Batched scoring: the workspace is the forward's parts for members * rows rows (scoring
-    never splits shards, so a small block's split area is not included); bad sizes, missing
-    outputs and short workspaces are rejected before any launch."""
+    """Batched scoring: the workspace is the forward one for members * rows rows, with shards
+    split into page ranges as each member's own replay block would split them; bad sizes,
+    missing outputs and short workspaces are rejected before any launch."""
     p = _prefix()
     lib = _lib.lib()
     assert lib.ls_score_workspace_bytes(C.byref(p), 3, 16) == lib.ls_fwd_workspace_bytes(C.byref(p), 48)
-    # 1,024 pages in 2 shards: a 16-row replay block splits them, a scoring call does not
+    # 1,024 pages in 2 shards: a 16-row block splits them (8 ranges a shard), with or without
+    # other members batched beside it
     big = _prefix(prefix_len=65536, n_phys_pages=1024, bounds=[0, 512, 1024])
     parts = 4 * 3 * 16 * 8 * 257
-    assert lib.ls_score_workspace_bytes(C.byref(big), 1, 16) == parts
-    assert lib.ls_fwd_workspace_bytes(C.byref(big), 16) > parts
+    assert lib.ls_fwd_workspace_bytes(C.byref(big), 16) == parts + 4 * 17 * 16 * 8 * 257
+    assert lib.ls_score_workspace_bytes(C.byref(big), 1, 16) == lib.ls_fwd_workspace_bytes(C.byref(big), 16)
+    assert lib.ls_score_workspace_bytes(C.byref(big), 3, 16) == 3 * lib.ls_fwd_workspace_bytes(C.byref(big), 16)
     assert lib.ls_score_workspace_bytes(C.byref(p), -1, 16) == 0 and "n_members" in _err()
     need = lib.ls_score_workspace_bytes(C.byref(p), 2, 16)
     score = lambda **kw: lib.ls_score_fwd(C.byref(p), kw.get("m", 2), kw.get("q", FAKE), 16, FAKE, FAKE,  # noqa: E731

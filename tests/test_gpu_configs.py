@@ -10,7 +10,7 @@
   hold exactly this block's contribution.  All 2,097,152 prompt keys' dK and dV, for every kv
   head, are compared with the oracle's contribution of the same 64 rows (streamed key chunk by
   key chunk, so host memory stays bounded); its O, LSE and dQ rows must also be those of the
-  full 1,024-row block (rows are independent).
+  full 1,024-row block (rows are independent) up to the order of float32 sums.
 (Explainer, "Serial replay makes G a schedule": exact attention; digest, "Method": the exact
 global output from the shards' local statistics.)
 """
@@ -126,12 +126,18 @@ def test_c2m_subset_block_all_prompt_gradients():
         torch.cuda.synchronize()
         return dict(o=o, lse=lse, dq=dq, dkr=dkr, dvr=dvr, dkp=dkp, dvp=dvp)
 
-    # rows are independent: the subset's O, LSE and dQ are the full block's rows, bit for bit
+    # rows are independent: the subset's O, LSE and dQ are the full block's rows, up to the order
+    # of float32 sums (a 64-row block splits the shards into page ranges, the full block does
+    # not).  O is stored in bf16, so a reordered sum can move its last bit (rel-L2 about 3e-3 at
+    # the bf16 rounding level), and delta = rowsum(dO * O) carries that into dS and dQ (about 2e-4).
     full = block(blk0, cfg.B)
     sub = block(off, n)
     r0 = off - blk0
-    for k in ("o", "lse", "dq"):
-        assert torch.equal(sub[k], full[k][r0:r0 + n]), k
+    for k, tol in (("o", 8e-3), ("lse", 1e-6), ("dq", 1e-3)):
+        a, b = sub[k].float(), full[k][r0:r0 + n].float()
+        rel = float((a - b).norm() / b.norm())
+        log(f"    {k} against the full block's rows: rel_l2={rel:.2e}")
+        assert rel <= tol, k
     del full
 
     kend = off + n

@@ -1,8 +1,9 @@
 """The no-allocation forward (ls_replay_fwd_noalloc, for callers that cannot allocate device memory)
 against the allocating forward (ls_replay_fwd) through the C ABI: the same kernels, so O and LSE
 must be equal bit for bit, on two calls in a row whose second is smaller (the scratch array
-keeps the first call's contents), for bf16 and float32; and a block whose forward workspace is
-larger than the scratch array is refused before any launch."""
+keeps the first call's contents), for bf16 and float32, and for small blocks over a long prompt
+(whose shards split into page ranges); and a block whose forward workspace is larger than the
+scratch array is refused before any launch."""
 import ctypes as C
 
 import pytest
@@ -28,7 +29,10 @@ def _noalloc(pre, q, q_start, kr, vr):
 
 
 @pytest.mark.parametrize("dtype,shape", [(torch.bfloat16, (3000, 512, 24, 4, 256, 3)),
-                                         (torch.float32, (700, 96, 4, 1, 64, 2))])
+                                         (torch.float32, (700, 96, 4, 1, 64, 2)),
+                                         # small blocks over a long prompt: the shards split into
+                                         # page ranges, whose results also live in the scratch array
+                                         (torch.bfloat16, (65536, 64, 6, 2, 256, 2))])
 def test_noalloc_forward_equals_the_allocating_forward(dtype, shape):
     P, R, hq, hkv, d, S = shape
     c = Case(P, R, hq, hkv, d, dtype, seed=41, S=S)
