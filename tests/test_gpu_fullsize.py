@@ -267,10 +267,14 @@ def test_block_size_does_not_change_the_result():
         torch.cuda.synchronize()
         out[B] = (r, grp)
     (a, ga), (b, gb) = out[1024], out[384]
+    # The blocks differ in size, so in the order of float32 sums (a 384-row block splits the
+    # shards into page ranges, a 1,024-row one does not): the bf16 O may move by its last bit,
+    # 2^-8 relative, and every other tensor stays within a fifth of the oracle bound.
     for name, x, y in (("O", a.o, b.o), ("LSE", a.lse, b.lse), ("dQ", a.dq, b.dq), ("dK_resp", a.dk_resp, b.dk_resp),
                        ("dV_resp", a.dv_resp, b.dv_resp), ("dK_pages", ga.dk_pages, gb.dk_pages),
                        ("dV_pages", ga.dv_pages, gb.dv_pages)):
-        assert_close(name, np32(y), np32(x).astype(np.float64), atol=ATOL, rel_l2=REL_L2 / 5)
+        rel = 2.0 ** -8 if name == "O" else REL_L2 / 5
+        assert_close(name, np32(y), np32(x).astype(np.float64), atol=ATOL, rel_l2=rel)
 
 
 def test_prefix_reuse_cycles_are_steady():
