@@ -1,7 +1,7 @@
 // Host-only checks of the C ABI front end (abi.cpp), built with the host compiler's address and
 // undefined-behaviour sanitizers against stand-in kernel launchers (abi_stubs.cpp): argument
-// validation, workspace sizing, the stored-dS chunk plan, the page-table check and the per-thread
-// error message.  Device pointers are fake and never dereferenced (no launch happens).  Prints
+// validation, workspace sizing, the stored-dS chunk plan, the small-block split, the page-table check
+// and the per-thread error message.  Device pointers are fake and never dereferenced (no launch happens).  Prints
 // one line per check and exits non-zero on the first failure.
 #include <cstdio>
 #include <cstring>
@@ -188,6 +188,103 @@ void chunk_plan_checks() {
            "f32 stores no dS");
 }
 
+// The sub-range split of a small block's shards (launch.hpp): how many ranges, their page
+// bounds, and what the front end launches and sizes for them.
+void split_checks() {
+    bool ok = true;
+    const int64_t tiles[] = {1, 2, 3, 5, 12, 48, 96, 200};
+    const int shards[] = {1, 2, 3, 8, 17, 64};
+    const int heads[] = {1, 2, 4, 8};
+    const int64_t pages[] = {0, 63, 64, 640, 1024, 32768, int64_t(1) << 20};
+    for (int64_t t : tiles)
+        for (int s : shards)
+            for (int h : heads)
+                for (int64_t pg : pages) {
+                    const int k = ls::sub_split(t, s, h, pg);
+                    const int64_t wg = t * s * h;  // workgroups with one range per shard
+                    bool c = k >= 1 && (int64_t)k * s <= ls::kMaxSubParts;
+                    if (wg >= 768) c = c && k == 1;                          // the chip is already full
+                    if (k > 1) c = c && (int64_t)k * s * 64 <= pg;            // >= 64 pages a range on average
+                    if (k > 1) c = c && (int64_t)(k - 1) * wg < 768;          // no more ranges than it takes
+                    if (wg < 768 && (int64_t)k * wg < 768)                    // short of the target only when capped
+                        c = c && ((int64_t)(k + 1) * s * 64 > pg || (k + 1) * s > ls::kMaxSubParts);
+                    if (!c) {
+                        std::printf("  sub_split(%lld, %d, %d, %lld) = %d\n", (long long)t, s, h, (long long)pg, k);
+                        ok = false;
+                    }
+                }
+    expect(ok, "sub_split: fills the chip, at least 64 pages a range, at most 256 ranges");
+    expect(ls::fwd_split(16, 6, 8, 4, 32832) > 1 && ls::fwd_split(1024, 6, 8, 4, 32832) == 1,
+           "a 16-row block splits, a 1,024-row block does not (8 shards, 4 kv heads)");
+
+    ok = true;
+    const std::vector<std::vector<int64_t>> cases = {{0, 5, 19, 32}, {0, 0, 3, 3, 10}, {0, 1}, {0, 1000}};
+    for (const auto& lo : cases)
+        for (int k = 1; k <= 8; k++) {
+            const int s = (int)lo.size() - 1;
+            int64_t out[ls::kMaxSubParts + 1];
+            ls::split_bounds(lo.data(), s, k, out);
+            for (int i = 0; i <= s; i++) ok = ok && out[i * k] == lo[i];  // the shard bounds stay bounds
+            for (int i = 0; i < s; i++)
+                for (int j = 0; j < k; j++) {
+                    const int64_t len = out[i * k + j + 1] - out[i * k + j], shard = lo[i + 1] - lo[i];
+                    ok = ok && len >= shard / k && len <= (shard + k - 1) / k;  // as even as pages allow
+                }
+        }
+    expect(ok, "split_bounds: keeps the shard bounds, ranges differ by at most one page");
+
+    // 16 rows over a 65,536-token prompt in two shards, 24 / 4 heads, d = 256: eight ranges a shard
+    Prefix big(24, 4, 256, LS_DTYPE_BF16, 65536, {0, 512, 1024});
+    const int64_t n = 16, rows_hq = n * 24;
+    const int k = ls::fwd_split(n, 6, 2, 4, 1024);
+    const size_t fw = ls_fwd_workspace_bytes(&big.p, n);
+    expect(k == 8 && fw == sizeof(float) * (size_t)rows_hq * 257 * (3 + 2 * 8 + 1),
+           "split forward workspace: the parts, then the ranges' results");
+    stub::last = stub::Record();
+    int rc = ls_replay_fwd(&big.p, fake(4), n, 0, fake(5), fake(6), n, fake(7), (float*)fake(8), fake(9), fw, nullptr);
+    bool bounds_ok = true;
+    for (int j = 0; j <= 16; j++) bounds_ok = bounds_ok && stub::last.args.shard_lo[j] == 64 * j;
+    expect(rc == LS_OK && stub::last.args.n_shards == 16 && stub::last.args.n_parts == 17 && bounds_ok &&
+               stub::last.args.o_parts == (float*)fake(9) + rows_hq * 257 * 3,
+           "split forward: one launch over 16 ranges and the response, after the parts");
+    const int* mp = stub::last.merge_parts;
+    expect(stub::last.merges == 4 && mp[0] == 8 && mp[1] == 8 && mp[2] == 1 && mp[3] == 3 && stub::last.calls == 5,
+           "split forward: a merge per shard, one for the response, then the final merge");
+    expect(ls_replay_fwd(&big.p, fake(4), n, 0, fake(5), fake(6), n, fake(7), (float*)fake(8), fake(9), fw - 1,
+                         nullptr) == LS_ERR_WORKSPACE,
+           "split forward: a workspace without the ranges' area is rejected");
+    Prefix big_f32(24, 4, 256, LS_DTYPE_F32, 65536, {0, 512, 1024});
+    expect(ls_fwd_workspace_bytes(&big_f32.p, n) == sizeof(float) * (size_t)rows_hq * 257 * 3,
+           "the vector-ALU forward does not split");
+
+    // the stored-dS dQ pass of the same block: eight ranges a shard, summed from their own area
+    const int64_t q0 = 0, kend = q0 + n;
+    const int kq = ls::dqs_split(n, 6, 2, 4, 1024);
+    const size_t rec = ls_bwd_workspace_bytes(&big.p, n);
+    const size_t all = ls_bwd_ds_workspace_bytes(&big.p, n, kend);
+    stub::last = stub::Record();
+    rc = bwd(&big.p, n, q0, all, 0);
+    const float* sub = stub::last.bwd.dq_sub;
+    const size_t sub_bytes = sizeof(float) * (size_t)(2 * kq + 1) * rows_hq * 256;
+    expect(rc == LS_OK && kq == 8 && stub::last.bwd.ds != nullptr && stub::last.bwd.dq_sub_k == kq &&
+               (char*)sub + sub_bytes == (char*)fake(15) + rec && ((char*)sub - (char*)fake(15)) % 256 == 0,
+           "split dQ pass: sub-range partials at the end of the backward workspace, 256-byte aligned");
+    expect(stub::last.sum_n == 2 * kq + 1 && stub::last.sum_src == sub, "split dQ pass: the sum reads the sub-ranges");
+    expect(ls_debug_owner_slots(&big.p, n, kend) ==
+               (size_t)ls::owner_slots(big.p.n_phys_pages, 4, 24, 2 * kq + 1, n, kend),
+           "split dQ pass: a counter slot per sub-range partial row");
+    stub::last = stub::Record();
+    rc = bwd(&big.p, n, q0, rec, 0);
+    expect(rc == LS_OK && stub::last.bwd.ds == nullptr && stub::last.bwd.dq_sub_k == 0 && stub::last.sum_n == 3,
+           "recomputing dQ pass: no split, the sum over the shard parts");
+    const size_t part_chunk = ls_bwd_ds_chunk_workspace_bytes(&big.p, n, kend, 1, 2);
+    stub::last = stub::Record();
+    rc = bwd(&big.p, n, q0, part_chunk, 0);
+    expect(rc == LS_OK && stub::last.bwd.ds != nullptr && stub::last.bwd.ds_parts < 3 &&
+               stub::last.bwd.dq_sub_k == 0 && stub::last.sum_n == 3,
+           "stored dS in key-part chunks: no split");
+}
+
 void thread_checks() {
     // the error message belongs to the calling thread
     const int32_t dup[2] = {1, 1};
@@ -210,6 +307,7 @@ int main() {
     dispatch_checks();
     noalloc_checks();
     chunk_plan_checks();
+    split_checks();
     thread_checks();
     std::printf("%s: %d failure(s)\n", g_failed ? "FAILED" : "PASSED", g_failed);
     return g_failed ? 1 : 0;

@@ -25,11 +25,18 @@ hipError_t launch_capture(const void*, const void*, int, int64_t, int64_t, const
 hipError_t launch_gather(const void*, int, const int32_t*, int64_t, int64_t, int64_t, int, int, void*, hipStream_t) {
     return note("gather");
 }
-hipError_t launch_lse_merge(int, int64_t, int, const float*, const float*, void*, int, float*, hipStream_t, bool) {
+hipError_t launch_lse_merge(int n_parts, int64_t, int, const float*, const float*, void*, int, float*, hipStream_t,
+                            bool) {
+    if (stub::last.merges < 8) stub::last.merge_parts[stub::last.merges] = n_parts;
+    stub::last.merges++;
     return note("lse_merge");
 }
 hipError_t launch_delta(const void*, const void*, int, int64_t, int, float*, hipStream_t) { return note("delta"); }
-hipError_t launch_sum_parts(int, int64_t, const float*, float*, hipStream_t) { return note("sum_parts"); }
+hipError_t launch_sum_parts(int n_parts, int64_t, const float* src, float*, hipStream_t) {
+    stub::last.sum_n = n_parts;
+    stub::last.sum_src = src;
+    return note("sum_parts");
+}
 hipError_t launch_zero(float*, int64_t, hipStream_t) { return note("zero"); }
 hipError_t launch_fwd_generic(const AttnArgs& a, hipStream_t) { return note("fwd_generic", &a); }
 hipError_t launch_bwd_generic(const AttnArgs& a, hipStream_t) { return note("bwd_generic", &a); }

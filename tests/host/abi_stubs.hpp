@@ -11,6 +11,10 @@ struct Record {
     const char* name = "";
     ls::AttnArgs args{};
     ls::AttnArgs bwd{};
+    int merges = 0;                   // LSE merge launches, and the parts of the first eight
+    int merge_parts[8] = {};
+    int sum_n = 0;                    // parts and source of the last dQ part sum
+    const float* sum_src = nullptr;
 };
 extern Record last;
 }  // namespace stub

@@ -1,7 +1,7 @@
 """The C ABI front end (abi.cpp) built for the host alone with the address and undefined-behaviour
 sanitizers, against stand-in kernel launchers (tests/host/abi_stubs.cpp), and run through
 tests/host/abi_host_check.cpp: argument validation, workspace sizes, the stored-dS chunk plan,
-the page-table check and the per-thread error message.  No GPU and no launch: the device pointers
+the small-block sub-range split, the page-table check and the per-thread error message.  No GPU and no launch: the device pointers
 are fake and the stand-ins only record their arguments."""
 import os
 import shutil
