@@ -196,6 +196,155 @@ def measured_ceilings() -> dict:
     return out
 
 
+class PowerSampler:
+    """GPU 0's power-management counters through amdsmi (read-only queries), polled on a
+    background thread.  The device refreshes its metrics table about once a second; every new
+    table is kept: the firmware's time base (ns), its energy counter, the count of its
+    accumulation ticks and of those ticks in which the package power limit (PPT) held the
+    clock down, the socket power it reports and the graphics clock of every XCD at that moment.
+    Between two consecutive tables, the energy and tick differences give the average power
+    and the fraction of time the chip was power-limited over that interval."""
+
+    def __init__(self, poll_s: float = 0.005):
+        import threading
+
+        import amdsmi
+        self.smi = amdsmi
+        amdsmi.amdsmi_init()
+        hs = amdsmi.amdsmi_get_processor_handles()
+        self.h = hs[0] if len(hs) == 1 else self._match(hs)
+        self.cap_w = amdsmi.amdsmi_get_power_cap_info(self.h)["power_cap"] / 1e6
+        self.energy_j = float(amdsmi.amdsmi_get_energy_count(self.h)["counter_resolution"]) * 1e-6
+        self.poll = poll_s
+        self.tables = []  # (host time, fw ns, energy, ppt ticks, ticks, socket W, mean XCD MHz, min XCD MHz)
+        self._stop = threading.Event()
+        self._thr = threading.Thread(target=self._run, daemon=True)
+
+    def _match(self, hs):
+        bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+        for h in hs:
+            if bus is not None and int(self.smi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus:
+                return h
+        raise RuntimeError("no amdsmi device matches cuda:0")
+
+    def _run(self):
+        last = None
+        while not self._stop.is_set():
+            m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+            # a table read while the device rewrites it can come back empty: skip it
+            if m["system_clock_counter"] not in (last, 0, "N/A") and m["energy_accumulator"] not in (0, "N/A"):
+                last = m["system_clock_counter"]
+                clks = [c for c in m["current_gfxclks"] if isinstance(c, int)]
+                self.tables.append((time.perf_counter(), m["system_clock_counter"], m["energy_accumulator"],
+                                    m["ppt_residency_acc"], m["accumulation_counter"], m["current_socket_power"],
+                                    sum(clks) / len(clks), min(clks)))
+            time.sleep(self.poll)
+
+    def start(self):
+        self._thr.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        self._thr.join()
+        self.smi.amdsmi_shut_down()
+
+    def window(self, t0: float, t1: float) -> dict:
+        """Averages over the refresh intervals that lie wholly inside host times [t0, t1]."""
+        tb = [x for x in self.tables if t0 <= x[0] <= t1]
+        if len(tb) < 2:
+            return {"intervals": 0}
+        ns = tb[-1][1] - tb[0][1]
+        ticks = tb[-1][4] - tb[0][4]
+        return {"intervals": len(tb) - 1, "s": round(ns * 1e-9, 3),
+               "avg_w": round((tb[-1][2] - tb[0][2]) * self.energy_j / (ns * 1e-9), 1) if ns > 0 else None,
+               "ppt_limited": round((tb[-1][3] - tb[0][3]) / ticks, 3) if ticks > 0 else None,
+               "reported_w": [x[5] for x in tb[1:]],
+               "gfxclk_mhz": round(float(np.mean([x[6] for x in tb[1:]])), 0),
+               "gfxclk_min_xcd_mhz": round(float(np.mean([x[7] for x in tb[1:]])), 0)}
+
+
+def power_phases(prefix, members, cfg, dump: str | None = None) -> dict:
+    """Average power, graphics clock and the fraction of time the package power limit held the
+    clock down, while the chip runs, one after another for several seconds each: nothing
+    (idle); chains of the matrix instruction on constant and on random operands and an HBM read
+    stream (the committed microbenchmarks); whole steps; the forward and the backward of one
+    block (the member's last rows, the first replayed), each called repeatedly.  The device's
+    counters advance once a second, so each figure covers the whole seconds inside its phase."""
+    import ctypes as C
+    lib = C.CDLL(MICROBENCH)
+    lib.mb_mfma_peak.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_double)]
+    lib.mb_hbm.argtypes = [C.c_int, C.c_size_t, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_double)]
+    v = C.c_double(0)
+    smp = PowerSampler().start()
+    out = {"source": "amdsmi GPU metrics of the device (read-only), refreshed about once a second",
+           "power_cap_w": smp.cap_w, "phases": []}
+    min_s = 5.0  # at least four whole refresh intervals per phase
+
+    def phase(name, fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        r = {}
+        while time.perf_counter() - t0 < min_s:
+            r = fn() or {}
+            torch.cuda.synchronize()
+        row = {"phase": name, **r}
+        row.update(smp.window(t0, time.perf_counter()))
+        out["phases"].append(row)
+        log(f"[bench] power: {row}")
+        return row
+
+    def mfma(rand):
+        rc = lib.mb_mfma_peak(256, 400000, 8, rand, C.byref(v))
+        assert rc == 0, rc
+        return {"tflops": round(v.value, 1)}
+
+    def hbm():
+        rc = lib.mb_hbm(0, 4 << 30, 1, 8192, 1000, C.byref(v))
+        assert rc == 0, rc
+        return {"gbs": round(v.value, 1)}
+
+    phase("idle", lambda: time.sleep(0.5))
+    phase("matrix-instruction chains, constant operands", lambda: mfma(0))
+    phase("matrix-instruction chains, random operands", lambda: mfma(1))
+    phase("HBM read stream", hbm)
+    phase("whole steps", lambda: run_steps(prefix, members, cfg, 1) and None)
+
+    # one block, the member's last rows (the first replayed), forward and backward on their own
+    dev = prefix.k_pages.device
+    m = members[0]
+    a, e = max(0, cfg.R - cfg.B), cfg.R
+    q, do = m["q"][a:e], m["do"][a:e]
+    o, lse, ws_f = api.replay_fwd(prefix, q, a, m["kr"], m["vr"])
+    dk_r = torch.zeros(m["kr"].shape, dtype=torch.float32, device=dev)
+    dv_r = torch.zeros_like(dk_r)
+    dk_p = torch.zeros(prefix.k_pages.shape, dtype=torch.float32, device=dev)
+    dv_p = torch.zeros_like(dk_p)
+    need = api.bwd_ds_workspace_bytes(prefix, e - a, e)
+    store = prefix.dtype == torch.bfloat16 and api.ds_fits(need, dev)
+    ws_b = torch.empty(((need if store else api.bwd_workspace_bytes(prefix, e - a)) + 3) // 4,
+                       dtype=torch.float32, device=dev)
+
+    def fwd_loop():
+        for _ in range(10):
+            api.replay_fwd(prefix, q, a, m["kr"], m["vr"], workspace=ws_f, o=o, lse=lse)
+
+    def bwd_loop():
+        for _ in range(4):
+            api.replay_bwd(prefix, q, a, m["kr"], m["vr"], o, lse, do, dk_r, dv_r, False, dk_p, dv_p,
+                           shard_first_touch=[False] * prefix.n_shards, workspace=ws_b)
+        return {"dq_form": "stored dS" if store else "recompute"}
+
+    phase(f"forward of rows [{a}, {e})", fwd_loop)
+    phase(f"backward of rows [{a}, {e})", bwd_loop)
+    smp.stop()
+    del ws_b, dk_p, dv_p
+    if dump:
+        with open(dump, "w") as f:
+            json.dump({"tables": smp.tables, "phases": out["phases"]}, f)
+    return out
+
+
 def build_prefix(cfg, dev):
     table = datagen.page_table(cfg.n_pages, datagen.seed(cfg.cfg_id, datagen.TAG_PERM), dev)
     kp, vp = datagen.prefix_kv(cfg, dev)
@@ -505,6 +654,11 @@ def main():
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
                     help="write the dominant kernel's HBM traffic summary from rocprofv3 --pmc output")
     ap.add_argument("--kernel", default="dkdv_mfma", help="kernel for --ingest-counters")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the power phases run after the timed steps (average power, clock and power-limit "
+                         "residency from the device's counters, read through amdsmi, for idle, the microbenchmarks, "
+                         "a step and one block's forward and backward)")
+    ap.add_argument("--power-dump", default=None, help="write the power phases' raw counter tables to this JSON file")
     ns = ap.parse_args()
     if ns.ingest_counters:
         ingest_counters(ns.config, ns.kernel, *ns.ingest_counters)
@@ -645,6 +799,14 @@ def main():
         out["cycle_peak_gb"] = [round(c[1] / 1e9, 3) for c in cycles]
     timed_peak, timed_form = grp.peak_bytes, plan.describe(prefix)
     del grp, results  # release the timed group's gradient pages before anything else runs
+    if not ns.no_power and cycles is None:
+        t = time.perf_counter()
+        try:
+            out["power"] = power_phases(prefix, members, cfg, ns.power_dump)
+        except Exception as exc:  # amdsmi missing or refused: the figures are context, not the metric
+            out["power"] = {"error": f"{type(exc).__name__}: {exc}"}
+        torch.cuda.synchronize()
+        log(f"[bench] power phases {time.perf_counter() - t:.1f} s")
     if not ns.no_memory_sweep and cycles is None:
         t = time.perf_counter()
         out["peak_mem_gb_vs_G"] = memory_vs_g(prefix, members, cfg, timed_peak, timed_form)
