@@ -8,7 +8,7 @@ namespace ls {
 
 constexpr int kMaxShards = 64;     // prompt shards a caller may use
 constexpr int kMaxSubParts = 256;  // key ranges a launch may split the prompt into (below)
-constexpr int kFwdTileRows = 128;  // group rows per forward workgroup
+constexpr int kFwdTileRows = 256;  // group rows per forward workgroup
 constexpr int kDqsTileRows = 256;  // group rows per workgroup of the stored-dS dQ pass
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
