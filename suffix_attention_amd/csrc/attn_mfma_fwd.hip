@@ -31,6 +31,8 @@
 // same softmax.
 #include <math.h>
 
+#include <type_traits>
+
 #include "mfma_tiles.hpp"
 
 namespace ls {
@@ -73,12 +75,13 @@ __device__ __forceinline__ void mask_tile(f32x16& s, int kt, int valid, int caus
 // The softmax of one 32-key tile for both row tiles, in units spread over a phase's steps.
 // Units 0-7 take the maximum of four scores of each row tile; unit 8 combines the two
 // half-waves' maxima and moves a row's reference if the tile exceeds it by more than
-// kLazyLog2; units 9-16 exponentiate and pack four scores of each row tile; unit 17 updates the
-// row sums.
-constexpr int kSmUnits = 18;
+// kLazyLog2; units 9-16 exponentiate and pack four scores of each row tile.  The row sums are
+// taken later from the packed words (row_sums), beside matrix work that has no vector work of
+// its own.
+constexpr int kSmUnits = 17;
 
 struct SmState {
-    float mx[kRT], alpha[kRT], m_use[kRT], lsum[kRT];
+    float mx[kRT], alpha[kRT], m_use[kRT];
 };
 
 // Each unit ends by pinning its results with an empty asm statement: without it, the compiler
@@ -104,25 +107,37 @@ __device__ __forceinline__ void sm_unit(int u, const f32x16 (&s)[kRT], SmState& 
                 m_ref[rt] = mx;
             }
             st.m_use[rt] = m_ref[rt] == -INFINITY ? 0.f : m_ref[rt];
-            st.lsum[rt] = 0.f;
             asm volatile("" : "+v"(st.alpha[rt]), "+v"(st.m_use[rt]), "+v"(m_ref[rt]));
         }
-    } else if (u < 17) {
+    } else {
         const int j = u - 9;
 #pragma unroll
         for (int rt = 0; rt < kRT; rt++) {
             const float p0 = fast_exp2(__builtin_fmaf(s[rt][2 * j], scale_log2, -st.m_use[rt]));
             const float p1 = fast_exp2(__builtin_fmaf(s[rt][2 * j + 1], scale_log2, -st.m_use[rt]));
-            st.lsum[rt] += p0 + p1;
             wd[rt][j] = pack_bf16x2(p0, p1);
-            asm volatile("" : "+v"(wd[rt][j]), "+v"(st.lsum[rt]));
+            asm volatile("" : "+v"(wd[rt][j]));
         }
-    } else {
+    }
+}
+
+// The row sums of one page: l = (l alpha0 + sum P0) alpha1 + sum P1, in the order the
+// reference moved, from the bf16 words the products used (v_dot2c_f32_bf16 against (1, 1), one
+// instruction per pair), so the weights O is normalised by are exactly those it summed.
+__device__ __forceinline__ void row_sums(float (&l)[kRT], const uint32_t (&wd0)[kRT][8], const uint32_t (&wd1)[kRT][8],
+                                         const SmState& st0, const SmState& st1, int step, int n_steps) {
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    const bf16x2v one = {(__bf16)1.f, (__bf16)1.f};
+    // 2 x kRT chains of 8 words, spread over the steps; each chain starts from its scaled l
 #pragma unroll
-        for (int rt = 0; rt < kRT; rt++) {
-            l[rt] = l[rt] * st.alpha[rt] + st.lsum[rt];
-            asm volatile("" : "+v"(l[rt]));
-        }
+    for (int c = step * 4 / n_steps; c < (step + 1) * 4 / n_steps; c++) {
+        const int half = c / kRT, rt = c % kRT;
+        const uint32_t(&wd)[kRT][8] = half ? wd1 : wd0;
+        float acc = l[rt] * (half ? st1.alpha[rt] : st0.alpha[rt]);
+#pragma unroll
+        for (int j = 0; j < 8; j++) acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, wd[rt][j]), one, acc, false);
+        l[rt] = acc;
+        asm volatile("" : "+v"(l[rt]));
     }
 }
 
@@ -141,62 +156,38 @@ __device__ __forceinline__ void rescale_o(f32x16 (&o)[DT][kRT], const float (&al
     agpr_write_gap();
 }
 
-// Phase 1 / 2: S^T of the 32 keys of tile kt for both row tiles.  K fragments (rows 32kt..,
-// d step ks) are read PD steps ahead; beside(ks) runs that step's share of the other work.
-template <int D, typename Beside>
-__device__ __forceinline__ void score_tile(f32x16 (&s)[kRT], const bf16x8 (&qb)[kRT][TileShape<D>::KS], uint32_t ak,
-                                           Beside&& beside) {
-    constexpr int KS = TileShape<D>::KS, PD = 2;
-    bf16x8 kbuf[PD];
-#pragma unroll
-    for (int j = 0; j < PD; j++) kbuf[j] = lds_b128(ak ^ (uint32_t)(j << 5));
-#pragma unroll
-    for (int rt = 0; rt < kRT; rt++) s[rt] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++) {
-        const bf16x8 kf = kbuf[ks % PD];
-        if (ks + PD < KS) kbuf[ks % PD] = lds_b128(ak ^ (uint32_t)((ks + PD) << 5));
-#pragma unroll
-        for (int rt = 0; rt < kRT; rt++) s[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qb[rt][ks], s[rt], 0, 0, 0);
-        beside(ks);
-        __builtin_amdgcn_sched_barrier(0);
+// The LDS operand fragments of one page, as one stream over its four phases of NS = D/16 steps
+// each: step i of phase 0 / 1 reads the K fragment of keys 32kt.. (kt = phase) at d step i
+// (natural read); step i = (j, dt) of phase 2 / 3 reads the V^T fragment of d tile dt and keys
+// 32kt + 16j + 0..15 (two transposing reads, the key order permuted inside the 16 as on P).
+// The page is walked with the stream read PF steps ahead across the phase boundaries, so only
+// the first read after the page's barrier is waited for.
+template <int D>
+struct PageFrags {
+    static constexpr int NS = TileShape<D>::KS;  // steps per phase (= 2 * DT)
+    uint32_t ak, sv;                             // lane bases of this page's K and V tiles
+    __device__ __forceinline__ bf16x8 read(int step) const {
+        const int ph = step / NS, i = step % NS;
+        if (ph < 2) {
+            uint32_t b = ak;  // formed per read (one xor) rather than held as 2 * NS addresses
+            asm volatile("" : "+v"(b));
+            return lds_b128((b + ph * 32 * 2 * D) ^ (uint32_t)(i << 5));
+        }
+        const int dt = i % TileShape<D>::DT, R = 32 * (ph - 2) + 16 * (i / TileShape<D>::DT);
+        const i16x4 lo = lds_tr4((sv ^ tr_x<D>(dt, R)) + R * 2 * D);
+        const i16x4 hi = lds_tr4((sv ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
-}
+};
 
-// Phase 3 / 4: O^T += V^T P^T over the 32 keys of tile kt (key steps ku = 2kt, 2kt + 1) for
-// both row tiles.  Step st = (ku, dt) with dt fastest; V^T fragments (rows 32kt + 16(ku&1) +
-// 0..7 and + 8..15 of d tile dt, through the transposing read) are read PV steps ahead.
-template <int D, typename Beside>
-__device__ __forceinline__ void output_tile(f32x16 (&o)[TileShape<D>::DT][kRT], const uint32_t (&wd)[kRT][8], int kt,
-                                            uint32_t sv, Beside&& beside) {
-    using F = TileShape<D>;
-    constexpr int NST = 2 * F::DT, PV = 2;
-    i16x4 vlo[PV], vhi[PV];
-    auto read_v = [&](int st, i16x4& lo, i16x4& hi) {
-        const int dt = st % F::DT, j = st / F::DT;
-        const int R = 32 * kt + 16 * j;
-        lo = lds_tr4((sv ^ tr_x<D>(dt, R)) + R * 2 * D);
-        hi = lds_tr4((sv ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D);
-    };
-    bf16x8 pb[kRT][2];
+// P^T operands of one 32-key tile: key steps j = 0, 1 of both row tiles, from the packed words.
+__device__ __forceinline__ void p_operands(bf16x8 (&pb)[kRT][2], const uint32_t (&wd)[kRT][8]) {
 #pragma unroll
     for (int rt = 0; rt < kRT; rt++)
 #pragma unroll
         for (int j = 0; j < 2; j++)
-            pb[rt][j] = __builtin_bit_cast(bf16x8, u32x4{wd[rt][4 * j], wd[rt][4 * j + 1], wd[rt][4 * j + 2],
-                                                         wd[rt][4 * j + 3]});
-#pragma unroll
-    for (int j = 0; j < PV; j++) read_v(j, vlo[j], vhi[j]);
-#pragma unroll
-    for (int st = 0; st < NST; st++) {
-        const int dt = st % F::DT, j = st / F::DT;
-        const bf16x8 va =
-            __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[st % PV], vhi[st % PV], 0, 1, 2, 3, 4, 5, 6, 7));
-        if (st + PV < NST) read_v(st + PV, vlo[st % PV], vhi[st % PV]);
-        mfma32_agpr2(o[dt][0], va, pb[0][j], o[dt][1], va, pb[1][j]);
-        beside(st);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+            pb[rt][j] =
+                __builtin_bit_cast(bf16x8, u32x4{wd[rt][4 * j], wd[rt][4 * j + 1], wd[rt][4 * j + 2], wd[rt][4 * j + 3]});
 }
 
 // Blocks (query tile, part, kv head), dealt to the XCDs as deal_block() orders them; the query
@@ -287,36 +278,40 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles) {
     constexpr int RPK = Tiles::RPK, JROWS = Tiles::JROWS;
     const int low = w * RPK + lane / F::KCH;
     const uint32_t cp_base = (uint32_t)low * kt.row_bytes + ((uint32_t)((lane % F::KCH) ^ swz<D>(low)) << 4);
-    auto copy_piece = [&](const char* src, int valid_rows, uint32_t lds, int j) {
+    auto copy_piece = [&](const i32x4& rsrc, uint32_t lds, int j) {
         const uint32_t off = (cp_base ^ ((uint32_t)swz<D>(j * JROWS) << 4)) + (uint32_t)(j * JROWS) * kt.row_bytes;
-        dma16(src, kt.bytes_of(valid_rows), off, lds + (j * kW + w) * 1024);
+        dma16r(rsrc, off, lds + (j * kW + w) * 1024);
     };
     // page-table entries are read through the scalar cache a page before their copies
     auto entry = [&](int i) { return i < nt ? kt.entry(i) : 0; };
     if (nt > 0) {
         const int32_t e0 = entry(0);
+        const i32x4 rk = buffer_rsrc(kt.tile(e0, 0, false), kt.bytes_of(kt.valid(0)));
+        const i32x4 rv = buffer_rsrc(kt.tile(e0, 0, true), kt.bytes_of(kt.valid(0)));
 #pragma unroll
         for (int j = 0; j < PW; j++) {
-            copy_piece(kt.tile(e0, 0, false), kt.valid(0), kb0, j);
-            copy_piece(kt.tile(e0, 0, true), kt.valid(0), vb0, j);
+            copy_piece(rk, kb0, j);
+            copy_piece(rv, vb0, j);
         }
     }
     int32_t e_next = entry(1);
 
-    for (int t = 0; t < nt; t++) {
+    // One page; MASKED (pages from tm on) adds the masks.  The pages before tm run without any
+    // mask code, so the hot loop carries neither its branches nor its registers.
+    auto page = [&](int t, auto mtag) {
+        constexpr bool MASKED = decltype(mtag)::value;
         const uint32_t kcur = kb0 + (uint32_t)(t & 1) * F::TILE, vcur = vb0 + (uint32_t)(t & 1) * F::TILE;
         const uint32_t knext = kb0 + (uint32_t)((t + 1) & 1) * F::TILE, vnext = vb0 + (uint32_t)((t + 1) & 1) * F::TILE;
         // the next page's copies; past the last page they repeat it into the free buffer
         const int tn = t + 1 < nt ? t + 1 : nt - 1;
         const int32_t e_cp = t + 1 < nt ? e_next : entry(tn);
-        const char* ksrc = kt.tile(e_cp, tn, false);
-        const char* vsrc = kt.tile(e_cp, tn, true);
         const int vn = kt.valid(tn);
+        const i32x4 rk = buffer_rsrc(kt.tile(e_cp, tn, false), kt.bytes_of(vn));
+        const i32x4 rv = buffer_rsrc(kt.tile(e_cp, tn, true), kt.bytes_of(vn));
         e_next = entry(t + 2);
         wait_vm_all();
         lds_barrier();  // page t is in LDS; every wave is done with page t - 1's buffers
 
-        const bool masked = t >= tm;
         const int valid = kt.valid(t);
         // the row's causal limit relative to the page's first key (response keys; else all)
         int causal[kRT] = {kPage, kPage};
@@ -324,7 +319,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles) {
         // (or spilled) across the loop: every register is taken by Q, S, P and the fragments.
         int ln = __lane_id();
         asm volatile("" : "+v"(ln));
-        if (masked && resp) {
+        if (MASKED && resp) {
             int64_t d = a.q_start - (int64_t)t * kPage;
             d = d < -(1 << 30) ? -(1 << 30) : (d > (1 << 30) ? (1 << 30) : d);
 #pragma unroll
@@ -339,40 +334,84 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles) {
 
         f32x16 s0[kRT], s1[kRT];
         uint32_t wd0[kRT][8], wd1[kRT][8];
+        bf16x8 pb[kRT][2];
         SmState st0, st1;
         st0.mx[0] = st0.mx[1] = st1.mx[0] = st1.mx[1] = -INFINITY;
+#pragma unroll
+        for (int rt = 0; rt < kRT; rt++) s0[rt] = s1[rt] = f32x16{};
 
-        // 1: scores of keys 0-31, the next page's copies beside
-        score_tile<D>(s0, qb, kcur + lk, [&](int ks) {
-            if (ks < PW) copy_piece(ksrc, vn, knext, ks);
-            else if (ks < 2 * PW) copy_piece(vsrc, vn, vnext, ks - PW);
-        });
-        if (masked) {
+        // The page in four phases (see the top of the file), one step = one fragment feeding two
+        // matrix instructions and a share of the phase's vector or copy work:
+        //   0  S^T of keys 0-31             beside: the next page's copies
+        //   1  S^T of keys 32-63            beside: the softmax of keys 0-31
+        //   2  O^T += V^T P^T, keys 0-31    beside: the softmax of keys 32-63
+        //   3  O^T += V^T P^T, keys 32-63   beside: the page's row sums
+        constexpr int NS = PageFrags<D>::NS, PF = 2;
+        const PageFrags<D> pg{kcur + lk, vcur + lv};
+        bf16x8 fb[PF];
+#pragma unroll
+        for (int j = 0; j < PF; j++) fb[j] = pg.read(j);
+        // step `step` of the page (phase step / NS): its fragment, the next read, its matrix
+        // instructions and its share of the phase's other work
+        auto one_step = [&](int step) {
+            const int ph = step / NS, i = step % NS;
+            const bf16x8 f = fb[step % PF];
+            if (step + PF < 4 * NS) fb[step % PF] = pg.read(step + PF);
+            if (ph == 0) {
+#pragma unroll
+                for (int rt = 0; rt < kRT; rt++) s0[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qb[rt][i], s0[rt], 0, 0, 0);
+                // the copy's LDS base passes through an empty asm so that the 2 * PW bases are
+                // formed one by one rather than all held in scalar registers across the phase
+                uint32_t kn = knext, vnx = vnext;
+                asm volatile("" : "+s"(kn), "+s"(vnx));
+                if (i < PW) copy_piece(rk, kn, i);
+                else if (i < 2 * PW) copy_piece(rv, vnx, i - PW);
+            } else if (ph == 1) {
+#pragma unroll
+                for (int rt = 0; rt < kRT; rt++) s1[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qb[rt][i], s1[rt], 0, 0, 0);
+#pragma unroll
+                for (int u = i * kSmUnits / NS; u < (i + 1) * kSmUnits / NS; u++)
+                    sm_unit(u, s0, st0, m_ref, l, wd0, a.scale_log2);
+            } else {
+                const int dt = i % F::DT, j = i / F::DT;
+                mfma32_agpr2(o[dt][0], f, pb[0][j], o[dt][1], f, pb[1][j]);
+                if (ph == 2) {
+#pragma unroll
+                    for (int u = i * kSmUnits / NS; u < (i + 1) * kSmUnits / NS; u++)
+                        sm_unit(u, s1, st1, m_ref, l, wd1, a.scale_log2);
+                } else {
+                    row_sums(l, wd0, wd1, st0, st1, i, NS);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // each phase is its own loop (a loop over the whole page is too large to be unrolled),
+        // with the masks and rescales between them; the reads run ahead across the boundaries
+#pragma unroll
+        for (int step = 0; step < NS; step++) one_step(step);
+        if constexpr (MASKED) {
 #pragma unroll
             for (int rt = 0; rt < kRT; rt++) mask_tile(s0[rt], 0, valid, causal[rt], ln >> 5);
         }
-        // 2: scores of keys 32-63, the softmax of keys 0-31 beside
-        score_tile<D>(s1, qb, kcur + lk + 32 * 2 * D, [&](int ks) {
 #pragma unroll
-            for (int u = ks * kSmUnits / F::KS; u < (ks + 1) * kSmUnits / F::KS; u++)
-                sm_unit(u, s0, st0, m_ref, l, wd0, a.scale_log2);
-        });
-        if (masked) {
+        for (int step = NS; step < 2 * NS; step++) one_step(step);
+        if constexpr (MASKED) {
 #pragma unroll
             for (int rt = 0; rt < kRT; rt++) mask_tile(s1[rt], 1, valid, causal[rt], ln >> 5);
         }
-        // 3: output over keys 0-31 (after any rescale the softmax of keys 0-31 asked for), the
-        // softmax of keys 32-63 beside
-        rescale_o<F::DT>(o, st0.alpha);
-        output_tile<D>(o, wd0, 0, vcur + lv, [&](int step) {
+        rescale_o<F::DT>(o, st0.alpha);  // any move the softmax of keys 0-31 made
+        p_operands(pb, wd0);
 #pragma unroll
-            for (int u = step * kSmUnits / (2 * F::DT); u < (step + 1) * kSmUnits / (2 * F::DT); u++)
-                sm_unit(u, s1, st1, m_ref, l, wd1, a.scale_log2);
-        });
-        // 4: output over keys 32-63
-        rescale_o<F::DT>(o, st1.alpha);
-        output_tile<D>(o, wd1, 1, vcur + lv, [&](int) {});
-    }
+        for (int step = 2 * NS; step < 3 * NS; step++) one_step(step);
+        rescale_o<F::DT>(o, st1.alpha);  // any move the softmax of keys 32-63 made
+        p_operands(pb, wd1);
+#pragma unroll
+        for (int step = 3 * NS; step < 4 * NS; step++) one_step(step);
+    };
+    const int t_split = tm < nt ? tm : nt;
+    int t = 0;
+    for (; t < t_split; t++) page(t, std::false_type{});
+    for (; t < nt; t++) page(t, std::true_type{});
     wait_vm_all();  // the last copies land before the workgroup's LDS is released
     mfma_drain();
 

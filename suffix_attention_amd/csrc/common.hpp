@@ -84,13 +84,19 @@ inline int pad_grid(int n) { return (n + kXcds - 1) / kXcds * kXcds; }
 // ----------------------------------------------------------------------------------------
 constexpr int kRawBufferWord3 = 0x00020000;  // 32-bit data format, no swizzle, no index
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void dma16(const void* base, uint32_t bytes, uint32_t off, uint32_t lds_wave_base) {
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
     const uint64_t b = (uint64_t)base;
-    const i32x4 rsrc = {__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)b),
-                        __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(b >> 32) & 0xffff),  // stride 0
-                        __builtin_amdgcn_readfirstlane((int32_t)bytes), kRawBufferWord3};
+    return i32x4{__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)b),
+                 __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(b >> 32) & 0xffff),  // stride 0
+                 __builtin_amdgcn_readfirstlane((int32_t)bytes), kRawBufferWord3};
+}
+// The same copy through a buffer resource built once (buffer_rsrc) for several copies.
+__device__ __forceinline__ void dma16r(const i32x4& rsrc, uint32_t off, uint32_t lds_wave_base) {
     asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc),
                  "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base)));
+}
+__device__ __forceinline__ void dma16(const void* base, uint32_t bytes, uint32_t off, uint32_t lds_wave_base) {
+    dma16r(buffer_rsrc(base, bytes), off, lds_wave_base);
 }
 
 // LDS byte address of a __shared__ object (folds to a constant for the kernel's own arrays).
