@@ -133,9 +133,9 @@ struct DkvState {
 // Phase 1 of a row tile: S = Q K^T and dP = dO V^T for 32 rows x 32 keys (element i is row
 // 8(i/4) + 4h + i%4 of the tile, key lane%32).  Q and dO fragments are read PD k-steps ahead;
 // sk is the stage's LDS address plus the lane's natural-read offset.
-template <int D, typename Copy>
+template <int D, typename Copy, typename Tail>
 __device__ __forceinline__ void tile_scores(const DkvState<D>& st, uint32_t sk, f32x16& s, f32x16& dp,
-                                            Copy&& copy_step) {
+                                            Copy&& copy_step, Tail&& tail_read) {
     using F = TileShape<D>;
     s = f32x16{};
     dp = f32x16{};
@@ -158,6 +158,7 @@ __device__ __forceinline__ void tile_scores(const DkvState<D>& st, uint32_t sk, 
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, st.kb[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, st.vb[ks], dp, 0, 0, 0);
         copy_step(ks);  // this step's share of a later tile's copies, beside the matrix work
+        tail_read(ks);  // the last steps, which read nothing of their own: phase 3's first reads
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -200,10 +201,26 @@ __device__ __forceinline__ f32x4 unit_lsd(int unit, uint32_t lsd_h) {
 // steps so that its vector work runs while the matrix core is busy.  Step st = (u, dt), dt
 // fastest; fragments read PT steps ahead.  sv is the stage's LDS address plus the lane's
 // transposed-read offset.
+constexpr int kPT = 2;  // phase-3 fragment reads in flight (steps ahead)
+
+// Fragment st of phase 3 (dO^T and Q^T of key step u = st / DT, d tile st % DT): four
+// transposing reads.  sv is the stage's LDS address plus the lane's transposed-read offset.
+template <int D>
+__device__ __forceinline__ void read_accumulate_frag(uint32_t sv, int st_, i16x4* f) {
+    const int dt = st_ % TileShape<D>::DT, u = st_ / TileShape<D>::DT;
+    const int R = 16 * u;
+    const uint32_t a0 = (sv ^ tr_x<D>(dt, R)) + R * 2 * D;
+    const uint32_t a1 = (sv ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D;
+    f[0] = lds_tr4(a0 + RowStage<D>::QBYTES);
+    f[1] = lds_tr4(a1 + RowStage<D>::QBYTES);
+    f[2] = lds_tr4(a0);
+    f[3] = lds_tr4(a1);
+}
+
 template <bool MASK, int D>
 __device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur, uint32_t sv, const f32x16& s_n,
                                                 const f32x16& dp_n, uint32_t lsd_n, int rmh_n, float scale_log2,
-                                                Prob& nxt) {
+                                                Prob& nxt, i16x4 (&fr)[kPT][4]) {
     using F = TileShape<D>;
     bf16x8 pa[2], sa[2];
 #pragma unroll
@@ -212,25 +229,14 @@ __device__ __forceinline__ void tile_accumulate(DkvState<D>& st, const Prob& cur
         sa[u] = __builtin_bit_cast(bf16x8, (u32x4{cur.wd[u][0], cur.wd[u][1], cur.wd[u][2], cur.wd[u][3]}));
     }
     constexpr int NST = 2 * F::DT;
-    constexpr int PT = 2;
+    constexpr int PT = kPT;
     constexpr int NU = 8;  // phase-2 units of the next tile
-    i16x4 fr[PT][4];
-    auto read_t = [&](int st_, i16x4* f) {
-        const int dt = st_ % F::DT, u = st_ / F::DT;
-        const int R = 16 * u;
-        const uint32_t a0 = (sv ^ tr_x<D>(dt, R)) + R * 2 * D;
-        const uint32_t a1 = (sv ^ tr_x<D>(dt, R + 8)) + (R + 8) * 2 * D;
-        f[0] = lds_tr4(a0 + RowStage<D>::QBYTES);
-        f[1] = lds_tr4(a1 + RowStage<D>::QBYTES);
-        f[2] = lds_tr4(a0);
-        f[3] = lds_tr4(a1);
-    };
+    // fragments 0 .. PT-1 were read at the end of phase 1 (fr)
+    auto read_t = [&](int st_, i16x4* f) { read_accumulate_frag<D>(sv, st_, f); };
     // each unit's (LSE, delta) pair is read one unit ahead: a read issued just before its use
     // would make the wait for it (LDS returns in order) drain the prefetched operand reads too
     f32x4 lb[2];
     lb[0] = unit_lsd(0, lsd_n);
-#pragma unroll
-    for (int j = 0; j < PT; j++) read_t(j, fr[j]);
 #pragma unroll
     for (int st_ = 0; st_ < NST; st_++) {
         const int dt = st_ % F::DT, u = st_ / F::DT;
@@ -271,9 +277,16 @@ __device__ __forceinline__ void dkdv_step(DkvState<D>& st, uint32_t stage_t, uin
     uint32_t lk = la.k, lv = la.v;
     asm volatile("" : "+v"(lk), "+v"(lv));
     f32x16 s_n, dp_n;
-    tile_scores<D>(st, stage_n + lk, s_n, dp_n, copy_step);
-    tile_accumulate<MASK, D>(st, cur, stage_t + lv, s_n, dp_n, stage_n + 2 * RowStage<D>::QBYTES + (lane >> 5) * 32, rmh_n,
-                       scale_log2, nxt);
+    // phase 3's first fragments (tile t, whose stage has landed) are read in phase 1's last
+    // steps, so that phase 3 does not start by waiting for them
+    i16x4 fr[kPT][4];
+    const uint32_t sv = stage_t + lv;
+    tile_scores<D>(st, stage_n + lk, s_n, dp_n, copy_step, [&](int ks) {
+        const int j = ks - (TileShape<D>::KS - kPT);
+        if (j >= 0) read_accumulate_frag<D>(sv, j, fr[j]);
+    });
+    tile_accumulate<MASK, D>(st, cur, sv, s_n, dp_n, stage_n + 2 * RowStage<D>::QBYTES + (lane >> 5) * 32, rmh_n,
+                             scale_log2, nxt, fr);
 }
 
 // One workgroup: 4 waves over two consecutive 64-key pages (wave w: page w/2, keys
@@ -379,7 +392,7 @@ void dkdv_mfma_kernel(AttnArgs a, GroupRows gr, int n_pp, int pair0, int n_pairs
         Prob cur;
         {
             f32x16 s0, dp0;
-            tile_scores<D>(st, stg0 + la.k, s0, dp0, [](int) {});
+            tile_scores<D>(st, stg0 + la.k, s0, dp0, [](int) {}, [](int) {});
             const int rmh0 = rmh_of(0);
             const uint32_t lsd0 = stg0 + 2 * RowStage<D>::QBYTES + h * 32;
 #pragma unroll
