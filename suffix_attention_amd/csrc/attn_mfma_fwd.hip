@@ -39,10 +39,10 @@ namespace ls {
 namespace {
 
 constexpr float kLazyLog2 = 8.f;
-constexpr int kW = 4;               // waves per workgroup, one per SIMD
-constexpr int kRT = 2;              // 32-row tiles per wave
-constexpr int kBM = 32 * kRT * kW;  // query rows per workgroup
-static_assert(kBM == kFwdTileRows, "the host's sub-part split assumes this tile");
+constexpr int kW = 4;  // waves per workgroup, one per SIMD
+// RT (template parameter below) is the number of 32-row tiles per wave: 2 (256 rows per
+// workgroup), or 1 (128 rows) for small blocks, which 256-row tiles would mostly pad
+// (fwd_tile_rows, shared with the host's sub-range split).
 
 template <int D>
 struct FwdLds {
@@ -80,24 +80,26 @@ __device__ __forceinline__ void mask_tile(f32x16& s, int kt, int valid, int caus
 // its own.
 constexpr int kSmUnits = 17;
 
+template <int RT>
 struct SmState {
-    float mx[kRT], alpha[kRT], m_use[kRT];
+    float mx[RT], alpha[RT], m_use[RT];
 };
 
 // Each unit ends by pinning its results with an empty asm statement: without it, the compiler
 // sinks the exponentials into the block that first uses them (past the rescale branch, into the
 // next phase), where no matrix work hides them.
-__device__ __forceinline__ void sm_unit(int u, const f32x16 (&s)[kRT], SmState& st, float (&m_ref)[kRT],
-                                        float (&l)[kRT], uint32_t (&wd)[kRT][8], float scale_log2) {
+template <int RT>
+__device__ __forceinline__ void sm_unit(int u, const f32x16 (&s)[RT], SmState<RT>& st, float (&m_ref)[RT],
+                                        float (&l)[RT], uint32_t (&wd)[RT][8], float scale_log2) {
     if (u < 8) {
 #pragma unroll
-        for (int rt = 0; rt < kRT; rt++) {
+        for (int rt = 0; rt < RT; rt++) {
             st.mx[rt] = max3f(st.mx[rt], s[rt][2 * u], s[rt][2 * u + 1]);
             asm volatile("" : "+v"(st.mx[rt]));
         }
     } else if (u == 8) {
 #pragma unroll
-        for (int rt = 0; rt < kRT; rt++) {
+        for (int rt = 0; rt < RT; rt++) {
             // max on raw scores: scale_log2 > 0 commutes with max
             const float mx = __builtin_elementwise_maximum(st.mx[rt], other_half(st.mx[rt])) * scale_log2;
             st.alpha[rt] = 1.f;
@@ -112,7 +114,7 @@ __device__ __forceinline__ void sm_unit(int u, const f32x16 (&s)[kRT], SmState& 
     } else {
         const int j = u - 9;
 #pragma unroll
-        for (int rt = 0; rt < kRT; rt++) {
+        for (int rt = 0; rt < RT; rt++) {
             const float p0 = fast_exp2(__builtin_fmaf(s[rt][2 * j], scale_log2, -st.m_use[rt]));
             const float p1 = fast_exp2(__builtin_fmaf(s[rt][2 * j + 1], scale_log2, -st.m_use[rt]));
             wd[rt][j] = pack_bf16x2(p0, p1);
@@ -124,15 +126,16 @@ __device__ __forceinline__ void sm_unit(int u, const f32x16 (&s)[kRT], SmState& 
 // The row sums of one page: l = (l alpha0 + sum P0) alpha1 + sum P1, in the order the
 // reference moved, from the bf16 words the products used (v_dot2c_f32_bf16 against (1, 1), one
 // instruction per pair), so the weights O is normalised by are exactly those it summed.
-__device__ __forceinline__ void row_sums(float (&l)[kRT], const uint32_t (&wd0)[kRT][8], const uint32_t (&wd1)[kRT][8],
-                                         const SmState& st0, const SmState& st1, int step, int n_steps) {
+template <int RT>
+__device__ __forceinline__ void row_sums(float (&l)[RT], const uint32_t (&wd0)[RT][8], const uint32_t (&wd1)[RT][8],
+                                         const SmState<RT>& st0, const SmState<RT>& st1, int step, int n_steps) {
     typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
     const bf16x2v one = {(__bf16)1.f, (__bf16)1.f};
-    // 2 x kRT chains of 8 words, spread over the steps; each chain starts from its scaled l
+    // 2 x RT chains of 8 words, spread over the steps; each chain starts from its scaled l
 #pragma unroll
-    for (int c = step * 4 / n_steps; c < (step + 1) * 4 / n_steps; c++) {
-        const int half = c / kRT, rt = c % kRT;
-        const uint32_t(&wd)[kRT][8] = half ? wd1 : wd0;
+    for (int c = step * 2 * RT / n_steps; c < (step + 1) * 2 * RT / n_steps; c++) {
+        const int half = c / RT, rt = c % RT;
+        const uint32_t(&wd)[RT][8] = half ? wd1 : wd0;
         float acc = l[rt] * (half ? st1.alpha[rt] : st0.alpha[rt]);
 #pragma unroll
         for (int j = 0; j < 8; j++) acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, wd[rt][j]), one, acc, false);
@@ -143,14 +146,17 @@ __device__ __forceinline__ void row_sums(float (&l)[kRT], const uint32_t (&wd0)[
 
 // O *= alpha per row (the lane's row of each row tile), in place in the AGPRs, if any row's
 // reference moved.  The products that used the old reference must have retired first.
-template <int DT>
-__device__ __forceinline__ void rescale_o(f32x16 (&o)[DT][kRT], const float (&alpha)[kRT]) {
-    if (__all(alpha[0] == 1.f && alpha[1] == 1.f)) return;
+template <int DT, int RT>
+__device__ __forceinline__ void rescale_o(f32x16 (&o)[DT][RT], const float (&alpha)[RT]) {
+    bool same = true;
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) same = same && alpha[rt] == 1.f;
+    if (__all(same)) return;
     mfma_drain();
 #pragma unroll
     for (int dt = 0; dt < DT; dt++)
 #pragma unroll
-        for (int rt = 0; rt < kRT; rt++)
+        for (int rt = 0; rt < RT; rt++)
 #pragma unroll
             for (int i = 0; i < 16; i++) o[dt][rt][i] = agpr_scaled(o[dt][rt][i], alpha[rt]);
     agpr_write_gap();
@@ -181,9 +187,10 @@ struct PageFrags {
 };
 
 // P^T operands of one 32-key tile: key steps j = 0, 1 of both row tiles, from the packed words.
-__device__ __forceinline__ void p_operands(bf16x8 (&pb)[kRT][2], const uint32_t (&wd)[kRT][8]) {
+template <int RT>
+__device__ __forceinline__ void p_operands(bf16x8 (&pb)[RT][2], const uint32_t (&wd)[RT][8]) {
 #pragma unroll
-    for (int rt = 0; rt < kRT; rt++)
+    for (int rt = 0; rt < RT; rt++)
 #pragma unroll
         for (int j = 0; j < 2; j++)
             pb[rt][j] =
@@ -193,9 +200,11 @@ __device__ __forceinline__ void p_operands(bf16x8 (&pb)[kRT][2], const uint32_t 
 // Blocks (query tile, part, kv head), dealt to the XCDs as deal_block() orders them; the query
 // tiles of each member (pre-step scoring runs several members at once) are numbered
 // member-major, n_qtiles_m per member.
-template <int D>
+template <int D, int RT>
 __global__ __attribute__((amdgpu_flat_work_group_size(kW * 64, kW * 64), amdgpu_waves_per_eu(1, 1)))
 void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles) {
+    constexpr int kRT = RT;
+    constexpr int kBM = 32 * RT * kW;  // query rows per workgroup
     using F = TileShape<D>;
     using Tiles = KeyTiles<D, kW>;
     constexpr int PW = Tiles::PER_WAVE;
@@ -243,7 +252,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles) {
     // this lane's rows: 32rt + n of the wave's 64; rows past the block (a partial last tile)
     // read a valid row, and their output is never stored
     auto lane_row = [&](int rt) {
-        const int64_t row = r0 + 64 * w + 32 * rt + n;
+        const int64_t row = r0 + 32 * kRT * w + 32 * rt + n;
         return row < rows_total ? row : rows_total - 1;
     };
     bf16x8 qb[kRT][F::KS];
@@ -261,7 +270,12 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles) {
     // would also wait for the page copies, which share the counter but which it does not see.
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
-    float m_ref[kRT] = {-INFINITY, -INFINITY}, l[kRT] = {0.f, 0.f};
+    float m_ref[kRT], l[kRT];
+#pragma unroll
+    for (int rt = 0; rt < kRT; rt++) {
+        m_ref[rt] = -INFINITY;
+        l[rt] = 0.f;
+    }
     f32x16 o[F::DT][kRT];
 #pragma unroll
     for (int dt = 0; dt < F::DT; dt++)
@@ -314,7 +328,9 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles) {
 
         const int valid = kt.valid(t);
         // the row's causal limit relative to the page's first key (response keys; else all)
-        int causal[kRT] = {kPage, kPage};
+        int causal[kRT];
+#pragma unroll
+        for (int rt = 0; rt < kRT; rt++) causal[rt] = kPage;
         // Lane-dependent values are re-formed from an opaque lane id each page rather than held
         // (or spilled) across the loop: every register is taken by Q, S, P and the fragments.
         int ln = __lane_id();
@@ -324,7 +340,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles) {
             d = d < -(1 << 30) ? -(1 << 30) : (d > (1 << 30) ? (1 << 30) : d);
 #pragma unroll
             for (int rt = 0; rt < kRT; rt++) {
-                int64_t row = r0 + 64 * w + 32 * rt + (ln & 31);
+                int64_t row = r0 + 32 * kRT * w + 32 * rt + (ln & 31);
                 row = row < rows_total ? row : rows_total - 1;
                 causal[rt] = (int)d + (int)(row / a.g);
             }
@@ -335,8 +351,9 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles) {
         f32x16 s0[kRT], s1[kRT];
         uint32_t wd0[kRT][8], wd1[kRT][8];
         bf16x8 pb[kRT][2];
-        SmState st0, st1;
-        st0.mx[0] = st0.mx[1] = st1.mx[0] = st1.mx[1] = -INFINITY;
+        SmState<kRT> st0, st1;
+#pragma unroll
+        for (int rt = 0; rt < kRT; rt++) st0.mx[rt] = st1.mx[rt] = -INFINITY;
 #pragma unroll
         for (int rt = 0; rt < kRT; rt++) s0[rt] = s1[rt] = f32x16{};
 
@@ -374,7 +391,8 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles) {
                     sm_unit(u, s0, st0, m_ref, l, wd0, a.scale_log2);
             } else {
                 const int dt = i % F::DT, j = i / F::DT;
-                mfma32_agpr2(o[dt][0], f, pb[0][j], o[dt][1], f, pb[1][j]);
+                if constexpr (kRT == 2) mfma32_agpr2(o[dt][0], f, pb[0][j], o[dt][1], f, pb[1][j]);
+                else mfma32_agpr(o[dt][0], f, pb[0][j]);
                 if (ph == 2) {
 #pragma unroll
                     for (int u = i * kSmUnits / NS; u < (i + 1) * kSmUnits / NS; u++)
@@ -419,7 +437,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles) {
 #pragma unroll
     for (int rt = 0; rt < kRT; rt++) {
         const float l_tot = l[rt] + other_half(l[rt]);
-        const int64_t row = r0 + 64 * w + 32 * rt + n;
+        const int64_t row = r0 + 32 * kRT * w + 32 * rt + n;
         if (row >= rows_total) continue;
         const int64_t orow = ((int64_t)part * a.part_rows + out_row0 + row / a.g) * a.hq + kvh * a.g + row % a.g;
         // l_tot is 0 exactly when the row sees no key of the part (LSE -inf, O 0); a NaN in the
@@ -440,16 +458,23 @@ void fwd_mfma_kernel(AttnArgs a, int n_qtiles_m, int n_qtiles) {
     }
 }
 
-template <int D>
-hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
-    const int64_t n_qtiles_m = (a.n_rows * a.g + kBM - 1) / kBM;
+template <int D, int RT>
+hipError_t launch_rt(const AttnArgs& a, hipStream_t s) {
+    constexpr int BM = 32 * RT * kW;
+    const int64_t n_qtiles_m = (a.n_rows * a.g + BM - 1) / BM;
     const int64_t n_qtiles = n_qtiles_m * a.n_members;
     const int64_t n_blocks = n_qtiles * a.n_parts * a.hkv;
     if (n_blocks == 0) return hipSuccess;
     const int grid = deal_grid(n_qtiles, a.n_shards, a.n_parts, a.hkv);
     KernelTimer kt("fwd_mfma", s);
-    fwd_mfma_kernel<D><<<grid, kW * 64, 0, s>>>(a, (int)n_qtiles_m, (int)n_qtiles);
+    fwd_mfma_kernel<D, RT><<<grid, kW * 64, 0, s>>>(a, (int)n_qtiles_m, (int)n_qtiles);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
+    static_assert(32 * 1 * kW == 128 && 32 * 2 * kW == 256, "fwd_tile_rows names these tiles");
+    return fwd_tile_rows(a.n_rows * a.g) == 128 ? launch_rt<D, 1>(a, s) : launch_rt<D, 2>(a, s);
 }
 
 }  // namespace

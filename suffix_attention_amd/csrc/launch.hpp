@@ -8,7 +8,6 @@ namespace ls {
 
 constexpr int kMaxShards = 64;     // prompt shards a caller may use
 constexpr int kMaxSubParts = 256;  // key ranges a launch may split the prompt into (below)
-constexpr int kFwdTileRows = 256;  // group rows per forward workgroup
 constexpr int kDqsTileRows = 256;  // group rows per workgroup of the stored-dS dQ pass
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -113,8 +112,13 @@ inline int sub_split(int64_t n_qtiles, int n_shards, int hkv, int64_t n_logical_
     if (k > kMaxSubParts / n_shards) k = kMaxSubParts / n_shards;
     return k < 1 ? 1 : (int)k;
 }
+// Group rows per forward workgroup for a block (per member) of `group_rows`: 256 (two 32-row
+// tiles per wave), or 128 (one) for blocks under 512 group rows, which 256-row tiles would
+// mostly pad.
+inline int fwd_tile_rows(int64_t group_rows) { return group_rows < 512 ? 128 : 256; }
 inline int fwd_split(int64_t n_rows, int g, int n_shards, int hkv, int64_t n_logical_pages) {
-    return sub_split((n_rows * g + kFwdTileRows - 1) / kFwdTileRows, n_shards, hkv, n_logical_pages);
+    const int tr = fwd_tile_rows(n_rows * g);
+    return sub_split((n_rows * g + tr - 1) / tr, n_shards, hkv, n_logical_pages);
 }
 inline int dqs_split(int64_t n_rows, int g, int n_shards, int hkv, int64_t n_logical_pages) {
     return sub_split((n_rows * g + kDqsTileRows - 1) / kDqsTileRows, n_shards, hkv, n_logical_pages);
