@@ -1,34 +1,37 @@
 // Split-prefix replay-attention forward on gfx950 bf16 matrix cores: one wave per SIMD, 64
-// query rows per wave.
+// query rows per wave (32 for small blocks).
 //
-// One workgroup handles 256 query rows of one kv head's group against the keys of one part (a
-// prompt shard walked through the page table, or the response keys the rows see) and writes
-// the part's normalised output and LSE, the owner-local statistics that the merge composes
-// into the exact result (LongStraw digest, "Method", Qwen implementation; explainer, "Two
-// incompatible architectures, same transaction").
+// One workgroup handles 256 query rows (128 for blocks under 512 group rows) of one kv head's
+// group against the keys of one part (a prompt shard walked through the page table, or the
+// response keys the rows see) and writes the part's normalised output and LSE, the owner-local
+// statistics that the merge composes into the exact result (LongStraw digest, "Method", Qwen
+// implementation; explainer, "Two incompatible architectures, same transaction").
 //
-// Each of the four waves owns two 32-row tiles and keeps their Q (the B operands of
-// S^T = K Q^T, 2 x D/2 registers) and their O^T accumulators (AGPRs) for the whole part.  Every
-// operand fragment read from LDS therefore feeds two matrix instructions, one per row tile: a
-// K fragment (32 keys x 16 d) both tiles' scores, a V^T fragment (32 d x 16 keys) both tiles'
-// outputs.  P never leaves the registers: keys are permuted inside each 16-key step
+// Each of the four waves owns RT = 2 (or 1) 32-row tiles and keeps their Q (the B operands of
+// S^T = K Q^T, RT x D/4 registers) and their O^T accumulators (AGPRs) for the whole part.
+// With two tiles every operand fragment read from LDS feeds two matrix instructions, one per
+// row tile: a K fragment (32 keys x 16 d) both tiles' scores, a V^T fragment (32 d x 16 keys)
+// both tiles' outputs.  P never leaves the registers: keys are permuted inside each 16-key step
 // identically on both operands of O^T += V^T P^T, so the score accumulators are, once
 // exponentiated and packed, already the B operand.
 //
-// A page (64 keys) runs in four phases of 2 * D/16 matrix instructions:
+// A page (64 keys) runs in four phases of D/16 steps, each step one operand fragment and RT
+// matrix instructions:
 //   1  S^T of keys 0-31                     beside: the copies of the next page
 //   2  S^T of keys 32-63                    beside: the softmax of keys 0-31
 //   3  O^T += V^T P^T over keys 0-31        beside: the softmax of keys 32-63
-//   4  O^T += V^T P^T over keys 32-63
+//   4  O^T += V^T P^T over keys 32-63       beside: the page's row sums
 // so the vector work of each half-page's softmax issues while the matrix core runs the other
-// half's products.  K and V pages are double-buffered in LDS (one barrier per page).
+// half's products.  The fragments are read two steps ahead across the phase boundaries.  K and
+// V pages are double-buffered in LDS (one barrier per page).
 //
 // The softmax keeps one running reference m per row and moves it only when a half-page's
 // maximum exceeds it by more than kLazyLog2 (base 2), so probabilities stay below 2^kLazyLog2
 // and the output is almost never rescaled; when it is, O is scaled in place (in the AGPRs)
 // after the products already taken relative to the old reference, before any taken relative
 // to the new one.  Every term and the sum are relative to the same m, so the result is the
-// same softmax.
+// same softmax.  The row sums add the bf16 words of P that the products use, so the weights O
+// is normalised by are exactly those it summed.
 #include <math.h>
 
 #include <type_traits>

@@ -32,6 +32,15 @@ def test_bf16_gqa6_ragged_blocks():
     check_against_oracle(c, 100, 200)
 
 
+@pytest.mark.parametrize("n", [85, 86])
+def test_bf16_both_sides_of_the_forward_tile_threshold(n):
+    """510 and 516 group rows (GQA 6): the forward runs 128-row workgroups below 512 group rows
+    and 256-row ones from there on, each with a ragged last tile (126 of 128 rows, 4 of 256)."""
+    log(f"case: bf16 P=1000 R=200 hq=24 hkv=4 d=256 S=3 rows [60, {60 + n}) = {6 * n} group rows")
+    c = Case(1000, 200, 24, 4, 256, torch.bfloat16, seed=11, S=3)
+    check_against_oracle(c, 60, n)
+
+
 def test_bf16_uneven_and_empty_shards():
     log("case: bf16 P=1280 (20 pages) bounds [0,0,3,3,11,20]")
     c = Case(1280, 64, 12, 4, 256, torch.bfloat16, seed=4, bounds=[0, 0, 3, 3, 11, 20])
