@@ -274,6 +274,7 @@ def power_phases(prefix, members, cfg, dump: str | None = None) -> dict:
     import ctypes as C
     lib = C.CDLL(MICROBENCH)
     lib.mb_mfma_peak.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_double)]
+    lib.mb_mfma_peak_16x16x32.argtypes = [C.c_int, C.c_int, C.c_int, C.POINTER(C.c_double)]
     lib.mb_hbm.argtypes = [C.c_int, C.c_size_t, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_double)]
     v = C.c_double(0)
     smp = PowerSampler().start()
@@ -299,6 +300,11 @@ def power_phases(prefix, members, cfg, dump: str | None = None) -> dict:
         assert rc == 0, rc
         return {"tflops": round(v.value, 1)}
 
+    def mfma16(blocks):
+        rc = lib.mb_mfma_peak_16x16x32(blocks, 400000 * 256 // blocks, 8, C.byref(v))
+        assert rc == 0, rc
+        return {"tflops": round(v.value, 1)}
+
     def hbm():
         rc = lib.mb_hbm(0, 4 << 30, 1, 8192, 1000, C.byref(v))
         assert rc == 0, rc
@@ -307,6 +313,9 @@ def power_phases(prefix, members, cfg, dump: str | None = None) -> dict:
     phase("idle", lambda: time.sleep(0.5))
     phase("matrix-instruction chains, constant operands", lambda: mfma(0))
     phase("matrix-instruction chains, random operands", lambda: mfma(1))
+    # the smaller matrix instruction on the same data, one and two waves per SIMD
+    phase("16x16x32 chains, random operands, 1 wave per SIMD", lambda: mfma16(256))
+    phase("16x16x32 chains, random operands, 2 waves per SIMD", lambda: mfma16(512))
     phase("HBM read stream", hbm)
     phase("whole steps", lambda: run_steps(prefix, members, cfg, 1) and None)
 

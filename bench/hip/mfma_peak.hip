@@ -6,7 +6,8 @@
 // peak clock; with random operands (sixteen operand registers of random bf16 of magnitude 1/4
 // to 2, rotated so that consecutive instructions see different bits, as real data do) the
 // switching power of the matrix cores alone lowers the clock, and that rate is the realistic
-// ceiling for kernels on N(0, 1)-like data.
+// ceiling for kernels on N(0, 1)-like data.  A second kernel runs the same on the 16x16x32
+// instruction, to compare the two shapes' rate and power on random data.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -14,6 +15,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kChains = 4;  // independent accumulators per wave: enough to keep the pipe full
 
@@ -70,6 +72,44 @@ __global__ __launch_bounds__(256) void mfma_chain_kernel(int iters, float* __res
         for (int i = 0; i < 16; i++) s += acc[c][i];
     if (s == 123456.789f) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;  // keeps the chains live
 }
+// The same on v_mfma_f32_16x16x32_bf16 (half the flops per instruction, a quarter of the
+// accumulator), random operands only: twice the instructions per iteration, so an iteration is
+// the same 2^19 flops per wave, over eight independent accumulators.  For the choice of shape:
+// the larger one does more work per unit of energy on such data.
+__global__ __launch_bounds__(256) void mfma16_chain_kernel(int iters, float* __restrict__ sink) {
+    const int lane = threadIdx.x & 63;
+    constexpr int NOP = 8;
+    bf16x8 a[NOP], b[NOP];
+#pragma unroll
+    for (int k = 0; k < NOP; k++) {
+        u32x4 ua, ub;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t h1 = mix((uint32_t)(lane * 131 + k * 17 + j + 1) + blockIdx.x * 7919u);
+            const uint32_t h2 = mix(h1 + 99991u);
+            ua[j] = rand_bf16(h1) | (rand_bf16(h1 >> 16) << 16);
+            ub[j] = rand_bf16(h2) | (rand_bf16(h2 >> 16) << 16);
+        }
+        a[k] = __builtin_bit_cast(bf16x8, ua);
+        b[k] = __builtin_bit_cast(bf16x8, ub);
+    }
+    constexpr int kChains16 = 8;
+    f32x4 acc[kChains16];
+#pragma unroll
+    for (int c = 0; c < kChains16; c++) acc[c] = f32x4{};
+    for (int it = 0; it < iters; it++) {
+#pragma unroll
+        for (int k = 0; k < 32; k++)
+            acc[k % kChains16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[k % NOP], b[(k * 3 + (k >> 3)) % NOP],
+                                                                         acc[k % kChains16], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < kChains16; c++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) s += acc[c][i];
+    if (s == 123456.789f) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
 }  // namespace
 
 extern "C" {
@@ -98,6 +138,35 @@ int mb_mfma_peak(int blocks, int iters, int reps, int random_operands, double* t
         float ms = 0.f;
         hipEventElapsedTime(&ms, t0, t1);
         const double flops = 2.0 * 32 * 32 * 16 * 16 * (double)iters * blocks * 4;
+        if (r >= 0 && ms > 0.f) best = flops / (ms * 1e-3) / 1e12 > best ? flops / (ms * 1e-3) / 1e12 : best;
+    }
+    hipEventDestroy(t0);
+    hipEventDestroy(t1);
+    hipFree(sink);
+    *tflops = best;
+    return e == hipSuccess ? 0 : (int)e;
+}
+
+
+// The 16x16x32 chains (random operands) in the same way: `blocks` workgroups of 4 waves for
+// `iters` iterations of 32 instructions (the same flops per iteration as above), `reps` timed
+// launches after a warm-up; best rate in TFLOP/s.  Returns 0, or the HIP error code.
+int mb_mfma_peak_16x16x32(int blocks, int iters, int reps, double* tflops) {
+    float* sink = nullptr;
+    hipError_t e = hipMalloc(&sink, (size_t)blocks * 256 * sizeof(float));
+    if (e != hipSuccess) return (int)e;
+    hipEvent_t t0, t1;
+    hipEventCreate(&t0);
+    hipEventCreate(&t1);
+    double best = 0.0;
+    for (int r = -1; r < reps && e == hipSuccess; r++) {
+        hipEventRecord(t0, nullptr);
+        mfma16_chain_kernel<<<blocks, 256, 0, nullptr>>>(iters, sink);
+        hipEventRecord(t1, nullptr);
+        e = hipEventSynchronize(t1);
+        float ms = 0.f;
+        hipEventElapsedTime(&ms, t0, t1);
+        const double flops = 2.0 * 16 * 16 * 32 * 32 * (double)iters * blocks * 4;
         if (r >= 0 && ms > 0.f) best = flops / (ms * 1e-3) / 1e12 > best ? flops / (ms * 1e-3) / 1e12 : best;
     }
     hipEventDestroy(t0);
