@@ -296,7 +296,9 @@ int ls_score_fwd(const ls_prefix_t* pre, int64_t n_members, const void* q, int64
  *   o               device [n_rows, hq, d] of pre->dtype: the forward's output.
  *   lse             device float32 [n_rows, hq]: the forward's LSE.
  *   dout            device [n_rows, hq, d] of pre->dtype: dL/dO.
- *   dq              device float32 [n_rows, hq, d]: overwritten with dL/dq.
+ *   dq              device float32 [n_rows, hq, d]: overwritten with dL/dq; or NULL, for the
+ *                   gradients of the keys and values only (no dQ pass and no stored dS: the
+ *                   caller formed dQ with ls_replay_fwd_dq).
  *   dk_resp,dv_resp device float32 [n_resp_keys, hkv, d]: gradients of response keys
  *                   [0, q_start + n_rows) are added in (written instead when
  *                   resp_first_touch != 0, in which case keys past that range are set
@@ -321,6 +323,36 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
                   float* dk_resp, float* dv_resp, int resp_first_touch, float* dk_pages,
                   float* dv_pages, const uint8_t* shard_first_touch, void* workspace,
                   size_t ws_bytes, ls_stream_t stream);
+
+/*
+ * ls_replay_fwd_dq -- the forward of one replayed response block and its dQ in one pass over
+ * the keys, for a dL/dO known before the forward (bf16 pages only).  O and LSE are those of
+ * ls_replay_fwd (exact attention; explainer "Two incompatible architectures, same transaction":
+ * the owners' softmax statistics compose into the exact global output), and dQ is that of
+ * ls_replay_bwd for the loss sum(O * dO):
+ *   dQ_i = scale sum_j P_ij (dP_ij - delta_i) K_j,  dP_ij = dO_i . V_j,  delta_i = dO_i . O_i.
+ * delta needs every key, so the pass keeps, relative to the online softmax's reference,
+ * sum p V, sum p dP K, sum p K, sum p and sum p dP per row and part, and forms
+ * dQ = scale (A / l - delta B / l) after the parts are merged.  The keys' and values'
+ * gradients then come from ls_replay_bwd with dq = NULL.  The results agree with
+ * ls_replay_fwd + ls_replay_bwd to rounding, not bit for bit: the products run on the
+ * 16x16x32 instruction, 16 rows per wave.
+ *
+ *   pre, q, n_rows, q_start, k_resp, v_resp, n_resp_keys, o, lse   as for ls_replay_fwd.
+ *   dout            device [n_rows, hq, d] bf16: dL/dO.
+ *   dq              device float32 [n_rows, hq, d]: overwritten with dL/dq.
+ *   workspace       device, ws_bytes >= ls_fwd_dq_workspace_bytes(pre, n_rows); layout
+ *                   (float32, n_parts = n_shards + 1): o_parts, A / l parts, B / l parts
+ *                   [n_parts, n_rows, hq, d] each, then lse_parts and delta parts
+ *                   [n_parts, n_rows, hq] each (delta part = sum p dP / sum p).
+ * The caller owns every buffer; nothing is retained.  Errors: as for ls_replay_fwd, and
+ * LS_ERR_INVALID for a NULL dout or dq, LS_ERR_UNSUPPORTED for float32 pages.
+ */
+size_t ls_fwd_dq_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows);
+int ls_replay_fwd_dq(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start,
+                     const void* k_resp, const void* v_resp, int64_t n_resp_keys, const void* dout,
+                     void* o, float* lse, float* dq, void* workspace, size_t ws_bytes,
+                     ls_stream_t stream);
 
 /*
  * ls_lse_merge -- compose local softmax results into the global one in float32 (digest,

@@ -60,6 +60,9 @@ _SIG = {
     "ls_score_fwd": (_I, [C.POINTER(ls_prefix_t), _I64, _P, _I64, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "ls_replay_bwd": (_I, [C.POINTER(ls_prefix_t), _P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _I,
                            _P, _P, _P, _P, C.c_size_t, _P]),
+    "ls_fwd_dq_workspace_bytes": (C.c_size_t, [C.POINTER(ls_prefix_t), _I64]),
+    "ls_replay_fwd_dq": (_I, [C.POINTER(ls_prefix_t), _P, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P, _P, C.c_size_t,
+                              _P]),
     "ls_lse_merge": (_I, [_I, _I64, _I, _P, _P, _P, _I, _P, _P]),
     "ls_lse_merge_bf16num": (_I, [_I, _I64, _I, _P, _P, _P, _I, _P, _P]),
     "ls_debug_owner_slots": (C.c_size_t, [C.POINTER(ls_prefix_t), _I64, _I64]),

@@ -299,11 +299,13 @@ def score_fwd(prefix: Prefix, q: torch.Tensor, k_resp: torch.Tensor, v_resp: tor
 
 def replay_bwd(prefix: Prefix, q, q_start: int, k_resp, v_resp, o, lse, dout, dk_resp, dv_resp,
                resp_first_touch: bool, dk_pages, dv_pages, shard_first_touch=None,
-               workspace: torch.Tensor | None = None, dq: torch.Tensor | None = None, store_ds: bool = False):
+               workspace: torch.Tensor | None = None, dq: torch.Tensor | None = None, store_ds: bool = False,
+               dq_pass: bool = True):
     """Backward of one block: returns dq (float32); accumulates or writes the response and
     prompt key/value gradients in place.  store_ds (when no workspace is given) allocates the
     larger workspace with which the library forms dQ from a stored dS; a given workspace
-    selects that path by its size alone."""
+    selects that path by its size alone.  dq_pass=False runs the key/value gradients only (dQ
+    formed by replay_fwd_dq) and returns None."""
     _dev(q, "q", dtype=prefix.dtype)
     n_rows = q.shape[0]
     _dev(o, "o", dtype=prefix.dtype, shape=q.shape)
@@ -314,9 +316,13 @@ def replay_bwd(prefix: Prefix, q, q_start: int, k_resp, v_resp, o, lse, dout, dk
     if prefix.prefix_len > 0:
         _dev(dk_pages, "dk_pages", dtype=torch.float32, shape=prefix.k_pages.shape)
         _dev(dv_pages, "dv_pages", dtype=torch.float32, shape=prefix.k_pages.shape)
-    if dq is None:
-        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    _dev(dq, "dq", dtype=torch.float32, shape=q.shape)
+    if not dq_pass:
+        dq = None
+        store_ds = False
+    else:
+        if dq is None:
+            dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        _dev(dq, "dq", dtype=torch.float32, shape=q.shape)
     flags = None
     if shard_first_touch is not None:
         flags = (C.c_uint8 * prefix.n_shards)(*[1 if f else 0 for f in shard_first_touch])
@@ -327,12 +333,47 @@ def replay_bwd(prefix: Prefix, q, q_start: int, k_resp, v_resp, o, lse, dout, dk
     ws = _workspace(ws_bytes, q.device, workspace)
     st = prefix.struct()
     check(lib().ls_replay_bwd(C.byref(st), _ptr(q), n_rows, q_start, _ptr(k_resp), _ptr(v_resp), k_resp.shape[0],
-                              _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk_resp), _ptr(dv_resp),
+                              _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq) if dq is not None else None,
+                              _ptr(dk_resp), _ptr(dv_resp),
                               1 if resp_first_touch else 0, _ptr(dk_pages) if dk_pages is not None else None,
                               _ptr(dv_pages) if dv_pages is not None else None,
                               C.cast(flags, C.c_void_p) if flags is not None else None,
                               _ptr(ws), ws.numel() * ws.element_size(), _stream()))
     return dq
+
+
+def fwd_dq_workspace_bytes(prefix: Prefix, n_rows: int) -> int:
+    st = prefix.struct()
+    n = lib().ls_fwd_dq_workspace_bytes(C.byref(st), n_rows)
+    if n == 0 and n_rows > 0:
+        raise LongStrawError(_lib.LS_ERR_INVALID, lib().ls_last_error().decode())
+    return n
+
+
+def replay_fwd_dq(prefix: Prefix, q: torch.Tensor, q_start: int, k_resp: torch.Tensor, v_resp: torch.Tensor,
+                  dout: torch.Tensor, workspace: torch.Tensor | None = None, o: torch.Tensor | None = None,
+                  lse: torch.Tensor | None = None, dq: torch.Tensor | None = None):
+    """Forward of response rows [q_start, q_start + n_rows) and their dQ for the given dL/dO, in
+    one pass over the keys (ls_replay_fwd_dq, bf16): returns (o, lse, dq, workspace).  The key
+    and value gradients then come from replay_bwd(..., dq_pass=False)."""
+    _dev(q, "q", dtype=prefix.dtype)
+    n_rows = q.shape[0]
+    _dev(k_resp, "k_resp", dtype=prefix.dtype)
+    _dev(v_resp, "v_resp", dtype=prefix.dtype, shape=k_resp.shape)
+    _dev(dout, "dout", dtype=prefix.dtype, shape=q.shape)
+    o = torch.empty_like(q) if o is None else _dev(o, "o", dtype=prefix.dtype, shape=q.shape)
+    if lse is None:
+        lse = torch.empty((n_rows, prefix.hq), dtype=torch.float32, device=q.device)
+    _dev(lse, "lse", dtype=torch.float32, shape=(n_rows, prefix.hq))
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _dev(dq, "dq", dtype=torch.float32, shape=q.shape)
+    ws = _workspace(fwd_dq_workspace_bytes(prefix, n_rows), q.device, workspace)
+    st = prefix.struct()
+    check(lib().ls_replay_fwd_dq(C.byref(st), _ptr(q), n_rows, q_start, _ptr(k_resp), _ptr(v_resp), k_resp.shape[0],
+                                 _ptr(dout), _ptr(o), _ptr(lse), _ptr(dq), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream()))
+    return o, lse, dq, ws
 
 
 def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype: torch.dtype = torch.float32,

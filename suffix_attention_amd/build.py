@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "liblongstraw.so")
 SOURCES = ["abi.cpp", "profile.cpp", "capture.hip", "reduce.hip", "attn_generic.hip", "attn_mfma_fwd.hip",
-           "attn_mfma_bwd.hip", "attn_mfma_dq.hip", "attn_mfma_dqs.hip", "noalloc.hip"]
+           "attn_mfma_bwd.hip", "attn_mfma_dq.hip", "attn_mfma_dqs.hip", "attn_mfma_fwd_dq.hip", "noalloc.hip"]
 
 ROOT = os.path.dirname(HERE)
 BENCH_HIP = os.path.join(ROOT, "bench", "hip")
@@ -46,7 +46,8 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
 PER_SOURCE = {"attn_mfma_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "attn_mfma_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "attn_mfma_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-              "attn_mfma_dqs.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+              "attn_mfma_dqs.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "attn_mfma_fwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src, extra, src_dir=CSRC, obj_dir=BUILD):

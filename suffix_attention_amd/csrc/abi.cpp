@@ -369,6 +369,54 @@ int ls_replay_fwd_noalloc(const ls_prefix_t* pre, const void* q, int64_t n_rows,
     return run_fwd(pre, q, n_rows, q_start, k_resp, v_resp, o, lse, scratch, stream);
 }
 
+// Fused forward + dQ workspace (float32): o, A / l and B / l parts [n_parts, n_rows, hq, d] each,
+// then the LSE and delta parts [n_parts, n_rows, hq] each.
+static size_t fwd_dq_ws(const ls_prefix_t* p, int64_t n_rows) {
+    return sizeof(float) * (size_t)(p->n_shards + 1) * (size_t)n_rows * (size_t)p->hq * (3 * (size_t)p->d + 2);
+}
+
+size_t ls_fwd_dq_workspace_bytes(const ls_prefix_t* pre, int64_t n_rows) {
+    g_err.clear();
+    if (check_prefix(pre) != LS_OK) return 0;
+    if (n_rows < 0) {
+        fail(LS_ERR_INVALID, "n_rows=%lld < 0", (long long)n_rows);
+        return 0;
+    }
+    return fwd_dq_ws(pre, n_rows);
+}
+
+int ls_replay_fwd_dq(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start, const void* k_resp,
+                     const void* v_resp, int64_t n_resp_keys, const void* dout, void* o, float* lse, float* dq,
+                     void* workspace, size_t ws_bytes, ls_stream_t stream) {
+    g_err.clear();
+    bool empty = false;
+    const int rc = check_fwd(pre, q, n_rows, q_start, k_resp, v_resp, n_resp_keys, o, lse, &empty);
+    if (rc != LS_OK || empty) return rc;
+    if (!dout || !dq) return fail(LS_ERR_INVALID, "dout/dq is NULL");
+    if (pre->dtype != LS_DTYPE_BF16) return fail(LS_ERR_UNSUPPORTED, "the fused forward + dQ pass takes bf16 pages only");
+    const size_t need = fwd_dq_ws(pre, n_rows);
+    if (!workspace || ws_bytes < need)
+        return fail(LS_ERR_WORKSPACE, "fused forward + dQ workspace of %zu bytes needed, %zu given", need,
+                    workspace ? ws_bytes : 0);
+    ls::AttnArgs a = make_args(pre, q, n_rows, q_start, k_resp, v_resp);
+    a.dout = dout;
+    const int64_t rows = n_rows * pre->hq;
+    const size_t part_elems = (size_t)a.n_parts * rows * pre->d;
+    a.o_parts = (float*)workspace;
+    float* a_parts = a.o_parts + part_elems;
+    float* b_parts = a_parts + part_elems;
+    a.lse_parts = b_parts + part_elems;
+    float* delta_parts = a.lse_parts + (size_t)a.n_parts * rows;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = ls::launch_fwd_dq_mfma(a, a_parts, b_parts, delta_parts, s);
+    if (e != hipSuccess) return hip_fail(e, "fused forward + dQ kernel");
+    e = ls::launch_lse_merge(a.n_parts, rows, pre->d, a.o_parts, a.lse_parts, o, pre->dtype, lse, s);
+    if (e != hipSuccess) return hip_fail(e, "LSE merge kernel");
+    e = ls::launch_fwd_dq_merge(a.n_parts, rows, pre->d, a.lse_parts, lse, a_parts, b_parts, delta_parts, a.scale, dq,
+                                s);
+    return e == hipSuccess ? LS_OK : hip_fail(e, "dQ merge kernel");
+}
+
 static int run_fwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t q_start, const void* k_resp,
                    const void* v_resp, void* o, float* lse, void* workspace, ls_stream_t stream) {
     ls::AttnArgs a = make_args(pre, q, n_rows, q_start, k_resp, v_resp);
@@ -447,7 +495,8 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
     if (rc != LS_OK) return rc;
     rc = check_block(pre, q, n_rows, q_start, k_resp, v_resp, n_resp_keys);
     if (rc != LS_OK) return rc;
-    if (n_rows > 0 && (!o || !lse || !dout || !dq)) return fail(LS_ERR_INVALID, "o/lse/dout/dq is NULL");
+    if (n_rows > 0 && (!o || !lse || !dout)) return fail(LS_ERR_INVALID, "o/lse/dout is NULL");
+    const bool skip_dq = dq == nullptr;  // dK/dV only
     if (n_resp_keys > 0 && (!dk_resp || !dv_resp)) return fail(LS_ERR_INVALID, "dk_resp/dv_resp is NULL");
     if (pre->prefix_len > 0 && (!dk_pages || !dv_pages)) return fail(LS_ERR_INVALID, "dk_pages/dv_pages is NULL");
     const size_t need = bwd_ws(pre, n_rows);
@@ -458,6 +507,7 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
     if (g_owner) {
         if (pre->dtype != LS_DTYPE_BF16)
             return fail(LS_ERR_UNSUPPORTED, "one-writer counters cover the bf16 matrix-core kernels only");
+        if (skip_dq) return fail(LS_ERR_UNSUPPORTED, "one-writer counters cover backward calls that form dQ");
         owner_slots = ls::owner_slots(pre->n_phys_pages, pre->hkv, pre->hq, dq_parts_formed(pre, n_rows), n_rows,
                                       a.key_end);
         if (g_owner_slots < (size_t)owner_slots)
@@ -478,6 +528,7 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
     a.dk_resp = dk_resp;
     a.dv_resp = dv_resp;
     a.resp_first_touch = resp_first_touch != 0;
+    a.skip_dq = skip_dq;
     a.first_touch_mask = 0;
     if (shard_first_touch)
         for (int s = 0; s < pre->n_shards; s++)
@@ -498,7 +549,9 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
         const size_t room = ws_bytes > off ? ws_bytes - off : 0;
         const size_t per_head = ds_head_bytes(pre, n_rows, a.key_end, n_all);
         int heads = 0, parts = n_all;
-        if (n_rows > 0 && per_head > 0 && room >= per_head) {
+        if (skip_dq) {
+            // no dQ pass: nothing reads a stored dS
+        } else if (n_rows > 0 && per_head > 0 && room >= per_head) {
             const size_t fit = room / per_head;
             heads = fit < (size_t)pre->hkv ? (int)fit : pre->hkv;
         } else if (n_rows > 0) {
@@ -526,7 +579,9 @@ int ls_replay_bwd(const ls_prefix_t* pre, const void* q, int64_t n_rows, int64_t
         if (e == hipSuccess) e = ls::launch_bwd_generic(a, s);
     }
     if (e != hipSuccess) return hip_fail(e, "backward kernels");
-    if (a.dq_sub_k > 1)
+    if (skip_dq)
+        e = hipSuccess;
+    else if (a.dq_sub_k > 1)
         e = ls::launch_sum_parts(pre->n_shards * a.dq_sub_k + 1, rows * pre->d, a.dq_sub, dq, s);
     else
         e = ls::launch_sum_parts(a.n_parts, rows * pre->d, a.dq_parts, dq, s);

@@ -560,7 +560,7 @@ hipError_t launch_bwd_d(const AttnArgs& a, hipStream_t s) {
         if (nbr > 0) dkdv_mfma_kernel<D, true, false><<<pad_grid(nbr), 256, 0, s>>>(a, gr, n_pp, n_pp, n_rp, nbr);
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.skip_dq) return e;
     // dQ parts recomputed (attn_mfma_dq.hip)
     return launch_dq_mfma(a, gr, s);
 }

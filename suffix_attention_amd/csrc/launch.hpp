@@ -94,6 +94,9 @@ struct AttnArgs {
     // of dq_parts.
     float* dq_sub;
     int dq_sub_k;
+    // The backward stops after dK/dV (the caller formed dQ elsewhere, e.g. in the fused
+    // forward + dQ pass); no stored dS then.
+    bool skip_dq;
 };
 
 // Sub-parts.  The forward and the stored-dS dQ pass run one workgroup per (query tile, part,
@@ -243,6 +246,13 @@ hipError_t launch_bwd_generic(const AttnArgs& a, hipStream_t s);
 
 // attn_mfma_fwd.hip / attn_mfma_bwd.hip: bf16 matrix-core kernels
 hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t s);
+// Fused forward + dQ for a dO known up front (a.dout): writes a.o_parts / a.lse_parts as the
+// forward does, and per part A / l, B / l ([n_parts, n_rows, hq, d]) and delta~ / l
+// ([n_parts, n_rows, hq]); launch_fwd_dq_merge then forms dQ from them and the merged LSE.
+hipError_t launch_fwd_dq_mfma(const AttnArgs& a, float* a_parts, float* b_parts, float* delta_parts, hipStream_t s);
+hipError_t launch_fwd_dq_merge(int n_parts, int64_t n_rows, int d, const float* lse_parts, const float* lse,
+                               const float* a_parts, const float* b_parts, const float* delta_parts, float scale,
+                               float* dq, hipStream_t s);
 hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t s);
 // bytes the matrix-core backward keeps after the dQ parts: (LSE * log2 e, delta) float32 pairs
 // and the bf16 Q and dO rows of every kv head's group, group-major and padded to a multiple of

@@ -299,6 +299,62 @@ void thread_checks() {
     expect(other.empty() && std::strstr(ls_last_error(), "already mapped") != nullptr, "per-thread error message");
 }
 
+// The fused forward + dQ pass: validation, the workspace layout it hands the kernels, and the
+// backward that then forms the key and value gradients only.
+void fused_checks() {
+    Prefix pb(24, 4, 256, LS_DTYPE_BF16, 2000, {0, 5, 19, 32});
+    const int64_t n = 100, rows = n * 24;
+    const size_t ws = ls_fwd_dq_workspace_bytes(&pb.p, n);
+    expect(ws == sizeof(float) * 4 * rows * (3 * 256 + 2), "fused workspace: three d-wide and two scalar parts");
+    auto call = [&](const void* dout, float* dq, size_t bytes) {
+        return ls_replay_fwd_dq(&pb.p, fake(4), n, 44, fake(5), fake(6), 144, dout, fake(7), (float*)fake(8), dq,
+                                fake(9), bytes, nullptr);
+    };
+    stub::last = stub::Record();
+    int rc = call(fake(16), (float*)fake(17), ws);
+    const float* base = (const float*)fake(9);
+    const size_t pe = (size_t)4 * rows * 256;
+    expect(rc == LS_OK && stub::last.calls == 3 && std::string(stub::last.name) == "fwd_dq_merge" &&
+               stub::last.merges == 1 && stub::last.merge_parts[0] == 4,
+           "fused: kernel, LSE merge, dQ merge");
+    expect(stub::last.args.o_parts == base && stub::last.fdq_a == base + pe && stub::last.fdq_b == base + 2 * pe &&
+               stub::last.args.lse_parts == base + 3 * pe && stub::last.fdq_delta == base + 3 * pe + 4 * rows &&
+               stub::last.args.dout == fake(16) && stub::last.args.key_end == 144 && stub::last.args.n_parts == 4,
+           "fused: workspace layout and arguments");
+    expect(stub::last.dqm_parts == 4 && stub::last.dqm_rows == rows && stub::last.dqm_dq == (float*)fake(17) &&
+               stub::last.dqm_lse == (const float*)fake(8) && stub::last.dqm_a == base + pe &&
+               stub::last.dqm_b == base + 2 * pe && stub::last.dqm_lse_parts == base + 3 * pe &&
+               stub::last.dqm_delta == base + 3 * pe + 4 * rows && stub::last.dqm_scale == 0.0625f,
+           "dQ merge: parts, merged LSE, output, scale");
+    stub::last = stub::Record();
+    expect(call(fake(16), (float*)fake(17), ws - 1) == LS_ERR_WORKSPACE && stub::last.calls == 0,
+           "fused: a short workspace is rejected before any launch");
+    expect(call(nullptr, (float*)fake(17), ws) == LS_ERR_INVALID && call(fake(16), nullptr, ws) == LS_ERR_INVALID,
+           "fused: NULL dout or dq is rejected");
+    Prefix pf(4, 1, 64, LS_DTYPE_F32, 4096, {0, 32, 64});
+    expect(ls_replay_fwd_dq(&pf.p, fake(4), 256, 0, fake(5), fake(6), 256, fake(16), fake(7), (float*)fake(8),
+                            (float*)fake(17), fake(9), ls_fwd_dq_workspace_bytes(&pf.p, 256), nullptr) ==
+               LS_ERR_UNSUPPORTED,
+           "fused: float32 pages are unsupported");
+    stub::last = stub::Record();
+    expect(ls_replay_fwd_dq(&pb.p, fake(4), 0, 44, fake(5), fake(6), 144, fake(16), fake(7), (float*)fake(8),
+                            (float*)fake(17), nullptr, 0, nullptr) == LS_OK &&
+               stub::last.calls == 0,
+           "fused: an empty block launches nothing");
+    // the backward without dQ: no stored dS even with room for it, no part sum
+    const size_t ds_ws = ls_bwd_ds_workspace_bytes(&pb.p, n, 144);
+    stub::last = stub::Record();
+    rc = ls_replay_bwd(&pb.p, fake(4), n, 44, fake(5), fake(6), 149, fake(7), (const float*)fake(8), fake(16),
+                       nullptr, (float*)fake(11), (float*)fake(12), 1, (float*)fake(13), (float*)fake(14), nullptr,
+                       fake(15), ds_ws, nullptr);
+    expect(rc == LS_OK && stub::last.bwd.skip_dq && stub::last.bwd.ds == nullptr && stub::last.sum_n == 0,
+           "backward with dq = NULL: key and value gradients only");
+    stub::last = stub::Record();
+    rc = bwd(&pb.p, n, 44, ds_ws);
+    expect(rc == LS_OK && !stub::last.bwd.skip_dq && stub::last.bwd.ds != nullptr && stub::last.sum_n > 0,
+           "backward with dq: the stored-dS dQ pass and its part sum, as before");
+}
+
 }  // namespace
 
 int main() {
@@ -308,6 +364,7 @@ int main() {
     noalloc_checks();
     chunk_plan_checks();
     split_checks();
+    fused_checks();
     thread_checks();
     std::printf("%s: %d failure(s)\n", g_failed ? "FAILED" : "PASSED", g_failed);
     return g_failed ? 1 : 0;

@@ -41,6 +41,26 @@ hipError_t launch_zero(float*, int64_t, hipStream_t) { return note("zero"); }
 hipError_t launch_fwd_generic(const AttnArgs& a, hipStream_t) { return note("fwd_generic", &a); }
 hipError_t launch_bwd_generic(const AttnArgs& a, hipStream_t) { return note("bwd_generic", &a); }
 hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t) { return note("fwd_mfma", &a); }
+hipError_t launch_fwd_dq_mfma(const AttnArgs& a, float* a_parts, float* b_parts, float* delta_parts, hipStream_t) {
+    stub::last.fdq_a = a_parts;
+    stub::last.fdq_b = b_parts;
+    stub::last.fdq_delta = delta_parts;
+    return note("fwd_dq_mfma", &a);
+}
+hipError_t launch_fwd_dq_merge(int n_parts, int64_t n_rows, int, const float* lse_parts, const float* lse,
+                               const float* a_parts, const float* b_parts, const float* delta_parts, float scale,
+                               float* dq, hipStream_t) {
+    stub::last.dqm_parts = n_parts;
+    stub::last.dqm_rows = n_rows;
+    stub::last.dqm_lse_parts = lse_parts;
+    stub::last.dqm_lse = lse;
+    stub::last.dqm_a = a_parts;
+    stub::last.dqm_b = b_parts;
+    stub::last.dqm_delta = delta_parts;
+    stub::last.dqm_scale = scale;
+    stub::last.dqm_dq = dq;
+    return note("fwd_dq_merge");
+}
 hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
     stub::last.calls++;
     stub::last.name = "noalloc_scratch";

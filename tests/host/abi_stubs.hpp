@@ -15,6 +15,13 @@ struct Record {
     int merge_parts[8] = {};
     int sum_n = 0;                    // parts and source of the last dQ part sum
     const float* sum_src = nullptr;
+    float *fdq_a = nullptr, *fdq_b = nullptr, *fdq_delta = nullptr;  // fused forward + dQ partials
+    int dqm_parts = 0;                // the dQ merge: parts, rows, inputs, output, scale
+    int64_t dqm_rows = 0;
+    const float *dqm_lse_parts = nullptr, *dqm_lse = nullptr, *dqm_a = nullptr, *dqm_b = nullptr,
+                *dqm_delta = nullptr;
+    float* dqm_dq = nullptr;
+    float dqm_scale = 0.f;
 };
 extern Record last;
 }  // namespace stub

@@ -28,7 +28,7 @@ import pytest
 
 from suffix_attention_amd import build
 
-SOURCES = ["attn_mfma_bwd.hip", "attn_mfma_dq.hip", "attn_mfma_dqs.hip", "attn_mfma_fwd.hip"]
+SOURCES = ["attn_mfma_bwd.hip", "attn_mfma_dq.hip", "attn_mfma_dqs.hip", "attn_mfma_fwd.hip", "attn_mfma_fwd_dq.hip"]
 # wait states from a 16-pass matrix instruction to a vector read or write of its result
 RESULT_WAIT = 18
 
