@@ -43,6 +43,9 @@ def replay_metric(cfg) -> str:
     if cfg == configs.CONFIGS["c2m"]:
         return METRIC
     return f"replay-attention fwd+bwd TFLOP/s and % bf16 MFMA peak at P={cfg.P}, G={cfg.G}, B={cfg.B}, S={cfg.S}"
+# --workload fused: the same step with the fused forward + dQ pass (dO known before the forward)
+FUSED_METRIC = ("replay-attention fwd+bwd TFLOP/s and % bf16 MFMA peak with the fused forward + dQ pass "
+                "(dO known before the forward) at P={P}, G={G}, B={B}, S={S}")
 # --workload score: the pre-step scoring pass (forward only, all G members batched)
 SCORE_METRIC = "pre-step scoring (forward-only, G members batched) TFLOP/s and % bf16 MFMA peak at P=2M, G=8"
 # --workload prefill: capture-side prefill (the prompt's causal attention, chunked, pages written)
@@ -57,7 +60,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 
 # Algorithmic matrix work per visible (row, key) pair and query head, in units of 2*d flops
 # (one multiply-add GEMM over the head dimension), for each kernel that does it.
-KERNEL_UNITS = {"fwd_mfma": 2, "dkdv_mfma": 4, "dq_mfma": 3, "dqs_mfma": 1}
+KERNEL_UNITS = {"fwd_mfma": 2, "dkdv_mfma": 4, "dq_mfma": 3, "dqs_mfma": 1, "fwd_dq_mfma": 5}
 
 # Measured HBM traffic of the dominant kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch,
 # scaled by the same counters on a copy of known size), written by --ingest-counters.  It is
@@ -379,6 +382,9 @@ STORE_DS = None
 DS_BUDGET = None
 
 
+FUSED = False  # --workload fused: every group runs the fused forward + dQ pass
+
+
 def run_steps(prefix, members, cfg, n, cycle_log=None, store_ds="default"):
     """n optimizer cycles: each a fresh group (gradient pages allocated at its first backward,
     released at its end) replaying every member, every member's peak device memory recorded.
@@ -391,7 +397,7 @@ def run_steps(prefix, members, cfg, n, cycle_log=None, store_ds="default"):
         if cycle_log is not None:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-        grp = driver.GroupReplay(prefix, store_ds=store_ds, ds_budget=DS_BUDGET, track_peak=True)
+        grp = driver.GroupReplay(prefix, store_ds=store_ds, ds_budget=DS_BUDGET, track_peak=True, fused=FUSED)
         results = [grp.replay_member(m["q"], m["kr"], m["vr"], m["do"], cfg.B, keep="none") for m in members]
         last = (grp, results)
         if cycle_log is not None:
@@ -641,11 +647,13 @@ def main():
     ap.add_argument("--B", type=int, default=None, help="override the response block size")
     ap.add_argument("--S", type=int, default=None, help="override the number of prompt shards")
     ap.add_argument("--sweep-B", default="16,64,256", help="block sizes of --workload blocksweep")
-    ap.add_argument("--workload", default="replay", choices=["replay", "score", "prefill", "reuse", "blocksweep"],
+    ap.add_argument("--workload", default="replay", choices=["replay", "score", "prefill", "reuse", "blocksweep",
+                                                             "fused"],
                     help="replay: the fwd+bwd step (the headline); score: batched forward-only scoring; "
                          "prefill: chunked capture-side prefill; reuse: consecutive G=8 cycles on one capture "
                          "at P=4,456,448 (--steps cycles, per-cycle times and peaks); blocksweep: member 0 at "
-                         "the block sizes of --sweep-B, algorithmic HBM GB/s")
+                         "the block sizes of --sweep-B, algorithmic HBM GB/s; fused: the replay step with the "
+                         "fused forward + dQ pass (dO known before the forward) and a backward without dQ")
     ap.add_argument("--prefill-tokens", type=int, default=524288)
     ap.add_argument("--prefill-chunk", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -691,8 +699,9 @@ def main():
         cfg = cfg.with_(B=ns.B)
     if ns.S:
         cfg = cfg.with_(S=ns.S)
-    global STORE_DS, DS_BUDGET
+    global STORE_DS, DS_BUDGET, FUSED
     STORE_DS = {"auto": None, "on": True, "off": False}[ns.store_ds]
+    FUSED = ns.workload == "fused"
     DS_BUDGET = None if ns.ds_budget_gb is None else int(ns.ds_budget_gb * 1e9)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -800,6 +809,9 @@ def main():
         out["pct_random_operand_mfma_ceiling"] = round(100 * tflops / rnd, 2)
         out["roofline"]["random_operand_peak"] = rnd
         out["roofline"]["frac_random_operand_peak"] = round(achieved / rnd, 4)
+    if FUSED:
+        out["metric"] = FUSED_METRIC.format(P=cfg.P, G=cfg.G, B=cfg.B, S=cfg.S)
+        out["backward"]["form"] = "fused forward + dQ pass, then the recomputing dK/dV pass without dQ"
     if cycles is not None:
         out["metric"] = REUSE_METRIC
         out["config"]["workload"] = (f"{cfg.name}: {ns.steps} consecutive optimizer cycles over one capture; "
@@ -808,7 +820,7 @@ def main():
         out["cycle_peak_gb"] = [round(c[1] / 1e9, 3) for c in cycles]
     timed_peak, timed_form = grp.peak_bytes, plan.describe(prefix)
     del grp, results  # release the timed group's gradient pages before anything else runs
-    if not ns.no_power and cycles is None:
+    if not ns.no_power and cycles is None and not FUSED:
         t = time.perf_counter()
         try:
             out["power"] = power_phases(prefix, members, cfg, ns.power_dump)
@@ -816,7 +828,7 @@ def main():
             out["power"] = {"error": f"{type(exc).__name__}: {exc}"}
         torch.cuda.synchronize()
         log(f"[bench] power phases {time.perf_counter() - t:.1f} s")
-    if not ns.no_memory_sweep and cycles is None:
+    if not ns.no_memory_sweep and cycles is None and not FUSED:
         t = time.perf_counter()
         out["peak_mem_gb_vs_G"] = memory_vs_g(prefix, members, cfg, timed_peak, timed_form)
         torch.cuda.synchronize()

@@ -73,6 +73,8 @@ class GroupReplay:
     each member's start); peak_bytes is then the largest over the group's members.
     check_owners: a debug run: every backward counts its writers (api.OwnerCounts) and the
     driver raises if a gradient half-page or a dQ part row had two (one host sync per block).
+    fused: each block runs the fused forward + dQ pass (replay_fwd_dq, dO known before the
+    forward) and then the backward without dQ (recomputing, no stored dS; bf16 only).
     Members, blocks and each block's forward and backward are roctx ranges (trace.py)."""
     prefix: api.Prefix
     store_ds: bool | None = None
@@ -85,10 +87,13 @@ class GroupReplay:
     peak_bytes: int = 0
     check_owners: bool = False
     members_done: int = 0
+    fused: bool = False
 
     def __post_init__(self):
         if not self.touched:
             self.touched = [False] * self.prefix.n_shards
+        if self.fused and self.check_owners:
+            raise ValueError("writer counting covers backward calls that form dQ; the fused step forms it earlier")
 
     def _grad_pages(self):
         if self.dk_pages is None and self.prefix.prefix_len > 0:
@@ -107,7 +112,7 @@ class GroupReplay:
     def _choose_plan(self, blocks, dev) -> BwdPlan:
         p = self.prefix
         n_all = p.n_shards + 1
-        if self.store_ds is False or p.dtype != torch.bfloat16:
+        if self.store_ds is False or p.dtype != torch.bfloat16 or self.fused:
             return BwdPlan(0, 0)
         cands = [BwdPlan(p.hkv, n_all)]
         cands += [BwdPlan(h, n_all) for h in range(p.hkv - 1, 0, -1) if p.hkv % h == 0]
@@ -153,11 +158,16 @@ class GroupReplay:
         dv_r = torch.empty(kr.shape, dtype=torch.float32, device=dev)
         blocks = _blocks(R, block)
         rows0 = max((e - a for a, e in blocks), default=0)
-        ws_f = torch.empty((api.fwd_workspace_bytes(p, rows0) + 3) // 4, dtype=torch.float32, device=dev)
+        f_bytes = api.fwd_dq_workspace_bytes(p, rows0) if self.fused else api.fwd_workspace_bytes(p, rows0)
+        ws_f = torch.empty((f_bytes + 3) // 4, dtype=torch.float32, device=dev)
         ws_b = None
         for i, (a, e) in enumerate(blocks):
             with trace_range(f"block [{a}, {e}) forward"):
-                api.replay_fwd(p, q[a:e], a, kr, vr, workspace=ws_f, o=o[a:e], lse=lse[a:e])
+                if self.fused:
+                    api.replay_fwd_dq(p, q[a:e], a, kr, vr, do[a:e], workspace=ws_f, o=o[a:e], lse=lse[a:e],
+                                      dq=dq[a:e])
+                else:
+                    api.replay_fwd(p, q[a:e], a, kr, vr, workspace=ws_f, o=o[a:e], lse=lse[a:e])
             if ws_b is None:
                 # the first backward: gradient pages (once per group), the plan (once per group),
                 # and this member's workspace, sized for the largest of its blocks
@@ -170,9 +180,10 @@ class GroupReplay:
             nbytes = self._ws_bytes(self.plan, e - a, e)
             first = [not t for t in self.touched]
             with trace_range(f"block [{a}, {e}) backward"):
+                kw = dict(shard_first_touch=first, workspace=ws_b[:(max(4, nbytes) + 3) // 4])
+                kw.update(dq_pass=False) if self.fused else kw.update(dq=dq[a:e])
                 self._backward((p, q[a:e], a, kr, vr, o[a:e], lse[a:e], do[a:e], dk_r, dv_r, i == 0, dk_p, dv_p),
-                               dict(shard_first_touch=first, workspace=ws_b[:(max(4, nbytes) + 3) // 4], dq=dq[a:e]),
-                               e - a, e, dev, f"member {self.members_done} block [{a}, {e})")
+                               kw, e - a, e, dev, f"member {self.members_done} block [{a}, {e})")
             self.touched = [True] * p.n_shards
             if on_block is not None:
                 on_block((a, e))
@@ -191,12 +202,12 @@ class GroupReplay:
 def replay_group(prefix: api.Prefix, members: Iterable, block: int, keep: str = "all",
                  on_member: Callable | None = None, store_ds: bool | None = None,
                  ds_budget: int | None = None, track_peak: bool = False,
-                 check_owners: bool = False) -> tuple[GroupReplay, list[MemberResult]]:
+                 check_owners: bool = False, fused: bool = False) -> tuple[GroupReplay, list[MemberResult]]:
     """Replay every member serially.  `members` yields dicts with q, kr, vr, do (device
     tensors), or callables returning one, so inputs can be produced one member at a time.
-    store_ds, ds_budget, track_peak and check_owners as for GroupReplay."""
+    store_ds, ds_budget, track_peak, check_owners and fused as for GroupReplay."""
     grp = GroupReplay(prefix, store_ds=store_ds, ds_budget=ds_budget, track_peak=track_peak,
-                      check_owners=check_owners)
+                      check_owners=check_owners, fused=fused)
     results = []
     for i, m in enumerate(members):
         inp = m() if callable(m) else m

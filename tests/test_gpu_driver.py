@@ -106,11 +106,14 @@ def _budget(pre, heads, parts):
 
 @pytest.mark.parametrize("form", ["stored dS, 1 kv head", "stored dS, 1 kv head x 2 key parts",
                                   "stored dS, all", "recompute",
-                                  "stored dS, 1 kv head x 2 key parts, writers counted"])
+                                  "stored dS, 1 kv head x 2 key parts, writers counted",
+                                  "fused forward + dQ"])
 def test_group_replay_matches_oracle(group_case, form):
     """The writers-counted form runs every backward with the one-writer counters registered
     (the driver raises if any gradient half-page or dQ part row gets two writers) and must
-    still match the oracle."""
+    still match the oracle.  The fused form forms dQ in the forward (ls_replay_fwd_dq) from the
+    unrounded O; against the oracle's dQ from the bf16-rounded O it stays within the same
+    bounds."""
     c = group_case
     pre = c["pre"]
     kw, plan = {
@@ -120,6 +123,7 @@ def test_group_replay_matches_oracle(group_case, form):
         "recompute": (dict(store_ds=False), driver.BwdPlan(0, 0)),
         "stored dS, 1 kv head x 2 key parts, writers counted": (
             dict(ds_budget=_budget(pre, 1, 2), check_owners=True), driver.BwdPlan(1, 2)),
+        "fused forward + dQ": (dict(fused=True), driver.BwdPlan(0, 0)),
     }[form]
     log(f"case: group of {G} members P={P} S=3 {BOUNDS} R={R} B={B} ({form})")
     _poison_allocator()
