@@ -36,6 +36,7 @@ constexpr int kFW = 4;               // waves per workgroup, one per SIMD
 constexpr int kFRows = 16;           // query rows per wave
 constexpr int kFBM = kFW * kFRows;   // query rows per workgroup
 constexpr float kFLazyLog2 = 8.f;    // the reference moves when a page's maximum exceeds it by this
+constexpr int kPF = 3;               // operand fragments read this many steps ahead
 
 template <int D>
 struct FdqLds {
@@ -161,8 +162,8 @@ void fwd_dq_mfma_kernel(AttnArgs a, FdqOut out, int n_qtiles) {
         const uint32_t kc = kb0 + (uint32_t)(t & 1) * F::TILE, vc = vb0 + (uint32_t)(t & 1) * F::TILE;
         // Lane bases of the page's reads, formed each page from an opaque lane id rather than
         // held across the loop (every register is taken by the operands and accumulators).  The
-        // swizzle is linear over xor and depends only on a row's low four bits, so a read is
-        // (lane base ^ step constant) + row constant (the constant goes into its immediate):
+        // swizzle (swz16) is linear over xor and depends only on a row's low four bits, so a read
+        // is (lane base ^ step constant) + row constant (the constant goes into its immediate):
         //  natural, rows 16 kb + n16, chunk 4 ks + G:     (nat ^ (ks << 6)) + 32 kb D
         //  transposed, rows 32 js + 4 G + n16 / 4 (+16),
         //  elements 16 dt + 4 (n16 % 4):                  (tr ^ (dt << 5)) + 64 js D (+32 D)
@@ -172,21 +173,46 @@ void fwd_dq_mfma_kernel(AttnArgs a, FdqOut out, int n_qtiles) {
         const uint32_t nat = (uint32_t)ln16 * (2 * D) + ((uint32_t)(lg ^ swz<D>(ln16)) << 4);
         const uint32_t tr = (uint32_t)rq * (2 * D) + ((uint32_t)(((ln16 & 3) >> 1) ^ swz<D>(rq)) << 4) + 8u * (ln16 & 1);
 
-        // S^T and dP^T of the page's four 16-key tiles: element i of tile kb is key 16 kb + 4 G + i
+        // S^T and dP^T of the page's four 16-key tiles: element i of tile kb is key 16 kb + 4 G + i.
+        // Step i = (ks, kb), kb fastest; its K and V fragments are read kPF steps ahead.
+        constexpr int NS1 = 4 * KS;
+        bf16x8 kfb[kPF + 1], vfb[kPF + 1];
+        auto sread = [&](int i) {
+            const uint32_t off = (nat ^ (uint32_t)((i / 4) << 6)) + (uint32_t)(32 * (i % 4) * D);
+            kfb[i % (kPF + 1)] = lds_b128(kc + off);
+            vfb[i % (kPF + 1)] = lds_b128(vc + off);
+        };
+#pragma unroll
+        for (int i = 0; i < kPF; i++) sread(i);
         f32x4 s[4], dp[4];
 #pragma unroll
         for (int kb = 0; kb < 4; kb++) s[kb] = dp[kb] = f32x4{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ks++)
+        for (int i = 0; i < NS1; i++) {
+            if (i + kPF < NS1) sread(i + kPF);
+            const int ks = i / 4, kb = i % 4;
+            s[kb] = mfma16(kfb[i % (kPF + 1)], qf[ks], s[kb]);
+            dp[kb] = mfma16(vfb[i % (kPF + 1)], df[ks], dp[kb]);
+            // the step's reads and products stay in place: hoisting every step's reads would need
+            // more registers than the accumulators leave
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // The accumulate phase's fragments: step i = (js, dt), dt fastest, four transposing reads
+        // each (V^T and K^T, low and high rows); the first kPF are issued here so that the softmax
+        // below runs while they are in flight.
+        constexpr int NS2 = 2 * DT;
+        i16x4 fr[kPF + 1][4];
+        auto aread = [&](int i) {
+            const uint32_t olo = (tr ^ (uint32_t)((i % DT) << 5)) + (uint32_t)(64 * (i / DT) * D), ohi = olo + 32 * D;
+            i16x4(&f)[4] = fr[i % (kPF + 1)];
+            f[0] = lds_tr4(vc + olo);
+            f[1] = lds_tr4(vc + ohi);
+            f[2] = lds_tr4(kc + olo);
+            f[3] = lds_tr4(kc + ohi);
+        };
 #pragma unroll
-            for (int kb = 0; kb < 4; kb++) {
-                const uint32_t off = (nat ^ (uint32_t)(ks << 6)) + (uint32_t)(32 * kb * D);
-                s[kb] = mfma16(lds_b128(kc + off), qf[ks], s[kb]);
-                dp[kb] = mfma16(lds_b128(vc + off), df[ks], dp[kb]);
-                // one step's operands at a time: hoisting every step's reads would need more
-                // registers than the accumulators leave
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int i = 0; i < kPF; i++) aread(i);
 
         // keys past the part's end or past the row's causal limit
         const int valid = kt.valid(t);
@@ -263,19 +289,16 @@ void fwd_dq_mfma_kernel(AttnArgs a, FdqOut out, int n_qtiles) {
         // of the step and elements 16 dt + 4 (n16 % 4) .. + 4, and receives d = 16 dt + n16 of the
         // group's four rows.
 #pragma unroll
-        for (int js = 0; js < 2; js++) {
-#pragma unroll
-            for (int dt = 0; dt < DT; dt++) {
-                const uint32_t olo = (tr ^ (uint32_t)(dt << 5)) + (uint32_t)(64 * js * D), ohi = olo + 32 * D;
-                const bf16x8 vt = __builtin_bit_cast(
-                    bf16x8, __builtin_shufflevector(lds_tr4(vc + olo), lds_tr4(vc + ohi), 0, 1, 2, 3, 4, 5, 6, 7));
-                const bf16x8 kt8 = __builtin_bit_cast(
-                    bf16x8, __builtin_shufflevector(lds_tr4(kc + olo), lds_tr4(kc + ohi), 0, 1, 2, 3, 4, 5, 6, 7));
-                mfma16_agpr(oc[dt], vt, pb[js]);
-                mfma16_agpr(ac[dt], kt8, pdb[js]);
-                mfma16_agpr(bc[dt], kt8, pb[js]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int i = 0; i < NS2; i++) {
+            if (i + kPF < NS2) aread(i + kPF);
+            const int js = i / DT, dt = i % DT;
+            const i16x4(&f)[4] = fr[i % (kPF + 1)];
+            const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(f[0], f[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            const bf16x8 kt8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(f[2], f[3], 0, 1, 2, 3, 4, 5, 6, 7));
+            mfma16_agpr(oc[dt], vt, pb[js]);
+            mfma16_agpr(ac[dt], kt8, pdb[js]);
+            mfma16_agpr(bc[dt], kt8, pb[js]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     wait_vm_all();  // the last copies land before the workgroup's LDS is released
