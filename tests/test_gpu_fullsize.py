@@ -30,12 +30,16 @@ def _prefix(cfg, kp, vp, table):
                       api.even_shard_bounds(cfg.n_pages, cfg.S))
 
 
-def _block(pre, m, q_start, n, store_ds=True, parts=None):
+def _block(pre, m, q_start, n, store_ds=True, parts=None, fused=False):
     """One replayed block (forward + first-touch backward) through the C ABI; by default with
     the stored-dS backward that the benchmark runs at the 2M-token size.  parts: run the
-    stored-dS backward one kv head by `parts` consecutive key parts at a time."""
+    stored-dS backward one kv head by `parts` consecutive key parts at a time.  fused: the fused
+    forward + dQ pass, then the backward without dQ (bench.py --workload fused)."""
     q, do = m["q"][q_start:q_start + n].contiguous(), m["do"][q_start:q_start + n].contiguous()
-    o, lse, _ = api.replay_fwd(pre, q, q_start, m["kr"], m["vr"])
+    if fused:
+        o, lse, dq, _ = api.replay_fwd_dq(pre, q, q_start, m["kr"], m["vr"], do)
+    else:
+        o, lse, _ = api.replay_fwd(pre, q, q_start, m["kr"], m["vr"])
     dkr = torch.empty(m["kr"].shape, dtype=torch.float32, device="cuda")
     dvr = torch.empty_like(dkr)
     dkp = torch.empty(pre.k_pages.shape, dtype=torch.float32, device="cuda")
@@ -44,22 +48,25 @@ def _block(pre, m, q_start, n, store_ds=True, parts=None):
     if parts is not None:
         nbytes = api.bwd_ds_workspace_bytes(pre, n, q_start + n, heads=1, parts=parts)
         ws = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device="cuda")
-    dq = api.replay_bwd(pre, q, q_start, m["kr"], m["vr"], o, lse, do, dkr, dvr, True, dkp, dvp,
-                        shard_first_touch=[True] * pre.n_shards, store_ds=store_ds, workspace=ws)
+    r = api.replay_bwd(pre, q, q_start, m["kr"], m["vr"], o, lse, do, dkr, dvr, True, dkp, dvp,
+                       shard_first_touch=[True] * pre.n_shards, store_ds=store_ds, workspace=ws,
+                       dq_pass=not fused)
+    dq = dq if fused else r
     del ws
     torch.cuda.synchronize()
     return dict(o=o, lse=lse, dq=dq, dkr=dkr, dvr=dvr, dkp=dkp, dvp=dvp, q=q, do=do)
 
 
-def _sampled_rows_and_gradient_sums(cfg, q_start, n, rows, store_ds, parts=None):
+def _sampled_rows_and_gradient_sums(cfg, q_start, n, rows, store_ds, parts=None, fused=False):
     """The block [q_start, q_start + n) of member 0 at the config's full size: sampled rows of
     one kv head against the oracle over every key they see, and the gradient identities over
-    all keys."""
+    all keys.  With the fused pass, dQ's reference takes delta from the exact output (it forms
+    delta = sum P dP from its own unrounded products)."""
     table = datagen.page_table(cfg.n_pages, datagen.seed(cfg.cfg_id, datagen.TAG_PERM), "cuda")
     kp, vp = datagen.prefix_kv(cfg, "cuda")
     pre = _prefix(cfg, kp, vp, table)
     m = datagen.member_inputs(cfg, 0, "cuda")
-    res = _block(pre, m, q_start, n, store_ds=store_ds, parts=parts)
+    res = _block(pre, m, q_start, n, store_ds=store_ds, parts=parts, fused=fused)
     g = cfg.g
     kend = q_start + n
 
@@ -73,7 +80,7 @@ def _sampled_rows_and_gradient_sums(cfg, q_start, n, rows, store_ds, parts=None)
         qr = np32(m["q"][pos:pos + 1, heads])
         dor = np32(m["do"][pos:pos + 1, heads])
         O, L = orc.forward(qr, kp1, vp1, kr1, vr1, pos)
-        gr = orc.backward(qr, kp1, vp1, kr1, vr1, dor, pos, o=orc.round_bf16(O), lse=L,
+        gr = orc.backward(qr, kp1, vp1, kr1, vr1, dor, pos, o=O if fused else orc.round_bf16(O), lse=L,
                           prefix_grad_sink=lambda *a: None)
         log(f"  row {pos}")
         assert_close("O", np32(res["o"][r:r + 1, heads]), O)
@@ -103,6 +110,14 @@ def test_c2m_block_sampled_rows_and_gradient_sums():
     q_start, n = cfg.R - cfg.B, cfg.B
     log(f"case: c2m P={cfg.P} block rows [{q_start}, {q_start + n}) sampled rows + gradient sums")
     _sampled_rows_and_gradient_sums(cfg, q_start, n, (0, 511, n - 1), store_ds=True)
+
+
+def test_c2m_block_fused_pass_sampled_rows_and_gradient_sums():
+    """The same block through the fused forward + dQ pass and the backward without dQ."""
+    cfg = C2M
+    q_start, n = cfg.R - cfg.B, cfg.B
+    log(f"case: c2m P={cfg.P} block rows [{q_start}, {q_start + n}) fused pass: sampled rows + gradient sums")
+    _sampled_rows_and_gradient_sums(cfg, q_start, n, (0, 511, n - 1), store_ds=False, fused=True)
 
 
 def test_c1m_block_sampled_rows_and_gradient_sums():
