@@ -162,8 +162,9 @@ void fwd_dq_mfma_kernel(AttnArgs a, FdqOut out, int n_qtiles) {
         const uint32_t kc = kb0 + (uint32_t)(t & 1) * F::TILE, vc = vb0 + (uint32_t)(t & 1) * F::TILE;
         // Lane bases of the page's reads, formed each page from an opaque lane id rather than
         // held across the loop (every register is taken by the operands and accumulators).  The
-        // swizzle (swz16) is linear over xor and depends only on a row's low four bits, so a read
-        // is (lane base ^ step constant) + row constant (the constant goes into its immediate):
+        // tile swizzle (swz, mfma_tiles.hpp) is linear over xor and depends only on a row's low
+        // four bits, so a read is (lane base ^ step constant) + row constant (the constant goes
+        // into its immediate):
         //  natural, rows 16 kb + n16, chunk 4 ks + G:     (nat ^ (ks << 6)) + 32 kb D
         //  transposed, rows 32 js + 4 G + n16 / 4 (+16),
         //  elements 16 dt + 4 (n16 % 4):                  (tr ^ (dt << 5)) + 64 js D (+32 D)
