@@ -144,6 +144,38 @@ def test_score_workspace_and_validation():
     assert score(m=0, ws=None, ws_bytes=0) == 0  # nothing to score
 
 
+def test_fused_workspace_and_validation():
+    """The fused forward + dQ pass: float32 o, A / l and B / l parts of d elements and the LSE
+    and delta parts, per part and (row, head); a NULL dout or dq, a short workspace and float32
+    pages are rejected before any launch; an empty block does nothing."""
+    p = _prefix()
+    lib = _lib.lib()
+    need = lib.ls_fwd_dq_workspace_bytes(C.byref(p), 16)
+    assert need == 4 * 3 * 16 * 8 * (3 * 256 + 2)
+    assert lib.ls_fwd_dq_workspace_bytes(C.byref(p), -1) == 0 and "n_rows" in _err()
+
+    def fused(p=p, n_rows=16, dout=FAKE, dq=FAKE, ws_bytes=need):
+        return lib.ls_replay_fwd_dq(C.byref(p), FAKE, n_rows, 0, FAKE, FAKE, 16, dout, FAKE, FAKE, dq, FAKE,
+                                    ws_bytes, None)
+    assert fused(dout=None) == LS_ERR_INVALID and "dout" in _err()
+    assert fused(dq=None) == LS_ERR_INVALID
+    assert fused(ws_bytes=need - 1) == LS_ERR_WORKSPACE
+    f = _prefix(dtype=LS_DTYPE_F32)
+    assert fused(p=f, ws_bytes=lib.ls_fwd_dq_workspace_bytes(C.byref(f), 16)) == LS_ERR_UNSUPPORTED
+    assert "bf16" in _err()
+    assert fused(n_rows=0, ws_bytes=0) == 0
+
+
+def test_fused_group_refuses_writer_counting():
+    """The one-writer counters cover backward calls that form dQ; a fused group forms it in
+    the forward, so the driver refuses the combination up front."""
+    import types
+
+    from suffix_attention_amd import driver
+    with pytest.raises(ValueError):
+        driver.GroupReplay(types.SimpleNamespace(n_shards=2), fused=True, check_owners=True)
+
+
 def test_empty_block_is_a_no_op():
     assert _fwd(_prefix(), n_rows=0, n_resp=0, ws=None, ws_bytes=0) == 0
 
