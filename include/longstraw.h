@@ -412,7 +412,8 @@ int ls_lse_merge_bf16num(int n_parts, int64_t n_rows, int d, const float* o_part
  *   caller, which keeps it alive while registered) for this thread's backward calls; NULL
  *   turns the counting off.  A registered ls_replay_bwd call fails with LS_ERR_INVALID if
  *   n_slots is below ls_debug_owner_slots for its block, and with LS_ERR_UNSUPPORTED for
- *   float32 descriptors (the counters cover the bf16 matrix-core kernels).
+ *   float32 descriptors (the counters cover the bf16 matrix-core kernels) and for dq = NULL
+ *   (the dQ part rows are among the counted slots).
  */
 size_t ls_debug_owner_slots(const ls_prefix_t* pre, int64_t n_rows, int64_t key_end);
 int ls_debug_set_owner_counts(uint32_t* counts, size_t n_slots);
